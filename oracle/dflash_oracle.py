@@ -1,0 +1,330 @@
+"""CPU oracle for the DFlash draft block-attention and greedy-verify hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the test-suite, the package smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code with the HIP library
+(no kernels, headers, helpers or tables); both sides consume the same seeded
+inputs from ``block_diffusion_draft_proj_amd.synth``, which draws data and
+computes nothing of the method.
+
+Everything is plain NumPy in float64, slow and literal: each function states
+the definition it writes out and the page passage it follows.  Pages:
+
+* "DFlash dual implementations: PyTorch vs MLX code architecture"
+  (hotelren.com/news/4396892) -- §1 model definition (RoPE reused from Qwen3),
+  §2 attention (dual-source K/V = [ctx ; block], Q from the block only,
+  non-causal inside the block), §3 KV cache (crop to the accepted prefix),
+  §4 target hidden states (select layers by id and concatenate).
+* "dflash-mlx: lossless speculative decoding" (dpshk.com/news/6100553) --
+  "what is lossless" (every emitted token is the target's greedy argmax),
+  "block-diffusion draft" (block = staged token + 15 mask slots; the draft
+  reads target hidden states), "single-forward verify" (the 9-step cycle),
+  guarantee 2 (acceptance = sum of cumprod of draft == posterior, no skipping;
+  the target token at the first rejected slot becomes the next staged token),
+  guarantee 3 (attention KV is cropped to the committed length).
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes): two-stage projection fc -> shared W_k/W_v with the context
+feature C held in bf16; rotate-half RoPE with base 1e6 applied to Q and K
+only; softmax scale d^-1/2; q head h uses kv head floor(h/G); block Q and K are
+rounded to bf16 after RoPE, ctx K/V are bf16 in the cache; argmax takes the
+lowest index among equal maxima, NaN ranks above everything, -0 == +0.
+
+Parity note: the projection/norm/RoPE structure of the real draft model is not
+fixed by the pages; the oracle pins the method *under the readings above*.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+BLOCK = 16
+
+
+# --------------------------------------------------------------------------
+# bf16 encode / decode (own implementation; bf16 = top 16 bits of float32)
+# --------------------------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact decode of bf16 bit patterns (uint16) to float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):      # NaN payloads convert quietly
+        return b.view(np.float32).astype(np.float64)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (ties to even), as float64.
+
+    bf16 keeps 8 significant bits.  Rounding is done once, from float64, by
+    scaling the mantissa to an integer grid and using round-half-even.  Values
+    below the smallest normal bf16 (2^-126) round on the subnormal grid 2^-133;
+    values beyond the largest finite bf16 become +-inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    xf = x[fin]
+    _, e = np.frexp(xf)                    # xf = m * 2^e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)                # below 2^-126 keep the subnormal spacing
+    q = np.ldexp(1.0, (e - 8).astype(np.int64))   # spacing of the 8-bit grid
+    r = np.rint(xf / q) * q                # np.rint rounds half to even
+    big = np.abs(r) > 3.3895313892515355e38  # largest finite bf16
+    r[big] = np.copysign(np.inf, r[big])
+    out[fin] = r
+    return out
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 to bf16 (nearest even) and return the uint16 bit patterns."""
+    r = round_bf16(x).astype(np.float32)   # exact: r is on the bf16 grid
+    bits = (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(np.asarray(x))
+    bits[nan] = 0x7FC0
+    return bits
+
+
+# --------------------------------------------------------------------------
+# RoPE  (page "DFlash dual implementations", §1: the draft reuses the Qwen3
+# rotary embedding).  Reading: rotate-half pairs (j, j + d/2), angle
+# theta_j(pos) = pos * base^(-2j/d), computed in float64.
+# --------------------------------------------------------------------------
+def rope_angles(pos: np.ndarray, head_dim: int, base: float) -> np.ndarray:
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * j / head_dim)
+    return np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
+
+
+def apply_rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Rotate x[..., n, H, d] at positions pos[n] (same position for every head).
+
+    For each pair (x_j, x_{j+d/2}):  (x_j cos - x_{j+d/2} sin,  x_{j+d/2} cos + x_j sin).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    th = rope_angles(pos, d, base)          # [n, d/2]
+    c = np.cos(th)[:, None, :]              # broadcast over heads
+    s = np.sin(th)[:, None, :]
+    lo, hi = x[..., : d // 2], x[..., d // 2:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+# --------------------------------------------------------------------------
+# a1-a3: context feature, projection to K/V, RoPE, cache rows
+# (page "DFlash dual implementations" §4: select target layers by id and
+# concatenate; §2: ctx K/V come from the projected target hidden states;
+# dflash-mlx page "block-diffusion draft": the draft reads target_hidden.)
+# --------------------------------------------------------------------------
+def ctx_proj_ref(x_layers: Sequence[np.ndarray], w_fc: np.ndarray, w_k: np.ndarray,
+                 w_v: np.ndarray, row_pos: np.ndarray, n_kv_heads: int, head_dim: int,
+                 base: float) -> dict:
+    """Context projection of M rows of target hidden states.
+
+    X_cat = [X_1 | ... | X_nt]  (feature concat, in the order given)
+    C     = X_cat W_fc^T, held as bf16 (the draft's context feature)
+    K     = RoPE(C W_k^T, pos),  V = C W_v^T  (per kv head), then bf16 in the cache.
+    Rows with pos < 0 are not committed; their K is returned unrotated.
+    Returns float64 arrays: C (exact), Cb (bf16-rounded), K, V (before the
+    final bf16 rounding) and Kb, Vb (rounded).
+    """
+    X = np.concatenate([bf16_to_f64(x) for x in x_layers], axis=1)
+    C = X @ bf16_to_f64(w_fc).T
+    Cb = round_bf16(C)
+    M = X.shape[0]
+    Kraw = (Cb @ bf16_to_f64(w_k).T).reshape(M, n_kv_heads, head_dim)
+    V = (Cb @ bf16_to_f64(w_v).T).reshape(M, n_kv_heads, head_dim)
+    pos = np.asarray(row_pos, dtype=np.int64)
+    K = Kraw.copy()
+    live = pos >= 0
+    if live.any():
+        K[live] = apply_rope(Kraw[live], pos[live], base)
+    return {"C": C, "Cb": Cb, "K": K, "V": V, "Kb": round_bf16(K), "Vb": round_bf16(V)}
+
+
+# --------------------------------------------------------------------------
+# a4-a6: dual-source non-causal block attention
+# (page "DFlash dual implementations" §2: K/V = [ctx ; block tokens], Q from
+# the block tokens only, non-causal inside the block.)
+# --------------------------------------------------------------------------
+def gather_pages(cache: np.ndarray, page_table: np.ndarray, b: int, length: int) -> np.ndarray:
+    """Dense [Hkv, length, d] view of sequence b from a paged [P, Hkv, ps, d] cache."""
+    ps = cache.shape[2]
+    t = np.arange(length)
+    pages = page_table[b, t // ps]
+    return np.transpose(cache[pages, :, t % ps, :], (1, 0, 2))
+
+
+def block_attn_unit_ref(q_b: np.ndarray, k_b: np.ndarray, v_b: np.ndarray,
+                        k_ctx: np.ndarray, v_ctx: np.ndarray, ctx_len: int, g: int,
+                        group: int, base: float, scale: Optional[float] = None,
+                        return_probs: bool = False):
+    """Attention of one (sequence, kv head g) unit.
+
+    q_b [16, Hq, d], k_b / v_b [16, Hkv, d] bf16 bits (q, k pre-RoPE);
+    k_ctx / v_ctx [>=ctx_len, d] bf16 bits of kv head g (K already rotated).
+    Block positions are ctx_len .. ctx_len+15.  For each q head h of the group:
+      Q_h   = bf16(RoPE(q_h))                        [16, d]
+      Keys  = [K_ctx[0:L] ; bf16(RoPE(k_blk[:, g]))] [L+16, d]
+      Vals  = [V_ctx[0:L] ; v_blk[:, g]]
+      S = Q_h Keys^T * scale,  P = softmax over all L+16 keys (no mask),  O = P Vals.
+    Returns O [16, group, d] float64 (and P [group, 16, L+16] if asked).
+    """
+    d = q_b.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    L = int(ctx_len)
+    pos = L + np.arange(BLOCK)
+    hs = slice(g * group, (g + 1) * group)
+    Q = round_bf16(apply_rope(bf16_to_f64(q_b[:, hs, :]), pos, base))          # [16, G, d]
+    Kblk = round_bf16(apply_rope(bf16_to_f64(k_b[:, g:g + 1, :]), pos, base))[:, 0, :]
+    Keys = np.concatenate([bf16_to_f64(k_ctx[:L]), Kblk], axis=0)
+    Vals = np.concatenate([bf16_to_f64(v_ctx[:L]), bf16_to_f64(v_b[:, g, :])], axis=0)
+    out = np.empty((BLOCK, group, d))
+    probs = np.empty((group, BLOCK, L + BLOCK))
+    for hh in range(group):
+        s = (Q[:, hh, :] @ Keys.T) * scale
+        s = s - s.max(axis=1, keepdims=True)
+        e = np.exp(s)
+        p = e / e.sum(axis=1, keepdims=True)
+        probs[hh] = p
+        out[:, hh, :] = p @ Vals
+    return (out, probs) if return_probs else out
+
+
+def block_attn_ref(q_blk: np.ndarray, k_blk: np.ndarray, v_blk: np.ndarray,
+                   k_cache: np.ndarray, v_cache: np.ndarray, ctx_len: np.ndarray,
+                   base: float, page_table: Optional[np.ndarray] = None,
+                   scale: Optional[float] = None,
+                   units: Optional[Sequence[Tuple[int, int]]] = None) -> np.ndarray:
+    """O [B, 16, Hq, d] float64 for every (b, kv head) unit, or only ``units``.
+
+    k_cache / v_cache: dense [B, Hkv, cap, d] or, with ``page_table``, paged
+    [P, Hkv, page, d]; the oracle gathers pages itself.  Entries of units not
+    computed are NaN.
+    """
+    B, _, Hq, d = q_blk.shape
+    Hkv = k_blk.shape[2]
+    G = Hq // Hkv
+    out = np.full((B, BLOCK, Hq, d), np.nan)
+    todo = units if units is not None else [(b, g) for b in range(B) for g in range(Hkv)]
+    for b, g in todo:
+        L = int(ctx_len[b])
+        if page_table is None:
+            kc, vc = k_cache[b, g], v_cache[b, g]
+        else:
+            kc = gather_pages(k_cache, page_table, b, L)[g]
+            vc = gather_pages(v_cache, page_table, b, L)[g]
+        out[b, :, g * G:(g + 1) * G, :] = block_attn_unit_ref(
+            q_blk[b], k_blk[b], v_blk[b], kc, vc, L, g, G, base, scale)
+    return out
+
+
+# --------------------------------------------------------------------------
+# a7-a9: greedy verify, prefix acceptance, commit and crop
+# (dflash-mlx page: "what is lossless" -- emitted tokens are the target's
+# greedy argmax; "single-forward verify" steps 6-9; guarantee 2 -- the
+# printed acceptance expression sum(cumprod(equal(drafted, posterior))) and
+# its no-skip reading, the first rejected slot's target token is the next
+# staged token; guarantee 3 / page "DFlash dual implementations" §3 -- the
+# attention KV cache is cropped to the committed length.)
+# --------------------------------------------------------------------------
+def argmax_first(values: np.ndarray) -> np.ndarray:
+    """Greedy token per row: the lowest index of the maximum.
+
+    NaN ranks above every number (the first NaN wins); -0 and +0 are equal.
+    numpy.argmax has exactly these semantics on float arrays.
+    """
+    return np.argmax(values, axis=-1).astype(np.int32)
+
+
+def verify_accept_ref(logits: np.ndarray, block_tokens: np.ndarray, kv_len: np.ndarray,
+                      page_size: int = 0) -> dict:
+    """One verify cycle for B sequences.
+
+    logits [B, 16, V] bf16 bits; block_tokens [B, 16] = [staged, d_1 .. d_15];
+    kv_len [B] = committed length before the block.
+      post[b, i]   = argmax_v logits[b, i, v]          (target greedy token after slot i)
+      accept[b]    = sum(cumprod(block_tokens[b, 1:] == post[b, :15]))   in [0, 15]
+      next[b]      = post[b, accept[b]]                 (next staged token)
+      kv_len'[b]   = kv_len[b] + 1 + accept[b]          (commit staged + accepted drafts)
+      commit[b, i] = kv_len[b] + i if i <= accept[b] else -1
+      n_pages[b]   = ceil(kv_len'[b] / page_size)       (paged caches only)
+    """
+    B = logits.shape[0]
+    post = np.empty((B, BLOCK), dtype=np.int32)
+    for b in range(B):                      # row-wise decode keeps memory bounded
+        post[b] = argmax_first(bf16_to_f64(logits[b]))
+    blk = np.asarray(block_tokens, dtype=np.int64)
+    matches = (blk[:, 1:] == post[:, :BLOCK - 1]).astype(np.int32)
+    accept = np.sum(np.cumprod(matches, axis=1), axis=1).astype(np.int32)
+    nxt = post[np.arange(B), accept].astype(np.int32)
+    kv_in = np.asarray(kv_len, dtype=np.int64)
+    kv_out = (kv_in + 1 + accept).astype(np.int32)
+    i = np.arange(BLOCK)[None, :]
+    commit = np.where(i <= accept[:, None], kv_in[:, None] + i, -1).astype(np.int32)
+    res = {"post": post, "accept": accept, "next": nxt, "kv_len": kv_out, "commit_pos": commit}
+    if page_size > 0:
+        res["n_pages"] = ((kv_out.astype(np.int64) + page_size - 1) // page_size).astype(np.int32)
+    return res
+
+
+# --------------------------------------------------------------------------
+# Brute-force twins for tiny shapes: scalar Python loops, float64 math.
+# --------------------------------------------------------------------------
+def argmax_brute(row: Sequence[float]) -> int:
+    best_i, best = 0, float(row[0])
+    for i in range(1, len(row)):
+        if math.isnan(best):
+            break
+        x = float(row[i])
+        if math.isnan(x) or x > best:
+            best_i, best = i, x
+    return best_i
+
+
+def accept_brute(drafts: Sequence[int], post: Sequence[int]) -> int:
+    """Length of the matched prefix: index of the first draft that differs from post."""
+    a = 0
+    while a < BLOCK - 1 and int(drafts[a + 1]) == int(post[a]):
+        a += 1
+    return a
+
+
+def rope_brute(vec: Sequence[float], pos: int, base: float) -> List[float]:
+    d = len(vec)
+    h = d // 2
+    out = [0.0] * d
+    for j in range(h):
+        th = pos * base ** (-2.0 * j / d)
+        c, s = math.cos(th), math.sin(th)
+        out[j] = vec[j] * c - vec[j + h] * s
+        out[j + h] = vec[j + h] * c + vec[j] * s
+    return out
+
+
+def block_attn_brute(q_b, k_b, v_b, k_ctx, v_ctx, ctx_len: int, g: int, group: int,
+                     base: float, scale: Optional[float] = None) -> np.ndarray:
+    """Scalar-loop twin of ``block_attn_unit_ref`` (same arguments), for tiny shapes."""
+    d = q_b.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    L = int(ctx_len)
+    f = lambda a: [float(t) for t in bf16_to_f64(a)]
+    keys, vals = [], []
+    for t in range(L):
+        keys.append(f(k_ctx[t]))
+        vals.append(f(v_ctx[t]))
+    for i in range(BLOCK):
+        keys.append([float(t) for t in round_bf16(np.array(rope_brute(f(k_b[i, g]), L + i, base)))])
+        vals.append(f(v_b[i, g]))
+    out = np.zeros((BLOCK, group, d))
+    for hh in range(group):
+        h = g * group + hh
+        for i in range(BLOCK):
+            q = [float(t) for t in round_bf16(np.array(rope_brute(f(q_b[i, h]), L + i, base)))]
+            sc = [sum(q[c] * key[c] for c in range(d)) * scale for key in keys]
+            m = max(sc)
+            w = [math.exp(s - m) for s in sc]
+            z = sum(w)
+            for c in range(d):
+                out[i, hh, c] = sum(w[t] * vals[t][c] for t in range(len(keys))) / z
+    return out
