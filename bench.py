@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of the DFlash draft hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch, in cycle order:
+  1. dflash_block_attn   dual-source block attention (draft layer) over [ctx ; block]
+  2. dflash_verify_accept greedy verify of the 16 block positions: argmax, accept,
+                          next staged token, commit positions, KV-length crop
+  3. dflash_ctx_proj     projection of the committed rows' target hidden states into
+                          the context cache (fc + K/V + RoPE + scatter)
+on seeded synthetic inputs of the batched-serving workload (B=8, L=8192, 32q/8kv,
+d=128, 5x4096 target features, V=151936).  Inputs are resident in HBM and rotated
+over several copies so the bytes touched between two uses of one copy exceed 1 GiB
+(4x the 256 MB Infinity Cache): the numbers are cold-cache numbers.
+
+Prints one JSON line.  `value` = draft tokens per second through the whole step
+(B*16 block tokens per step).  `roofline` describes the dominant kernel (block
+attention): algorithmic HBM bytes per launch over its mean launch time, measured
+with HIP events on the launch stream inside the timed region.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="batched")
+    ap.add_argument("--rotate", type=int, default=0, help="input copies (0 = enough for >= 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def attn_bytes(cfg, ctx_len):
+    B, Hq, Hkv, d = len(ctx_len), cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    b = 4 * Hkv * d * int(ctx_len.sum()) + 2 * 16 * B * Hq * d + 4 * 16 * B * Hkv * d + 4 * 16 * B * Hq * d + 4 * B
+    if cfg.page_size:
+        b += 4 * int(((ctx_len + 15) // 16).sum())
+    return b
+
+
+def verify_bytes(cfg, B):
+    return 2 * 16 * B * cfg.vocab + 4 * 16 * B * 3 + 4 * B * 4
+
+
+def proj_bytes(cfg, M, committed):
+    kvw = cfg.n_kv_heads * cfg.head_dim
+    return (2 * cfg.hidden * cfg.ctx_width + 2 * 2 * kvw * cfg.hidden + 2 * M * cfg.ctx_width
+            + 2 * 2 * committed * kvw + 8 * M)
+
+
+def cpu_baseline(cfg, at, vi, pj, row_pos, t_budget=20.0):
+    """Oracle on a bounded sample of the same step, scaled to draft tokens/s."""
+    import numpy as np
+    from oracle import dflash_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    B, Hkv = len(at.ctx_len), cfg.n_kv_heads
+    units = [(b, g) for b in range(B) for g in range(Hkv)]
+    n_u = 0
+    t0 = time.perf_counter()
+    for (b, g) in units:
+        orc.block_attn_ref(at.q_blk, at.k_blk, at.v_blk, at.k_cache, at.v_cache, at.ctx_len, cfg.rope_base,
+                           units=[(b, g)])
+        n_u += 1
+        if time.perf_counter() - t0 > t_budget * 0.4:
+            break
+    t_attn = (time.perf_counter() - t0) / n_u * len(units)
+    nb = max(1, min(B, 2))
+    t0 = time.perf_counter()
+    orc.verify_accept_ref(vi.logits[:nb], vi.block_tokens[:nb], vi.kv_len[:nb])
+    t_ver = (time.perf_counter() - t0) / nb * B
+    m = 32
+    t0 = time.perf_counter()
+    orc.ctx_proj_ref([x[:m] for x in pj.x_layers], pj.w_fc, pj.w_k, pj.w_v, row_pos[:m], Hkv, cfg.head_dim,
+                     cfg.rope_base)
+    t_proj = (time.perf_counter() - t0) / m * len(row_pos)
+    t_step = t_attn + t_ver + t_proj
+    return {"value": 16 * B / t_step, "unit": "draft tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_u} of {len(units)} attention units, verify of {nb} of {B} sequences, "
+                      f"projection of {m} of {len(row_pos)} rows; scaled to one full step "
+                      f"({t_step:.2f} s/step: attn {t_attn:.2f}, verify {t_ver:.2f}, proj {t_proj:.2f})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is a "
+              f"design note, not a built path.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from block_diffusion_draft_proj_amd import dflash as dfl
+    from block_diffusion_draft_proj_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.CONFIGS[args.config]
+    u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).to(dev)
+
+    at = synth.attn_inputs(cfg)
+    vi = synth.verify_inputs(cfg, kv_len=at.ctx_len)
+    B = len(at.ctx_len)
+    M = 16 * B
+    pj = synth.ctx_proj_inputs(cfg, M)
+    Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    max_ctx = int(at.ctx_len.max())
+    max_pos = max_ctx + 2 * synth.BLOCK
+
+    dims = dfl.make_dims(B, Hq, Hkv, d, hidden=cfg.hidden, page_size=cfg.page_size, kv_capacity=at.capacity,
+                         num_pages=at.num_pages)
+    a_b = attn_bytes(cfg, at.ctx_len)
+    v_b = verify_bytes(cfg, B)
+    committed = int((vi.planted_accept + 1).sum())
+    p_b = proj_bytes(cfg, M, committed)
+    step_bytes = a_b + v_b + p_b
+    R = args.rotate or max(2, int(np.ceil(2 * (1 << 30) / step_bytes)))  # >= 2 GiB between reuses
+
+    # resident inputs: copy 0 from the seeded recipe, copies 1..R-1 are clones (cold addresses)
+    q, k, v = u16(at.q_blk), u16(at.k_blk), u16(at.v_blk)
+    kc0, vc0 = u16(at.k_cache), u16(at.v_cache)
+    lg0 = u16(vi.logits)
+    xs0 = [u16(x) for x in pj.x_layers]
+    wfc0 = u16(pj.w_fc)
+    kcs, vcs, lgs, xss, wfcs = [kc0], [vc0], [lg0], [xs0], [wfc0]
+    for _ in range(R - 1):
+        kcs.append(kc0.clone()); vcs.append(vc0.clone()); lgs.append(lg0.clone())
+        xss.append([x.clone() for x in xs0]); wfcs.append(wfc0.clone())
+    wk, wv = u16(pj.w_k), u16(pj.w_v)
+    table = i32(at.page_table) if at.page_table is not None else None
+    ctx = i32(at.ctx_len)
+    blk = i32(vi.block_tokens)
+    kv_in = i32(vi.kv_len)
+    row_seq = i32(np.repeat(np.arange(B), 16))
+    cos = torch.empty(max_pos, d // 2, dtype=torch.float32, device=dev)
+    sin = torch.empty_like(cos)
+    dfl.dflash_rope_tables(cfg.rope_base, d, max_pos, cos, sin)
+    out = torch.empty(B, 16, Hq, d, dtype=torch.float32, device=dev)
+    z = lambda *s: torch.zeros(*s, dtype=torch.int32, device=dev)
+    post, acc, nxt, kv_out, commit = z(B, 16), z(B), z(B), z(B), z(B, 16)
+    ws_a = dfl.workspace(dfl.dflash_block_attn_workspace_size(dims, max_ctx), dev)
+    ws_v = dfl.workspace(dfl.dflash_verify_workspace_size(B, 16, cfg.vocab), dev)
+    ws_p = dfl.workspace(dfl.dflash_ctx_proj_workspace_size(dims, M, cfg.n_target_layers, cfg.target_hidden), dev)
+    torch.cuda.synchronize()
+
+    ev = []
+
+    def step(i, timed):
+        if timed:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+        dfl.dflash_block_attn(dims, q, k, v, kcs[i], vcs[i], table, ctx, max_ctx, cos, sin, out, ws_a)
+        if timed:
+            e[1].record()
+        dfl.dflash_verify_accept(lgs[i], blk, kv_in, post, acc, nxt, kv_out, commit, 0, None, ws_v)
+        if timed:
+            e[2].record()
+        dfl.dflash_ctx_proj(dims, xss[i], row_seq, commit.view(-1), wfcs[i], wk, wv, cos, sin, None, kcs[i],
+                            vcs[i], table, ws_p)
+        if timed:
+            e[3].record()
+            ev.append(e)
+
+    for s in range(args.warmup):
+        step(s % R, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(s % R, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) / args.steps * 1e3
+    t_attn = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_ver = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    t_proj = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) * 1e-3
+    ok = bool(np.array_equal(acc.cpu().numpy(), vi.planted_accept))
+    attn_gbs = a_b / t_attn / 1e9
+    res = {
+        "metric": "block-attn draft tokens/s & HBM GB/s (% peak); verify cycles/s at 1 GPU",
+        "value": round(16 * B / (ms_step * 1e-3), 1),
+        "unit": "draft tokens/s (whole hot-path step)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded, resident in HBM, %d rotated copies, cold cache)" % R,
+        "config": {"workload": f"{cfg.name}: B={B}, block=16, L={max_ctx if cfg.ragged is None else 'ragged'}, "
+                               f"{Hq}q/{Hkv}kv, d={d}, ctx {cfg.n_target_layers}x{cfg.target_hidden}->"
+                               f"{cfg.hidden}, V={cfg.vocab}", "batch": B, "block": 16},
+        "block_attn": {"us": round(t_attn * 1e6, 2), "draft_tokens_per_s": round(16 * B / t_attn, 1),
+                       "GB_s": round(attn_gbs, 1), "pct_hbm_peak": round(100 * attn_gbs / HBM_PEAK_GBS, 2),
+                       "bytes": a_b},
+        "verify": {"us": round(t_ver * 1e6, 2), "cycles_per_s": round(1 / t_ver, 1),
+                   "committed_tokens_per_s": round(committed / t_ver, 1),
+                   "GB_s": round(v_b / t_ver / 1e9, 1), "bytes": v_b, "accept_matches_planted": ok},
+        "ctx_proj": {"us": round(t_proj * 1e6, 2), "GB_s": round(p_b / t_proj / 1e9, 1), "bytes": p_b,
+                     "rows": M, "committed_rows": committed},
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, at, vi, pj, commit.view(-1).cpu().numpy())
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,314 @@
+// C ABI of the DFlash hot path: host-side validation, workspace planning and
+// kernel dispatch.  Every check runs before the first HIP call, so invalid
+// arguments are reported without touching the device (and are testable on a
+// machine without a GPU).  The library keeps no state beyond a per-device
+// cache of the architecture check.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/dflash.h"
+#include "launch.h"
+
+using namespace dflash;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Current device must be a gfx950 (MI355X class) part: the kernels use its MFMA
+// and bf16 conversion instructions.
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DFLASH_ERR_UNSUPPORTED;
+  if (dev < 0 || dev >= kMaxDevices) return DFLASH_ERR_UNSUPPORTED;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DFLASH_ERR_UNSUPPORTED;
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? DFLASH_OK : DFLASH_ERR_UNSUPPORTED;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_LAUNCH; }
+
+// Shape checks shared by attention and projection.
+int check_cache_dims(const dflash_dims* d) {
+  if (!d) return DFLASH_ERR_NULL;
+  if (d->batch < 1 || d->batch > (1 << 20)) return DFLASH_ERR_SHAPE;
+  if (d->block != DFLASH_BLOCK) return DFLASH_ERR_SHAPE;
+  if (d->n_kv_heads < 1 || d->n_kv_heads > 1024) return DFLASH_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return DFLASH_ERR_UNSUPPORTED;
+  if (d->page_size != 0 && d->page_size != 16) return DFLASH_ERR_UNSUPPORTED;
+  if (d->kv_capacity < 1) return DFLASH_ERR_SHAPE;
+  if (d->page_size > 0 && d->num_pages < 1) return DFLASH_ERR_SHAPE;
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_status_str(int status) {
+  switch (status) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_ERR_NULL: return "required pointer is NULL";
+    case DFLASH_ERR_SHAPE: return "size out of range or inconsistent";
+    case DFLASH_ERR_ALIGN: return "pointer or stride misaligned (16-byte pointers, strides multiple of 8)";
+    case DFLASH_ERR_WORKSPACE: return "workspace missing or too small";
+    case DFLASH_ERR_CAPACITY: return "cache or RoPE table too small for the request";
+    case DFLASH_ERR_UNSUPPORTED: return "unsupported device (needs gfx950) or size";
+    case DFLASH_ERR_LAUNCH: return "HIP runtime reported an error at launch";
+  }
+  return "unknown status";
+}
+
+int dflash_version(void) { return (1 << 16) | 0; }
+
+int dflash_rope_tables(float base, int32_t head_dim, int32_t max_pos, float* cos_out, float* sin_out,
+                       hipStream_t stream) {
+  if (!cos_out || !sin_out) return DFLASH_ERR_NULL;
+  if (!(base > 1.0f) || !isfinite(base)) return DFLASH_ERR_SHAPE;
+  if (head_dim < 2 || head_dim > 256 || (head_dim & 1)) return DFLASH_ERR_SHAPE;
+  if (max_pos < 1 || (int64_t)max_pos * (head_dim / 2) > (int64_t)1 << 31) return DFLASH_ERR_SHAPE;
+  if (!aligned16(cos_out) || !aligned16(sin_out)) return DFLASH_ERR_ALIGN;
+  int st = check_device();
+  if (st != DFLASH_OK) return st;
+  return launch_status(launch_rope_tables((double)base, head_dim, max_pos, cos_out, sin_out, stream));
+}
+
+// ------------------------------------------------------------------ verify
+size_t dflash_verify_workspace_size(int32_t batch, int32_t block, int32_t vocab) {
+  if (batch < 1 || block != DFLASH_BLOCK || vocab < 1) return 0;
+  const size_t n_chunks = ((size_t)vocab + kVerifyChunk - 1) / kVerifyChunk;
+  const size_t counts = ((sizeof(uint32_t) * (size_t)batch) + 255) & ~(size_t)255;
+  return 256 + counts + sizeof(uint64_t) * (size_t)batch * DFLASH_BLOCK * n_chunks;
+}
+
+int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab, const void* logits, int64_t ld_logits,
+                         const int32_t* block_tokens, const int32_t* kv_len_in, int32_t* posterior,
+                         int32_t* accept_len, int32_t* next_token, int32_t* kv_len_out, int32_t* commit_pos,
+                         int32_t page_size, int32_t* n_pages, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (!logits || !block_tokens || !kv_len_in || !posterior || !accept_len || !next_token || !kv_len_out)
+    return DFLASH_ERR_NULL;
+  if (batch < 1 || block != DFLASH_BLOCK || vocab < 1 || vocab == 0x7fffffff) return DFLASH_ERR_SHAPE;
+  if (ld_logits < vocab) return DFLASH_ERR_SHAPE;
+  if (page_size < 0 || (n_pages && page_size == 0)) return DFLASH_ERR_SHAPE;
+  if ((ld_logits & 7) || !aligned16(logits)) return DFLASH_ERR_ALIGN;
+  const int64_t n_chunks = ((int64_t)vocab + kVerifyChunk - 1) / kVerifyChunk;
+  if ((int64_t)batch * DFLASH_BLOCK * n_chunks > 0x7fffffffLL) return DFLASH_ERR_SHAPE;
+  const size_t need = dflash_verify_workspace_size(batch, block, vocab);
+  if (!workspace || workspace_bytes < need) return DFLASH_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DFLASH_ERR_ALIGN;
+  int st = check_device();
+  if (st != DFLASH_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  const size_t counts = ((sizeof(uint32_t) * (size_t)batch) + 255) & ~(size_t)255;
+  VerifyParams p{};
+  p.logits = static_cast<const uint16_t*>(logits);
+  p.ld = ld_logits;
+  p.vocab = vocab;
+  p.n_chunks = (int)n_chunks;
+  p.block_tokens = block_tokens;
+  p.kv_len_in = kv_len_in;
+  p.posterior = posterior;
+  p.accept_len = accept_len;
+  p.next_token = next_token;
+  p.kv_len_out = kv_len_out;
+  p.commit_pos = commit_pos;
+  p.n_pages = n_pages;
+  p.page_size = page_size;
+  p.count = reinterpret_cast<uint32_t*>(ws + 256);
+  p.part = reinterpret_cast<uint64_t*>(ws + 256 + counts);
+  return launch_status(launch_verify_accept(p, batch, stream));
+}
+
+// ------------------------------------------------------------------ block attention
+size_t dflash_block_attn_workspace_size(const dflash_dims* dims, int32_t max_ctx_len) {
+  if (check_cache_dims(dims) != DFLASH_OK || max_ctx_len < 0) return 0;
+  if (dims->n_q_heads < dims->n_kv_heads || dims->n_q_heads % dims->n_kv_heads) return 0;
+  return plan_block_attn(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim, max_ctx_len, kPlanCUs)
+      .ws_bytes;
+}
+
+int dflash_block_attn(const dflash_dims* dims, const void* q_blk, const void* k_blk, const void* v_blk,
+                      const void* k_cache, const void* v_cache, const int32_t* page_table, const int32_t* ctx_len,
+                      int32_t max_ctx_len, const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                      float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_cache_dims(dims);
+  if (st != DFLASH_OK) return st;
+  if (!q_blk || !k_blk || !v_blk || !k_cache || !v_cache || !ctx_len || !rope_cos || !rope_sin || !out)
+    return DFLASH_ERR_NULL;
+  if (dims->page_size > 0 && !page_table) return DFLASH_ERR_NULL;
+  if (dims->n_q_heads < dims->n_kv_heads || dims->n_q_heads % dims->n_kv_heads) return DFLASH_ERR_SHAPE;
+  const int group = dims->n_q_heads / dims->n_kv_heads;
+  if (group > 8) return DFLASH_ERR_UNSUPPORTED;
+  if (max_ctx_len < 0 || max_ctx_len > (1 << 24)) return DFLASH_ERR_SHAPE;
+  const int64_t cap_tokens =
+      dims->page_size > 0 ? (int64_t)dims->kv_capacity * dims->page_size : (int64_t)dims->kv_capacity;
+  if (max_ctx_len > cap_tokens) return DFLASH_ERR_CAPACITY;
+  if ((int64_t)max_pos < (int64_t)max_ctx_len + DFLASH_BLOCK) return DFLASH_ERR_CAPACITY;
+  const void* ptrs[] = {q_blk, k_blk, v_blk, k_cache, v_cache, rope_cos, rope_sin, out};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DFLASH_ERR_ALIGN;
+  const AttnPlan pl =
+      plan_block_attn(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim, max_ctx_len, kPlanCUs);
+  if (!workspace || workspace_bytes < pl.ws_bytes) return DFLASH_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DFLASH_ERR_ALIGN;
+  const int64_t grid = (int64_t)8 * pl.n_splits * (((int64_t)dims->batch * dims->n_kv_heads + 7) / 8);
+  if (grid > 0x7fffffffLL) return DFLASH_ERR_SHAPE;
+  st = check_device();
+  if (st != DFLASH_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  AttnParams p{};
+  p.q_blk = static_cast<const uint16_t*>(q_blk);
+  p.k_blk = static_cast<const uint16_t*>(k_blk);
+  p.v_blk = static_cast<const uint16_t*>(v_blk);
+  p.k_cache = static_cast<const uint16_t*>(k_cache);
+  p.v_cache = static_cast<const uint16_t*>(v_cache);
+  p.page_table = page_table;
+  p.ctx_len = ctx_len;
+  p.rope_cos = rope_cos;
+  p.rope_sin = rope_sin;
+  p.out = out;
+  p.ws_o = reinterpret_cast<float*>(ws + pl.off_o);
+  p.ws_ml = reinterpret_cast<float*>(ws + pl.off_ml);
+  p.count = reinterpret_cast<uint32_t*>(ws + pl.off_count);
+  p.err = reinterpret_cast<uint32_t*>(ws);
+  p.batch = dims->batch;
+  p.n_q_heads = dims->n_q_heads;
+  p.n_kv_heads = dims->n_kv_heads;
+  p.capacity = dims->kv_capacity;
+  p.num_pages = dims->page_size > 0 ? dims->num_pages : 0;
+  p.max_ctx = max_ctx_len;
+  p.kps = pl.kps;
+  p.n_splits = pl.n_splits;
+  p.n_units = dims->batch * dims->n_kv_heads;
+  const double scale = dims->softmax_scale > 0.f ? (double)dims->softmax_scale : 1.0 / sqrt((double)dims->head_dim);
+  p.scale_log2 = (float)(scale * 1.4426950408889634);
+  return launch_status(launch_block_attn(p, dims->head_dim, group, dims->page_size > 0, stream));
+}
+
+// ------------------------------------------------------------------ context projection
+size_t dflash_ctx_proj_workspace_size(const dflash_dims* dims, int32_t n_rows, int32_t n_layers, int32_t d_target) {
+  if (check_cache_dims(dims) != DFLASH_OK || n_rows < 0 || n_layers < 1 || d_target < 1) return 0;
+  // Planned for the fc path; the same size also serves a call without fc.
+  return plan_ctx_proj(n_rows, n_layers * d_target, dims->hidden, 2 * dims->n_kv_heads * dims->head_dim, true,
+                       kPlanCUs)
+      .ws_bytes;
+}
+
+int dflash_ctx_proj(const dflash_dims* dims, int32_t n_rows, const void* const* x_layers, int32_t n_layers,
+                    int32_t d_target, int64_t ld_x, const int32_t* row_seq, const int32_t* row_pos,
+                    const void* w_fc, const void* w_k, const void* w_v, const float* rope_cos,
+                    const float* rope_sin, int32_t max_pos, void* c_out, void* k_cache, void* v_cache,
+                    const int32_t* page_table, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_cache_dims(dims);
+  if (st != DFLASH_OK) return st;
+  if (!x_layers || !row_seq || !row_pos || !w_k || !w_v || !rope_cos || !rope_sin || !k_cache || !v_cache)
+    return DFLASH_ERR_NULL;
+  if (dims->page_size > 0 && !page_table) return DFLASH_ERR_NULL;
+  if (n_rows < 0 || n_rows > (1 << 22)) return DFLASH_ERR_SHAPE;
+  if (n_layers < 1 || n_layers > kMaxLayers) return DFLASH_ERR_SHAPE;
+  if (dims->hidden < 64 || dims->hidden % 64 || dims->hidden > (1 << 16)) return DFLASH_ERR_SHAPE;
+  if (d_target < 64 || d_target % 64 || d_target > (1 << 16)) return DFLASH_ERR_SHAPE;
+  if (ld_x < d_target) return DFLASH_ERR_SHAPE;
+  if (!w_fc && (n_layers != 1 || d_target != dims->hidden || c_out)) return DFLASH_ERR_SHAPE;
+  if (max_pos < 1) return DFLASH_ERR_CAPACITY;
+  if (ld_x & 7) return DFLASH_ERR_ALIGN;
+  for (int l = 0; l < n_layers; ++l) {
+    if (!x_layers[l]) return DFLASH_ERR_NULL;
+    if (!aligned16(x_layers[l])) return DFLASH_ERR_ALIGN;
+  }
+  const void* ptrs[] = {w_k, w_v, rope_cos, rope_sin, k_cache, v_cache};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DFLASH_ERR_ALIGN;
+  if ((w_fc && !aligned16(w_fc)) || (c_out && !aligned16(c_out))) return DFLASH_ERR_ALIGN;
+  const bool has_fc = w_fc != nullptr;
+  const int kv_width = 2 * dims->n_kv_heads * dims->head_dim;
+  const int k_fc = n_layers * d_target;
+  const ProjPlan pl = plan_ctx_proj(n_rows, k_fc, dims->hidden, kv_width, true, kPlanCUs);
+  if (!workspace || workspace_bytes < pl.ws_bytes) return DFLASH_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DFLASH_ERR_ALIGN;
+  if (n_rows == 0) return DFLASH_OK;
+  st = check_device();
+  if (st != DFLASH_OK) return st;
+
+  char* ws = static_cast<char*>(workspace);
+  const uint16_t* c_src;
+  int64_t ld_c;
+  if (has_fc) {
+    GemmParams g{};
+    for (int l = 0; l < n_layers; ++l) g.a_seg[l] = static_cast<const uint16_t*>(x_layers[l]);
+    g.lda = ld_x;
+    g.seg_k = d_target;
+    g.b0 = static_cast<const uint16_t*>(w_fc);
+    g.b1 = g.b0;
+    g.n_b0 = dims->hidden;
+    g.M = n_rows;
+    g.N = dims->hidden;
+    g.K = k_fc;
+    g.k_per_split = pl.fc_kps;
+    g.out = reinterpret_cast<float*>(ws + pl.off_fc);
+    hipError_t e = launch_gemm_nt(g, pl.fc_splits, pl.fc_small, stream);
+    if (e != hipSuccess) return DFLASH_ERR_LAUNCH;
+    FcReduceParams r{};
+    r.part = g.out;
+    r.splits = pl.fc_splits;
+    r.M = n_rows;
+    r.N = dims->hidden;
+    r.c_buf = reinterpret_cast<uint16_t*>(ws + pl.off_c);
+    r.c_out = static_cast<uint16_t*>(c_out);
+    e = launch_fc_reduce(r, stream);
+    if (e != hipSuccess) return DFLASH_ERR_LAUNCH;
+    c_src = r.c_buf;
+    ld_c = dims->hidden;
+  } else {
+    c_src = static_cast<const uint16_t*>(x_layers[0]);
+    ld_c = ld_x;
+  }
+  GemmParams g{};
+  g.a_seg[0] = c_src;
+  g.lda = ld_c;
+  g.seg_k = dims->hidden;
+  g.b0 = static_cast<const uint16_t*>(w_k);
+  g.b1 = static_cast<const uint16_t*>(w_v);
+  g.n_b0 = dims->n_kv_heads * dims->head_dim;
+  g.M = n_rows;
+  g.N = kv_width;
+  g.K = dims->hidden;
+  g.k_per_split = pl.kv_kps;
+  g.out = reinterpret_cast<float*>(ws + pl.off_kv);
+  hipError_t e = launch_gemm_nt(g, pl.kv_splits, pl.kv_small, stream);
+  if (e != hipSuccess) return DFLASH_ERR_LAUNCH;
+  KvEpilogueParams k{};
+  k.part = g.out;
+  k.splits = pl.kv_splits;
+  k.M = n_rows;
+  k.n_kv_heads = dims->n_kv_heads;
+  k.head_dim = dims->head_dim;
+  k.row_seq = row_seq;
+  k.row_pos = row_pos;
+  k.rope_cos = rope_cos;
+  k.rope_sin = rope_sin;
+  k.max_pos = max_pos;
+  k.k_cache = static_cast<uint16_t*>(k_cache);
+  k.v_cache = static_cast<uint16_t*>(v_cache);
+  k.page_table = page_table;
+  k.batch = dims->batch;
+  k.page_size = dims->page_size;
+  k.capacity = dims->kv_capacity;
+  k.num_pages = dims->page_size > 0 ? dims->num_pages : 0;
+  k.err = reinterpret_cast<uint32_t*>(ws);
+  return launch_status(launch_kv_epilogue(k, stream));
+}
+
+}  // extern "C"

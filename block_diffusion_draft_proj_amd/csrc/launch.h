@@ -1,0 +1,122 @@
+// Internal kernel parameter blocks and launchers (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+// Split plans are made for the MI355X CU count so the workspace-size queries
+// (which run without a device) and the launches always agree.
+constexpr int kPlanCUs = 256;
+
+// ---------------------------------------------------------------- verify
+constexpr int kVerifyChunk = 8192;  // logits per workgroup (256 threads x 4 x 8)
+
+struct VerifyParams {
+  const uint16_t* logits;
+  int64_t ld;
+  int vocab;
+  int n_chunks;
+  const int32_t* block_tokens;
+  const int32_t* kv_len_in;
+  int32_t* posterior;
+  int32_t* accept_len;
+  int32_t* next_token;
+  int32_t* kv_len_out;
+  int32_t* commit_pos;  // may be null
+  int32_t* n_pages;     // may be null
+  int32_t page_size;
+  uint32_t* count;      // [batch] arrival counters (self-resetting)
+  uint64_t* part;       // [batch*16*n_chunks] per-chunk keys
+};
+hipError_t launch_verify_accept(const VerifyParams& p, int batch, hipStream_t stream);
+
+// ---------------------------------------------------------------- RoPE tables
+hipError_t launch_rope_tables(double base, int head_dim, int max_pos, float* cos_out, float* sin_out,
+                              hipStream_t stream);
+
+// ---------------------------------------------------------------- block attention
+struct AttnParams {
+  const uint16_t* q_blk;
+  const uint16_t* k_blk;
+  const uint16_t* v_blk;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* page_table;
+  const int32_t* ctx_len;
+  const float* rope_cos;
+  const float* rope_sin;
+  float* out;
+  float* ws_o;      // [units][n_splits][G][D/16][64 lanes][4] partial outputs
+  float* ws_ml;     // [units][n_splits][G][16][2] running max (log2 domain) and sum
+  uint32_t* count;  // [units] arrival counters (self-resetting)
+  uint32_t* err;    // sticky device error word
+  int batch, n_q_heads, n_kv_heads;
+  int capacity;     // dense rows per (seq, head) | page-table columns
+  int num_pages;
+  int max_ctx;
+  int kps;          // context keys per split (multiple of 64)
+  int n_splits;     // splits per unit at max_ctx
+  int n_units;      // batch * n_kv_heads
+  float scale_log2; // softmax scale * log2(e)
+};
+struct AttnPlan {
+  int kps;
+  int n_splits;
+  size_t ws_bytes;
+  size_t off_count, off_ml, off_o;
+};
+AttnPlan plan_block_attn(int batch, int n_q_heads, int n_kv_heads, int head_dim, int max_ctx, int num_cu);
+hipError_t launch_block_attn(const AttnParams& p, int head_dim, int group, bool paged, hipStream_t stream);
+
+// ---------------------------------------------------------------- context projection
+constexpr int kMaxLayers = 8;
+
+struct GemmParams {
+  const uint16_t* a_seg[kMaxLayers];  // A = [seg_0 | seg_1 | ...] along K, each [M][lda]
+  int64_t lda;
+  int seg_k;                           // K width of one segment (multiple of 64)
+  const uint16_t* b0;                  // rows [0, n_b0) of B, each [K]
+  const uint16_t* b1;                  // rows [n_b0, N) of B (row index - n_b0)
+  int n_b0;
+  int M, N, K;
+  int k_per_split;                     // multiple of 64
+  float* out;                          // [splits][M][N] fp32 partial sums
+};
+struct ProjPlan {
+  int fc_splits, kv_splits;
+  int fc_kps, kv_kps;       // K elements per split (multiples of 64)
+  bool fc_small, kv_small;  // small-M tile shape (M <= 128)
+  size_t ws_bytes;
+  size_t off_fc, off_c, off_kv;
+};
+ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_fc, int num_cu);
+hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStream_t stream);
+
+struct FcReduceParams {
+  const float* part;   // [splits][M][N]
+  int splits, M, N;
+  uint16_t* c_buf;     // [M][N] bf16
+  uint16_t* c_out;     // optional copy
+};
+hipError_t launch_fc_reduce(const FcReduceParams& p, hipStream_t stream);
+
+struct KvEpilogueParams {
+  const float* part;   // [splits][M][2*Hkv*d]
+  int splits, M;
+  int n_kv_heads, head_dim;
+  const int32_t* row_seq;
+  const int32_t* row_pos;
+  const float* rope_cos;
+  const float* rope_sin;
+  int max_pos;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  const int32_t* page_table;
+  int batch, page_size, capacity, num_pages;
+  uint32_t* err;
+};
+hipError_t launch_kv_epilogue(const KvEpilogueParams& p, hipStream_t stream);
+
+}  // namespace dflash

@@ -1,0 +1,195 @@
+// Greedy verify: vocab-wide argmax at the 16 block positions, matched-prefix
+// accept length, next staged token, commit positions and crop of the KV length.
+//
+// Pages: "dflash-mlx: lossless speculative decoding" -- "what is lossless"
+// (every emitted token is the target's greedy argmax), "single-forward verify"
+// steps 6-9, guarantee 2 (accept = sum(cumprod(draft == posterior)), no skipping
+// past a mismatch; the target token at the first rejected slot is the next staged
+// token) and guarantee 3 / "DFlash dual implementations" §3 (crop the attention KV
+// to the committed length).
+//
+// Design (HBM-bound stream of B*16*V bf16 logits):
+//  * one workgroup per (row, 8192-element chunk): 256 threads, 4 x 16-byte
+//    coalesced loads per thread, all issued before any arithmetic;
+//  * values are mapped to order-preserving 16-bit keys with packed 16-bit integer
+//    ops (two elements per instruction), so the per-element cost is ~2.5 VALU ops;
+//  * the first index of the chunk maximum is found in a second pass over the keys
+//    held in registers, by only the threads whose own maximum matched;
+//  * each chunk publishes one 64-bit key (value key << 32 | ~index), so the row
+//    maximum with the lowest index is an order-independent max();
+//  * the last-arriving workgroup of a sequence (per-sequence arrival counter in the
+//    workspace, reset by that workgroup) reduces the 16 rows and runs accept /
+//    commit / crop.  No host round trip, one launch.
+#include "common.h"
+#include "launch.h"
+
+namespace dflash {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVec = 4;
+
+// Ordered keys of two packed bf16 values: negative -> ~bits, non-negative -> bits|0x8000.
+// Monotone in value for non-NaN inputs, except -0 (0x7fff) sits just below +0 (0x8000).
+// Positive NaNs land above +inf (0xff80), negative NaNs below -inf (0x007f).
+__device__ __forceinline__ uint32_t order_keys(uint32_t w) {
+  const i16x2 v = __builtin_bit_cast(i16x2, w);
+  const uint32_t s = __builtin_bit_cast(uint32_t, (i16x2)(v >> (i16x2){15, 15}));
+  return w ^ (s | 0x80008000u);
+}
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_min(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+constexpr uint32_t kKeyNegInf = 0x007fu;  // key of -inf; masked tail elements use it too
+constexpr uint32_t kKeyPosInf = 0xff80u;
+constexpr uint32_t kNegInfBits2 = 0xff80ff80u;
+
+__device__ __forceinline__ bool is_zero_key(uint32_t k) { return k == 0x7fffu || k == 0x8000u; }
+__device__ __forceinline__ bool is_nan_key(uint32_t k) { return k < kKeyNegInf || k > kKeyPosInf; }
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wg_reduce(T v, Op op, T* s_buf) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = op(v, __shfl_xor(v, off));
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_buf[wave] = v;
+  __syncthreads();
+  T r = s_buf[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / kWave; ++w) r = op(r, s_buf[w]);
+  return r;
+}
+
+__global__ __launch_bounds__(kThreads) void verify_accept_kernel(VerifyParams p) {
+  __shared__ uint32_t s_red[kThreads / kWave];
+  __shared__ int32_t s_post[kBlock];
+  __shared__ int32_t s_accept, s_kvin;
+  __shared__ uint32_t s_last;
+
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x / p.n_chunks;
+  const int chunk = blockIdx.x - row * p.n_chunks;
+  const int b = row / kBlock;
+  const uint16_t* rp = p.logits + (int64_t)row * p.ld;
+  const int c0 = chunk * kVerifyChunk;
+  const int c1 = min(p.vocab, c0 + kVerifyChunk);
+
+  // Pass 1: all loads first, then order keys with running packed max / min.
+  u32x4 w[kVec];
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    const int e = c0 + (i * kThreads + tid) * 8;
+    // ld is a multiple of 8 and >= vocab, so a vector that starts inside the row
+    // ends inside the row's allocation.
+    w[i] = (e < c1) ? ld16(rp + e) : (u32x4){kNegInfBits2, kNegInfBits2, kNegInfBits2, kNegInfBits2};
+  }
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    const int e = c0 + (i * kThreads + tid) * 8;
+    if (e < c1 && e + 8 > c1) {  // partial vector at the end of the row
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t x = w[i][j];
+        if (e + 2 * j >= c1) x = (x & 0xffff0000u) | 0xff80u;
+        if (e + 2 * j + 1 >= c1) x = (x & 0x0000ffffu) | 0xff800000u;
+        w[i][j] = x;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t k = order_keys(w[i][j]);
+      w[i][j] = k;
+      kmax = pk_max(kmax, k);
+      kmin = pk_min(kmin, k);
+    }
+  }
+  const uint32_t tmax = max(kmax & 0xffffu, kmax >> 16);
+  const uint32_t tmin = min(kmin & 0xffffu, kmin >> 16);
+  const uint32_t cmax = wg_reduce(tmax, [](uint32_t a, uint32_t c) { return max(a, c); }, s_red);
+  const uint32_t cmin = wg_reduce(tmin, [](uint32_t a, uint32_t c) { return min(a, c); }, s_red);
+
+  // Pass 2: first element index holding the chunk maximum.
+  const bool has_nan = (cmin < kKeyNegInf) || (cmax > kKeyPosInf);
+  const bool zero = !has_nan && is_zero_key(cmax);
+  bool mine;
+  if (has_nan) mine = is_nan_key(tmin) || is_nan_key(tmax);
+  else mine = zero ? is_zero_key(tmax) : (tmax == cmax);
+  uint32_t idx = 0xffffffffu;
+  if (mine) {
+#pragma unroll
+    for (int i = kVec - 1; i >= 0; --i) {  // descending so the last hit is the lowest index
+      const int e = c0 + (i * kThreads + tid) * 8;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+#pragma unroll
+        for (int h = 1; h >= 0; --h) {
+          const uint32_t k = (w[i][j] >> (16 * h)) & 0xffffu;
+          const bool hit = has_nan ? is_nan_key(k) : (zero ? is_zero_key(k) : (k == cmax));
+          if (hit) idx = (uint32_t)(e + 2 * j + h);
+        }
+      }
+    }
+  }
+  idx = wg_reduce(idx, [](uint32_t a, uint32_t c) { return min(a, c); }, s_red);
+
+  if (tid == 0) {
+    const uint64_t canon = has_nan ? 0x10000u : (zero ? 0x8000u : cmax);
+    const uint64_t key = (canon << 32) | (uint64_t)(0xffffffffu - idx);
+    __hip_atomic_store(p.part + (int64_t)row * p.n_chunks + chunk, key, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(p.count + b, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == (uint32_t)(kBlock * p.n_chunks - 1)) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // Last workgroup of sequence b: reduce rows, then accept / commit / crop.
+  __atomic_thread_fence(__ATOMIC_ACQUIRE);
+  if (tid < kBlock) {
+    const uint64_t* pr = p.part + (int64_t)(b * kBlock + tid) * p.n_chunks;
+    uint64_t best = 0;
+    for (int c = 0; c < p.n_chunks; ++c) {
+      const uint64_t k = __hip_atomic_load(pr + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      best = k > best ? k : best;
+    }
+    const int32_t post = (int32_t)(0xffffffffu - (uint32_t)best);
+    s_post[tid] = post;
+    p.posterior[b * kBlock + tid] = post;
+  }
+  if (tid == 0) s_kvin = p.kv_len_in[b];
+  __syncthreads();
+  if (tid == 0) {
+    const int32_t* blk = p.block_tokens + b * kBlock;
+    int a = 0;
+    while (a < kBlock - 1 && blk[a + 1] == s_post[a]) ++a;
+    s_accept = a;
+    const int32_t kv_out = s_kvin + 1 + a;
+    p.accept_len[b] = a;
+    p.next_token[b] = s_post[a];
+    p.kv_len_out[b] = kv_out;
+    if (p.n_pages) p.n_pages[b] = (int32_t)(((int64_t)kv_out + p.page_size - 1) / p.page_size);
+    __hip_atomic_store(p.count + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (p.commit_pos && tid < kBlock)
+    p.commit_pos[b * kBlock + tid] = (tid <= s_accept) ? s_kvin + tid : -1;
+}
+
+}  // namespace
+
+hipError_t launch_verify_accept(const VerifyParams& p, int batch, hipStream_t stream) {
+  const int grid = batch * kBlock * p.n_chunks;
+  hipLaunchKernelGGL(verify_accept_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -1,0 +1,196 @@
+"""Python binding of the DFlash hot-path C ABI (``include/dflash.h``).
+
+Argument marshalling only: each function checks tensor dtypes / devices /
+contiguity, passes raw device pointers and the current HIP stream to the entry
+point of the same name in ``lib/libdflash.so``, and raises ``DflashError`` on a
+non-zero status.  All computation happens in the library's HIP kernels; there is
+no fallback path.  Importing this module fails loudly if the library has not
+been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libdflash.so")
+
+BLOCK = 16
+DEVERR_CTX_LEN, DEVERR_PAGE_ID, DEVERR_ROW = 1, 2, 4
+
+_c_int, _c_i64, _c_sz, _c_f, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+
+
+class dflash_dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", _c_int), ("block", _c_int), ("n_q_heads", _c_int), ("n_kv_heads", _c_int),
+        ("head_dim", _c_int), ("hidden", _c_int), ("page_size", _c_int), ("kv_capacity", _c_int),
+        ("num_pages", _c_int), ("softmax_scale", _c_f),
+    ]
+
+
+class DflashError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn}: status {code} ({msg})")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build the HIP library first "
+                          f"(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(dflash_dims)
+    sig = {
+        "dflash_status_str": (ctypes.c_char_p, [_c_int]),
+        "dflash_version": (_c_int, []),
+        "dflash_rope_tables": (_c_int, [_c_f, _c_int, _c_int, _vp, _vp, _vp]),
+        "dflash_ctx_proj_workspace_size": (_c_sz, [P, _c_int, _c_int, _c_int]),
+        "dflash_ctx_proj": (_c_int, [P, _c_int, ctypes.POINTER(_vp), _c_int, _c_int, _c_i64, _vp, _vp,
+                                     _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
+        "dflash_block_attn_workspace_size": (_c_sz, [P, _c_int]),
+        "dflash_block_attn": (_c_int, [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int,
+                                       _vp, _vp, _c_sz, _vp]),
+        "dflash_verify_workspace_size": (_c_sz, [_c_int, _c_int, _c_int]),
+        "dflash_verify_accept": (_c_int, [_c_int, _c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _vp, _vp,
+                                          _vp, _vp, _c_int, _vp, _vp, _c_sz, _vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+LIB_PATH = _LIB_PATH
+
+# Names the public header declares (kept in step with include/dflash.h).
+EXPORTS = (
+    "dflash_status_str", "dflash_version", "dflash_rope_tables", "dflash_ctx_proj_workspace_size",
+    "dflash_ctx_proj", "dflash_block_attn_workspace_size", "dflash_block_attn",
+    "dflash_verify_workspace_size", "dflash_verify_accept",
+)
+
+
+def _check(fn: str, code: int) -> None:
+    if code != 0:
+        raise DflashError(fn, code, dflash_status_str(code))
+
+
+def _stream(stream) -> _vp:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtypes, contiguous: bool = True) -> _vp:
+    if t is None:
+        return _vp(None)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return _vp(t.data_ptr())
+
+
+def make_dims(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, hidden: int = 0,
+              page_size: int = 0, kv_capacity: int = 0, num_pages: int = 0,
+              softmax_scale: float = 0.0) -> dflash_dims:
+    return dflash_dims(batch, BLOCK, n_q_heads, n_kv_heads, head_dim, hidden, page_size, kv_capacity,
+                       num_pages, softmax_scale)
+
+
+def dflash_status_str(code: int) -> str:
+    return _lib.dflash_status_str(code).decode()
+
+
+def dflash_version() -> int:
+    return int(_lib.dflash_version())
+
+
+def dflash_rope_tables(base: float, head_dim: int, max_pos: int, cos_out: torch.Tensor,
+                       sin_out: torch.Tensor, stream=None) -> None:
+    _check("dflash_rope_tables", _lib.dflash_rope_tables(
+        base, head_dim, max_pos, _dev(cos_out, "cos_out", (torch.float32,)),
+        _dev(sin_out, "sin_out", (torch.float32,)), _stream(stream)))
+
+
+def dflash_ctx_proj_workspace_size(dims: dflash_dims, n_rows: int, n_layers: int, d_target: int) -> int:
+    return int(_lib.dflash_ctx_proj_workspace_size(ctypes.byref(dims), n_rows, n_layers, d_target))
+
+
+def dflash_ctx_proj(dims: dflash_dims, x_layers: Sequence[torch.Tensor], row_seq: torch.Tensor,
+                    row_pos: torch.Tensor, w_fc: Optional[torch.Tensor], w_k: torch.Tensor,
+                    w_v: torch.Tensor, rope_cos: torch.Tensor, rope_sin: torch.Tensor,
+                    c_out: Optional[torch.Tensor], k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    page_table: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
+    x0 = x_layers[0]
+    n_rows, d_target = int(x0.shape[0]), int(x0.shape[1])
+    ld = int(x0.stride(0))
+    for i, x in enumerate(x_layers):
+        if x.dim() != 2 or x.stride(1) != 1 or tuple(x.shape) != (n_rows, d_target) or x.stride(0) != ld:
+            raise ValueError(f"x_layers[{i}] must be [n_rows, d_target] with unit inner stride and a common row stride")
+        _dev(x, f"x_layers[{i}]", _BF16, contiguous=False)
+    arr = (_vp * len(x_layers))(*[x.data_ptr() for x in x_layers])
+    _check("dflash_ctx_proj", _lib.dflash_ctx_proj(
+        ctypes.byref(dims), n_rows, arr, len(x_layers), d_target, ld,
+        _dev(row_seq, "row_seq", (torch.int32,)), _dev(row_pos, "row_pos", (torch.int32,)),
+        _dev(w_fc, "w_fc", _BF16), _dev(w_k, "w_k", _BF16), _dev(w_v, "w_v", _BF16),
+        _dev(rope_cos, "rope_cos", (torch.float32,)), _dev(rope_sin, "rope_sin", (torch.float32,)),
+        int(rope_cos.shape[0]), _dev(c_out, "c_out", _BF16), _dev(k_cache, "k_cache", _BF16),
+        _dev(v_cache, "v_cache", _BF16), _dev(page_table, "page_table", (torch.int32,)),
+        _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
+
+
+def dflash_block_attn_workspace_size(dims: dflash_dims, max_ctx_len: int) -> int:
+    return int(_lib.dflash_block_attn_workspace_size(ctypes.byref(dims), max_ctx_len))
+
+
+def dflash_block_attn(dims: dflash_dims, q_blk: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor,
+                      k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: Optional[torch.Tensor],
+                      ctx_len: torch.Tensor, max_ctx_len: int, rope_cos: torch.Tensor,
+                      rope_sin: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                      stream=None) -> None:
+    _check("dflash_block_attn", _lib.dflash_block_attn(
+        ctypes.byref(dims), _dev(q_blk, "q_blk", _BF16), _dev(k_blk, "k_blk", _BF16),
+        _dev(v_blk, "v_blk", _BF16), _dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16),
+        _dev(page_table, "page_table", (torch.int32,)), _dev(ctx_len, "ctx_len", (torch.int32,)),
+        max_ctx_len, _dev(rope_cos, "rope_cos", (torch.float32,)),
+        _dev(rope_sin, "rope_sin", (torch.float32,)), int(rope_cos.shape[0]),
+        _dev(out, "out", (torch.float32,)), _dev(workspace, "workspace", (torch.uint8,)),
+        workspace.numel(), _stream(stream)))
+
+
+def dflash_verify_workspace_size(batch: int, block: int, vocab: int) -> int:
+    return int(_lib.dflash_verify_workspace_size(batch, block, vocab))
+
+
+def dflash_verify_accept(logits: torch.Tensor, block_tokens: torch.Tensor, kv_len_in: torch.Tensor,
+                         posterior: torch.Tensor, accept_len: torch.Tensor, next_token: torch.Tensor,
+                         kv_len_out: torch.Tensor, commit_pos: Optional[torch.Tensor],
+                         page_size: int, n_pages: Optional[torch.Tensor], workspace: torch.Tensor,
+                         vocab: Optional[int] = None, stream=None) -> None:
+    """logits [B, 16, ld] (ld >= vocab, multiple of 8); vocab defaults to ld."""
+    if logits.dim() != 3 or logits.stride(2) != 1 or logits.stride(1) != logits.shape[2] \
+            or logits.stride(0) != logits.shape[1] * logits.shape[2]:
+        raise ValueError("logits must be a contiguous [B, 16, ld] tensor")
+    B, blk, ld = (int(s) for s in logits.shape)
+    _check("dflash_verify_accept", _lib.dflash_verify_accept(
+        B, blk, ld if vocab is None else vocab, _dev(logits, "logits", _BF16), ld,
+        _dev(block_tokens, "block_tokens", (torch.int32,)), _dev(kv_len_in, "kv_len_in", (torch.int32,)),
+        _dev(posterior, "posterior", (torch.int32,)), _dev(accept_len, "accept_len", (torch.int32,)),
+        _dev(next_token, "next_token", (torch.int32,)), _dev(kv_len_out, "kv_len_out", (torch.int32,)),
+        _dev(commit_pos, "commit_pos", (torch.int32,)), page_size, _dev(n_pages, "n_pages", (torch.int32,)),
+        _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace buffer (the zero fill is needed once, before first use)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)

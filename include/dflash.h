@@ -1,0 +1,185 @@
+/*
+ * dflash.h -- C ABI of the DFlash draft block-attention / greedy-verify hot path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (pages cited by title and section):
+ *   - context projection: target-layer hidden states, selected by layer id and
+ *     concatenated, are projected into the draft's context K/V ("DFlash dual
+ *     implementations: PyTorch vs MLX", §4 target hidden states and §2
+ *     attention; "dflash-mlx: lossless speculative decoding", section
+ *     "block-diffusion draft": the draft reads the target's hidden states);
+ *   - dual-source block attention: Q from the 16 block tokens only, K/V =
+ *     [context ; block], no causal mask inside the block ("DFlash dual
+ *     implementations", §2 attention), RoPE as in Qwen3 (same page, §1);
+ *   - greedy verify: target argmax at the 16 block positions, accepted prefix
+ *     length sum(cumprod(draft == posterior)), next staged token, commit of
+ *     1 + accept tokens and crop of the KV length ("dflash-mlx", "single-forward
+ *     verify" steps 6-9 and guarantees 2-3; "DFlash dual implementations", §3).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are DEVICE pointers owned by the caller unless a
+ *     comment says "host".  The library allocates no memory, never copies
+ *     between host and device and never synchronizes: work is enqueued on the
+ *     caller's stream and the call returns at once.
+ *   - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16).  Pointers must
+ *     be 16-byte aligned; innermost strides are 1 element; row strides given
+ *     explicitly must be multiples of 8 elements.
+ *   - Every argument is validated on the host BEFORE anything is launched.  On
+ *     any error nothing is enqueued and no output is touched.
+ *   - Workspaces are caller-owned device buffers of at least the size the
+ *     matching *_workspace_size() query returns.  A workspace must be
+ *     zero-filled once before its first use; every call returns the counters
+ *     it used to zero, so the buffer can be reused by later calls on the same
+ *     stream without clearing.  Calls that run concurrently (different streams)
+ *     need distinct workspaces.
+ *   - Word 0 of every workspace is a sticky device-side error mask
+ *     (DFLASH_DEVERR_*): data-dependent faults found by the kernels (a context
+ *     length, page id or row position out of range) are clamped or skipped so
+ *     no access leaves its buffer, and the fault is OR-ed into this word.  The
+ *     library never clears it; the caller may read and reset it.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define DFLASH_OK               0
+#define DFLASH_ERR_NULL        -1  /* a required pointer is NULL */
+#define DFLASH_ERR_SHAPE       -2  /* a size is out of range or inconsistent */
+#define DFLASH_ERR_ALIGN       -3  /* a pointer or stride is misaligned */
+#define DFLASH_ERR_WORKSPACE   -4  /* workspace missing or too small */
+#define DFLASH_ERR_CAPACITY    -5  /* cache or RoPE table too small for the request */
+#define DFLASH_ERR_UNSUPPORTED -6  /* current device is not gfx950, or a size has no kernel */
+#define DFLASH_ERR_LAUNCH      -7  /* the HIP runtime reported an error at launch */
+
+/* ---- device-side error bits (workspace word 0) ------------------------- */
+#define DFLASH_DEVERR_CTX_LEN   1u  /* ctx_len[b] < 0 or > max_ctx_len (clamped) */
+#define DFLASH_DEVERR_PAGE_ID   2u  /* page-table entry < 0 or >= num_pages (page 0 read instead) */
+#define DFLASH_DEVERR_ROW       4u  /* row_seq / row_pos out of range (row's cache write skipped) */
+
+/* Block of draft tokens: the staged token plus 15 mask slots
+ * ("dflash-mlx", "block-diffusion draft"). */
+#define DFLASH_BLOCK 16
+
+/* Shapes of the draft attention.  A context cache is either
+ *   dense: k_cache / v_cache [batch][n_kv_heads][kv_capacity][head_dim] bf16, or
+ *   paged: k_cache / v_cache [num_pages][n_kv_heads][page_size][head_dim] bf16
+ *          with page_table [batch][kv_capacity] int32 (page ids; token t of
+ *          sequence b lives in page page_table[b][t / page_size], row t % page_size). */
+typedef struct dflash_dims {
+    int32_t batch;         /* B >= 1 sequences                                   */
+    int32_t block;         /* tokens per draft block; must be DFLASH_BLOCK (16)  */
+    int32_t n_q_heads;     /* Hq; a multiple of n_kv_heads, Hq / Hkv in [1, 8]    */
+    int32_t n_kv_heads;    /* Hkv >= 1                                           */
+    int32_t head_dim;      /* d: 64 or 128                                       */
+    int32_t hidden;        /* D: draft hidden size, width of the context feature */
+    int32_t page_size;     /* 0 = dense cache, 16 = paged cache                  */
+    int32_t kv_capacity;   /* dense: token rows per (seq, kv head);
+                              paged: page-table columns per sequence             */
+    int32_t num_pages;     /* paged: pages in the pool; dense: ignored           */
+    float   softmax_scale; /* <= 0 selects 1/sqrt(head_dim)                      */
+} dflash_dims;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* dflash_status_str(int status);
+
+/* ABI version: (major << 16) | minor. */
+int dflash_version(void);
+
+/* ---- RoPE tables --------------------------------------------------------
+ * cos_out / sin_out [max_pos][head_dim/2] fp32, device.  Entry (p, j) holds
+ * cos / sin of p * base^(-2j/head_dim), computed in double precision and
+ * rounded to fp32 (rotary embedding reused from Qwen3, "DFlash dual
+ * implementations" §1).  head_dim even in [2, 256], max_pos >= 1, base > 1. */
+int dflash_rope_tables(float base, int32_t head_dim, int32_t max_pos,
+                       float* cos_out, float* sin_out, hipStream_t stream);
+
+/* ---- context projection (a1-a3) -----------------------------------------
+ * For every row r < n_rows of target hidden states:
+ *   X_cat[r] = [x_layers[0][r] | ... | x_layers[n_layers-1][r]]   (n_layers*d_target)
+ *   C[r]     = bf16(X_cat[r] W_fc^T)                               (hidden)
+ *   K[r]     = bf16(RoPE(C[r] W_k^T, row_pos[r])),  V[r] = bf16(C[r] W_v^T)
+ * and K[r], V[r] (n_kv_heads x head_dim each) are written to the context cache
+ * of sequence row_seq[r] at token position row_pos[r].  Rows with row_pos < 0
+ * are computed but not written (uncommitted block slots).  fp32 accumulation.
+ *
+ *   x_layers   HOST array of n_layers (1..8) device pointers, each [n_rows][ld_x] bf16
+ *   d_target   width of each target layer (multiple of 64); ld_x >= d_target, % 8 == 0
+ *   row_seq    [n_rows] int32 in [0, batch);  row_pos [n_rows] int32
+ *   w_fc       [hidden][n_layers*d_target] bf16 (nn.Linear layout); NULL means the
+ *              rows already are C: then n_layers must be 1, d_target == hidden and
+ *              c_out NULL
+ *   w_k, w_v   [n_kv_heads*head_dim][hidden] bf16
+ *   rope_*     tables from dflash_rope_tables (max_pos rows)
+ *   c_out      optional [n_rows][hidden] bf16 copy of C (NULL = not stored)
+ *   k_cache, v_cache, page_table: the context cache described by dims
+ * A row whose row_seq or row_pos exceeds the cache, or whose row_pos >= max_pos,
+ * is skipped and DFLASH_DEVERR_ROW is set.  hidden % 64 == 0. */
+size_t dflash_ctx_proj_workspace_size(const dflash_dims* dims, int32_t n_rows,
+                                      int32_t n_layers, int32_t d_target);
+int dflash_ctx_proj(const dflash_dims* dims, int32_t n_rows,
+                    const void* const* x_layers, int32_t n_layers, int32_t d_target,
+                    int64_t ld_x, const int32_t* row_seq, const int32_t* row_pos,
+                    const void* w_fc, const void* w_k, const void* w_v,
+                    const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                    void* c_out, void* k_cache, void* v_cache, const int32_t* page_table,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- dual-source block attention (a4-a6) ---------------------------------
+ * For sequence b with L = ctx_len[b] committed context tokens and q head h
+ * (kv head g = h / (Hq/Hkv)), block rows i = 0..15 sit at positions L + i:
+ *   Q   = bf16(RoPE(q_blk[b,i,h]))                                 [16, d]
+ *   Keys= [ K_cache[b,g,0:L] ; bf16(RoPE(k_blk[b,:,g])) ]          [L+16, d]
+ *   Vals= [ V_cache[b,g,0:L] ; v_blk[b,:,g] ]
+ *   out[b,i,h,:] = softmax(Q Keys^T * scale) Vals   over all L+16 keys, no mask.
+ * bf16 operands, fp32 accumulation, fp32 output.
+ *
+ *   q_blk   [B][16][Hq][d] bf16, before RoPE
+ *   k_blk   [B][16][Hkv][d] bf16, before RoPE;  v_blk [B][16][Hkv][d] bf16
+ *   k_cache, v_cache, page_table: context cache (K already rotated), see dims
+ *   ctx_len [B] int32 device; max_ctx_len: host bound >= every ctx_len[b]
+ *           (dense: <= kv_capacity; paged: <= kv_capacity*page_size)
+ *   rope_*  tables with max_pos >= max_ctx_len + 16
+ *   out     [B][16][Hq][d] fp32 */
+size_t dflash_block_attn_workspace_size(const dflash_dims* dims, int32_t max_ctx_len);
+int dflash_block_attn(const dflash_dims* dims, const void* q_blk, const void* k_blk,
+                      const void* v_blk, const void* k_cache, const void* v_cache,
+                      const int32_t* page_table, const int32_t* ctx_len, int32_t max_ctx_len,
+                      const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                      float* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- greedy verify, accept, commit and crop (a7-a9) ----------------------
+ * For each sequence b (block == 16):
+ *   posterior[b,i] = lowest index of the maximum of logits[b,i,0:vocab]
+ *                    (NaN ranks above every number; -0 == +0)
+ *   accept_len[b]  = sum_i cumprod_i(block_tokens[b,i+1] == posterior[b,i]),  i < 15
+ *   next_token[b]  = posterior[b, accept_len[b]]        (the next staged token)
+ *   kv_len_out[b]  = kv_len_in[b] + 1 + accept_len[b]   (staged + accepted drafts)
+ *   commit_pos[b,i]= kv_len_in[b] + i if i <= accept_len[b] else -1   (optional)
+ *   n_pages[b]     = ceil(kv_len_out[b] / page_size)     (optional, page_size > 0)
+ *
+ *   logits       [B][16][ld_logits] bf16, ld_logits >= vocab, ld_logits % 8 == 0
+ *   block_tokens [B][16] int32: staged token then drafts d_1..d_15
+ *   kv_len_in    [B] int32 committed length before the block; kv_len_out may alias it
+ *   posterior [B][16], accept_len [B], next_token [B], kv_len_out [B]: int32 outputs
+ *   commit_pos   [B][16] int32 or NULL;  n_pages [B] int32 or NULL (needs page_size > 0)
+ * vocab in [1, 2^31 - 1).  Results are bit-exact and independent of launch shape. */
+size_t dflash_verify_workspace_size(int32_t batch, int32_t block, int32_t vocab);
+int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab,
+                         const void* logits, int64_t ld_logits, const int32_t* block_tokens,
+                         const int32_t* kv_len_in, int32_t* posterior, int32_t* accept_len,
+                         int32_t* next_token, int32_t* kv_len_out, int32_t* commit_pos,
+                         int32_t page_size, int32_t* n_pages,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

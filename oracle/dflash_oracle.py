@@ -29,6 +29,9 @@ feature C held in bf16; rotate-half RoPE with base 1e6 applied to Q and K
 only; softmax scale d^-1/2; q head h uses kv head floor(h/G); block Q and K are
 rounded to bf16 after RoPE, ctx K/V are bf16 in the cache; argmax takes the
 lowest index among equal maxima, NaN ranks above everything, -0 == +0.
+The bf16 rounding of the rotated block Q / K is a quantisation decision and is
+taken in the kernel's precision (float32 tables, float32 products and sums, no
+fused multiply-add); everything else is float64.
 
 Parity note: the projection/norm/RoPE structure of the real draft model is not
 fixed by the pages; the oracle pins the method *under the readings above*.
@@ -109,6 +112,25 @@ def apply_rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
 
 
+def rope_to_bf16(x_bits: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """bf16(RoPE(x)) for bf16 inputs x[..., n, H, d], as float64 values.
+
+    Rounding to bf16 is a quantisation decision, so it is taken in the precision
+    the kernel computes it in: cos / sin of the float64 angle rounded to float32,
+    then, per pair, fl32(fl32(x_j c) - fl32(x_{j+d/2} s)) and
+    fl32(fl32(x_{j+d/2} c) + fl32(x_j s)) -- every product and sum rounded to
+    float32, no fused multiply-add -- then round-to-nearest-even to bf16.
+    """
+    x = bf16_to_f64(x_bits).astype(np.float32)   # exact
+    d = x.shape[-1]
+    th = rope_angles(pos, d, base)
+    c = np.cos(th).astype(np.float32)[:, None, :]
+    s = np.sin(th).astype(np.float32)[:, None, :]
+    lo, hi = x[..., : d // 2], x[..., d // 2:]
+    y = np.concatenate([(lo * c) - (hi * s), (hi * c) + (lo * s)], axis=-1)  # float32 ops
+    return round_bf16(y.astype(np.float64))
+
+
 # --------------------------------------------------------------------------
 # a1-a3: context feature, projection to K/V, RoPE, cache rows
 # (page "DFlash dual implementations" §4: select target layers by id and
@@ -167,7 +189,8 @@ def block_attn_unit_ref(q_b: np.ndarray, k_b: np.ndarray, v_b: np.ndarray,
       Keys  = [K_ctx[0:L] ; bf16(RoPE(k_blk[:, g]))] [L+16, d]
       Vals  = [V_ctx[0:L] ; v_blk[:, g]]
       S = Q_h Keys^T * scale,  P = softmax over all L+16 keys (no mask),  O = P Vals.
-    Returns O [16, group, d] float64 (and P [group, 16, L+16] if asked).
+    The bf16 roundings of the rotated block rows follow ``rope_to_bf16``; the
+    rest is float64.  Returns O [16, group, d] (and P [group, 16, L+16] if asked).
     """
     d = q_b.shape[-1]
     if scale is None:
@@ -175,8 +198,8 @@ def block_attn_unit_ref(q_b: np.ndarray, k_b: np.ndarray, v_b: np.ndarray,
     L = int(ctx_len)
     pos = L + np.arange(BLOCK)
     hs = slice(g * group, (g + 1) * group)
-    Q = round_bf16(apply_rope(bf16_to_f64(q_b[:, hs, :]), pos, base))          # [16, G, d]
-    Kblk = round_bf16(apply_rope(bf16_to_f64(k_b[:, g:g + 1, :]), pos, base))[:, 0, :]
+    Q = rope_to_bf16(q_b[:, hs, :], pos, base)                                   # [16, G, d]
+    Kblk = rope_to_bf16(k_b[:, g:g + 1, :], pos, base)[:, 0, :]
     Keys = np.concatenate([bf16_to_f64(k_ctx[:L]), Kblk], axis=0)
     Vals = np.concatenate([bf16_to_f64(v_ctx[:L]), bf16_to_f64(v_b[:, g, :])], axis=0)
     out = np.empty((BLOCK, group, d))
@@ -302,6 +325,21 @@ def rope_brute(vec: Sequence[float], pos: int, base: float) -> List[float]:
     return out
 
 
+def rope_brute_bf16(vec: Sequence[float], pos: int, base: float) -> List[float]:
+    """Scalar twin of ``rope_to_bf16`` for one bf16-valued vector: float32 scalar steps."""
+    d = len(vec)
+    h = d // 2
+    f32 = np.float32
+    out = [0.0] * d
+    for j in range(h):
+        th = pos * base ** (-2.0 * j / d)
+        c, s = f32(math.cos(th)), f32(math.sin(th))
+        a, b = f32(vec[j]), f32(vec[j + h])
+        out[j] = float(f32(f32(a * c) - f32(b * s)))
+        out[j + h] = float(f32(f32(b * c) + f32(a * s)))
+    return [float(v) for v in round_bf16(np.array(out))]
+
+
 def block_attn_brute(q_b, k_b, v_b, k_ctx, v_ctx, ctx_len: int, g: int, group: int,
                      base: float, scale: Optional[float] = None) -> np.ndarray:
     """Scalar-loop twin of ``block_attn_unit_ref`` (same arguments), for tiny shapes."""
@@ -314,13 +352,13 @@ def block_attn_brute(q_b, k_b, v_b, k_ctx, v_ctx, ctx_len: int, g: int, group: i
         keys.append(f(k_ctx[t]))
         vals.append(f(v_ctx[t]))
     for i in range(BLOCK):
-        keys.append([float(t) for t in round_bf16(np.array(rope_brute(f(k_b[i, g]), L + i, base)))])
+        keys.append(rope_brute_bf16(f(k_b[i, g]), L + i, base))
         vals.append(f(v_b[i, g]))
     out = np.zeros((BLOCK, group, d))
     for hh in range(group):
         h = g * group + hh
         for i in range(BLOCK):
-            q = [float(t) for t in round_bf16(np.array(rope_brute(f(q_b[i, h]), L + i, base)))]
+            q = rope_brute_bf16(f(q_b[i, h]), L + i, base)
             sc = [sum(q[c] * key[c] for c in range(d)) * scale for key in keys]
             m = max(sc)
             w = [math.exp(s - m) for s in sc]

@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+public header declares, sizes workspaces, and rejects bad arguments on the host
+before any HIP call (so nothing is launched and no output is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from block_diffusion_draft_proj_amd import dflash as dfl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+# Validation-failure calls below pass fake (but aligned) addresses; they must never
+# reach a device.  On a machine with a GPU a test bug could launch on them, so
+# these run only where no device is visible.
+no_device = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="host-only validation tests")
+
+FAKE = ctypes.c_void_p(0x100000)
+MIS = ctypes.c_void_p(0x100008)  # 8-byte aligned, not 16
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) == 9, names
+    lib = ctypes.CDLL(dfl.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(dfl.EXPORTS) == names
+
+
+def test_status_strings_and_version():
+    assert dfl.dflash_status_str(0) == "ok"
+    for code in range(-7, 0):
+        s = dfl.dflash_status_str(code)
+        assert s and s != "unknown status"
+    assert dfl.dflash_status_str(-99) == "unknown status"
+    assert dfl.dflash_version() >> 16 == 1
+
+
+def test_workspace_sizes():
+    v = dfl.dflash_verify_workspace_size(8, 16, 151936)
+    n_chunks = -(-151936 // 8192)
+    assert v == 256 + 256 + 8 * 8 * 16 * n_chunks
+    assert dfl.dflash_verify_workspace_size(0, 16, 10) == 0
+    assert dfl.dflash_verify_workspace_size(1, 15, 10) == 0
+    dims = dfl.make_dims(8, 32, 8, 128, hidden=4096, kv_capacity=8208)
+    a = dfl.dflash_block_attn_workspace_size(dims, 8192)
+    assert a > 8 * 8 * 4 and a % 256 == 0
+    assert dfl.dflash_block_attn_workspace_size(dims, 16384) >= a
+    bad = dfl.make_dims(8, 30, 8, 128, kv_capacity=8208)
+    assert dfl.dflash_block_attn_workspace_size(bad, 8192) == 0
+    p = dfl.dflash_ctx_proj_workspace_size(dims, 128, 5, 4096)
+    assert p > 128 * 4096 * 2
+    assert dfl.dflash_ctx_proj_workspace_size(dims, 0, 5, 4096) > 0
+
+
+def _attn(dims, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, pt=None, ctx=FAKE, maxc=64, cos=FAKE, sin=FAKE,
+             maxpos=128, out=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return dfl._lib.dflash_block_attn(ctypes.byref(dims), a["q"], a["k"], a["v"], a["kc"], a["vc"], a["pt"],
+                                      a["ctx"], a["maxc"], a["cos"], a["sin"], a["maxpos"], a["out"], a["ws"],
+                                      a["wsb"], None)
+
+
+@no_device
+def test_block_attn_rejects_bad_arguments():
+    good = dfl.make_dims(2, 8, 2, 64, kv_capacity=80)
+    assert _attn(dfl.make_dims(0, 8, 2, 64, kv_capacity=80)) == -2
+    assert _attn(dfl.make_dims(2, 8, 3, 64, kv_capacity=80)) == -2           # Hq % Hkv
+    assert _attn(dfl.make_dims(2, 18, 2, 64, kv_capacity=80)) == -6          # group 9
+    assert _attn(dfl.make_dims(2, 8, 2, 96, kv_capacity=80)) == -6           # head_dim
+    assert _attn(dfl.make_dims(2, 8, 2, 64, page_size=8, kv_capacity=80)) == -6
+    d = dfl.make_dims(2, 8, 2, 64, kv_capacity=80)
+    d.block = 15
+    assert _attn(d) == -2
+    assert _attn(good, q=ctypes.c_void_p(None)) == -1
+    assert _attn(good, ctx=ctypes.c_void_p(None)) == -1
+    assert _attn(good, q=MIS) == -3
+    assert _attn(good, maxc=81) == -5                                          # beyond capacity
+    assert _attn(good, maxc=64, maxpos=79) == -5                               # RoPE table short
+    assert _attn(good, maxc=-1) == -2
+    assert _attn(good, ws=ctypes.c_void_p(None)) == -4
+    assert _attn(good, wsb=16) == -4
+    paged = dfl.make_dims(2, 8, 2, 64, page_size=16, kv_capacity=5, num_pages=10)
+    assert _attn(paged) == -1                                                  # no page table
+    assert _attn(paged, pt=FAKE, maxc=81) == -5                                # 5 pages * 16 = 80
+
+
+def _verify(**kw):
+    a = dict(B=2, blk=16, V=1000, logits=FAKE, ld=1000, bt=FAKE, kvi=FAKE, post=FAKE, acc=FAKE, nxt=FAKE,
+             kvo=FAKE, cp=None, ps=0, npg=None, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return dfl._lib.dflash_verify_accept(a["B"], a["blk"], a["V"], a["logits"], a["ld"], a["bt"], a["kvi"],
+                                         a["post"], a["acc"], a["nxt"], a["kvo"], a["cp"], a["ps"], a["npg"],
+                                         a["ws"], a["wsb"], None)
+
+
+@no_device
+def test_verify_rejects_bad_arguments():
+    assert _verify(B=0) == -2
+    assert _verify(blk=8) == -2
+    assert _verify(V=0) == -2
+    assert _verify(ld=999) == -2
+    assert _verify(ld=1004) == -3             # row stride not a multiple of 8
+    assert _verify(logits=MIS) == -3
+    assert _verify(post=ctypes.c_void_p(None)) == -1
+    assert _verify(npg=FAKE, ps=0) == -2      # page count needs a page size
+    assert _verify(ws=ctypes.c_void_p(None)) == -4
+    assert _verify(wsb=100) == -4
+    assert _verify(ws=MIS) == -3
+
+
+def _proj(dims, n_layers=2, **kw):
+    xs = (ctypes.c_void_p * 8)(*([0x100000] * 8))
+    a = dict(n=32, xs=xs, nl=n_layers, dt=256, ld=256, seq=FAKE, pos=FAKE, wfc=FAKE, wk=FAKE, wv=FAKE,
+             cos=FAKE, sin=FAKE, maxpos=128, cout=None, kc=FAKE, vc=FAKE, pt=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return dfl._lib.dflash_ctx_proj(ctypes.byref(dims), a["n"], a["xs"], a["nl"], a["dt"], a["ld"], a["seq"],
+                                    a["pos"], a["wfc"], a["wk"], a["wv"], a["cos"], a["sin"], a["maxpos"],
+                                    a["cout"], a["kc"], a["vc"], a["pt"], a["ws"], a["wsb"], None)
+
+
+@no_device
+def test_ctx_proj_rejects_bad_arguments():
+    dims = dfl.make_dims(1, 4, 2, 64, hidden=256, kv_capacity=80)
+    assert _proj(dims, dt=100) == -2                    # d_target not a multiple of 64
+    assert _proj(dims, nl=9) == -2
+    assert _proj(dims, nl=0) == -2
+    assert _proj(dims, ld=128) == -2                    # ld < d_target
+    assert _proj(dims, ld=260) == -3                    # ld % 8
+    assert _proj(dims, n=-1) == -2
+    assert _proj(dims, wk=ctypes.c_void_p(None)) == -1
+    assert _proj(dims, wfc=ctypes.c_void_p(None)) == -2  # no fc needs 1 layer of width hidden
+    assert _proj(dims, wk=MIS) == -3
+    assert _proj(dims, ws=ctypes.c_void_p(None)) == -4
+    assert _proj(dims, wsb=64) == -4
+    assert _proj(dims, maxpos=0) == -5
+    xs = (ctypes.c_void_p * 8)(*([0x100000] + [0] * 7))
+    assert _proj(dims, xs=xs) == -1                     # second layer pointer NULL
+    h = dfl.make_dims(1, 4, 2, 64, hidden=200, kv_capacity=80)
+    assert _proj(h) == -2                               # hidden % 64
+    paged = dfl.make_dims(1, 4, 2, 64, hidden=256, page_size=16, kv_capacity=5, num_pages=4)
+    assert _proj(paged) == -1                           # page table missing

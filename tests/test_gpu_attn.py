@@ -1,0 +1,119 @@
+"""GPU parity of dflash_block_attn against the oracle (max-abs error <= 2e-2 on
+fp32 outputs, bf16 operands): small shapes spanning several key tiles, ragged
+tails, split boundaries, every group size and both head dims, dense and paged
+caches; the five workload configurations at full size (all units, or a spread
+sample of units for the ragged batch); determinism and device-side error flags."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from block_diffusion_draft_proj_amd import dflash as dfl
+from block_diffusion_draft_proj_amd import synth
+from oracle import dflash_oracle as orc
+from tests.gpu_util import DEV, log, run_block_attn
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _paged_copy(at: synth.AttnInputs, seed=0) -> synth.AttnInputs:
+    """Same logical cache content in a shuffled 16-token page layout."""
+    B, Hkv, cap, d = at.k_cache.shape
+    width = (cap + 15) // 16
+    perm = np.random.default_rng(seed).permutation(B * width).astype(np.int32)
+    table = perm.reshape(B, width)
+    kp = np.zeros((B * width, Hkv, 16, d), np.uint16)
+    vp = np.zeros_like(kp)
+    for b in range(B):
+        for p in range(width):
+            t0, t1 = p * 16, min(cap, p * 16 + 16)
+            kp[table[b, p], :, :t1 - t0] = at.k_cache[b, :, t0:t1]
+            vp[table[b, p], :, :t1 - t0] = at.v_cache[b, :, t0:t1]
+    return dataclasses.replace(at, k_cache=kp, v_cache=vp, page_table=table, capacity=width,
+                               num_pages=B * width)
+
+
+def _check(cfg, at, units=None, tol=TOL, label=""):
+    out, ws = run_block_attn(cfg, at)
+    got = out.cpu().numpy()
+    ref = orc.block_attn_ref(at.q_blk, at.k_blk, at.v_blk, at.k_cache, at.v_cache, at.ctx_len, cfg.rope_base,
+                             page_table=at.page_table, units=units)
+    mask = ~np.isnan(ref)
+    err = float(np.max(np.abs(got[mask] - ref[mask])))
+    log(f"attn {label}: max-abs err {err:.3e}")
+    assert np.all(np.isfinite(got)), "non-finite output"
+    assert err <= tol, err
+    assert ws[:4].cpu().numpy().view(np.uint32)[0] == 0
+    return got, err
+
+
+SMALL = [  # (L per sequence, Hq, Hkv, d)
+    ([0], 4, 2, 64), ([1], 4, 2, 64), ([15, 16], 4, 2, 64), ([63, 64, 65], 4, 4, 128),
+    ([100, 7], 8, 2, 128), ([300], 3, 1, 64), ([257, 255, 256], 5, 1, 128), ([1000, 0], 8, 1, 64),
+    ([130], 6, 2, 128), ([700, 513], 7, 1, 128), ([64], 1, 1, 128), ([777, 33], 32, 8, 128),
+]
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"L{c[0]}_h{c[1]}x{c[2]}_d{c[3]}")
+def test_attn_small_shapes(case, paged):
+    lens, hq, hkv, d = case
+    cfg = dataclasses.replace(synth.CONFIGS["qwen3_8b"], n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                              seed=hash((tuple(lens), hq, hkv, d)) & 0xFFFF)
+    at = synth.attn_inputs(cfg, ctx_len=np.array(lens), page_size=0)
+    if paged:
+        at = _paged_copy(at, seed=len(lens))
+    _check(cfg, at, label=f"small {case} paged={paged}")
+
+
+def test_attn_split_boundaries_and_many_splits():
+    # 6 units over <= 4097 keys split into 256-key pieces (the plan's minimum):
+    # 16 full splits, 16 full + a 1-key split, and a 255-key last split.
+    cfg = dataclasses.replace(synth.CONFIGS["qwen3_8b"], n_q_heads=8, n_kv_heads=2)
+    at = synth.attn_inputs(cfg, ctx_len=np.array([4096, 4097, 4095]))
+    _check(cfg, at, label="split boundaries around multiples of 256")
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b", "batched", "long_ctx"])
+def test_attn_full_size(name):
+    cfg = synth.CONFIGS[name]
+    log(f"attn full {name}: generating inputs")
+    at = synth.attn_inputs(cfg)
+    _check(cfg, at, label=f"full {name}")
+
+
+def test_attn_ragged_paged_full_size_sampled():
+    cfg = synth.CONFIGS["ragged"]
+    log("attn ragged: generating inputs")
+    at = synth.attn_inputs(cfg)
+    order = np.argsort(at.ctx_len)
+    bs = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] + list(range(0, 32, 5))))
+    units = [(b, g) for b in bs for g in (0, cfg.n_kv_heads - 1)]
+    _check(cfg, at, units=units, label=f"ragged sampled {len(units)} units, L {at.ctx_len.min()}..{at.ctx_len.max()}")
+
+
+def test_attn_deterministic():
+    cfg = synth.CONFIGS["batched"]
+    at = synth.attn_inputs(cfg, ctx_len=np.array([8192, 3000, 17, 5000]))
+    a, ws = run_block_attn(cfg, at)
+    b, _ = run_block_attn(cfg, at, ws=ws)
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+
+
+def test_attn_device_error_flags_clamp_without_fault():
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], batch=2)
+    at = synth.attn_inputs(cfg, ctx_len=np.array([40, 64]))
+    # ctx_len beyond max_ctx_len: clamped to max_ctx_len, flag raised
+    out, ws = run_block_attn(cfg, at, max_ctx=64, ctx_len_override=np.array([40, 90], np.int32))
+    assert ws[:4].cpu().numpy().view(np.uint32)[0] & dfl.DEVERR_CTX_LEN
+    ref = orc.block_attn_ref(at.q_blk, at.k_blk, at.v_blk, at.k_cache, at.v_cache, np.array([40, 64]),
+                             cfg.rope_base)
+    assert np.max(np.abs(out.cpu().numpy() - ref)) <= TOL
+    # a page id outside the pool: page 0 is read instead and the flag is raised
+    pat = _paged_copy(synth.attn_inputs(cfg, ctx_len=np.array([40, 64])))
+    pat.page_table[1, 1] = pat.num_pages + 5
+    out, ws = run_block_attn(cfg, pat)
+    assert ws[:4].cpu().numpy().view(np.uint32)[0] & dfl.DEVERR_PAGE_ID
+    assert np.all(np.isfinite(out.cpu().numpy()))

@@ -1,0 +1,188 @@
+"""GPU parity of dflash_ctx_proj against the oracle.
+
+Tolerance (derived from the arithmetic): the cache holds bf16(K) and bf16(V); the
+oracle's K/V are exact (float64) functions of the bf16-rounded context feature C.
+The GPU accumulates in fp32, so (a) its C differs from the oracle's C by one bf16
+step wherever the exact C lies within fp32 accumulation error of a rounding
+midpoint (a few entries in 10^4), and each such flip moves the K/V entries of
+that row by ulp(C_i) * |W[o, i]| <= 2^-7 |C_i| |W[o, i]|, which at 4-sigma C and
+W is up to 0.125/sqrt(hidden) of rms(K) -- 6e-3 rms at hidden 256; (b) its final
+rounding of K/V can land one ulp off where the fp32 result straddles a bf16
+midpoint.  Hence per element |gpu - ref| <= 1 ulp_bf16(ref) + 6e-3 * rms(ref);
+the normwise relative error must stay <= 4e-3 (bf16 rounding alone gives
+~1.6e-3), and at least 99% of entries must be within half an ulp plus 1e-4 rms
+(so the flip allowance cannot hide a systematic error).  Rows with a negative
+position must leave the cache untouched; the optional C copy must round the
+exact C to bf16 up to the same flips (on < 0.1% of entries).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_draft_proj_amd import dflash as dfl
+from block_diffusion_draft_proj_amd import synth
+from oracle import dflash_oracle as orc
+from tests.gpu_util import DEV, host_u16, i32, log, rope_tables, u16
+
+pytestmark = pytest.mark.gpu
+
+
+def ulp_bf16(x):
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def _close(got, ref, label):
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = np.abs(got - ref)
+    bound = ulp_bf16(ref) + 6e-3 * rms
+    worst = float(np.max(err / bound))
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    tight = float(np.mean(err <= 0.5 * ulp_bf16(ref) + 1e-4 * rms))
+    log(f"ctx_proj {label}: max err/bound {worst:.3f}, normwise rel {rel:.2e}, "
+        f"within half-ulp {100 * tight:.3f}%, rms {rms:.3f}")
+    assert worst <= 1.0, worst
+    assert rel <= 4e-3, rel
+    assert tight >= 0.99, tight
+
+
+def _commit_positions(kv_len, rng):
+    B = len(kv_len)
+    pos = np.full((B, 16), -1, np.int32)
+    for b in range(B):
+        a = int(rng.integers(0, 16))
+        pos[b, :a + 1] = kv_len[b] + np.arange(a + 1)
+    return pos.reshape(-1)
+
+
+def _run(cfg, n_rows, row_seq, row_pos, capacity, paged_table=None, num_pages=0, with_fc=True,
+         c_out=True, seed=None):
+    pj = synth.ctx_proj_inputs(cfg, n_rows, seed=seed)
+    Hkv, d, D = cfg.n_kv_heads, cfg.head_dim, cfg.hidden
+    B = cfg.batch
+    if paged_table is None:
+        kc = torch.zeros(B, Hkv, capacity, d, dtype=torch.int16, device=DEV)
+        dims = dfl.make_dims(B, cfg.n_q_heads, Hkv, d, hidden=D, kv_capacity=capacity)
+    else:
+        kc = torch.zeros(num_pages, Hkv, 16, d, dtype=torch.int16, device=DEV)
+        dims = dfl.make_dims(B, cfg.n_q_heads, Hkv, d, hidden=D, page_size=16,
+                             kv_capacity=paged_table.shape[1], num_pages=num_pages)
+    vc = torch.zeros_like(kc)
+    max_pos = int(max(np.max(row_pos), 0)) + 32
+    cos, sin = rope_tables(d, max_pos, cfg.rope_base)
+    if with_fc:
+        xs, wfc, n_layers, dt = pj.x_layers, pj.w_fc, cfg.n_target_layers, cfg.target_hidden
+    else:  # the rows already are the context feature C
+        xs = [synth.normal_bf16(synth.streams(7)["x_ctx"], (n_rows, D), 2.86)]
+        wfc, n_layers, dt = None, 1, D
+    ws = dfl.workspace(dfl.dflash_ctx_proj_workspace_size(dims, n_rows, n_layers, dt), DEV)
+    cbuf = torch.zeros(n_rows, D, dtype=torch.int16, device=DEV) if (c_out and with_fc) else None
+    log(f"ctx_proj {cfg.name}: M={n_rows} K={n_layers * dt} D={D} paged={paged_table is not None}")
+    dfl.dflash_ctx_proj(dims, [u16(x) for x in xs], i32(row_seq), i32(row_pos),
+                        None if wfc is None else u16(wfc), u16(pj.w_k), u16(pj.w_v), cos, sin, cbuf, kc, vc,
+                        None if paged_table is None else i32(paged_table), ws)
+    torch.cuda.synchronize()
+    if with_fc:
+        ref = orc.ctx_proj_ref(xs, wfc, pj.w_k, pj.w_v, row_pos, Hkv, d, cfg.rope_base)
+    else:
+        eye = orc.f64_to_bf16_bits(np.eye(D))
+        ref = orc.ctx_proj_ref(xs, eye, pj.w_k, pj.w_v, row_pos, Hkv, d, cfg.rope_base)
+    err = int(ws[:4].cpu().numpy().view(np.uint32)[0])
+    return ref, host_u16(kc), host_u16(vc), (None if cbuf is None else host_u16(cbuf)), err
+
+
+def _gather_rows(cache, row_seq, row_pos, table=None):
+    """[n_live, Hkv, d] cache rows at the committed (seq, pos) of each live row."""
+    live = np.nonzero(row_pos >= 0)[0]
+    rows = []
+    for m in live:
+        s, p = int(row_seq[m]), int(row_pos[m])
+        rows.append(cache[s, :, p] if table is None else cache[table[s, p // 16], :, p % 16])
+    return live, orc.bf16_to_f64(np.stack(rows))
+
+
+def _check(cfg, n_rows, row_seq, row_pos, capacity, table=None, num_pages=0, with_fc=True, label=""):
+    ref, kc, vc, cb, err = _run(cfg, n_rows, row_seq, row_pos, capacity, table, num_pages, with_fc)
+    assert err == 0
+    live, k = _gather_rows(kc, row_seq, row_pos, table)
+    _, v = _gather_rows(vc, row_seq, row_pos, table)
+    _close(k, ref["K"][live], label + " K")
+    _close(v, ref["V"][live], label + " V")
+    # only committed rows were written
+    written = np.count_nonzero(np.any(kc != 0, axis=-1))
+    assert written == len(live) * cfg.n_kv_heads
+    if cb is not None:
+        c = orc.bf16_to_f64(cb)
+        same = np.mean(c == ref["Cb"])
+        assert same >= 0.999, same
+        # half a bf16 step plus fp32 accumulation error; the latter scales with the
+        # running partial sums (~ rms(C)), not with |C|, so it dominates tiny entries
+        rms_c = float(np.sqrt(np.mean(ref["C"] ** 2)))
+        assert np.all(np.abs(c - ref["C"]) <= 0.5 * ulp_bf16(ref["C"]) + 1e-4 * rms_c)
+
+
+def test_ctx_proj_tiny_prefill_dense_and_paged():
+    cfg = synth.CONFIGS["tiny"]
+    n = 64
+    seq = np.zeros(n, np.int32)
+    pos = np.arange(n, dtype=np.int32)
+    _check(cfg, n, seq, pos, capacity=80, label="tiny prefill dense")
+    table = np.array([[3, 0, 4, 1, 2]], np.int32)
+    _check(cfg, n, seq, pos, capacity=0, table=table, num_pages=6, label="tiny prefill paged")
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b", "batched", "long_ctx"])
+def test_ctx_proj_committed_block_rows(name):
+    cfg = synth.CONFIGS[name]
+    kv_len = synth.context_lengths(cfg)
+    rng = np.random.default_rng(cfg.seed)
+    pos = _commit_positions(kv_len, rng)
+    seq = np.repeat(np.arange(cfg.batch, dtype=np.int32), 16)
+    _check(cfg, 16 * cfg.batch, seq, pos, capacity=int(kv_len.max()) + 16, label=f"{name} block rows")
+
+
+def test_ctx_proj_ragged_paged_block_rows():
+    cfg = synth.CONFIGS["ragged"]
+    at_len = synth.context_lengths(cfg)
+    rng = np.random.default_rng(11)
+    pos = _commit_positions(at_len, rng)
+    seq = np.repeat(np.arange(cfg.batch, dtype=np.int32), 16)
+    width = int((at_len.max() + 16 + 15) // 16)
+    # Only the pages holding committed rows are backed (a shuffled pool); the
+    # kernel reads the table only at those rows.
+    need = sorted({(int(s), int(p) // 16) for s, p in zip(seq, pos) if p >= 0})
+    perm = rng.permutation(len(need)).astype(np.int32)
+    table = np.full((cfg.batch, width), -1, np.int32)
+    for (s, pg), phys in zip(need, perm):
+        table[s, pg] = phys
+    _check(cfg, 16 * cfg.batch, seq, pos, capacity=0, table=table, num_pages=len(need), label="ragged paged")
+
+
+def test_ctx_proj_prefill_chunk_with_ragged_row_tail():
+    cfg = dataclasses.replace(synth.CONFIGS["qwen3_8b"], n_target_layers=2)
+    n = 300
+    seq = np.zeros(n, np.int32)
+    pos = np.arange(n, dtype=np.int32) + 1000
+    pos[::7] = -1
+    _check(cfg, n, seq, pos, capacity=1400, label="prefill 300 rows")
+
+
+def test_ctx_proj_without_fc():
+    cfg = synth.CONFIGS["tiny"]
+    n = 40
+    seq = np.zeros(n, np.int32)
+    pos = np.arange(n, dtype=np.int32)
+    _check(cfg, n, seq, pos, capacity=80, with_fc=False, label="no fc")
+
+
+def test_ctx_proj_bad_rows_flagged_and_skipped():
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], batch=2)
+    n = 16
+    seq = np.array([0] * 8 + [5] * 8, np.int32)          # sequence 5 does not exist
+    pos = np.arange(n, dtype=np.int32)
+    pos[3] = 500                                          # beyond capacity
+    ref, kc, vc, cb, err = _run(cfg, n, seq, pos, capacity=80)
+    assert err & dfl.DEVERR_ROW
+    assert np.count_nonzero(np.any(kc != 0, axis=-1)) == 7 * cfg.n_kv_heads

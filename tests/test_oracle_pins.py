@@ -129,6 +129,58 @@ def test_rope_matches_scalar_brute_force():
             assert np.allclose(got[n, h], orc.rope_brute(list(x[n, h]), int(pos[n]), 1e6), atol=1e-12)
 
 
+def test_rope_to_bf16_matches_scalar_twin():
+    rng = np.random.default_rng(30)
+    xb = orc.f64_to_bf16_bits(rng.standard_normal((5, 2, 32)) * 2.0)
+    pos = np.array([0, 3, 999, 8191, 32767])
+    got = orc.rope_to_bf16(xb, pos, 1e6)
+    for n in range(5):
+        for h in range(2):
+            assert np.array_equal(got[n, h], orc.rope_brute_bf16(list(orc.bf16_to_f64(xb[n, h])), int(pos[n]), 1e6))
+
+
+@pytest.mark.parametrize("case", _golden("rope_cases.txt"), ids=lambda c: f"d{c['d']}p{c['pos']}j{c['j']}")
+def test_rope_to_bf16_closed_form_golden(case):
+    d, j, pos = case["d"], case["j"], case["pos"]
+    e = np.zeros((1, 1, d), np.uint16)
+    e[0, 0, j] = 0x3F80                                   # unit vector e_j
+    got = orc.rope_to_bf16(e, np.array([pos]), case["base"])[0, 0]
+    want = np.zeros(d)
+    want[j] = orc.round_bf16(np.array([float(np.float32(math.cos(case["theta"])))]))[0]
+    want[j + d // 2] = orc.round_bf16(np.array([float(np.float32(math.sin(case["theta"])))]))[0]
+    assert np.allclose(got, want, atol=1e-15, rtol=0)
+
+
+def test_rope_to_bf16_differs_from_exact_rounding_only_at_midpoints():
+    # The kernel-precision rounding equals bf16(exact RoPE) except where the exact
+    # value lies within float32 resolution of a bf16 rounding midpoint; there the
+    # two choices are adjacent bf16 values.
+    rng = np.random.default_rng(31)
+    xb = orc.f64_to_bf16_bits(rng.standard_normal((400, 8, 128)) * 1.3)
+    pos = rng.integers(0, 33000, 400)
+    a = orc.rope_to_bf16(xb, pos, 1e6)
+    x = orc.bf16_to_f64(xb)
+    exact = orc.apply_rope(x, pos, 1e6)
+    b = orc.round_bf16(exact)
+    # float32 evaluation error scales with the summed product magnitudes |x_j c| + |x_j' s|
+    th = orc.rope_angles(pos, 128, 1e6)[:, None, :]
+    lo, hi = np.abs(x[..., :64]), np.abs(x[..., 64:])
+    c, s = np.abs(np.cos(th)), np.abs(np.sin(th))
+    mag = np.concatenate([lo * c + hi * s, hi * c + lo * s], axis=-1)
+    diff = a != b
+    assert 0 < diff.sum() and diff.mean() < 1e-3
+    # everywhere: a is a bf16 value within half a bf16 step (of a) plus float32
+    # evaluation error of the exact rotation
+    half_step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(a), 2.0 ** -126))) - 8)
+    assert np.all(np.abs(a - exact) <= half_step + 2.0 ** -22 * mag)
+    # where the two roundings disagree, the exact value sits within float32 error of
+    # the boundary between them
+    ex, av, bv, mg = exact[diff], a[diff], b[diff], mag[diff]
+    boundary = np.where(np.abs(ex - av) < np.abs(ex - bv), av, bv)
+    assert np.all(np.abs(ex - (av + bv) / 2) <= 2.0 ** -22 * mg + np.abs(av - bv) / 2)
+    assert np.all(np.abs(ex - boundary) <= np.abs(av - bv))
+
+
 # ----------------------------------------------------------------------------- ctx projection
 def _tiny_proj(seed=0, M=3, nt=2, Dt=4, D=8, Hkv=2, d=4):
     rng = np.random.default_rng(seed)
@@ -243,7 +295,7 @@ def test_attn_two_level_logistic_closed_form():
     out = orc.block_attn_unit_ref(q, k, v, kc, vc, L, 0, 1, 1e6)
     ks = orc.bf16_to_f64(kstar)
     for i in range(16):
-        Qi = orc.round_bf16(np.array(orc.rope_brute(list(orc.bf16_to_f64(q[i, 0])), L + i, 1e6)))
+        Qi = np.array(orc.rope_brute_bf16(list(orc.bf16_to_f64(q[i, 0])), L + i, 1e6))
         s = float(Qi @ ks) / math.sqrt(d)
         want = 1.0 / (1.0 + (16.0 / L) * math.exp(-s))
         assert out[i, 0, 0] == pytest.approx(want, rel=1e-12)
@@ -304,8 +356,8 @@ def test_attn_matches_torch_sdpa_float64(L, G, Hkv, d):
     for b in range(B):
         Lb = int(ctx[b])
         pos = Lb + np.arange(16)
-        Q = orc.round_bf16(orc.apply_rope(orc.bf16_to_f64(q[b]), pos, 1e6))
-        Kb = orc.round_bf16(orc.apply_rope(orc.bf16_to_f64(k[b]), pos, 1e6))
+        Q = orc.rope_to_bf16(q[b], pos, 1e6)          # rotation rounding is pinned separately
+        Kb = orc.rope_to_bf16(k[b], pos, 1e6)
         K = np.concatenate([orc.bf16_to_f64(kc[b][:, :Lb]), Kb.transpose(1, 0, 2)], axis=1)
         Vv = np.concatenate([orc.bf16_to_f64(vc[b][:, :Lb]), orc.bf16_to_f64(v[b]).transpose(1, 0, 2)], axis=1)
         ref = torch.nn.functional.scaled_dot_product_attention(
