@@ -88,8 +88,7 @@ int dflash_rope_tables(float base, int32_t head_dim, int32_t max_pos, float* cos
 size_t dflash_verify_workspace_size(int32_t batch, int32_t block, int32_t vocab) {
   if (batch < 1 || block != DFLASH_BLOCK || vocab < 1) return 0;
   const size_t n_chunks = ((size_t)vocab + kVerifyChunk - 1) / kVerifyChunk;
-  const size_t counts = ((sizeof(uint32_t) * (size_t)batch) + 255) & ~(size_t)255;
-  return 256 + counts + sizeof(uint64_t) * (size_t)batch * DFLASH_BLOCK * n_chunks;
+  return 256 + sizeof(uint64_t) * (size_t)batch * DFLASH_BLOCK * n_chunks;
 }
 
 int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab, const void* logits, int64_t ld_logits,
@@ -111,7 +110,6 @@ int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab, const void
   int st = check_device();
   if (st != DFLASH_OK) return st;
   char* ws = static_cast<char*>(workspace);
-  const size_t counts = ((sizeof(uint32_t) * (size_t)batch) + 255) & ~(size_t)255;
   VerifyParams p{};
   p.logits = static_cast<const uint16_t*>(logits);
   p.ld = ld_logits;
@@ -126,8 +124,7 @@ int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab, const void
   p.commit_pos = commit_pos;
   p.n_pages = n_pages;
   p.page_size = page_size;
-  p.count = reinterpret_cast<uint32_t*>(ws + 256);
-  p.part = reinterpret_cast<uint64_t*>(ws + 256 + counts);
+  p.part = reinterpret_cast<uint64_t*>(ws + 256);
   return launch_status(launch_verify_accept(p, batch, stream));
 }
 
@@ -181,7 +178,6 @@ int dflash_block_attn(const dflash_dims* dims, const void* q_blk, const void* k_
   p.out = out;
   p.ws_o = reinterpret_cast<float*>(ws + pl.off_o);
   p.ws_ml = reinterpret_cast<float*>(ws + pl.off_ml);
-  p.count = reinterpret_cast<uint32_t*>(ws + pl.off_count);
   p.err = reinterpret_cast<uint32_t*>(ws);
   p.batch = dims->batch;
   p.n_q_heads = dims->n_q_heads;

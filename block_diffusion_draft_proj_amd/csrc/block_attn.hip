@@ -21,9 +21,11 @@
 //  * K and V^T tiles use XOR-swizzled 16-byte chunks: every 16-lane read group
 //    and every row-wide write touches distinct banks;
 //  * the context is split over workgroups (flash-decoding); each split keeps
-//    (max, sum, O) in the workspace and the last workgroup of the unit to
-//    arrive merges them (log-sum-exp), so there is one launch and no host work;
-//    all splits of a unit are placed on one XCD so their partials meet in one L2;
+//    (max, sum, O) in the workspace and a small second kernel merges them
+//    (log-sum-exp).  The kernel boundary is the handoff: merging inside the
+//    kernel would cost an L2 writeback (agent-scope release) per workgroup,
+//    measured at several times the merge itself.  All splits of a unit sit on
+//    one XCD, so their partials are written and re-read through one L2;
 //  * probabilities enter the PV product as a bf16 hi/lo pair (P = P_hi + P_lo),
 //    so the only rounding of operands is the bf16 storage of Q, K and V.
 #include <math.h>
@@ -224,7 +226,6 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
   constexpr int KS = D / 32, DT = D / 16, HALF = D / 2;
   __shared__ __attribute__((aligned(16))) char lds_k[TK * D * 2];
   __shared__ __attribute__((aligned(16))) char lds_v[D * TK * 2];
-  __shared__ uint32_t s_last;
 
   // XCD-aware decode: WG i runs on XCD i % 8; every split of a unit shares one XCD.
   const int i_wg = blockIdx.x;
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
     return;
   }
 
-  // Split partials, then the last arriving workgroup of the unit merges them.
+  // Split partials; attn_merge_kernel combines them after this kernel.
   const int64_t slot = ((int64_t)u * p.n_splits + s) * G + w;
   float* po = p.ws_o + slot * (DT * 256);
 #pragma unroll
@@ -344,16 +345,22 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
     p.ws_ml[(slot * 16 + r) * 2 + 0] = m;
     p.ws_ml[(slot * 16 + r) * 2 + 1] = lt;
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(p.count + u, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (uint32_t)(ns - 1)) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
+// Log-sum-exp merge of the split partials of one unit: wave w = query head
+// g*G + w, lane = (row r, dims 4q..4q+3 of every 16-dim tile).
+template <int D, int G>
+__global__ __launch_bounds__(64 * G) void attn_merge_kernel(AttnParams p) {
+  constexpr int DT = D / 16;
+  const int u = blockIdx.x;
+  const int b = u / p.n_kv_heads, g = u - b * p.n_kv_heads;
+  int L = p.ctx_len[b];
+  L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
+  const int ns = L > 0 ? (L + p.kps - 1) / p.kps : 1;
+  if (ns == 1) return;  // written directly by the split kernel
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int h = g * G + w;
   float mmax = -INFINITY;
   for (int sp = 0; sp < ns; ++sp) {
     const int64_t sl = ((int64_t)u * p.n_splits + sp) * G + w;
@@ -372,9 +379,9 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
     for (int dt = 0; dt < DT; ++dt) acc[dt] += wgt * *reinterpret_cast<const f32x4*>(ps + (dt * 64 + lane) * 4);
   }
   const float inv = 1.f / den;
+  float* outp = p.out + (((int64_t)b * kBlock + r) * p.n_q_heads + h) * D + 4 * q;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(outp + dt * 16) = acc[dt] * inv;
-  if (tid == 0) __hip_atomic_store(p.count + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int G, bool PAGED>
@@ -382,6 +389,7 @@ hipError_t launch_t(const AttnParams& p, hipStream_t stream) {
   const int groups = (p.n_units + kNumXcd - 1) / kNumXcd;
   const int grid = kNumXcd * p.n_splits * groups;
   hipLaunchKernelGGL((block_attn_kernel<D, G, PAGED, true>), dim3(grid), dim3(64 * G), 0, stream, p);
+  if (p.n_splits > 1) hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(p.n_units), dim3(64 * G), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -417,8 +425,6 @@ AttnPlan plan_block_attn(int batch, int n_q_heads, int n_kv_heads, int head_dim,
   pl.n_splits = max_ctx > 0 ? (int)((max_ctx + kps - 1) / kps) : 1;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 256;  // word 0: device error mask
-  pl.off_count = off;
-  off = align(off + sizeof(uint32_t) * (size_t)units);
   pl.off_ml = off;
   off = align(off + sizeof(float) * 2 * 16 * (size_t)group * pl.n_splits * units);
   pl.off_o = off;

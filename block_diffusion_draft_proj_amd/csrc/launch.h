@@ -27,7 +27,6 @@ struct VerifyParams {
   int32_t* commit_pos;  // may be null
   int32_t* n_pages;     // may be null
   int32_t page_size;
-  uint32_t* count;      // [batch] arrival counters (self-resetting)
   uint64_t* part;       // [batch*16*n_chunks] per-chunk keys
 };
 hipError_t launch_verify_accept(const VerifyParams& p, int batch, hipStream_t stream);
@@ -50,7 +49,6 @@ struct AttnParams {
   float* out;
   float* ws_o;      // [units][n_splits][G][D/16][64 lanes][4] partial outputs
   float* ws_ml;     // [units][n_splits][G][16][2] running max (log2 domain) and sum
-  uint32_t* count;  // [units] arrival counters (self-resetting)
   uint32_t* err;    // sticky device error word
   int batch, n_q_heads, n_kv_heads;
   int capacity;     // dense rows per (seq, head) | page-table columns
@@ -65,7 +63,7 @@ struct AttnPlan {
   int kps;
   int n_splits;
   size_t ws_bytes;
-  size_t off_count, off_ml, off_o;
+  size_t off_ml, off_o;
 };
 AttnPlan plan_block_attn(int batch, int n_q_heads, int n_kv_heads, int head_dim, int max_ctx, int num_cu);
 hipError_t launch_block_attn(const AttnParams& p, int head_dim, int group, bool paged, hipStream_t stream);

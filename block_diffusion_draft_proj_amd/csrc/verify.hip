@@ -17,9 +17,10 @@
 //    held in registers, by only the threads whose own maximum matched;
 //  * each chunk publishes one 64-bit key (value key << 32 | ~index), so the row
 //    maximum with the lowest index is an order-independent max();
-//  * the last-arriving workgroup of a sequence (per-sequence arrival counter in the
-//    workspace, reset by that workgroup) reduces the 16 rows and runs accept /
-//    commit / crop.  No host round trip, one launch.
+//  * a second kernel (one workgroup per sequence) reduces the 16 rows and runs
+//    accept / commit / crop.  A kernel boundary is the cheapest device-wide
+//    handoff on this part: handing off inside one kernel would need an L2
+//    writeback (agent-scope release) from every workgroup.  No host round trip.
 #include "common.h"
 #include "launch.h"
 
@@ -68,16 +69,12 @@ __device__ __forceinline__ T wg_reduce(T v, Op op, T* s_buf) {
   return r;
 }
 
-__global__ __launch_bounds__(kThreads) void verify_accept_kernel(VerifyParams p) {
+__global__ __launch_bounds__(kThreads) void verify_argmax_kernel(VerifyParams p) {
   __shared__ uint32_t s_red[kThreads / kWave];
-  __shared__ int32_t s_post[kBlock];
-  __shared__ int32_t s_accept, s_kvin;
-  __shared__ uint32_t s_last;
 
   const int tid = threadIdx.x;
   const int row = blockIdx.x / p.n_chunks;
   const int chunk = blockIdx.x - row * p.n_chunks;
-  const int b = row / kBlock;
   const uint16_t* rp = p.logits + (int64_t)row * p.ld;
   const int c0 = chunk * kVerifyChunk;
   const int c1 = min(p.vocab, c0 + kVerifyChunk);
@@ -143,24 +140,22 @@ __global__ __launch_bounds__(kThreads) void verify_accept_kernel(VerifyParams p)
 
   if (tid == 0) {
     const uint64_t canon = has_nan ? 0x10000u : (zero ? 0x8000u : cmax);
-    const uint64_t key = (canon << 32) | (uint64_t)(0xffffffffu - idx);
-    __hip_atomic_store(p.part + (int64_t)row * p.n_chunks + chunk, key, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t prev = __hip_atomic_fetch_add(p.count + b, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (uint32_t)(kBlock * p.n_chunks - 1)) ? 1u : 0u;
+    p.part[(int64_t)row * p.n_chunks + chunk] = (canon << 32) | (uint64_t)(0xffffffffu - idx);
   }
-  __syncthreads();
-  if (!s_last) return;
+}
 
-  // Last workgroup of sequence b: reduce rows, then accept / commit / crop.
-  __atomic_thread_fence(__ATOMIC_ACQUIRE);
+// One workgroup per sequence: reduce the chunk keys of its 16 rows, then accept,
+// next staged token, KV-length crop, commit positions and page count.  Running
+// after the argmax kernel on the same stream, it sees every chunk key without
+// any device-wide fence.
+__global__ __launch_bounds__(kWave) void verify_accept_kernel(VerifyParams p) {
+  __shared__ int32_t s_post[kBlock];
+  __shared__ int32_t s_accept, s_kvin;
+  const int b = blockIdx.x, tid = threadIdx.x;
   if (tid < kBlock) {
     const uint64_t* pr = p.part + (int64_t)(b * kBlock + tid) * p.n_chunks;
     uint64_t best = 0;
-    for (int c = 0; c < p.n_chunks; ++c) {
-      const uint64_t k = __hip_atomic_load(pr + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      best = k > best ? k : best;
-    }
+    for (int c = 0; c < p.n_chunks; ++c) best = pr[c] > best ? pr[c] : best;
     const int32_t post = (int32_t)(0xffffffffu - (uint32_t)best);
     s_post[tid] = post;
     p.posterior[b * kBlock + tid] = post;
@@ -177,7 +172,6 @@ __global__ __launch_bounds__(kThreads) void verify_accept_kernel(VerifyParams p)
     p.next_token[b] = s_post[a];
     p.kv_len_out[b] = kv_out;
     if (p.n_pages) p.n_pages[b] = (int32_t)(((int64_t)kv_out + p.page_size - 1) / p.page_size);
-    __hip_atomic_store(p.count + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (p.commit_pos && tid < kBlock)
@@ -188,7 +182,8 @@ __global__ __launch_bounds__(kThreads) void verify_accept_kernel(VerifyParams p)
 
 hipError_t launch_verify_accept(const VerifyParams& p, int batch, hipStream_t stream) {
   const int grid = batch * kBlock * p.n_chunks;
-  hipLaunchKernelGGL(verify_accept_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(verify_argmax_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(verify_accept_kernel, dim3(batch), dim3(kWave), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -27,16 +27,15 @@
  *   - Every argument is validated on the host BEFORE anything is launched.  On
  *     any error nothing is enqueued and no output is touched.
  *   - Workspaces are caller-owned device buffers of at least the size the
- *     matching *_workspace_size() query returns.  A workspace must be
- *     zero-filled once before its first use; every call returns the counters
- *     it used to zero, so the buffer can be reused by later calls on the same
- *     stream without clearing.  Calls that run concurrently (different streams)
- *     need distinct workspaces.
+ *     matching *_workspace_size() query returns.  Apart from word 0 their
+ *     contents need no initialisation and carry nothing between calls, so one
+ *     buffer can serve any number of calls on the same stream.  Calls that run
+ *     concurrently (different streams) need distinct workspaces.
  *   - Word 0 of every workspace is a sticky device-side error mask
  *     (DFLASH_DEVERR_*): data-dependent faults found by the kernels (a context
  *     length, page id or row position out of range) are clamped or skipped so
  *     no access leaves its buffer, and the fault is OR-ed into this word.  The
- *     library never clears it; the caller may read and reset it.
+ *     library never clears it: zero it once, and read / reset it at will.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
