@@ -9,17 +9,22 @@
 //
 // Mapping onto gfx950:
 //  * workgroup = one (unit, split of the context) with G waves, wave w = query
-//    head g*G+w and its 16 block rows; the K/V tile is staged once in LDS and
-//    shared by the G heads (the context K/V stream is the HBM-bound part);
+//    head g*G+w and its 16 block rows; each K/V tile is brought into LDS once
+//    and shared by the G heads (the context K/V stream is the HBM-bound part);
+//  * context K/V tiles go HBM -> LDS with global_load_lds (16 bytes per lane, no
+//    register staging) through an NST-stage ring of TK-key stages, so NST-1
+//    stages are always in flight while one is consumed;
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16: keys are the
 //    MFMA row dimension, so the score tile comes out with one query row per lane
 //    column, the online-softmax statistics stay per lane, and the score
 //    registers are already the B operand of the PV product (the key order of the
 //    two 16-key score tiles is interleaved so each lane owns 8 consecutive keys);
-//  * V is transposed on its way into LDS (4 keys x 8 dims per thread through
-//    byte permutes) so the V^T operand is one 16-byte LDS read per lane;
-//  * K and V^T tiles use XOR-swizzled 16-byte chunks: every 16-lane read group
-//    and every row-wide write touches distinct banks;
+//  * V stays row-major in LDS; the V^T operand is read with ds_read_b64_tr_b16
+//    (LDS transpose read): lane j of a 16-lane group points at 4 dims of key row
+//    j/4 and lane i receives one dim of 4 consecutive keys;
+//  * both tiles use XOR-swizzled 16-byte chunks, chosen on the global side of
+//    the LDS load (the LDS side of global_load_lds is lane-contiguous), so the
+//    16-lane K reads and the 8-row transpose reads hit distinct banks;
 //  * the context is split over workgroups (flash-decoding); each split keeps
 //    (max, sum, O) in the workspace and a small second kernel merges them
 //    (log-sum-exp).  The kernel boundary is the handoff: merging inside the
@@ -37,18 +42,38 @@ namespace dflash {
 
 namespace {
 
-constexpr int TK = 64;  // keys per tile
+#define LDS_AS __attribute__((address_space(3)))
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int TK = 32;   // keys per pipeline stage
+constexpr int NST = 4;   // stages in the LDS ring
 
 template <int D>
-__device__ __forceinline__ int k_swz(int t) {
+struct Geo {
+  static constexpr int NCH = D / 8;                  // 16-byte chunks per key row
+  static constexpr int ROW = D * 2;                  // bytes per key row
+  static constexpr int TILE = TK * ROW;              // one K or V tile
+  static constexpr int STAGE = 2 * TILE;             // K tile, then V tile
+  static constexpr int RPL = 64 / NCH;               // key rows per wave-wide 1 KB load
+  static constexpr int LOADS = 2 * TK / RPL;         // wave-wide loads per stage (K + V)
+};
+
+// Chunk swizzles (row t of a tile, 16-byte chunk c stored at c ^ swz(t)).
+// K: the 16 rows 8(r/4) + 4j + r%4 read by one 16-lane group map to 16 distinct
+// bank quads (d=128: 16 chunks per 256-byte row) or (row parity, chunk) pairs (d=64).
+template <int D>
+__device__ __forceinline__ int kswz(int t) {
   if constexpr (D == 128) return (t & 3) | (((t >> 3) & 3) << 2);
   else return ((t >> 1) & 1) | (((t >> 3) & 3) << 1);
 }
-// K tile: row t = one key (D bf16); 16-byte chunk c of row t lives at chunk c ^ k_swz(t).
+// V: a transpose read of one 16-dim tile touches 32 bytes of each of the rows
+// {0..3, 8..11} (+4, +16, +24); those 32-byte pieces land in distinct banks.
 template <int D>
-__device__ __forceinline__ int k_off(int t, int c) { return t * (D * 2) + ((c ^ k_swz<D>(t)) << 4); }
-// V^T tile: row d = one head dimension (TK keys = 128 bytes); 8-key chunk lc at lc ^ ((d>>1)&7).
-__device__ __forceinline__ int v_off(int d, int lc) { return d * (TK * 2) + ((lc ^ ((d >> 1) & 7)) << 4); }
+__device__ __forceinline__ int vswz(int t) {
+  if constexpr (D == 128) return 2 * ((t & 3) | (((t >> 3) & 1) << 2));
+  else return 2 * (((t >> 1) & 1) | (((t >> 3) & 1) << 1));
+}
 
 template <bool PAGED>
 __device__ __forceinline__ const uint16_t* key_row(const AttnParams& p, const uint16_t* cache, int b, int g,
@@ -65,167 +90,148 @@ __device__ __forceinline__ const uint16_t* key_row(const AttnParams& p, const ui
   }
 }
 
-template <int D, int NT, bool PAGED>
-struct TileRegs {
-  static constexpr int NCH = D / 8;
-  static constexpr int KCH = TK * NCH;
-  static constexpr int KPER = (KCH + NT - 1) / NT;
-  static constexpr int VIT = (TK / 4) * NCH;
-  static constexpr int VPER = (VIT + NT - 1) / NT;
-  u32x4 kr[KPER];
-  u32x4 vr[VPER][4];
+// 16 bytes per lane from `src` into LDS at `lds_base` + 16 * lane (global_load_lds).
+// Issued as inline assembly on purpose: the compiler cannot tell which LDS
+// bytes the DMA writes, so with the builtin it waits for every outstanding load
+// before each transpose read, which empties the stage ring.  Completion is
+// tracked by hand (wait_stages + barrier); loads the compiler does not see can
+// only make its own vmcnt waits stricter, never looser.
+// The context stream is read exactly once, so the loads are non-temporal (nt):
+// measured on this part, that lifts a plain streaming read from ~6.2 to ~7.1 TB/s.
+__device__ __forceinline__ void lds_dma16(const void* src, char* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "s"(m0) : "memory", "m0");
+}
 
-  // Context keys [t0, t0+TK) of unit (b, g); keys >= tend become zero rows.
-  __device__ __forceinline__ void load(const AttnParams& p, int b, int g, int t0, int tend, int tid) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
+// Issue this wave's share of the global->LDS loads of one stage: keys [t0, t0+TK)
+// of unit (b, g), clamped to tend-1 (rows past the range hold a real, finite key
+// row whose scores are masked, so no stale LDS data can leak in).
+template <int D, int G, bool PAGED>
+__device__ __forceinline__ void issue_stage(const AttnParams& p, char* stage, int b, int g, int t0, int tend,
+                                            int w, int lane) {
+  using GE = Geo<D>;
+  const int rsub = lane / GE::NCH, pch = lane % GE::NCH;
 #pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int cid = tid + NT * i;
-      const int t = t0 + cid / NCH;
-      kr[i] = z;
-      if ((KCH % NT == 0 || cid < KCH) && t < tend)
-        kr[i] = ld16(key_row<PAGED>(p, p.k_cache, b, g, t, D) + (cid % NCH) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      const int id = tid + NT * i;
-      const int t = t0 + (id / NCH) * 4;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) vr[i][k] = z;
-      if ((VIT % NT == 0 || id < VIT) && t < tend) {
-        // 4 consecutive keys never cross a 16-token page.
-        const uint16_t* src = key_row<PAGED>(p, p.v_cache, b, g, t, D) + (id % NCH) * 8;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (t + k < tend) vr[i][k] = ld16(src + k * D);
-      }
-    }
+  for (int li = w; li < GE::LOADS; li += G) {
+    const bool is_v = li >= GE::LOADS / 2;
+    const int rb = is_v ? li - GE::LOADS / 2 : li;
+    const int row = rb * GE::RPL + rsub;
+    const int key = min(t0 + row, tend - 1);
+    const int c = pch ^ (is_v ? vswz<D>(row) : kswz<D>(row));
+    // a 1 KB load covers RPL (4 or 8) aligned rows: never crosses a 16-token page
+    const uint16_t* src = key_row<PAGED>(p, is_v ? p.v_cache : p.k_cache, b, g, key, D) + c * 8;
+    char* dst = stage + (is_v ? GE::TILE : 0) + rb * 1024;
+    lds_dma16(src, dst);
   }
+}
 
-  __device__ __forceinline__ void store(char* lds_k, char* lds_v, int tid) const {
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int cid = tid + NT * i;
-      if (KCH % NT == 0 || cid < KCH)
-        *reinterpret_cast<u32x4*>(lds_k + k_off<D>(cid / NCH, cid % NCH)) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      const int id = tid + NT * i;
-      if (VIT % NT == 0 || id < VIT) {
-        const int dc = id % NCH, kq = id / NCH;
-        const int half = (kq & 1) * 8;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t x0 = vr[i][0][j], x1 = vr[i][1][j], x2 = vr[i][2][j], x3 = vr[i][3][j];
-          const int d = dc * 8 + 2 * j;
-          *reinterpret_cast<u32x2*>(lds_v + v_off(d, kq >> 1) + half) =
-              (u32x2){pack_lo16(x0, x1), pack_lo16(x2, x3)};
-          *reinterpret_cast<u32x2*>(lds_v + v_off(d + 1, kq >> 1) + half) =
-              (u32x2){pack_hi16(x0, x1), pack_hi16(x2, x3)};
-        }
-      }
-    }
-  }
-};
+// Wait until at most `after` stages of this wave's loads are still in flight.
+// Waves issue at least LOADS/G loads per stage, so counting with that minimum
+// can only wait for more completions than needed.
+template <int D, int G>
+__device__ __forceinline__ void wait_stages(int after) {
+  constexpr int L = Geo<D>::LOADS / G;
+  // s_waitcnt immediate for gfx9: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4]<<14
+#define DFLASH_VMCNT(n) ((((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14)))
+  if (after >= 2) __builtin_amdgcn_s_waitcnt(DFLASH_VMCNT(2 * L < 63 ? 2 * L : 63));
+  else if (after == 1) __builtin_amdgcn_s_waitcnt(DFLASH_VMCNT(L < 63 ? L : 63));
+  else __builtin_amdgcn_s_waitcnt(DFLASH_VMCNT(0));
+#undef DFLASH_VMCNT
+}
 
-// One wave: 16 block rows of one query head against the TK-key tile in LDS.
-// nvalid: keys [0, nvalid) of the tile are real, the rest are masked out.
+// One wave: 16 block rows of one query head against one TK-key stage in LDS.
+// Keys [0, nvalid) of the stage are real, the rest are masked out.
 template <int D, bool PLO>
-__device__ __forceinline__ void attend_tile(const char* lds_k, const char* lds_v, const bf16x8* qB, f32x4* o,
-                                            float& m, float& lsum, int lane, int nvalid, float scale_log2) {
+__device__ __forceinline__ void attend_stage(const char* stage, const bf16x8* qB, f32x4* o, float& m,
+                                             float& lsum, int lane, int nvalid, float scale_log2) {
+  using GE = Geo<D>;
   constexpr int KS = D / 32, DT = D / 16;
   const int r = lane & 15, q = lane >> 4;
-  const int nkk = nvalid > 32 ? 2 : 1;
-  float x[2][2][4];
+  const char* kt = stage;
+  const char* vt = stage + GE::TILE;
+  float x[2][4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int j = 0; j < 2; ++j) {
+    const int t = 8 * (r >> 2) + 4 * j + (r & 3);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (kk < nkk) {
-        const int t = 32 * kk + 8 * (r >> 2) + 4 * j + (r & 3);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds_k + k_off<D>(t, ks * 4 + q));
-          acc = mfma16x16x32(a, qB[ks], acc);
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) x[kk][j][v] = acc[v] * scale_log2;
-      } else {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) x[kk][j][v] = -INFINITY;
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + t * GE::ROW + (((ks * 4 + q) ^ kswz<D>(t)) << 4));
+      acc = mfma16x16x32(a, qB[ks], acc);
     }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) x[j][v] = acc[v] * scale_log2;
   }
   if (nvalid < TK) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (32 * kk + 8 * q + 4 * j + v >= nvalid) x[kk][j][v] = -INFINITY;
-  }
-  float mt = x[0][0][0];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) mt = fmaxf(mt, x[kk][j][v]);
+      for (int v = 0; v < 4; ++v)
+        if (8 * q + 4 * j + v >= nvalid) x[j][v] = -INFINITY;
+  }
+  float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                   fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
   mt = fmaxf(mt, __shfl_xor(mt, 16));
   mt = fmaxf(mt, __shfl_xor(mt, 32));
-  const float mnew = fmaxf(m, mt);
-  const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-  const float alpha = __builtin_amdgcn_exp2f(m - mref);
+  // Lazy rescaling: the reference max m moves only when a stage max exceeds it
+  // by more than 8 (log2 units), so probabilities stay <= 2^8 and the O / sum
+  // rescale (32 accumulators) runs a handful of times per split instead of once
+  // per stage.  O and the sum always share the reference, so the result is the
+  // same softmax.  Every stage has a real key, so mt is finite.
+  if (__builtin_amdgcn_ballot_w64(mt > m + 8.f)) {
+    const float mnew = fmaxf(m, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // m = -inf on the first stage -> 0
+    lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    m = mnew;
+  }
   float psum = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float e = __builtin_amdgcn_exp2f(x[kk][j][v] - mref);
-        x[kk][j][v] = e;
-        psum += e;
-      }
-  lsum = lsum * alpha + psum;
-  m = mnew;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    for (int v = 0; v < 4; ++v) {
+      const float e = __builtin_amdgcn_exp2f(x[j][v] - m);
+      x[j][v] = e;
+      psum += e;
+    }
+  lsum += psum;
 
-  bf16x8 ph[2], pl[2];
+  bf16x8 ph, pl;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const __bf16 hi = static_cast<__bf16>(x[kk][j][v]);
-        ph[kk][4 * j + v] = hi;
-        if constexpr (PLO) pl[kk][4 * j + v] = static_cast<__bf16>(x[kk][j][v] - static_cast<float>(hi));
-      }
-  }
+    for (int v = 0; v < 4; ++v) {
+      const __bf16 hi = static_cast<__bf16>(x[j][v]);
+      ph[4 * j + v] = hi;
+      if constexpr (PLO) pl[4 * j + v] = static_cast<__bf16>(x[j][v] - static_cast<float>(hi));
+    }
+  // V^T operand via transpose reads: lane (group q, index i) points at key row
+  // 8q + 4h + i/4, dims 4(i%4)..+3 of the 16-dim tile; it receives dim dt*16 + i
+  // of keys 8q + 4h .. +3.
+  const int trow0 = 8 * q + (r >> 2);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
+    i16x4 part[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      if (kk < nkk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds_v + v_off(dt * 16 + r, 4 * kk + q));
-        o[dt] = mfma16x16x32(a, ph[kk], o[dt]);
-        if constexpr (PLO) o[dt] = mfma16x16x32(a, pl[kk], o[dt]);
-      }
+    for (int h = 0; h < 2; ++h) {
+      const int t = trow0 + 4 * h;
+      const int c = 2 * dt + ((r & 3) >> 1);
+      const char* addr = vt + t * GE::ROW + ((c ^ vswz<D>(t)) << 4) + (r & 1) * 8;
+      part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(addr));
     }
+    const i16x8 cat = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, cat);
+    o[dt] = mfma16x16x32(a, ph, o[dt]);
+    if constexpr (PLO) o[dt] = mfma16x16x32(a, pl, o[dt]);
   }
 }
 
 template <int D, int G, bool PAGED, bool PLO>
 __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
-  constexpr int NT = 64 * G;
+  using GE = Geo<D>;
   constexpr int KS = D / 32, DT = D / 16, HALF = D / 2;
-  __shared__ __attribute__((aligned(16))) char lds_k[TK * D * 2];
-  __shared__ __attribute__((aligned(16))) char lds_v[D * TK * 2];
+  __shared__ __attribute__((aligned(1024))) char lds[NST * GE::STAGE];
 
   // XCD-aware decode: WG i runs on XCD i % 8; every split of a unit shares one XCD.
   const int i_wg = blockIdx.x;
@@ -247,9 +253,16 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
   const int ke = min(L, kb + p.kps);
   const bool last_split = (s == ns - 1);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
   const int h = g * G + w;
+
+  // Start the context stream before anything else.
+  const int n_st = (ke - kb + TK - 1) / TK;
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < n_st) issue_stage<D, G, PAGED>(p, lds + st * GE::STAGE, b, g, kb + st * TK, ke, w, lane);
 
   // Q of head h: rows at positions L + r, RoPE in fp32, rounded to bf16, as the
   // B operand of S^T = K Q^T (lane holds dims 32*ks + 8*q .. +8 of row r).
@@ -286,28 +299,27 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
   for (int dt = 0; dt < DT; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
 
-  // Context keys [kb, ke): register-prefetched tiles through LDS.
-  const int n_tiles = (ke - kb + TK - 1) / TK;
-  TileRegs<D, NT, PAGED> regs;
-  if (n_tiles > 0) regs.load(p, b, g, kb, ke, tid);
-  for (int it = 0; it < n_tiles; ++it) {
-    const int t0 = kb + it * TK;
-    if (it > 0) __syncthreads();
-    regs.store(lds_k, lds_v, tid);
-    __syncthreads();
-    if (it + 1 < n_tiles) regs.load(p, b, g, t0 + TK, ke, tid);
-    attend_tile<D, PLO>(lds_k, lds_v, qB, o, m, lsum, lane, min(TK, ke - t0), p.scale_log2);
+  // Context keys [kb, ke) through the stage ring.
+  for (int it = 0; it < n_st; ++it) {
+    wait_stages<D, G>(min(NST - 2, n_st - 1 - it));
+    __syncthreads();  // stage `it` landed for every wave; stage it-1 is free again
+    if (it + NST - 1 < n_st)
+      issue_stage<D, G, PAGED>(p, lds + ((it + NST - 1) % NST) * GE::STAGE, b, g, kb + (it + NST - 1) * TK, ke,
+                               w, lane);
+    attend_stage<D, PLO>(lds + (it % NST) * GE::STAGE, qB, o, m, lsum, lane, min(TK, ke - kb - it * TK),
+                         p.scale_log2);
   }
 
-  // Block keys (positions L .. L+15), handled by the last split of the unit.
+  // Block keys (positions L .. L+15), handled by the last split of the unit:
+  // rotated K rows and V rows written into stage 0, rows 16..31 zero.
   if (last_split) {
     __syncthreads();
-    for (int off = tid * 16; off < TK * D * 2; off += NT * 16) {
-      *reinterpret_cast<u32x4*>(lds_k + off) = (u32x4){0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(lds_v + off) = (u32x4){0u, 0u, 0u, 0u};
-    }
+    char* kt = lds;
+    char* vt = lds + GE::TILE;
+    for (int off = tid * 16; off < GE::STAGE; off += 64 * G * 16)
+      *reinterpret_cast<u32x4*>(lds + off) = (u32x4){0u, 0u, 0u, 0u};
     __syncthreads();
-    for (int id = tid; id < kBlock * HALF; id += NT) {
+    for (int id = tid; id < kBlock * HALF; id += 64 * G) {
       const int t = id / HALF, j = id - t * HALF;
       const int64_t rowoff = (((int64_t)b * kBlock + t) * p.n_kv_heads + g) * D;
       const uint16_t* kr = p.k_blk + rowoff;
@@ -316,13 +328,14 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
       const float sn = p.rope_sin[(int64_t)(L + t) * HALF + j];
       float y0, y1;
       rope_pair(bf16_to_f32(kr[j]), bf16_to_f32(kr[j + HALF]), c, sn, y0, y1);
-      *reinterpret_cast<uint16_t*>(lds_k + k_off<D>(t, j >> 3) + 2 * (j & 7)) = f32_to_bf16(y0);
-      *reinterpret_cast<uint16_t*>(lds_k + k_off<D>(t, (j + HALF) >> 3) + 2 * (j & 7)) = f32_to_bf16(y1);
-      *reinterpret_cast<uint16_t*>(lds_v + v_off(j, t >> 3) + 2 * (t & 7)) = vr[j];
-      *reinterpret_cast<uint16_t*>(lds_v + v_off(j + HALF, t >> 3) + 2 * (t & 7)) = vr[j + HALF];
+      const int j2 = j + HALF;
+      *reinterpret_cast<uint16_t*>(kt + t * GE::ROW + (((j >> 3) ^ kswz<D>(t)) << 4) + 2 * (j & 7)) = f32_to_bf16(y0);
+      *reinterpret_cast<uint16_t*>(kt + t * GE::ROW + (((j2 >> 3) ^ kswz<D>(t)) << 4) + 2 * (j2 & 7)) = f32_to_bf16(y1);
+      *reinterpret_cast<uint16_t*>(vt + t * GE::ROW + (((j >> 3) ^ vswz<D>(t)) << 4) + 2 * (j & 7)) = vr[j];
+      *reinterpret_cast<uint16_t*>(vt + t * GE::ROW + (((j2 >> 3) ^ vswz<D>(t)) << 4) + 2 * (j2 & 7)) = vr[j2];
     }
     __syncthreads();
-    attend_tile<D, PLO>(lds_k, lds_v, qB, o, m, lsum, lane, kBlock, p.scale_log2);
+    attend_stage<D, PLO>(lds, qB, o, m, lsum, lane, kBlock, p.scale_log2);
   }
 
   float lt = lsum + __shfl_xor(lsum, 16);
@@ -347,41 +360,40 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
   }
 }
 
-// Log-sum-exp merge of the split partials of one unit: wave w = query head
-// g*G + w, lane = (row r, dims 4q..4q+3 of every 16-dim tile).
-template <int D, int G>
-__global__ __launch_bounds__(64 * G) void attn_merge_kernel(AttnParams p) {
-  constexpr int DT = D / 16;
-  const int u = blockIdx.x;
+// Log-sum-exp merge of the split partials: one workgroup per (unit, query head),
+// thread = (row r, 8 consecutive dims).  Partials are stored in the split
+// kernel's lane order: dims 16*dt + 4*q + v of row r at lane r + 16*q.
+template <int D>
+__global__ __launch_bounds__(2 * D) void attn_merge_kernel(AttnParams p, int group) {
+  constexpr int DT = D / 16, NCH = D / 8;
+  const int u = blockIdx.x / group, w = blockIdx.x - u * group;
   const int b = u / p.n_kv_heads, g = u - b * p.n_kv_heads;
   int L = p.ctx_len[b];
   L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
   const int ns = L > 0 ? (L + p.kps - 1) / p.kps : 1;
   if (ns == 1) return;  // written directly by the split kernel
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r = lane & 15, q = lane >> 4;
-  const int h = g * G + w;
+  const int r = threadIdx.x / NCH, c = threadIdx.x % NCH;
+  const int dt = c >> 1, q0 = 2 * (c & 1);
+  const int h = g * group + w;
+  const int64_t slot0 = (int64_t)u * p.n_splits * group + w;  // slot of split sp: slot0 + sp * group
   float mmax = -INFINITY;
-  for (int sp = 0; sp < ns; ++sp) {
-    const int64_t sl = ((int64_t)u * p.n_splits + sp) * G + w;
-    mmax = fmaxf(mmax, p.ws_ml[(sl * 16 + r) * 2]);
-  }
+  for (int sp = 0; sp < ns; ++sp) mmax = fmaxf(mmax, p.ws_ml[((slot0 + (int64_t)sp * group) * 16 + r) * 2]);
   float den = 0.f;
-  f32x4 acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int sp = 0; sp < ns; ++sp) {
-    const int64_t sl = ((int64_t)u * p.n_splits + sp) * G + w;
-    const float wgt = __builtin_amdgcn_exp2f(p.ws_ml[(sl * 16 + r) * 2] - mmax);
-    den += wgt * p.ws_ml[(sl * 16 + r) * 2 + 1];
-    const float* ps = p.ws_o + sl * (DT * 256);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] += wgt * *reinterpret_cast<const f32x4*>(ps + (dt * 64 + lane) * 4);
+    const int64_t sl = slot0 + (int64_t)sp * group;
+    const float* ml = p.ws_ml + (sl * 16 + r) * 2;
+    const float wgt = __builtin_amdgcn_exp2f(ml[0] - mmax);
+    den += wgt * ml[1];
+    const float* ps = p.ws_o + sl * (DT * 256) + (dt * 64 + r + 16 * q0) * 4;
+    a0 += wgt * *reinterpret_cast<const f32x4*>(ps);
+    a1 += wgt * *reinterpret_cast<const f32x4*>(ps + 64);
   }
   const float inv = 1.f / den;
-  float* outp = p.out + (((int64_t)b * kBlock + r) * p.n_q_heads + h) * D + 4 * q;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(outp + dt * 16) = acc[dt] * inv;
+  float* outp = p.out + (((int64_t)b * kBlock + r) * p.n_q_heads + h) * D + 8 * c;
+  *reinterpret_cast<f32x4*>(outp) = a0 * inv;
+  *reinterpret_cast<f32x4*>(outp + 4) = a1 * inv;
 }
 
 template <int D, int G, bool PAGED>
@@ -389,7 +401,7 @@ hipError_t launch_t(const AttnParams& p, hipStream_t stream) {
   const int groups = (p.n_units + kNumXcd - 1) / kNumXcd;
   const int grid = kNumXcd * p.n_splits * groups;
   hipLaunchKernelGGL((block_attn_kernel<D, G, PAGED, true>), dim3(grid), dim3(64 * G), 0, stream, p);
-  if (p.n_splits > 1) hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(p.n_units), dim3(64 * G), 0, stream, p);
+  if (p.n_splits > 1) hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(p.n_units * G), dim3(2 * D), 0, stream, p, G);
   return hipGetLastError();
 }
 
