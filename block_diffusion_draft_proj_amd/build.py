@@ -24,7 +24,10 @@ SOURCES = ["api.cpp", "verify.hip", "rope.hip", "block_attn.hip", "ctx_proj.hip"
 HIP_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-ffp-contract=fast-honor-pragmas",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    # MFMA accumulators in VGPRs: keeps the online-softmax rescale from copying
+    # every accumulator between AGPRs and VGPRs once per key stage.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    "-Wall", "-Wno-unused-function", "-Wno-pass-failed",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

@@ -42,7 +42,6 @@ namespace dflash {
 
 namespace {
 
-#define LDS_AS __attribute__((address_space(3)))
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
@@ -90,19 +89,6 @@ __device__ __forceinline__ const uint16_t* key_row(const AttnParams& p, const ui
   }
 }
 
-// 16 bytes per lane from `src` into LDS at `lds_base` + 16 * lane (global_load_lds).
-// Issued as inline assembly on purpose: the compiler cannot tell which LDS
-// bytes the DMA writes, so with the builtin it waits for every outstanding load
-// before each transpose read, which empties the stage ring.  Completion is
-// tracked by hand (wait_stages + barrier); loads the compiler does not see can
-// only make its own vmcnt waits stricter, never looser.
-// The context stream is read exactly once, so the loads are non-temporal (nt):
-// measured on this part, that lifts a plain streaming read from ~6.2 to ~7.1 TB/s.
-__device__ __forceinline__ void lds_dma16(const void* src, char* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "s"(m0) : "memory", "m0");
-}
-
 // Issue this wave's share of the global->LDS loads of one stage: keys [t0, t0+TK)
 // of unit (b, g), clamped to tend-1 (rows past the range hold a real, finite key
 // row whose scores are masked, so no stale LDS data can leak in).
@@ -121,7 +107,7 @@ __device__ __forceinline__ void issue_stage(const AttnParams& p, char* stage, in
     // a 1 KB load covers RPL (4 or 8) aligned rows: never crosses a 16-token page
     const uint16_t* src = key_row<PAGED>(p, is_v ? p.v_cache : p.k_cache, b, g, key, D) + c * 8;
     char* dst = stage + (is_v ? GE::TILE : 0) + rb * 1024;
-    lds_dma16(src, dst);
+    lds_dma16_nt(src, dst);
   }
 }
 
@@ -131,51 +117,65 @@ __device__ __forceinline__ void issue_stage(const AttnParams& p, char* stage, in
 template <int D, int G>
 __device__ __forceinline__ void wait_stages(int after) {
   constexpr int L = Geo<D>::LOADS / G;
-  // s_waitcnt immediate for gfx9: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4]<<14
-#define DFLASH_VMCNT(n) ((((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14)))
-  if (after >= 2) __builtin_amdgcn_s_waitcnt(DFLASH_VMCNT(2 * L < 63 ? 2 * L : 63));
-  else if (after == 1) __builtin_amdgcn_s_waitcnt(DFLASH_VMCNT(L < 63 ? L : 63));
-  else __builtin_amdgcn_s_waitcnt(DFLASH_VMCNT(0));
-#undef DFLASH_VMCNT
+  if (after >= 2) wait_vmcnt<(2 * L < 63 ? 2 * L : 63)>();
+  else if (after == 1) wait_vmcnt<(L < 63 ? L : 63)>();
+  else wait_vmcnt<0>();
 }
 
-// One wave: 16 block rows of one query head against one TK-key stage in LDS.
-// Keys [0, nvalid) of the stage are real, the rest are masked out.
+// One wave: 16 block rows of one query head against one TK-key stage in LDS,
+// in NKK = TK/32 sub-steps of 32 keys.  Keys [0, nvalid) of the stage are real,
+// the rest are masked out (sub-steps past nvalid are skipped).
 template <int D, bool PLO>
 __device__ __forceinline__ void attend_stage(const char* stage, const bf16x8* qB, f32x4* o, float& m,
                                              float& lsum, int lane, int nvalid, float scale_log2) {
   using GE = Geo<D>;
-  constexpr int KS = D / 32, DT = D / 16;
+  constexpr int KS = D / 32, DT = D / 16, NKK = TK / 32;
   const int r = lane & 15, q = lane >> 4;
   const char* kt = stage;
   const char* vt = stage + GE::TILE;
-  float x[2][4];
+  const int nkk = (nvalid + 31) >> 5;
+  float x[NKK][2][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int t = 8 * (r >> 2) + 4 * j + (r & 3);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + t * GE::ROW + (((ks * 4 + q) ^ kswz<D>(t)) << 4));
-      acc = mfma16x16x32(a, qB[ks], acc);
+    for (int j = 0; j < 2; ++j) {
+      if (kk < nkk) {
+        const int t = 32 * kk + 8 * (r >> 2) + 4 * j + (r & 3);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + t * GE::ROW + (((ks * 4 + q) ^ kswz<D>(t)) << 4));
+          acc = mfma16x16x32(a, qB[ks], acc);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[kk][j][v] = acc[v] * scale_log2;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[kk][j][v] = -INFINITY;
+      }
     }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) x[j][v] = acc[v] * scale_log2;
   }
   if (nvalid < TK) {
 #pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (32 * kk + 8 * q + 4 * j + v >= nvalid) x[kk][j][v] = -INFINITY;
+  }
+  float mt = x[0][0][0];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (8 * q + 4 * j + v >= nvalid) x[j][v] = -INFINITY;
-  }
-  float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                   fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      for (int v = 0; v < 4; ++v) mt = fmaxf(mt, x[kk][j][v]);
   mt = fmaxf(mt, __shfl_xor(mt, 16));
   mt = fmaxf(mt, __shfl_xor(mt, 32));
   // Lazy rescaling: the reference max m moves only when a stage max exceeds it
   // by more than 8 (log2 units), so probabilities stay <= 2^8 and the O / sum
-  // rescale (32 accumulators) runs a handful of times per split instead of once
+  // rescale (all accumulators) runs a handful of times per split instead of once
   // per stage.  O and the sum always share the reference, so the result is the
   // same softmax.  Every stage has a real key, so mt is finite.
   if (__builtin_amdgcn_ballot_w64(mt > m + 8.f)) {
@@ -188,42 +188,48 @@ __device__ __forceinline__ void attend_stage(const char* stage, const bf16x8* qB
   }
   float psum = 0.f;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float e = __builtin_amdgcn_exp2f(x[j][v] - m);
-      x[j][v] = e;
-      psum += e;
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float e = __builtin_amdgcn_exp2f(x[kk][j][v] - m);
+        x[kk][j][v] = e;
+        psum += e;
+      }
   lsum += psum;
 
-  bf16x8 ph, pl;
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const __bf16 hi = static_cast<__bf16>(x[j][v]);
-      ph[4 * j + v] = hi;
-      if constexpr (PLO) pl[4 * j + v] = static_cast<__bf16>(x[j][v] - static_cast<float>(hi));
-    }
   // V^T operand via transpose reads: lane (group q, index i) points at key row
-  // 8q + 4h + i/4, dims 4(i%4)..+3 of the 16-dim tile; it receives dim dt*16 + i
-  // of keys 8q + 4h .. +3.
+  // 32kk + 8q + 4h + i/4, dims 4(i%4)..+3 of the 16-dim tile; it receives dim
+  // dt*16 + i of keys 32kk + 8q + 4h .. +3.
   const int trow0 = 8 * q + (r >> 2);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    i16x4 part[2];
+  for (int kk = 0; kk < NKK; ++kk) {
+    if (kk >= nkk) break;
+    bf16x8 ph, pl;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = trow0 + 4 * h;
-      const int c = 2 * dt + ((r & 3) >> 1);
-      const char* addr = vt + t * GE::ROW + ((c ^ vswz<D>(t)) << 4) + (r & 1) * 8;
-      part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(addr));
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const __bf16 hi = static_cast<__bf16>(x[kk][j][v]);
+        ph[4 * j + v] = hi;
+        if constexpr (PLO) pl[4 * j + v] = static_cast<__bf16>(x[kk][j][v] - static_cast<float>(hi));
+      }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      i16x4 part[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = 32 * kk + trow0 + 4 * h;
+        const int c = 2 * dt + ((r & 3) >> 1);
+        const char* addr = vt + t * GE::ROW + ((c ^ vswz<D>(t)) << 4) + (r & 1) * 8;
+        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(addr));
+      }
+      const i16x8 cat = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, cat);
+      o[dt] = mfma16x16x32(a, ph, o[dt]);
+      if constexpr (PLO) o[dt] = mfma16x16x32(a, pl, o[dt]);
     }
-    const i16x8 cat = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    const bf16x8 a = __builtin_bit_cast(bf16x8, cat);
-    o[dt] = mfma16x16x32(a, ph, o[dt]);
-    if constexpr (PLO) o[dt] = mfma16x16x32(a, pl, o[dt]);
   }
 }
 

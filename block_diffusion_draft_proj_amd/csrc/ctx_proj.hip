@@ -13,13 +13,13 @@
 //
 // gfx950 mapping: both products are "A x W^T" with K contiguous in both
 // operands, which is exactly the MFMA operand layout (each lane holds 8
-// consecutive K elements of one row), so A and W tiles go global -> registers ->
-// XOR-swizzled LDS -> v_mfma_f32_16x16x32_bf16 with no transposes.  The
-// concatenation is implicit: the K loop walks the layer pointers.  For the
-// per-cycle case (M = B*16 rows) the product is a weight stream, so K is split
-// over workgroups to put >= 2 workgroups on every CU; fp32 partial sums are
-// reduced by small epilogue kernels (bf16 rounding of C; RoPE, bf16 rounding
-// and cache scatter of K/V).
+// consecutive K elements of one row), so A and W tiles go global -> XOR-swizzled
+// LDS (global_load_lds, no register staging) -> v_mfma_f32_16x16x32_bf16 with no
+// transposes.  The concatenation is implicit: the K loop walks the layer
+// pointers.  For the per-cycle case (M = B*16 rows) the product is a weight
+// stream, so K is split over workgroups to put ~2 workgroups on every CU; fp32
+// partial sums are reduced by small epilogue kernels (bf16 rounding of C; RoPE,
+// bf16 rounding and cache scatter of K/V).
 #include "common.h"
 #include "launch.h"
 
@@ -27,96 +27,101 @@ namespace dflash {
 
 namespace {
 
+// Tile of one workgroup: 128 rows (A / activations) x 64 columns (B / weight
+// rows), K consumed in 64-element stages.  Each stage lands in LDS through
+// global_load_lds (A tile 16 KB, B tile 8 KB) in a 3-stage ring, so two stages
+// are in flight while one feeds the MFMAs; two workgroups fit on a CU.
+// Eight waves each own 16 rows x 64 columns of the tile.  The 24 wave-wide
+// 1 KB loads of a stage are dealt round-robin (load i to wave i % 8), so the
+// weight loads, which miss every cache, are spread over all waves instead of
+// queueing behind one wave's memory counter (measured: 2.4x faster than giving
+// each wave a contiguous run of loads).
+// The weights are read exactly once (non-temporal); the activation tile is
+// re-read by every column tile and is left cacheable.
 constexpr int BK = 64;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kGemmWaves = kThreads / kWave;
+constexpr int GBM = 128, GBN = 64, GNST = 3;
+constexpr int A_TILE = GBM * BK * 2;
+constexpr int B_TILE = GBN * BK * 2;
+constexpr int G_STAGE = A_TILE + B_TILE;
+constexpr int G_LOADS_W = G_STAGE / 1024 / kGemmWaves;  // wave-wide 1 KB loads per wave per stage (3)
+static_assert(GBM == 16 * kGemmWaves, "one 16-row MFMA strip per wave");
+static_assert(G_STAGE % (1024 * kGemmWaves) == 0, "stage loads split evenly over the waves");
 
+// 128-byte rows (64 bf16 of K); 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7):
+// the 16 rows read by one 16-lane MFMA operand group hit distinct banks.
 __device__ __forceinline__ int swz_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
-template <int MT, int NTW>
 __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
-  constexpr int BM = 16 * MT, BN = 64 * NTW;
-  constexpr int APER = BM * 8 / kThreads, BPER = BN * 8 / kThreads;
-  static_assert(APER >= 1 && BPER >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) char lds_a[BM * 128];
-  __shared__ __attribute__((aligned(16))) char lds_b[BN * 128];
-
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM, z = blockIdx.z;
+  __shared__ __attribute__((aligned(1024))) char lds[GNST * G_STAGE];
+  const int n0 = blockIdx.x * GBN, m0 = blockIdx.y * GBM, z = blockIdx.z;
   const int kbeg = z * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n_st = (kend - kbeg) / BK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
+  const int lrow = lane >> 3, pch = lane & 7;  // one wave-wide load = 8 rows x 128 bytes
 
-  u32x4 ar[APER], br[BPER];
-  auto load = [&](int k0) {
+  // Rows past M or N are clamped to the last real row: every load is in bounds
+  // and the extra results are never stored.
+  auto issue = [&](int st) {
+    const int k0 = kbeg + st * BK;
     const int seg = k0 / p.seg_k;
     const uint16_t* abase = p.a_seg[seg] + (k0 - seg * p.seg_k);
+    char* stage = lds + (st % GNST) * G_STAGE;
 #pragma unroll
-    for (int i = 0; i < APER; ++i) {
-      const int cid = tid + kThreads * i, row = cid >> 3, c = cid & 7;
-      const int m = m0 + row;
-      ar[i] = m < p.M ? ld16(abase + (int64_t)m * p.lda + 8 * c) : (u32x4){0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < BPER; ++i) {
-      const int cid = tid + kThreads * i, row = cid >> 3, c = cid & 7;
-      const int n = n0 + row;
-      if (n < p.N) {
-        const uint16_t* brow = n < p.n_b0 ? p.b0 + (int64_t)n * p.K : p.b1 + (int64_t)(n - p.n_b0) * p.K;
-        br[i] = ld16(brow + k0 + 8 * c);
+    for (int i = 0; i < G_LOADS_W; ++i) {
+      const int li = i * kGemmWaves + w;  // 0..15: A tile, 16..23: B tile (wave-uniform)
+      if (li < A_TILE / 1024) {
+        const int row = li * 8 + lrow;
+        const int m = min(m0 + row, p.M - 1);
+        lds_dma16(abase + (int64_t)m * p.lda + ((pch ^ ((row >> 1) & 7)) << 3), stage + li * 1024);
       } else {
-        br[i] = (u32x4){0u, 0u, 0u, 0u};
+        const int row = (li - A_TILE / 1024) * 8 + lrow;
+        const int n = min(n0 + row, p.N - 1);
+        const uint16_t* brow = n < p.n_b0 ? p.b0 + (int64_t)n * p.K : p.b1 + (int64_t)(n - p.n_b0) * p.K;
+        lds_dma16_nt(brow + k0 + ((pch ^ ((row >> 1) & 7)) << 3), stage + li * 1024);
       }
     }
   };
 
-  f32x4 acc[MT][NTW];
+  f32x4 acc[4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  if (kbeg < kend) load(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += BK) {
-    if (k0 > kbeg) __syncthreads();
 #pragma unroll
-    for (int i = 0; i < APER; ++i) {
-      const int cid = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(lds_a + swz_off(cid >> 3, cid & 7)) = ar[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BPER; ++i) {
-      const int cid = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(lds_b + swz_off(cid >> 3, cid & 7)) = br[i];
-    }
+  for (int st = 0; st < GNST - 1; ++st)
+    if (st < n_st) issue(st);
+  for (int it = 0; it < n_st; ++it) {
+    if (it + 1 < n_st) wait_vmcnt<G_LOADS_W>();  // stage it landed, stage it+1 may still fly
+    else wait_vmcnt<0>();
     __syncthreads();
-    if (k0 + BK < kend) load(k0 + BK);
+    if (it + GNST - 1 < n_st) issue(it + GNST - 1);
+    const char* sa = lds + (it % GNST) * G_STAGE;
+    const char* sb = sa + A_TILE;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 a[MT];
+      bf16x8 b[4];
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sa + swz_off(w * 16 + r, ks * 4 + q));
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        a[mt] = *reinterpret_cast<const bf16x8*>(lds_a + swz_off(mt * 16 + r, ks * 4 + q));
+      for (int nt = 0; nt < 4; ++nt) b[nt] = *reinterpret_cast<const bf16x8*>(sb + swz_off(nt * 16 + r, ks * 4 + q));
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(lds_b + swz_off((w * NTW + nt) * 16 + r, ks * 4 + q));
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = mfma16x16x32(a[mt], bb, acc[mt][nt]);
-      }
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = mfma16x16x32(a, b[nt], acc[nt]);
     }
   }
 
+  // C tile: lane holds column n0 + 16nt + r, rows m0 + 16w + 4q + v.
   float* out = p.out + (int64_t)z * p.M * p.N;
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const int n = n0 + (w * NTW + nt) * 16 + r;
+  for (int nt = 0; nt < 4; ++nt) {
+    const int n = n0 + nt * 16 + r;
     if (n >= p.N) continue;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + mt * 16 + 4 * q + v;
-        if (m < p.M) out[(int64_t)m * p.N + n] = acc[mt][nt][v];
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + w * 16 + 4 * q + v;
+      if (m < p.M) out[(int64_t)m * p.N + n] = acc[nt][v];
     }
   }
 }
@@ -198,15 +203,17 @@ __global__ __launch_bounds__(256) void kv_epilogue_kernel(KvEpilogueParams p) {
   *reinterpret_cast<u32x2*>(vd + j + half) = (u32x2){pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
 }
 
-constexpr int kPlanBM = 128;
-
-int split_count(int tiles, int K, int target) {
+// Split K so that ~2 workgroups land on every CU, while the fp32 partial sums
+// (splits x M x N x 4 bytes, written and read back once) stay under a quarter of
+// the weight bytes (N x K x 2) and every split keeps >= 4 stages.
+int split_count(int tiles, int M, int K, int target) {
   if (tiles < 1) tiles = 1;
   int splits = (target + tiles - 1) / tiles;
-  const int max_splits = K / (4 * BK) > 0 ? K / (4 * BK) : 1;  // keep >= 4 k-tiles per split
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
-  return splits;
+  const int by_traffic = (int)((int64_t)K / (8 * (int64_t)(M > 0 ? M : 1)));
+  const int by_depth = K / (4 * BK);
+  splits = min(splits, max(1, by_traffic));
+  splits = min(splits, max(1, by_depth));
+  return max(1, splits);
 }
 
 int k_per_split(int K, int splits) {
@@ -219,14 +226,13 @@ int k_per_split(int K, int splits) {
 ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_fc, int num_cu) {
   ProjPlan pl{};
   const int target = 2 * (num_cu > 0 ? num_cu : 256);
-  const int mtiles = (n_rows + kPlanBM - 1) / kPlanBM;
-  pl.fc_small = pl.kv_small = n_rows <= kPlanBM;
-  const int bn = pl.fc_small ? 256 : 128;
+  const int mtiles = (n_rows + GBM - 1) / GBM;
+  pl.fc_small = pl.kv_small = n_rows <= GBM;
   if (has_fc) {
-    pl.fc_kps = k_per_split(k_fc, split_count(mtiles * ((hidden + bn - 1) / bn), k_fc, target));
+    pl.fc_kps = k_per_split(k_fc, split_count(mtiles * ((hidden + GBN - 1) / GBN), n_rows, k_fc, target));
     pl.fc_splits = (k_fc + pl.fc_kps - 1) / pl.fc_kps;  // every split has a non-empty K range
   }
-  pl.kv_kps = k_per_split(hidden, split_count(mtiles * ((kv_width + bn - 1) / bn), hidden, target));
+  pl.kv_kps = k_per_split(hidden, split_count(mtiles * ((kv_width + GBN - 1) / GBN), n_rows, hidden, target));
   pl.kv_splits = (hidden + pl.kv_kps - 1) / pl.kv_kps;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 256;  // word 0: device error mask
@@ -240,15 +246,9 @@ ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_
   return pl;
 }
 
-hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStream_t stream) {
-  const int mt = (p.M + kPlanBM - 1) / kPlanBM;
-  if (small_m) {
-    dim3 grid((p.N + 255) / 256, mt, splits);
-    hipLaunchKernelGGL((gemm_nt_kernel<8, 4>), grid, dim3(kThreads), 0, stream, p);
-  } else {
-    dim3 grid((p.N + 127) / 128, mt, splits);
-    hipLaunchKernelGGL((gemm_nt_kernel<8, 2>), grid, dim3(kThreads), 0, stream, p);
-  }
+hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool /*small_m*/, hipStream_t stream) {
+  dim3 grid((p.N + GBN - 1) / GBN, (p.M + GBM - 1) / GBM, splits);
+  hipLaunchKernelGGL(gemm_nt_kernel, grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
