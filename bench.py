@@ -28,6 +28,47 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
+# HBM bytes per block-attention call (split kernel + merge kernel) on the batched
+# workload, from two rocprofv3 counter passes over this script (FETCH_SIZE, then
+# WRITE_SIZE), each scaled by what the same counter reads for a device-to-device
+# copy of known size (--copy-mib).  Valid only for the kernel sources it was taken
+# on: any change to them turns the reported traffic into null.
+ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
+                        "block_diffusion_draft_proj_amd/csrc/common.h",
+                        "block_diffusion_draft_proj_amd/csrc/launch.h",
+                        "block_diffusion_draft_proj_amd/csrc/api.cpp")
+ATTN_TRAFFIC = {"sha256": "f33ee127f08db17423a8161d4527a0751630d76cab1d72fa838abf66b9adffe9",
+                "workload": "batched", "read": 287334767, "write": 19136533}
+
+
+def sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    t = ATTN_TRAFFIC
+    if t is None or t["workload"] != workload or t["sha256"] != sources_sha256(ATTN_TRAFFIC_SOURCES):
+        return None
+    return int(t["read"] + t["write"])
+
+
+def copy_yardstick(mib):
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -37,6 +78,9 @@ def parse():
     ap.add_argument("--config", default="batched")
     ap.add_argument("--rotate", type=int, default=0, help="input copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the step, copy a buffer of this many MiB device to device 5 times: the "
+                         "yardstick that converts the HBM byte counters of a profiler into bytes")
     return ap.parse_args()
 
 
@@ -100,6 +144,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is a "
               f"design note, not a built path.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_mib:
+        copy_yardstick(args.copy_mib)
+        return
     import numpy as np
     import torch
     from block_diffusion_draft_proj_amd import dflash as dfl
@@ -209,7 +256,8 @@ def main():
         "ctx_proj": {"us": round(t_proj * 1e6, 2), "GB_s": round(p_b / t_proj / 1e9, 1), "bytes": p_b,
                      "rows": M, "committed_rows": committed},
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name),
+                     "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": a_b},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, at, vi, pj, commit.view(-1).cpu().numpy())
