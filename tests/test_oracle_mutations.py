@@ -1,0 +1,66 @@
+"""The oracle's pins must reject plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of the oracle source -- a dropped term,
+a wrong sign, an off-by-one position or alignment, a transposed head, a missing
+rounding -- and runs the pin suite against that copy in a fresh interpreter.
+The pins pass on the real oracle (tests/test_oracle_pins.py); here every mutant
+must make at least one of them fail.  The real oracle file is never modified.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ORACLE = os.path.join(ROOT, "oracle", "dflash_oracle.py")
+
+MUTANTS = {
+    "rope_sign": ("return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)",
+                  "return np.concatenate([lo * c + hi * s, hi * c - lo * s], axis=-1)"),
+    "rope_freq": ("inv_freq = base ** (-2.0 * j / head_dim)", "inv_freq = base ** (-1.0 * j / head_dim)"),
+    "q_not_rounded": ("Q = rope_to_bf16(q_b[:, hs, :], pos, base)",
+                      "Q = apply_rope(bf16_to_f64(q_b[:, hs, :]), pos, base)"),
+    "drop_block_keys": ("Keys = np.concatenate([bf16_to_f64(k_ctx[:L]), Kblk], axis=0)\n"
+                        "    Vals = np.concatenate([bf16_to_f64(v_ctx[:L]), bf16_to_f64(v_b[:, g, :])], axis=0)",
+                        "Keys = bf16_to_f64(k_ctx[:L+16])\n    Vals = bf16_to_f64(v_ctx[:L+16])"),
+    "softmax_scale": ("scale = 1.0 / math.sqrt(d)\n    L = int(ctx_len)\n    pos",
+                      "scale = 1.0 / d\n    L = int(ctx_len)\n    pos"),
+    "accept_alignment": ("matches = (blk[:, 1:] == post[:, :BLOCK - 1])",
+                         "matches = (blk[:, :BLOCK - 1] == post[:, :BLOCK - 1])"),
+    "commit_count": ("kv_out = (kv_in + 1 + accept)", "kv_out = (kv_in + accept)"),
+    "block_positions": ("pos = L + np.arange(BLOCK)\n    hs", "pos = L + 1 + np.arange(BLOCK)\n    hs"),
+    "wrong_kv_head": ("kc, vc = k_cache[b, g], v_cache[b, g]",
+                      "kc, vc = k_cache[b, (g + 1) % Hkv], v_cache[b, (g + 1) % Hkv]"),
+    "c_not_rounded": ("Cb = round_bf16(C)", "Cb = C"),
+    "commit_positions": ("np.where(i <= accept[:, None]", "np.where(i < accept[:, None]"),
+    "rope_on_v": ("V = (Cb @ bf16_to_f64(w_v).T).reshape(M, n_kv_heads, head_dim)",
+                  "V = apply_rope((Cb @ bf16_to_f64(w_v).T).reshape(M, n_kv_heads, head_dim), "
+                  "np.maximum(np.asarray(row_pos), 0), base)"),
+}
+
+
+def _run_pins(mutant_path):
+    env = dict(os.environ, DFLASH_ORACLE_MUTANT=mutant_path)
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        "-x", "-q", "-p", "no:cacheprovider"], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=600)
+    return r.returncode, (r.stdout.strip().splitlines() or [""])[-1]
+
+
+def test_every_planted_mistake_fails_a_pin(tmp_path):
+    src = open(ORACLE).read()
+    paths = {}
+    for name, (good, bad) in MUTANTS.items():
+        assert src.count(good) == 1, f"mutation site of {name} not found once in the oracle"
+        p = tmp_path / f"mutant_{name}.py"
+        p.write_text(src.replace(good, bad))
+        paths[name] = str(p)
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = dict(zip(paths, ex.map(_run_pins, paths.values())))
+    survivors = {n: last for n, (rc, last) in results.items() if rc == 0}
+    assert not survivors, f"mutants that pass every pin: {survivors}"
+    # a collection or import error is not a pin failure
+    for n, (rc, last) in results.items():
+        assert rc == 1, f"{n}: pytest exit {rc} ({last})"

@@ -12,8 +12,23 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import dflash_oracle as orc
 from block_diffusion_draft_proj_amd import synth
+
+
+def _oracle_under_test():
+    """The oracle module; for the mutation check only, a copy with a planted mistake."""
+    path = os.environ.get("DFLASH_ORACLE_MUTANT")
+    if not path:
+        from oracle import dflash_oracle
+        return dflash_oracle
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("dflash_oracle_mutant", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+orc = _oracle_under_test()
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
