@@ -179,6 +179,8 @@ int dflash_block_attn(const dflash_dims* dims, const void* q_blk, const void* k_
   p.ws_o = reinterpret_cast<float*>(ws + pl.off_o);
   p.ws_ml = reinterpret_cast<float*>(ws + pl.off_ml);
   p.err = reinterpret_cast<uint32_t*>(ws);
+  p.count = reinterpret_cast<uint32_t*>(ws + pl.off_cnt);
+  p.fused = pl.fused ? 1 : 0;
   p.batch = dims->batch;
   p.n_q_heads = dims->n_q_heads;
   p.n_kv_heads = dims->n_kv_heads;

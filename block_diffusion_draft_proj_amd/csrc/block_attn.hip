@@ -45,8 +45,15 @@ namespace {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int TK = 32;   // keys per pipeline stage
-constexpr int NST = 4;   // stages in the LDS ring
+constexpr int TK = 32;        // keys per pipeline stage
+constexpr int NST = 8;        // stages in the LDS ring
+constexpr int kMaxFused = 8;  // up to this many splits per unit merge inside the split kernel
+
+// Wave groups per workgroup: group k consumes stage NGRP*pack + k of every pack of
+// NGRP consecutive stages.  Two groups while the workgroup stays within 10 waves
+// (so a wave keeps >= 168 VGPRs), one for larger query groups.
+template <int G>
+constexpr int ngrp() { return G <= 5 ? 2 : 1; }
 
 template <int D>
 struct Geo {
@@ -89,90 +96,81 @@ __device__ __forceinline__ const uint16_t* key_row(const AttnParams& p, const ui
   }
 }
 
-// Issue this wave's share of the global->LDS loads of one stage: keys [t0, t0+TK)
-// of unit (b, g), clamped to tend-1 (rows past the range hold a real, finite key
-// row whose scores are masked, so no stale LDS data can leak in).
-template <int D, int G, bool PAGED>
-__device__ __forceinline__ void issue_stage(const AttnParams& p, char* stage, int b, int g, int t0, int tend,
-                                            int w, int lane) {
+// One wave-wide 1 KB load (index li of the stage's LOADS) of the stage holding keys
+// [t0, t0+TK) of unit (b, g), clamped to tend-1 (rows past the range hold a real,
+// finite key row whose scores are masked, so no stale LDS data can leak in).
+template <int D, bool PAGED>
+__device__ __forceinline__ void issue_load(const AttnParams& p, uint32_t stage, int b, int g, int t0, int tend,
+                                           int li, int lane) {
   using GE = Geo<D>;
   const int rsub = lane / GE::NCH, pch = lane % GE::NCH;
-#pragma unroll
-  for (int li = w; li < GE::LOADS; li += G) {
-    const bool is_v = li >= GE::LOADS / 2;
-    const int rb = is_v ? li - GE::LOADS / 2 : li;
-    const int row = rb * GE::RPL + rsub;
-    const int key = min(t0 + row, tend - 1);
-    const int c = pch ^ (is_v ? vswz<D>(row) : kswz<D>(row));
-    // a 1 KB load covers RPL (4 or 8) aligned rows: never crosses a 16-token page
-    const uint16_t* src = key_row<PAGED>(p, is_v ? p.v_cache : p.k_cache, b, g, key, D) + c * 8;
-    char* dst = stage + (is_v ? GE::TILE : 0) + rb * 1024;
-    lds_dma16_nt(src, dst);
-  }
+  const bool is_v = li >= GE::LOADS / 2;
+  const int rb = is_v ? li - GE::LOADS / 2 : li;
+  const int row = rb * GE::RPL + rsub;
+  const int key = min(t0 + row, tend - 1);
+  const int c = pch ^ (is_v ? vswz<D>(row) : kswz<D>(row));
+  // a 1 KB load covers RPL (4 or 8) aligned rows: never crosses a 16-token page
+  const uint16_t* src = key_row<PAGED>(p, is_v ? p.v_cache : p.k_cache, b, g, key, D) + c * 8;
+  lds_dma16_nt_m0(src, stage + (is_v ? GE::TILE : 0) + rb * 1024);
 }
 
-// Wait until at most `after` stages of this wave's loads are still in flight.
-// Waves issue at least LOADS/G loads per stage, so counting with that minimum
-// can only wait for more completions than needed.
-template <int D, int G>
-__device__ __forceinline__ void wait_stages(int after) {
-  constexpr int L = Geo<D>::LOADS / G;
-  if (after >= 2) wait_vmcnt<(2 * L < 63 ? 2 * L : 63)>();
-  else if (after == 1) wait_vmcnt<(L < 63 ? L : 63)>();
-  else wait_vmcnt<0>();
+// Max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with the
+// gfx950 row-swap permutes (VALU, no LDS round trip).
+__device__ __forceinline__ float max_across_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
-// One wave: 16 block rows of one query head against one TK-key stage in LDS,
-// in NKK = TK/32 sub-steps of 32 keys.  Keys [0, nvalid) of the stage are real,
-// the rest are masked out (sub-steps past nvalid are skipped).
-template <int D, bool PLO>
+// bf16 hi/lo split of two probabilities: hi = RNE(x), lo = RNE(x - hi), packed.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0, x1}, b16x2));
+  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0 - h0, x1 - h1}, b16x2));
+}
+
+// One wave: 16 block rows of one query head against one 32-key stage in LDS.
+// Keys [0, nvalid) of the stage are real (nvalid >= 1), the rest are masked out.
+// Scores stay unscaled until the exponent: p = exp2(s * scale_log2 - m), with the
+// running max m kept in scaled units (scale > 0, so max and scaling commute).
+template <int D>
 __device__ __forceinline__ void attend_stage(const char* stage, const bf16x8* qB, f32x4* o, float& m,
                                              float& lsum, int lane, int nvalid, float scale_log2) {
   using GE = Geo<D>;
-  constexpr int KS = D / 32, DT = D / 16, NKK = TK / 32;
+  static_assert(TK == 32, "one 32-key MFMA step per stage");
+  constexpr int KS = D / 32, DT = D / 16;
   const int r = lane & 15, q = lane >> 4;
   const char* kt = stage;
   const char* vt = stage + GE::TILE;
-  const int nkk = (nvalid + 31) >> 5;
-  float x[NKK][2][4];
+
+  // S^T = K Q^T for the two 16-key tiles j: MFMA row r of tile j is key
+  // 8(r/4) + 4j + r%4, so lane (r, q) ends up with keys 8q + 4j + v.  The two
+  // accumulation chains are interleaved.
+  bf16x8 ka[2][KS];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
+  for (int j = 0; j < 2; ++j) {
+    const int t = 8 * (r >> 2) + 4 * j + (r & 3);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (kk < nkk) {
-        const int t = 32 * kk + 8 * (r >> 2) + 4 * j + (r & 3);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + t * GE::ROW + (((ks * 4 + q) ^ kswz<D>(t)) << 4));
-          acc = mfma16x16x32(a, qB[ks], acc);
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) x[kk][j][v] = acc[v] * scale_log2;
-      } else {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) x[kk][j][v] = -INFINITY;
-      }
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      ka[j][ks] = *reinterpret_cast<const bf16x8*>(kt + t * GE::ROW + (((ks * 4 + q) ^ kswz<D>(t)) << 4));
   }
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    s0 = mfma16x16x32(ka[0][ks], qB[ks], s0);
+    s1 = mfma16x16x32(ka[1][ks], qB[ks], s1);
+  }
+  float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};  // key 8q + e
   if (nvalid < TK) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (32 * kk + 8 * q + 4 * j + v >= nvalid) x[kk][j][v] = -INFINITY;
+    for (int e = 0; e < 8; ++e)
+      if (8 * q + e >= nvalid) x[e] = -INFINITY;
   }
-  float mt = x[0][0][0];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) mt = fmaxf(mt, x[kk][j][v]);
-  mt = fmaxf(mt, __shfl_xor(mt, 16));
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  mt = max_across_rows(mt) * scale_log2;
   // Lazy rescaling: the reference max m moves only when a stage max exceeds it
   // by more than 8 (log2 units), so probabilities stay <= 2^8 and the O / sum
   // rescale (all accumulators) runs a handful of times per split instead of once
@@ -188,56 +186,161 @@ __device__ __forceinline__ void attend_stage(const char* stage, const bf16x8* qB
   }
   float psum = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float e = __builtin_amdgcn_exp2f(x[kk][j][v] - m);
-        x[kk][j][v] = e;
-        psum += e;
-      }
+  for (int e = 0; e < 8; ++e) {
+    x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], scale_log2, -m));
+    psum += x[e];
+  }
   lsum += psum;
 
+  // P as the B operand of O^T += V^T P^T, as a bf16 hi/lo pair (P = hi + lo).
+  u32x4 hw, lw;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t hh, ll;
+    split_bf16x2(x[2 * i], x[2 * i + 1], hh, ll);
+    hw[i] = hh;
+    lw[i] = ll;
+  }
+  const bf16x8 ph = __builtin_bit_cast(bf16x8, hw), pl = __builtin_bit_cast(bf16x8, lw);
+
   // V^T operand via transpose reads: lane (group q, index i) points at key row
-  // 32kk + 8q + 4h + i/4, dims 4(i%4)..+3 of the 16-dim tile; it receives dim
-  // dt*16 + i of keys 32kk + 8q + 4h .. +3.
+  // 8q + 4h + i/4, dims 4(i%4)..+3 of the 16-dim tile; it receives dim dt*16 + i
+  // of keys 8q + 4h .. +3.
   const int trow0 = 8 * q + (r >> 2);
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    if (kk >= nkk) break;
-    bf16x8 ph, pl;
+  for (int dt = 0; dt < DT; ++dt) {
+    i16x4 part[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const __bf16 hi = static_cast<__bf16>(x[kk][j][v]);
-        ph[4 * j + v] = hi;
-        if constexpr (PLO) pl[4 * j + v] = static_cast<__bf16>(x[kk][j][v] - static_cast<float>(hi));
-      }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      i16x4 part[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = 32 * kk + trow0 + 4 * h;
-        const int c = 2 * dt + ((r & 3) >> 1);
-        const char* addr = vt + t * GE::ROW + ((c ^ vswz<D>(t)) << 4) + (r & 1) * 8;
-        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(addr));
-      }
-      const i16x8 cat = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, cat);
-      o[dt] = mfma16x16x32(a, ph, o[dt]);
-      if constexpr (PLO) o[dt] = mfma16x16x32(a, pl, o[dt]);
+    for (int h = 0; h < 2; ++h) {
+      const int t = trow0 + 4 * h;
+      const int c = 2 * dt + ((r & 3) >> 1);
+      const char* addr = vt + t * GE::ROW + ((c ^ vswz<D>(t)) << 4) + (r & 1) * 8;
+      part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(addr));
     }
+    const i16x8 cat = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, cat);
+    o[dt] = mfma16x16x32(a, ph, o[dt]);
+    o[dt] = mfma16x16x32(a, pl, o[dt]);
   }
 }
 
-template <int D, int G, bool PAGED, bool PLO>
-__global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
+// Partial results of a split go through to memory (system-scope stores bypass
+// every cache and complete only once written), so the workgroup that merges them
+// can read them with system-scope loads without any cache maintenance: no L2
+// writeback or invalidate is needed for the hand-off, only completion of the
+// stores before the arrival counter is bumped.
+__device__ __forceinline__ void st_through(float* dst, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+// 16-byte form (the completion is awaited with an explicit vmcnt wait).
+__device__ __forceinline__ void st_through4(float* dst, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" : : "v"(dst), "v"(v) : "memory");
+}
+__device__ __forceinline__ void ld_through(const float* src, float& a, float& b) {
+  const uint64_t v =
+      __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  a = __uint_as_float((uint32_t)v);
+  b = __uint_as_float((uint32_t)(v >> 32));
+}
+__device__ __forceinline__ f32x4 ld_through4(const float* src) {
+  float a0, a1, a2, a3;
+  ld_through(src, a0, a1);
+  ld_through(src + 2, a2, a3);
+  return (f32x4){a0, a1, a2, a3};
+}
+
+// Issue this wave's share of the loads of stage pack `pk` (stages NP*pk ..
+// NP*pk + NP-1): NP * LOADS wave-wide loads dealt round-robin over the NW waves.
+// Clamped per-row addressing (used for paged caches and for a pack that reaches
+// past the split's last key).
+template <int D, int NW, int NP, bool PAGED>
+__device__ __forceinline__ void issue_pack(const AttnParams& p, uint32_t ring, int b, int g, int kb, int ke, int pk,
+                                           int w, int lane) {
   using GE = Geo<D>;
+#pragma unroll
+  for (int li = w; li < NP * GE::LOADS; li += NW) {
+    const int sub = li / GE::LOADS;
+    const int st = NP * pk + sub;
+    issue_load<D, PAGED>(p, ring + (st % NST) * GE::STAGE, b, g, kb + st * TK, ke, li - sub * GE::LOADS, lane);
+  }
+}
+
+// Per-wave load plan of a dense cache for packs that lie inside the split: load k
+// of this wave (index li = w + k*NW of the pack) reads from the K or V base of
+// the pack at a per-lane byte offset that is the same for every pack.
+template <int D, int NW, int NP>
+struct DensePlan {
+  static constexpr int NL = (NP * Geo<D>::LOADS + NW - 1) / NW;  // loads per wave per pack (upper bound)
+  uint32_t voff[NL];   // per-lane byte offset from the pack base
+  uint32_t lds_off[NL];  // LDS byte offset of the load within the ring, for pack 0
+  bool is_v[NL];
+  bool live[NL];
+};
+
+template <int D, int NW, int NP>
+__device__ __forceinline__ DensePlan<D, NW, NP> dense_plan(int w, int lane) {
+  using GE = Geo<D>;
+  DensePlan<D, NW, NP> pl;
+  const int rsub = lane / GE::NCH, pch = lane % GE::NCH;
+#pragma unroll
+  for (int k = 0; k < pl.NL; ++k) {
+    const int li = w + k * NW;
+    pl.live[k] = li < NP * GE::LOADS;
+    const int sub = li / GE::LOADS, lj = li - sub * GE::LOADS;
+    const bool is_v = lj >= GE::LOADS / 2;
+    const int rb = is_v ? lj - GE::LOADS / 2 : lj;
+    const int row = rb * GE::RPL + rsub;
+    const int c = pch ^ (is_v ? vswz<D>(row) : kswz<D>(row));
+    pl.is_v[k] = is_v;
+    pl.voff[k] = (uint32_t)((sub * TK + row) * GE::ROW + c * 16);
+    pl.lds_off[k] = (uint32_t)(sub * GE::STAGE + (is_v ? GE::TILE : 0) + rb * 1024);
+  }
+  return pl;
+}
+
+// Fast issue of pack `pk` of a dense cache (every key of the pack < ke):
+// k_pack / v_pack are the byte addresses of the pack's first key row.
+template <int D, int NW, int NP>
+__device__ __forceinline__ void issue_pack_dense(const DensePlan<D, NW, NP>& pl, const char* k_pack,
+                                                 const char* v_pack, uint32_t lds_ring, int pk) {
+  using GE = Geo<D>;
+  const uint32_t slot = (uint32_t)((pk % (NST / NP)) * NP * GE::STAGE);
+#pragma unroll
+  for (int k = 0; k < pl.NL; ++k)
+    if (pl.live[k]) lds_dma16_nt_sv(pl.is_v[k] ? v_pack : k_pack, pl.voff[k], lds_ring + slot + pl.lds_off[k]);
+}
+
+// Wait until this wave has at most `after` (<= A) packs of loads in flight.  Every
+// wave issues at least L loads per pack; counting with that minimum (and capping
+// at the counter's 63) can only wait for more completions than needed.
+template <int L, int A>
+__device__ __forceinline__ void wait_packs(int after) {
+  if constexpr (A == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (after >= A) wait_vmcnt<(A * L < 63 ? A * L : 63)>();
+    else wait_packs<L, A - 1>(after);
+  }
+}
+
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnParams p) {
+  using GE = Geo<D>;
+  constexpr int NGRP = ngrp<G>();
+  constexpr int NW = NGRP * G;    // waves per workgroup
+  constexpr int NPK = NST / NGRP;  // packs in the ring
+  constexpr int LPK = NGRP * GE::LOADS / NW;  // loads per wave per pack (minimum)
   constexpr int KS = D / 32, DT = D / 16, HALF = D / 2;
-  __shared__ __attribute__((aligned(1024))) char lds[NST * GE::STAGE];
+  static_assert(NST % NGRP == 0 && NPK >= 3, "ring of stage packs, two or more packs in flight");
+  static_assert(LPK >= 1, "every wave issues loads in every pack");
+  // The stage ring, then (two wave groups only) the Q rows [16][G*D] bf16 and the
+  // cos and sin rows [16][D/2] fp32 of positions L..L+15, staged through LDS by the
+  // same DMA as the context.
+  constexpr int QST = NGRP > 1 ? 32 * D * (G + 2) : 0;
+  __shared__ __attribute__((aligned(1024))) char lds[NST * GE::STAGE + QST];
+  char* const qst = lds + NST * GE::STAGE;
+  __shared__ uint32_t s_last;
 
   // XCD-aware decode: WG i runs on XCD i % 8; every split of a unit shares one XCD.
   const int i_wg = blockIdx.x;
@@ -261,19 +364,83 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w / G, hw = w - grp * G;  // wave group, head within the kv group
   const int r = lane & 15, q = lane >> 4;
-  const int h = g * G + w;
+  const int h = g * G + hw;
 
-  // Start the context stream before anything else.
+  // Start the context stream before anything else: packs 0 .. NPK-2.  Dense
+  // packs inside the split take the scalar-base path; the rest clamp per row.
   const int n_st = (ke - kb + TK - 1) / TK;
+  const int n_pk = (n_st + NGRP - 1) / NGRP;
+  const int n_fast = PAGED ? 0 : (ke - kb) / (NGRP * TK);  // packs with every key < ke
+  const DensePlan<D, NW, NGRP> dpl = dense_plan<D, NW, NGRP>(w, lane);
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)(LDS_AS char*)lds;
+  const uint32_t qst_lds = lds_ring + NST * GE::STAGE;
+  const int64_t unit_row0 = ((int64_t)b * p.n_kv_heads + g) * p.capacity + kb;  // dense: row of key kb
+  const char* k_split = reinterpret_cast<const char*>(p.k_cache) + unit_row0 * GE::ROW;
+  const char* v_split = reinterpret_cast<const char*>(p.v_cache) + unit_row0 * GE::ROW;
+  auto issue = [&](int pk) {
+    if (pk < n_fast) {
+      const int64_t off = (int64_t)pk * NGRP * TK * GE::ROW;
+      issue_pack_dense<D, NW, NGRP>(dpl, k_split + off, v_split + off, lds_ring, pk);
+    } else {
+      issue_pack<D, NW, NGRP, PAGED>(p, lds_ring, b, g, kb, ke, pk, w, lane);
+    }
+  };
+  constexpr int QL = G * D / 32, CL = D / 32;  // wave loads: Q rows, cos rows (sin the same)
+  if constexpr (NGRP > 1) {
+    // Q / cos / sin go first, so that waiting for them leaves the context stream in flight.
+    const int qrow_chunks = G * D / 8;
+    const char* qsrc = reinterpret_cast<const char*>(p.q_blk + (((int64_t)b * kBlock) * p.n_q_heads + g * G) * D);
+    const char* csrc = reinterpret_cast<const char*>(p.rope_cos + (int64_t)L * HALF);
+    const char* ssrc = reinterpret_cast<const char*>(p.rope_sin + (int64_t)L * HALF);
 #pragma unroll
-  for (int st = 0; st < NST - 1; ++st)
-    if (st < n_st) issue_stage<D, G, PAGED>(p, lds + st * GE::STAGE, b, g, kb + st * TK, ke, w, lane);
+    for (int li = w; li < QL + 2 * CL; li += NW) {
+      if (li < QL) {
+        const int ci = li * 64 + lane, row = ci / qrow_chunks, col = ci - row * qrow_chunks;
+        lds_dma16_m0(qsrc + ((int64_t)row * p.n_q_heads * D + col * 8) * 2, qst_lds + li * 1024);
+      } else if (li < QL + CL) {
+        lds_dma16_m0(csrc + (int64_t)((li - QL) * 64 + lane) * 16, qst_lds + li * 1024);
+      } else {
+        lds_dma16_m0(ssrc + (int64_t)((li - QL - CL) * 64 + lane) * 16, qst_lds + li * 1024);
+      }
+    }
+  }
+#pragma unroll
+  for (int pk = 0; pk < NPK - 1; ++pk)
+    if (pk < n_pk) issue(pk);
 
   // Q of head h: rows at positions L + r, RoPE in fp32, rounded to bf16, as the
   // B operand of S^T = K Q^T (lane holds dims 32*ks + 8*q .. +8 of row r).
   bf16x8 qB[KS];
-  {
+  if constexpr (NGRP > 1) {
+    wait_packs<LPK, NPK - 1>(n_pk);  // this wave's Q / cos / sin loads landed
+    __syncthreads();                 // ... and every other wave's
+    const char* qrow = qst + (r * G * D + hw * D) * 2;
+    const float* cr = reinterpret_cast<const float*>(qst + 32 * G * D) + r * HALF;
+    const float* sr = reinterpret_cast<const float*>(qst + 32 * G * D + 32 * D) + r * HALF;
+    u32x4 raw[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) raw[ks] = *reinterpret_cast<const u32x4*>(qrow + (32 * ks + 8 * q) * 2);
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks) {
+      const int j0 = 32 * ks + 8 * q;
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(cr + j0), c1 = *reinterpret_cast<const f32x4*>(cr + j0 + 4);
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(sr + j0), s1 = *reinterpret_cast<const f32x4*>(sr + j0 + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t wl = raw[ks][e >> 1], wh = raw[ks + KS / 2][e >> 1];
+        const float lo = (e & 1) ? bf16_hi(wl) : bf16_lo(wl);
+        const float hi = (e & 1) ? bf16_hi(wh) : bf16_lo(wh);
+        const float c = e < 4 ? c0[e] : c1[e - 4];
+        const float sn = e < 4 ? s0[e] : s1[e - 4];
+        float ylo, yhi;
+        rope_pair(lo, hi, c, sn, ylo, yhi);
+        qB[ks][e] = static_cast<__bf16>(ylo);
+        qB[ks + KS / 2][e] = static_cast<__bf16>(yhi);
+      }
+    }
+  } else {
     const uint16_t* qrow = p.q_blk + (((int64_t)b * kBlock + r) * p.n_q_heads + h) * D;
     u32x4 raw[KS];
 #pragma unroll
@@ -305,27 +472,27 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
   for (int dt = 0; dt < DT; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
 
-  // Context keys [kb, ke) through the stage ring.
-  for (int it = 0; it < n_st; ++it) {
-    wait_stages<D, G>(min(NST - 2, n_st - 1 - it));
-    __syncthreads();  // stage `it` landed for every wave; stage it-1 is free again
-    if (it + NST - 1 < n_st)
-      issue_stage<D, G, PAGED>(p, lds + ((it + NST - 1) % NST) * GE::STAGE, b, g, kb + (it + NST - 1) * TK, ke,
-                               w, lane);
-    attend_stage<D, PLO>(lds + (it % NST) * GE::STAGE, qB, o, m, lsum, lane, min(TK, ke - kb - it * TK),
-                         p.scale_log2);
+  // Context keys [kb, ke): wave group grp consumes stage NGRP*pk + grp of each pack.
+  for (int pk = 0; pk < n_pk; ++pk) {
+    wait_packs<LPK, NPK - 2>(n_pk - 1 - pk);
+    __syncthreads();  // pack pk landed for every wave; pack pk-1 is free again
+    if (pk + NPK - 1 < n_pk) issue(pk + NPK - 1);
+    const int st = NGRP * pk + grp;
+    if (st < n_st)
+      attend_stage<D>(lds + (st % NST) * GE::STAGE, qB, o, m, lsum, lane, min(TK, ke - kb - st * TK),
+                            p.scale_log2);
   }
 
-  // Block keys (positions L .. L+15), handled by the last split of the unit:
+  // Block keys (positions L .. L+15), handled by wave group 0 of the last split:
   // rotated K rows and V rows written into stage 0, rows 16..31 zero.
   if (last_split) {
     __syncthreads();
     char* kt = lds;
     char* vt = lds + GE::TILE;
-    for (int off = tid * 16; off < GE::STAGE; off += 64 * G * 16)
+    for (int off = tid * 16; off < GE::STAGE; off += 64 * NW * 16)
       *reinterpret_cast<u32x4*>(lds + off) = (u32x4){0u, 0u, 0u, 0u};
     __syncthreads();
-    for (int id = tid; id < kBlock * HALF; id += 64 * G) {
+    for (int id = tid; id < kBlock * HALF; id += 64 * NW) {
       const int t = id / HALF, j = id - t * HALF;
       const int64_t rowoff = (((int64_t)b * kBlock + t) * p.n_kv_heads + g) * D;
       const uint16_t* kr = p.k_blk + rowoff;
@@ -341,8 +508,39 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
       *reinterpret_cast<uint16_t*>(vt + t * GE::ROW + (((j2 >> 3) ^ vswz<D>(t)) << 4) + 2 * (j2 & 7)) = vr[j2];
     }
     __syncthreads();
-    attend_stage<D, PLO>(lds, qB, o, m, lsum, lane, kBlock, p.scale_log2);
+    if (grp == 0) attend_stage<D>(lds, qB, o, m, lsum, lane, kBlock, p.scale_log2);
   }
+
+  // Combine the wave groups in LDS (stage slots 2.. are free: every wave passed
+  // its last stage): group g > 0 hands over (m, lsum, O) per lane, group 0 folds.
+  // Lane layout of O: dims 16*dt + 4*q + v of row r.
+  if constexpr (NGRP > 1) {
+    __syncthreads();
+    float* xo = reinterpret_cast<float*>(lds + 2 * GE::STAGE);          // [NGRP-1][G][DT][64][4]
+    float* xml = xo + (NGRP - 1) * G * DT * 256;                          // [NGRP-1][G][64][2]
+    if (grp > 0) {
+      float* po = xo + ((grp - 1) * G + hw) * DT * 256;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (dt * 64 + lane) * 4) = o[dt];
+      xml[(((grp - 1) * G + hw) * 64 + lane) * 2 + 0] = m;
+      xml[(((grp - 1) * G + hw) * 64 + lane) * 2 + 1] = lsum;
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int k = 1; k < NGRP; ++k) {
+      const float* po = xo + ((k - 1) * G + hw) * DT * 256;
+      const float mk = xml[(((k - 1) * G + hw) * 64 + lane) * 2 + 0];
+      const float lk = xml[(((k - 1) * G + hw) * 64 + lane) * 2 + 1];
+      const float mn = fmaxf(m, mk);  // finite: group 0 always saw a key
+      const float a0 = __builtin_amdgcn_exp2f(m - mn), a1 = __builtin_amdgcn_exp2f(mk - mn);
+      lsum = lsum * a0 + lk * a1;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] = o[dt] * a0 + *reinterpret_cast<const f32x4*>(po + (dt * 64 + lane) * 4) * a1;
+      m = mn;
+    }
+  }
+  // From here on only wave group 0 (G waves, one per query head) runs.
 
   float lt = lsum + __shfl_xor(lsum, 16);
   lt += __shfl_xor(lt, 32);
@@ -355,15 +553,89 @@ __global__ __launch_bounds__(64 * G) void block_attn_kernel(AttnParams p) {
     return;
   }
 
-  // Split partials; attn_merge_kernel combines them after this kernel.
-  const int64_t slot = ((int64_t)u * p.n_splits + s) * G + w;
+  const int64_t slot = ((int64_t)u * p.n_splits + s) * G + hw;
   float* po = p.ws_o + slot * (DT * 256);
+  if (!p.fused) {
+    // attn_merge_kernel combines the splits after this kernel.
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (dt * 64 + lane) * 4) = o[dt];
-  if (q == 0) {
-    p.ws_ml[(slot * 16 + r) * 2 + 0] = m;
-    p.ws_ml[(slot * 16 + r) * 2 + 1] = lt;
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (dt * 64 + lane) * 4) = o[dt];
+    if (q == 0) {
+      p.ws_ml[(slot * 16 + r) * 2 + 0] = m;
+      p.ws_ml[(slot * 16 + r) * 2 + 1] = lt;
+    }
+    return;
   }
+
+  // Fused merge: write the partial through, count arrivals per unit; the split
+  // that arrives last combines all of them (log-sum-exp, in split order).
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) st_through4(po + (dt * 64 + lane) * 4, o[dt]);
+  if (q == 0) st_through(p.ws_ml + (slot * 16 + r) * 2, m, lt);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_vmcnt<0>();  // this wave's partial is in memory
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();  // ... and every other wave's of this group (group 1 has exited)
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(p.count + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t last = prev == (uint32_t)(ns - 1) ? 1u : 0u;
+    if (last) __hip_atomic_store(p.count + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(s_last)) return;
+
+  // Merge in chunks of CH splits.  The loads of the first chunk and of every
+  // split's (m, l) are all issued before any result is used (addresses clamped to
+  // a real split, the own split re-read and ignored), so for up to CH splits the
+  // merge costs one memory round trip.  CH = 4 needs ~210 VGPRs, which only
+  // workgroups of up to 8 waves (2 per SIMD) can give a wave.
+  constexpr int CH = NW <= 8 ? 4 : 2;
+  const int64_t slot0 = (int64_t)u * p.n_splits * G + hw;  // slot of split sp: slot0 + sp * G
+  f32x4 part[CH][DT];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const float* ps = p.ws_o + (slot0 + (int64_t)min(c0 + k, ns - 1) * G) * (DT * 256);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) part[k][dt] = ld_through4(ps + (dt * 64 + lane) * 4);
+    }
+  };
+  load_chunk(0);
+  float mv[kMaxFused], lv[kMaxFused];
+#pragma unroll
+  for (int sp = 0; sp < kMaxFused; ++sp) {
+    const int spc = min(sp, ns - 1);
+    ld_through(p.ws_ml + ((slot0 + (int64_t)spc * G) * 16 + r) * 2, mv[sp], lv[sp]);
+  }
+#pragma unroll
+  for (int sp = 0; sp < kMaxFused; ++sp) {
+    if (sp == s) { mv[sp] = m; lv[sp] = lt; }
+    if (sp >= ns) { mv[sp] = -INFINITY; lv[sp] = 0.f; }
+  }
+  float mmax = mv[0];
+#pragma unroll
+  for (int sp = 1; sp < kMaxFused; ++sp) mmax = fmaxf(mmax, mv[sp]);
+  float den = 0.f;
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c0 = 0; c0 < kMaxFused; c0 += CH) {
+    if (c0 >= ns) break;
+    if (c0 > 0) load_chunk(c0);
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int sp = c0 + k;
+      if (sp >= ns) break;
+      const float wgt = __builtin_amdgcn_exp2f(mv[sp] - mmax);
+      den += wgt * lv[sp];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] += wgt * (sp == s ? o[dt] : part[k][dt]);
+    }
+  }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(outp + dt * 16) = acc[dt] * inv;
 }
 
 // Log-sum-exp merge of the split partials: one workgroup per (unit, query head),
@@ -406,8 +678,9 @@ template <int D, int G, bool PAGED>
 hipError_t launch_t(const AttnParams& p, hipStream_t stream) {
   const int groups = (p.n_units + kNumXcd - 1) / kNumXcd;
   const int grid = kNumXcd * p.n_splits * groups;
-  hipLaunchKernelGGL((block_attn_kernel<D, G, PAGED, true>), dim3(grid), dim3(64 * G), 0, stream, p);
-  if (p.n_splits > 1) hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(p.n_units * G), dim3(2 * D), 0, stream, p, G);
+  hipLaunchKernelGGL((block_attn_kernel<D, G, PAGED>), dim3(grid), dim3(64 * ngrp<G>() * G), 0, stream, p);
+  if (p.n_splits > 1 && !p.fused)
+    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(p.n_units * G), dim3(2 * D), 0, stream, p, G);
   return hipGetLastError();
 }
 
@@ -432,17 +705,20 @@ AttnPlan plan_block_attn(int batch, int n_q_heads, int n_kv_heads, int head_dim,
   AttnPlan pl{};
   const int64_t units = (int64_t)batch * n_kv_heads;
   const int group = n_q_heads / n_kv_heads;
-  // Aim for ~2 workgroups per CU over the longest sequence, with at least 256 keys
-  // per split so the per-split fixed cost (Q load, partial write) stays small.
-  const int64_t target_wg = 2LL * (num_cu > 0 ? num_cu : 256);
+  // One workgroup per CU over the longest sequence, with at least 256 keys per
+  // split so the per-split fixed cost (Q load, partial write) stays small.
+  const int64_t target_wg = num_cu > 0 ? num_cu : 256;
   int64_t kps = (units * (int64_t)max_ctx + target_wg - 1) / target_wg;
-  kps = ((kps + TK - 1) / TK) * TK;
+  kps = ((kps + 2 * TK - 1) / (2 * TK)) * (2 * TK);
   if (kps < 256) kps = 256;
   if (kps > 8192) kps = 8192;
   pl.kps = (int)kps;
   pl.n_splits = max_ctx > 0 ? (int)((max_ctx + kps - 1) / kps) : 1;
+  pl.fused = pl.n_splits <= kMaxFused;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 256;  // word 0: device error mask
+  pl.off_cnt = off;  // per-unit arrival counters (fused merge), left at zero by every call
+  off = align(off + sizeof(uint32_t) * (size_t)units);
   pl.off_ml = off;
   off = align(off + sizeof(float) * 2 * 16 * (size_t)group * pl.n_splits * units);
   pl.off_o = off;

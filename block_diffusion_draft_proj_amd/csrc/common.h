@@ -79,6 +79,29 @@ __device__ __forceinline__ void lds_dma16(const void* src, char* lds_base) {
                : "=&s"(saved) : "v"(src), "s"(m0) : "memory");
 }
 
+// Same load addressed as a wave-uniform base (SGPR pair) plus a 32-bit per-lane
+// byte offset, into LDS byte address `m0` (wave-uniform): no 64-bit address math
+// per lane.
+__device__ __forceinline__ void lds_dma16_nt_sv(const void* sbase, uint32_t voff, uint32_t m0) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(m0) : "memory");
+}
+
+// Non-temporal global_load_lds into LDS byte address `m0` (wave-uniform).
+__device__ __forceinline__ void lds_dma16_nt_m0(const void* src, uint32_t m0) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(m0) : "memory");
+}
+
+// global_load_lds (cached) into LDS byte address `m0` (wave-uniform).
+__device__ __forceinline__ void lds_dma16_m0(const void* src, uint32_t m0) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(m0) : "memory");
+}
+
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
 template <int N>

@@ -50,6 +50,8 @@ struct AttnParams {
   float* ws_o;      // [units][n_splits][G][D/16][64 lanes][4] partial outputs
   float* ws_ml;     // [units][n_splits][G][16][2] running max (log2 domain) and sum
   uint32_t* err;    // sticky device error word
+  uint32_t* count;  // [units] arrival counters of the fused merge (zero between calls)
+  int fused;        // 1: the last split of a unit merges; 0: attn_merge_kernel does
   int batch, n_q_heads, n_kv_heads;
   int capacity;     // dense rows per (seq, head) | page-table columns
   int num_pages;
@@ -62,8 +64,9 @@ struct AttnParams {
 struct AttnPlan {
   int kps;
   int n_splits;
+  bool fused;
   size_t ws_bytes;
-  size_t off_ml, off_o;
+  size_t off_cnt, off_ml, off_o;
 };
 AttnPlan plan_block_attn(int batch, int n_q_heads, int n_kv_heads, int head_dim, int max_ctx, int num_cu);
 hipError_t launch_block_attn(const AttnParams& p, int head_dim, int group, bool paged, hipStream_t stream);

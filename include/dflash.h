@@ -27,9 +27,11 @@
  *   - Every argument is validated on the host BEFORE anything is launched.  On
  *     any error nothing is enqueued and no output is touched.
  *   - Workspaces are caller-owned device buffers of at least the size the
- *     matching *_workspace_size() query returns.  Apart from word 0 their
- *     contents need no initialisation and carry nothing between calls, so one
- *     buffer can serve any number of calls on the same stream.  Calls that run
+ *     matching *_workspace_size() query returns.  Zero a workspace once before
+ *     its first use; every call leaves it fit for the next one (the block
+ *     attention keeps per-sequence-head arrival counters in it, which each call
+ *     returns to zero), so one buffer can serve any number of calls on the same
+ *     stream, at any sizes up to the ones it was sized for.  Calls that run
  *     concurrently (different streams) need distinct workspaces.
  *   - Word 0 of every workspace is a sticky device-side error mask
  *     (DFLASH_DEVERR_*): data-dependent faults found by the kernels (a context
