@@ -526,30 +526,35 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
       xml[(((grp - 1) * G + hw) * 64 + lane) * 2 + 1] = lsum;
     }
     __syncthreads();
-    if (grp > 0) return;
+    if (grp == 0) {
 #pragma unroll
-    for (int k = 1; k < NGRP; ++k) {
-      const float* po = xo + ((k - 1) * G + hw) * DT * 256;
-      const float mk = xml[(((k - 1) * G + hw) * 64 + lane) * 2 + 0];
-      const float lk = xml[(((k - 1) * G + hw) * 64 + lane) * 2 + 1];
-      const float mn = fmaxf(m, mk);  // finite: group 0 always saw a key
-      const float a0 = __builtin_amdgcn_exp2f(m - mn), a1 = __builtin_amdgcn_exp2f(mk - mn);
-      lsum = lsum * a0 + lk * a1;
+      for (int k = 1; k < NGRP; ++k) {
+        const float* po = xo + ((k - 1) * G + hw) * DT * 256;
+        const float mk = xml[(((k - 1) * G + hw) * 64 + lane) * 2 + 0];
+        const float lk = xml[(((k - 1) * G + hw) * 64 + lane) * 2 + 1];
+        const float mn = fmaxf(m, mk);  // finite: group 0 always saw a key
+        const float a0 = __builtin_amdgcn_exp2f(m - mn), a1 = __builtin_amdgcn_exp2f(mk - mn);
+        lsum = lsum * a0 + lk * a1;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] = o[dt] * a0 + *reinterpret_cast<const f32x4*>(po + (dt * 64 + lane) * 4) * a1;
-      m = mn;
+        for (int dt = 0; dt < DT; ++dt)
+          o[dt] = o[dt] * a0 + *reinterpret_cast<const f32x4*>(po + (dt * 64 + lane) * 4) * a1;
+        m = mn;
+      }
     }
   }
-  // From here on only wave group 0 (G waves, one per query head) runs.
+  // Group 0 now holds the split's (m, lsum, O) of query head hw; the other
+  // groups only help with the merge below.
 
   float lt = lsum + __shfl_xor(lsum, 16);
   lt += __shfl_xor(lt, 32);
 
   float* outp = p.out + (((int64_t)b * kBlock + r) * p.n_q_heads + h) * D + 4 * q;
   if (ns == 1) {
-    const float inv = 1.f / lt;
+    if (grp == 0) {
+      const float inv = 1.f / lt;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(outp + dt * 16) = o[dt] * inv;
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(outp + dt * 16) = o[dt] * inv;
+    }
     return;
   }
 
@@ -557,24 +562,28 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   float* po = p.ws_o + slot * (DT * 256);
   if (!p.fused) {
     // attn_merge_kernel combines the splits after this kernel.
+    if (grp == 0) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (dt * 64 + lane) * 4) = o[dt];
-    if (q == 0) {
-      p.ws_ml[(slot * 16 + r) * 2 + 0] = m;
-      p.ws_ml[(slot * 16 + r) * 2 + 1] = lt;
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (dt * 64 + lane) * 4) = o[dt];
+      if (q == 0) {
+        p.ws_ml[(slot * 16 + r) * 2 + 0] = m;
+        p.ws_ml[(slot * 16 + r) * 2 + 1] = lt;
+      }
     }
     return;
   }
 
   // Fused merge: write the partial through, count arrivals per unit; the split
   // that arrives last combines all of them (log-sum-exp, in split order).
+  if (grp == 0) {
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) st_through4(po + (dt * 64 + lane) * 4, o[dt]);
-  if (q == 0) st_through(p.ws_ml + (slot * 16 + r) * 2, m, lt);
+    for (int dt = 0; dt < DT; ++dt) st_through4(po + (dt * 64 + lane) * 4, o[dt]);
+    if (q == 0) st_through(p.ws_ml + (slot * 16 + r) * 2, m, lt);
+  }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   wait_vmcnt<0>();  // this wave's partial is in memory
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();  // ... and every other wave's of this group (group 1 has exited)
+  __syncthreads();  // ... and every other wave's
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(p.count + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t last = prev == (uint32_t)(ns - 1) ? 1u : 0u;
@@ -584,41 +593,46 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(s_last)) return;
 
-  // Merge in chunks of CH splits.  The loads of the first chunk and of every
-  // split's (m, l) are all issued before any result is used (addresses clamped to
-  // a real split, the own split re-read and ignored), so for up to CH splits the
-  // merge costs one memory round trip.  CH = 4 needs ~210 VGPRs, which only
-  // workgroups of up to 8 waves (2 per SIMD) can give a wave.
-  constexpr int CH = NW <= 8 ? 4 : 2;
-  const int64_t slot0 = (int64_t)u * p.n_splits * G + hw;  // slot of split sp: slot0 + sp * G
-  f32x4 part[CH][DT];
+  // The merge: every wave (all groups) takes DTG of the DT dimension tiles of its
+  // head and reads every split's partial, its own included, from memory with
+  // system-scope (sc0 sc1) buffer loads.  All loads of a chunk of CH splits, and
+  // every split's (m, l), are issued before any is used (addresses clamped to a
+  // real split), so up to CH splits cost one memory round trip.
+  constexpr int DTG = DT / NGRP;
+  constexpr int CH = (DTG * 4 * kMaxFused <= 128 && NW <= 8) ? kMaxFused : (NW <= 8 ? 4 : 2);
+  constexpr int kSys = 1 | 16;  // cache policy sc0 | sc1: coherent with every agent
+  const int dt0 = grp * DTG;
+  const int64_t slot0 = (int64_t)u * p.n_splits * G;  // first slot of the unit
+  const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
+      p.ws_o + slot0 * (DT * 256), 0, p.n_splits * G * DT * 1024, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_ml = __builtin_amdgcn_make_buffer_rsrc(
+      p.ws_ml + slot0 * 32, 0, p.n_splits * G * 16 * 8, 0x00020000);
+  u32x4 part[CH][DTG];
   auto load_chunk = [&](int c0) {
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      const float* ps = p.ws_o + (slot0 + (int64_t)min(c0 + k, ns - 1) * G) * (DT * 256);
+      const int sl = min(c0 + k, ns - 1) * G + hw;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) part[k][dt] = ld_through4(ps + (dt * 64 + lane) * 4);
+      for (int j = 0; j < DTG; ++j)
+        part[k][j] = __builtin_amdgcn_raw_buffer_load_b128(rs_o, (sl * DT * 64 + (dt0 + j) * 64 + lane) * 16, 0, kSys);
     }
   };
   load_chunk(0);
   float mv[kMaxFused], lv[kMaxFused];
 #pragma unroll
   for (int sp = 0; sp < kMaxFused; ++sp) {
-    const int spc = min(sp, ns - 1);
-    ld_through(p.ws_ml + ((slot0 + (int64_t)spc * G) * 16 + r) * 2, mv[sp], lv[sp]);
-  }
-#pragma unroll
-  for (int sp = 0; sp < kMaxFused; ++sp) {
-    if (sp == s) { mv[sp] = m; lv[sp] = lt; }
-    if (sp >= ns) { mv[sp] = -INFINITY; lv[sp] = 0.f; }
+    const int sl = min(sp, ns - 1) * G + hw;
+    const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rs_ml, (sl * 16 + r) * 8, 0, kSys);
+    mv[sp] = sp < ns ? __uint_as_float(ml[0]) : -INFINITY;
+    lv[sp] = sp < ns ? __uint_as_float(ml[1]) : 0.f;
   }
   float mmax = mv[0];
 #pragma unroll
   for (int sp = 1; sp < kMaxFused; ++sp) mmax = fmaxf(mmax, mv[sp]);
   float den = 0.f;
-  f32x4 acc[DT];
+  f32x4 acc[DTG];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < DTG; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c0 = 0; c0 < kMaxFused; c0 += CH) {
     if (c0 >= ns) break;
@@ -630,12 +644,12 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
       const float wgt = __builtin_amdgcn_exp2f(mv[sp] - mmax);
       den += wgt * lv[sp];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] += wgt * (sp == s ? o[dt] : part[k][dt]);
+      for (int j = 0; j < DTG; ++j) acc[j] += wgt * __builtin_bit_cast(f32x4, part[k][j]);
     }
   }
   const float inv = 1.f / den;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(outp + dt * 16) = acc[dt] * inv;
+  for (int j = 0; j < DTG; ++j) *reinterpret_cast<f32x4*>(outp + (dt0 + j) * 16) = acc[j] * inv;
 }
 
 // Log-sum-exp merge of the split partials: one workgroup per (unit, query head),
