@@ -243,11 +243,26 @@ int dflash_ctx_proj(const dflash_dims* dims, int32_t n_rows, const void* const* 
   char* ws = static_cast<char*>(workspace);
   const uint16_t* c_src;
   int64_t ld_c;
+  uint16_t* c_pack = pl.kv_small ? reinterpret_cast<uint16_t*>(ws + pl.off_cp) : nullptr;
   if (has_fc) {
     GemmParams g{};
     for (int l = 0; l < n_layers; ++l) g.a_seg[l] = static_cast<const uint16_t*>(x_layers[l]);
     g.lda = ld_x;
     g.seg_k = d_target;
+    if (pl.fc_small) {
+      // the skinny product reads its activations packed step by step
+      PackParams pk{};
+      for (int l = 0; l < n_layers; ++l) pk.a_seg[l] = g.a_seg[l];
+      pk.lda = ld_x;
+      pk.seg_k = d_target;
+      pk.M = n_rows;
+      pk.K = k_fc;
+      pk.mp = pl.mp;
+      pk.xp = reinterpret_cast<uint16_t*>(ws + pl.off_xp);
+      if (launch_pack_rows(pk, stream) != hipSuccess) return DFLASH_ERR_LAUNCH;
+      g.xp = pk.xp;
+      g.mp = pl.mp;
+    }
     g.b0 = static_cast<const uint16_t*>(w_fc);
     g.b1 = g.b0;
     g.n_b0 = dims->hidden;
@@ -263,8 +278,10 @@ int dflash_ctx_proj(const dflash_dims* dims, int32_t n_rows, const void* const* 
     r.splits = pl.fc_splits;
     r.M = n_rows;
     r.N = dims->hidden;
-    r.c_buf = reinterpret_cast<uint16_t*>(ws + pl.off_c);
+    r.c_buf = pl.kv_small ? nullptr : reinterpret_cast<uint16_t*>(ws + pl.off_c);
     r.c_out = static_cast<uint16_t*>(c_out);
+    r.c_pack = c_pack;
+    r.mp = pl.mp;
     e = launch_fc_reduce(r, stream);
     if (e != hipSuccess) return DFLASH_ERR_LAUNCH;
     c_src = r.c_buf;
@@ -272,8 +289,21 @@ int dflash_ctx_proj(const dflash_dims* dims, int32_t n_rows, const void* const* 
   } else {
     c_src = static_cast<const uint16_t*>(x_layers[0]);
     ld_c = ld_x;
+    if (c_pack) {
+      PackParams pk{};
+      pk.a_seg[0] = c_src;
+      pk.lda = ld_x;
+      pk.seg_k = dims->hidden;
+      pk.M = n_rows;
+      pk.K = dims->hidden;
+      pk.mp = pl.mp;
+      pk.xp = c_pack;
+      if (launch_pack_rows(pk, stream) != hipSuccess) return DFLASH_ERR_LAUNCH;
+    }
   }
   GemmParams g{};
+  g.xp = c_pack;
+  g.mp = pl.mp;
   g.a_seg[0] = c_src;
   g.lda = ld_c;
   g.seg_k = dims->hidden;

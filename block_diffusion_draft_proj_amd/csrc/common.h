@@ -110,6 +110,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also orders global
+// memory, which makes every wave wait for all of its outstanding global loads
+// (vmcnt(0)) and so drains any register prefetch at each barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void set_dev_error(uint32_t* err_word, uint32_t bit) {
   __hip_atomic_fetch_or(err_word, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

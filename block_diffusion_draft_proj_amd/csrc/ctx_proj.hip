@@ -126,7 +126,161 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
   }
 }
 
-// C = bf16(sum over splits): 4 columns per thread.
+// Skinny product (M <= 128 rows of activations, the per-cycle case): a weight
+// stream.  Each workgroup owns 128 weight rows (4 waves x 32) and one K range,
+// and sees all 16*MT activation rows.  A 64-K stage holds the weight tile
+// (128 rows, 16 KB) and the activation tile (16*MT rows, MT x 2 KB); stages go
+// global -> swizzled LDS by global_load_lds through an SK_NS-stage ring (all of
+// LDS at MT = 8), so SK_NS-1 stages are in flight while one feeds the MFMAs.
+// Per stage a wave reads its own 32 weight rows (4 KB) and the whole activation
+// tile from LDS and does 2 x MT x 2 MFMAs; each weight byte crosses LDS twice
+// and each activation byte five times (vs. thirteen for a square-tile GEMM).
+// The activations come pre-packed step by step ([K/64][16*MT rows][64], see
+// pack_rows_kernel): a step's tile is one contiguous 16*MT x 128-byte block.
+// Read in place, its rows would be lda apart, and that strided pattern measured
+// 2.5x slower for the whole product at 128 rows x 20480 x 4096.
+constexpr int SK_WAVES = 4;
+constexpr int SK_RT = 2;                        // 16-row weight tiles per wave
+constexpr int SK_ROWS = SK_WAVES * SK_RT * 16;  // weight rows per workgroup (128)
+
+template <int MT>
+struct SkGeo {
+  static constexpr int W_TILE = SK_ROWS * BK * 2;             // 16 KB
+  static constexpr int X_TILE = 16 * MT * BK * 2;             // MT x 2 KB
+  static constexpr int STAGE = W_TILE + X_TILE;
+  static constexpr int NS = (160 * 1024) / STAGE < 6 ? (160 * 1024) / STAGE : 6;  // ring stages
+  static constexpr int LOADS = STAGE / 1024;                  // wave-wide 1 KB loads per stage
+  static constexpr int LW = LOADS / SK_WAVES;                 // per wave (every wave the same)
+  static_assert(LOADS % SK_WAVES == 0, "stage loads split evenly over the waves");
+  static_assert(NS >= 3, "two stages in flight");
+};
+
+template <int MT>
+__global__ __launch_bounds__(SK_WAVES * 64) void gemm_skinny_kernel(GemmParams p) {
+  using SG = SkGeo<MT>;
+  __shared__ __attribute__((aligned(1024))) char lds[SG::NS * SG::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, q = lane >> 4;
+  const int lrow = lane >> 3, pch = lane & 7;  // one wave-wide load = 8 rows x 128 bytes
+  // XCD-aware decode (workgroup i runs on XCD i % 8): every XCD works on as few K
+  // ranges as possible, so the activation slice of its range (16*MT rows x K/splits)
+  // stays in that XCD's L2 while all column tiles stream their weights past it.
+  // The planner makes `splits` a divisor or a multiple of 8.
+  const int splits = (p.K + p.k_per_split - 1) / p.k_per_split;
+  const int id = blockIdx.x;
+  int z, col;
+  if (splits % kNumXcd == 0) {
+    const int per = splits / kNumXcd, j = id / kNumXcd;
+    z = id % kNumXcd + kNumXcd * (j % per);
+    col = j / per;
+  } else {
+    z = id % splits;
+    col = id / splits;
+  }
+  const int n0 = col * SK_ROWS;
+  const int kbeg = z * p.k_per_split;
+  const int kend = min(p.K, kbeg + p.k_per_split);
+  const int n_st = (kend - kbeg) / BK;
+  const uint32_t ring = (uint32_t)(uintptr_t)(LDS_AS char*)lds;
+
+  // Loads of stage st: li < 16 weight rows 8li..8li+7, then activation rows
+  // 8(li-16).. (rows past N / M clamp to the last real row: every load stays in
+  // bounds and the extra results are never stored).
+  // Column tiles walk their K range from different starting steps, so the
+  // activation steps read at one time are spread over the range.
+  const int rot = n_st > 0 ? col % n_st : 0;
+  auto issue = [&](int st) {
+    const int ks = st + rot < n_st ? st + rot : st + rot - n_st;
+    const int k0 = kbeg + ks * BK;
+    const uint16_t* xstep = p.xp + (int64_t)(k0 / BK) * p.mp * BK;
+    const uint32_t stage = ring + (uint32_t)((st % SG::NS) * SG::STAGE);
+#pragma unroll
+    for (int i = 0; i < SG::LW; ++i) {
+      const int li = i * SK_WAVES + w;  // wave-uniform
+      if (li < SG::W_TILE / 1024) {
+        const int row = li * 8 + lrow;
+        const int n = min(n0 + row, p.N - 1);
+        const uint16_t* brow = n < p.n_b0 ? p.b0 + (int64_t)n * p.K : p.b1 + (int64_t)(n - p.n_b0) * p.K;
+        lds_dma16_nt_m0(brow + k0 + ((pch ^ ((row >> 1) & 7)) << 3), stage + li * 1024);
+      } else {
+        // packed activations: the 16*MT rows of step ks are one contiguous block
+        const int row = (li - SG::W_TILE / 1024) * 8 + lrow;
+        lds_dma16_m0(xstep + row * BK + ((pch ^ ((row >> 1) & 7)) << 3), stage + li * 1024);
+      }
+    }
+  };
+
+  f32x4 acc[SK_RT][MT];
+#pragma unroll
+  for (int rt = 0; rt < SK_RT; ++rt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < SG::NS - 1; ++st)
+    if (st < n_st) issue(st);
+  for (int it = 0; it < n_st; ++it) {
+    // stage `it` landed for this wave: at most min(NS-2, n_st-1-it) younger stages in flight
+    const int after = min(SG::NS - 2, n_st - 1 - it);
+    if (after >= 4) wait_vmcnt<(4 * SG::LW < 63 ? 4 * SG::LW : 63)>();
+    else if (after == 3) wait_vmcnt<3 * SG::LW>();
+    else if (after == 2) wait_vmcnt<2 * SG::LW>();
+    else if (after == 1) wait_vmcnt<SG::LW>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // every wave's part of stage `it` landed; stage it-1 is free again
+    if (it + SG::NS - 1 < n_st) issue(it + SG::NS - 1);
+    const char* sw = lds + (it % SG::NS) * SG::STAGE;
+    const char* sx = sw + SG::W_TILE;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      bf16x8 a[SK_RT], xb[MT];
+#pragma unroll
+      for (int rt = 0; rt < SK_RT; ++rt)
+        a[rt] = *reinterpret_cast<const bf16x8*>(sw + swz_off(w * 32 + rt * 16 + r, kh * 4 + q));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xb[mt] = *reinterpret_cast<const bf16x8*>(sx + swz_off(mt * 16 + r, kh * 4 + q));
+#pragma unroll
+      for (int rt = 0; rt < SK_RT; ++rt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = mfma16x16x32(a[rt], xb[mt], acc[rt][mt]);
+    }
+  }
+
+  // D layout: lane holds activation row 16*mt + r and weight rows 4q .. 4q+3 of
+  // the 16-row tile: 4 consecutive outputs of one row, one 16-byte store.
+  float* out = p.out + (int64_t)z * p.M * p.N;
+#pragma unroll
+  for (int rt = 0; rt < SK_RT; ++rt) {
+    const int n = n0 + w * 32 + rt * 16 + 4 * q;
+    if (n >= p.N) continue;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r;
+      if (m < p.M) *reinterpret_cast<f32x4*>(out + (int64_t)m * p.N + n) = acc[rt][mt];
+    }
+  }
+}
+
+// Activation rows -> [K/64][mp][64] packed steps (rows >= M zero): one 16-byte
+// chunk per thread, reads and writes both coalesced.
+__global__ __launch_bounds__(256) void pack_rows_kernel(PackParams p) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // chunk index
+  const int64_t per_step = (int64_t)p.mp * 8;
+  if (i >= (int64_t)(p.K / 64) * per_step) return;
+  const int st = (int)(i / per_step);
+  const int rem = (int)(i - st * per_step);
+  const int row = rem >> 3, c = rem & 7;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (row < p.M) {
+    const int k = st * 64 + c * 8;
+    const int seg = k / p.seg_k;
+    v = ld16(p.a_seg[seg] + (int64_t)row * p.lda + (k - seg * p.seg_k));
+  }
+  st16(p.xp + i * 8, v);
+}
+
+// C = bf16(sum over splits): 4 columns per thread; written row-major and/or packed.
 __global__ __launch_bounds__(256) void fc_reduce_kernel(FcReduceParams p) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
   const int64_t total = (int64_t)p.M * p.N / 4;
@@ -134,8 +288,13 @@ __global__ __launch_bounds__(256) void fc_reduce_kernel(FcReduceParams p) {
   f32x4 s = *reinterpret_cast<const f32x4*>(p.part + 4 * i);
   for (int z = 1; z < p.splits; ++z) s += *reinterpret_cast<const f32x4*>(p.part + (int64_t)z * p.M * p.N + 4 * i);
   const u32x2 v = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
-  *reinterpret_cast<u32x2*>(p.c_buf + 4 * i) = v;
+  if (p.c_buf) *reinterpret_cast<u32x2*>(p.c_buf + 4 * i) = v;
   if (p.c_out) *reinterpret_cast<u32x2*>(p.c_out + 4 * i) = v;
+  if (p.c_pack) {
+    const int64_t m = 4 * i / p.N;
+    const int n = (int)(4 * i - m * p.N);
+    *reinterpret_cast<u32x2*>(p.c_pack + ((int64_t)(n >> 6) * p.mp + m) * 64 + (n & 63)) = v;
+  }
 }
 
 // K/V rows: sum splits, rotate K (pairs j, j+d/2) at the row's position, round to
@@ -223,16 +382,35 @@ int k_per_split(int K, int splits) {
 
 }  // namespace
 
+// Skinny plan: one workgroup of 128 weight rows per CU, K split to fill the CUs,
+// while the fp32 partial sums (splits x M x N x 4 bytes, written and read back
+// once) stay within the weight bytes (N x K x 2) and every split keeps >= 2 steps.
+int skinny_splits(int N, int M, int K, int num_cu) {
+  const int tiles = (N + SK_ROWS - 1) / SK_ROWS;
+  int splits = (num_cu + tiles - 1) / tiles;
+  splits = min(splits, max(1, (int)((int64_t)K / (2 * (int64_t)(M > 0 ? M : 1)))));
+  splits = min(splits, max(1, K / (2 * BK)));
+  splits = max(1, splits);
+  // a divisor of 8 (1, 2, 4) or a multiple of 8, for the XCD-aware decode
+  if (splits >= 8) return splits - splits % 8;
+  return splits >= 4 ? 4 : (splits >= 2 ? 2 : 1);
+}
+
 ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_fc, int num_cu) {
   ProjPlan pl{};
-  const int target = 2 * (num_cu > 0 ? num_cu : 256);
+  const int cus = num_cu > 0 ? num_cu : 256;
+  const int target = 2 * cus;
   const int mtiles = (n_rows + GBM - 1) / GBM;
-  pl.fc_small = pl.kv_small = n_rows <= GBM;
+  pl.fc_small = pl.kv_small = n_rows <= GBM;  // skinny weight-streaming kernel
   if (has_fc) {
-    pl.fc_kps = k_per_split(k_fc, split_count(mtiles * ((hidden + GBN - 1) / GBN), n_rows, k_fc, target));
+    const int sp = pl.fc_small ? skinny_splits(hidden, n_rows, k_fc, cus)
+                               : split_count(mtiles * ((hidden + GBN - 1) / GBN), n_rows, k_fc, target);
+    pl.fc_kps = k_per_split(k_fc, sp);
     pl.fc_splits = (k_fc + pl.fc_kps - 1) / pl.fc_kps;  // every split has a non-empty K range
   }
-  pl.kv_kps = k_per_split(hidden, split_count(mtiles * ((kv_width + GBN - 1) / GBN), n_rows, hidden, target));
+  const int sp = pl.kv_small ? skinny_splits(kv_width, n_rows, hidden, cus)
+                             : split_count(mtiles * ((kv_width + GBN - 1) / GBN), n_rows, hidden, target);
+  pl.kv_kps = k_per_split(hidden, sp);
   pl.kv_splits = (hidden + pl.kv_kps - 1) / pl.kv_kps;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 256;  // word 0: device error mask
@@ -242,13 +420,41 @@ ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_
   if (has_fc) off = align(off + 2 * (size_t)n_rows * hidden);
   pl.off_kv = off;
   off = align(off + sizeof(float) * (size_t)pl.kv_splits * n_rows * kv_width);
+  pl.mp = 32 * ((n_rows + 31) / 32);
+  pl.off_xp = off;
+  if (pl.fc_small && has_fc) off = align(off + 2 * (size_t)k_fc * pl.mp);
+  pl.off_cp = off;
+  if (pl.kv_small) off = align(off + 2 * (size_t)hidden * pl.mp);
   pl.ws_bytes = off;
   return pl;
 }
 
-hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool /*small_m*/, hipStream_t stream) {
+template <int MT>
+void launch_skinny(const GemmParams& p, int splits, hipStream_t stream) {
+  dim3 grid(((p.N + SK_ROWS - 1) / SK_ROWS) * splits, 1, 1);
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT>), grid, dim3(SK_WAVES * 64), 0, stream, p);
+}
+
+hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStream_t stream) {
+  if (small_m) {
+    // activation tiles in pairs of 16 rows (stage loads split evenly over 4 waves)
+    switch ((p.M + 31) / 32) {
+      case 0:
+      case 1: launch_skinny<2>(p, splits, stream); break;
+      case 2: launch_skinny<4>(p, splits, stream); break;
+      case 3: launch_skinny<6>(p, splits, stream); break;
+      default: launch_skinny<8>(p, splits, stream); break;
+    }
+    return hipGetLastError();
+  }
   dim3 grid((p.N + GBN - 1) / GBN, (p.M + GBM - 1) / GBM, splits);
   hipLaunchKernelGGL(gemm_nt_kernel, grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_rows(const PackParams& p, hipStream_t stream) {
+  const int64_t n = (int64_t)(p.K / 64) * p.mp * 8;
+  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -84,13 +84,24 @@ struct GemmParams {
   int M, N, K;
   int k_per_split;                     // multiple of 64
   float* out;                          // [splits][M][N] fp32 partial sums
+  const uint16_t* xp;                  // skinny path: A packed as [K/64][mp][64] (64-K steps)
+  int mp;                              // rows of a packed step (M rounded up to 32)
 };
+struct PackParams {
+  const uint16_t* a_seg[kMaxLayers];  // as GemmParams
+  int64_t lda;
+  int seg_k, M, K, mp;
+  uint16_t* xp;                        // [K/64][mp][64]; rows >= M are zero
+};
+hipError_t launch_pack_rows(const PackParams& p, hipStream_t stream);
 struct ProjPlan {
   int fc_splits, kv_splits;
   int fc_kps, kv_kps;       // K elements per split (multiples of 64)
   bool fc_small, kv_small;  // small-M tile shape (M <= 128)
   size_t ws_bytes;
   size_t off_fc, off_c, off_kv;
+  int mp;                   // skinny path: packed activation rows (M rounded up to 32)
+  size_t off_xp, off_cp;    // skinny path: packed fc input, packed C
 };
 ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_fc, int num_cu);
 hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStream_t stream);
@@ -98,8 +109,10 @@ hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStre
 struct FcReduceParams {
   const float* part;   // [splits][M][N]
   int splits, M, N;
-  uint16_t* c_buf;     // [M][N] bf16
+  uint16_t* c_buf;     // [M][N] bf16 (row-major; may be null when c_pack is set)
   uint16_t* c_out;     // optional copy
+  uint16_t* c_pack;    // optional: C packed as [N/64][mp][64] for the skinny K/V product
+  int mp;
 };
 hipError_t launch_fc_reduce(const FcReduceParams& p, hipStream_t stream);
 
