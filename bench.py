@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per block-attention call (split kernel + merge kernel) on the batched
+# HBM bytes per block-attention call (one kernel; splits merged inside it) on the batched
 # workload, from two rocprofv3 counter passes over this script (FETCH_SIZE, then
 # WRITE_SIZE), each scaled by what the same counter reads for a device-to-device
 # copy of known size (--copy-mib).  Valid only for the kernel sources it was taken
@@ -37,8 +37,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "f33ee127f08db17423a8161d4527a0751630d76cab1d72fa838abf66b9adffe9",
-                "workload": "batched", "read": 287334767, "write": 19136533}
+ATTN_TRAFFIC = {"sha256": "8e25ee115dc9d7c9a67ed4d1a2f9d10604a4217d122f06e14795ef0810a64610",
+                "workload": "batched", "read": 278858273, "write": 10627072}
 
 
 def sources_sha256(paths):

@@ -130,8 +130,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
 // stream.  Each workgroup owns 128 weight rows (4 waves x 32) and one K range,
 // and sees all 16*MT activation rows.  A 64-K stage holds the weight tile
 // (128 rows, 16 KB) and the activation tile (16*MT rows, MT x 2 KB); stages go
-// global -> swizzled LDS by global_load_lds through an SK_NS-stage ring (all of
-// LDS at MT = 8), so SK_NS-1 stages are in flight while one feeds the MFMAs.
+// global -> swizzled LDS by global_load_lds through a 4-stage ring (128 KB at
+// MT = 8), so three stages are in flight while one feeds the MFMAs.
 // Per stage a wave reads its own 32 weight rows (4 KB) and the whole activation
 // tile from LDS and does 2 x MT x 2 MFMAs; each weight byte crosses LDS twice
 // and each activation byte five times (vs. thirteen for a square-tile GEMM).
@@ -148,7 +148,7 @@ struct SkGeo {
   static constexpr int W_TILE = SK_ROWS * BK * 2;             // 16 KB
   static constexpr int X_TILE = 16 * MT * BK * 2;             // MT x 2 KB
   static constexpr int STAGE = W_TILE + X_TILE;
-  static constexpr int NS = (160 * 1024) / STAGE < 6 ? (160 * 1024) / STAGE : 6;  // ring stages
+  static constexpr int NS = (160 * 1024) / STAGE < 4 ? (160 * 1024) / STAGE : 4;  // ring stages
   static constexpr int LOADS = STAGE / 1024;                  // wave-wide 1 KB loads per stage
   static constexpr int LW = LOADS / SK_WAVES;                 // per wave (every wave the same)
   static_assert(LOADS % SK_WAVES == 0, "stage loads split evenly over the waves");
@@ -384,11 +384,12 @@ int k_per_split(int K, int splits) {
 
 // Skinny plan: one workgroup of 128 weight rows per CU, K split to fill the CUs,
 // while the fp32 partial sums (splits x M x N x 4 bytes, written and read back
-// once) stay within the weight bytes (N x K x 2) and every split keeps >= 2 steps.
+// once) stay within half the weight bytes (N x K x 2) and every split keeps >= 2
+// steps.
 int skinny_splits(int N, int M, int K, int num_cu) {
   const int tiles = (N + SK_ROWS - 1) / SK_ROWS;
   int splits = (num_cu + tiles - 1) / tiles;
-  splits = min(splits, max(1, (int)((int64_t)K / (2 * (int64_t)(M > 0 ? M : 1)))));
+  splits = min(splits, max(1, (int)((int64_t)K / (4 * (int64_t)(M > 0 ? M : 1)))));
   splits = min(splits, max(1, K / (2 * BK)));
   splits = max(1, splits);
   // a divisor of 8 (1, 2, 4) or a multiple of 8, for the XCD-aware decode
