@@ -38,8 +38,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "8e25ee115dc9d7c9a67ed4d1a2f9d10604a4217d122f06e14795ef0810a64610",
-                "workload": "batched", "read": 278858273, "write": 10627072}
+ATTN_TRAFFIC = {"sha256": "4169a6e0e5fd5ede34ee03fb81917e36420b43b32353e54e26ce910d9aeea9ba",
+                "workload": "batched", "read": 278872544, "write": 10627072}
 
 
 def sources_sha256(paths):

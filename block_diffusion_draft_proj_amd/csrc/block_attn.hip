@@ -26,11 +26,11 @@
 //    the LDS load (the LDS side of global_load_lds is lane-contiguous), so the
 //    16-lane K reads and the 8-row transpose reads hit distinct banks;
 //  * the context is split over workgroups (flash-decoding); each split keeps
-//    (max, sum, O) in the workspace and a small second kernel merges them
-//    (log-sum-exp).  The kernel boundary is the handoff: merging inside the
-//    kernel would cost an L2 writeback (agent-scope release) per workgroup,
-//    measured at several times the merge itself.  All splits of a unit sit on
-//    one XCD, so their partials are written and re-read through one L2;
+//    (max, sum, O) in the workspace and the last split of a unit to finish
+//    merges them (log-sum-exp).  All splits of a unit sit on one XCD, so the
+//    partials and the arrival counter are handed over inside one L2, without
+//    the L2 writeback a device-scope release costs.  Above 8 splits a small
+//    second kernel merges instead;
 //  * probabilities enter the PV product as a bf16 hi/lo pair (P = P_hi + P_lo),
 //    so the only rounding of operands is the bf16 storage of Q, K and V.
 #include <math.h>
@@ -224,31 +224,18 @@ __device__ __forceinline__ void attend_stage(const char* stage, const bf16x8* qB
   }
 }
 
-// Partial results of a split go through to memory (system-scope stores bypass
-// every cache and complete only once written), so the workgroup that merges them
-// can read them with system-scope loads without any cache maintenance: no L2
-// writeback or invalidate is needed for the hand-off, only completion of the
-// stores before the arrival counter is bumped.
-__device__ __forceinline__ void st_through(float* dst, float a, float b) {
-  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-// 16-byte form (the completion is awaited with an explicit vmcnt wait).
-__device__ __forceinline__ void st_through4(float* dst, f32x4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" : : "v"(dst), "v"(v) : "memory");
-}
-__device__ __forceinline__ void ld_through(const float* src, float& a, float& b) {
-  const uint64_t v =
-      __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  a = __uint_as_float((uint32_t)v);
-  b = __uint_as_float((uint32_t)(v >> 32));
-}
-__device__ __forceinline__ f32x4 ld_through4(const float* src) {
-  float a0, a1, a2, a3;
-  ld_through(src, a0, a1);
-  ld_through(src + 2, a2, a3);
-  return (f32x4){a0, a1, a2, a3};
-}
+// Split hand-off inside one L2.  Workgroup i runs on XCD i % 8 (round-robin
+// dispatch; any partition into 1, 2, 4 or 8 XCDs keeps equal i % 8 on one XCD), and
+// the decode below gives every split of a unit the same i % 8, so all of them share
+// one L2.  A split stores its partial with plain stores (the vector L1 writes
+// through; the L2 acknowledges each store once it holds the data), waits for the
+// acknowledgements, and bumps the unit's arrival counter with an atomic performed in
+// that same L2 (no device-scope bit: a device-scope atomic or write-through goes
+// past the L2 to memory and costs microseconds).  The last arrival invalidates its
+// L1 and reads the partials from the L2.  Each counter has a 128-byte line of its
+// own, so no two XCDs ever hold one counter line in a launch; across launches the
+// kernel-boundary L2 writeback and invalidate keep the counters coherent.
+constexpr int kCntStride = 32;  // uint32 words per arrival counter (one 128-byte line)
 
 // Issue this wave's share of the loads of stage pack `pk` (stages NP*pk ..
 // NP*pk + NP-1): NP * LOADS wave-wide loads dealt round-robin over the NW waves.
@@ -405,6 +392,29 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
         lds_dma16_m0(ssrc + (int64_t)((li - QL - CL) * 64 + lane) * 16, qst_lds + li * 1024);
       }
     }
+    if (last_split) {
+      // Block keys (positions L .. L+15) of the last split go into the ring slot of
+      // the last pack, which the context stream first fills inside the loop: V rows
+      // straight into their swizzled places (rows 16..31 zero), raw K rows into
+      // rows 16..31 of the K tile for the RoPE pass below.
+      constexpr int BL = kBlock / GE::RPL;  // wave loads per block tile
+      const uint32_t bslot = lds_ring + (NST - 1) * GE::STAGE;
+      const int64_t brow0 = ((int64_t)b * kBlock * p.n_kv_heads + g) * D;  // element offset of row t = 0
+      const int64_t bstride = (int64_t)p.n_kv_heads * D;                   // elements between rows t
+#pragma unroll
+      for (int li = w; li < 2 * BL; li += NW) {
+        const int is_v = li >= BL;
+        const int t = (li - is_v * BL) * GE::RPL + lane / GE::NCH, pch = lane % GE::NCH;
+        const uint16_t* src = (is_v ? p.v_blk : p.k_blk) + brow0 + t * bstride;
+        if (is_v)
+          lds_dma16_m0(src + ((pch ^ vswz<D>(t)) << 3), bslot + GE::TILE + (li - BL) * 1024);
+        else
+          lds_dma16_m0(src + (pch << 3), bslot + kBlock * GE::ROW + li * 1024);
+      }
+      char* vz = lds + (NST - 1) * GE::STAGE + GE::TILE + kBlock * GE::ROW;
+      for (int off = tid * 16; off < (TK - kBlock) * GE::ROW; off += 64 * NW * 16)
+        *reinterpret_cast<u32x4*>(vz + off) = (u32x4){0u, 0u, 0u, 0u};
+    }
   }
 #pragma unroll
   for (int pk = 0; pk < NPK - 1; ++pk)
@@ -472,6 +482,41 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   for (int dt = 0; dt < DT; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
 
+  if constexpr (NGRP > 1) {
+    if (last_split) {
+      // The block tile first (its loads landed with Q): rotate the raw K rows with
+      // the cos / sin rows of the same positions, one 8-dim chunk pair per thread,
+      // then wave group 0 attends to the 16 block keys while the context streams in.
+      char* kt = lds + (NST - 1) * GE::STAGE;
+      const float* cq = reinterpret_cast<const float*>(qst + 32 * G * D);
+      const float* sq = reinterpret_cast<const float*>(qst + 32 * G * D + 32 * D);
+      constexpr int HC = HALF / 8;  // chunks per half row
+      for (int it = tid; it < kBlock * HC; it += 64 * NW) {
+        const int t = it / HC, c = it - t * HC;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(kt + (kBlock + t) * GE::ROW + c * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(kt + (kBlock + t) * GE::ROW + (c + HC) * 16);
+        u32x4 ylo, yhi;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          float y[2][2];
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const int j = 8 * c + 2 * e2 + hb;
+            const float xl = hb ? bf16_hi(lo[e2]) : bf16_lo(lo[e2]);
+            const float xh = hb ? bf16_hi(hi[e2]) : bf16_lo(hi[e2]);
+            rope_pair(xl, xh, cq[t * HALF + j], sq[t * HALF + j], y[0][hb], y[1][hb]);
+          }
+          ylo[e2] = (uint32_t)f32_to_bf16(y[0][0]) | ((uint32_t)f32_to_bf16(y[0][1]) << 16);
+          yhi[e2] = (uint32_t)f32_to_bf16(y[1][0]) | ((uint32_t)f32_to_bf16(y[1][1]) << 16);
+        }
+        *reinterpret_cast<u32x4*>(kt + t * GE::ROW + ((c ^ kswz<D>(t)) << 4)) = ylo;
+        *reinterpret_cast<u32x4*>(kt + t * GE::ROW + (((c + HC) ^ kswz<D>(t)) << 4)) = yhi;
+      }
+      __syncthreads();
+      if (grp == 0) attend_stage<D>(kt, qB, o, m, lsum, lane, kBlock, p.scale_log2);
+    }
+  }
+
   // Context keys [kb, ke): wave group grp consumes stage NGRP*pk + grp of each pack.
   for (int pk = 0; pk < n_pk; ++pk) {
     wait_packs<LPK, NPK - 2>(n_pk - 1 - pk);
@@ -483,9 +528,9 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
                             p.scale_log2);
   }
 
-  // Block keys (positions L .. L+15), handled by wave group 0 of the last split:
-  // rotated K rows and V rows written into stage 0, rows 16..31 zero.
-  if (last_split) {
+  // One wave group: block keys (positions L .. L+15) after the context, in the
+  // last split: rotated K rows and V rows written into stage 0, rows 16..31 zero.
+  if (NGRP == 1 && last_split) {
     __syncthreads();
     char* kt = lds;
     char* vt = lds + GE::TILE;
@@ -573,34 +618,36 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
     return;
   }
 
-  // Fused merge: write the partial through, count arrivals per unit; the split
+  // Fused merge: store the partial, count arrivals per unit; the split
   // that arrives last combines all of them (log-sum-exp, in split order).
   if (grp == 0) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st_through4(po + (dt * 64 + lane) * 4, o[dt]);
-    if (q == 0) st_through(p.ws_ml + (slot * 16 + r) * 2, m, lt);
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (dt * 64 + lane) * 4) = o[dt];
+    if (q == 0) *reinterpret_cast<float2*>(p.ws_ml + (slot * 16 + r) * 2) = make_float2(m, lt);
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  wait_vmcnt<0>();  // this wave's partial is in memory
+  wait_vmcnt<0>();  // this wave's partial is in the L2
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();  // ... and every other wave's
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(p.count + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t* cnt = p.count + (int64_t)u * kCntStride;
+    const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const uint32_t last = prev == (uint32_t)(ns - 1) ? 1u : 0u;
-    if (last) __hip_atomic_store(p.count + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     s_last = last;
   }
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(s_last)) return;
 
   // The merge: every wave (all groups) takes DTG of the DT dimension tiles of its
-  // head and reads every split's partial, its own included, from memory with
-  // system-scope (sc0 sc1) buffer loads.  All loads of a chunk of CH splits, and
+  // head and reads every split's partial, its own included, from the shared L2
+  // (L1 invalidated first; sc0 loads).  All loads of a chunk of CH splits, and
   // every split's (m, l), are issued before any is used (addresses clamped to a
   // real split), so up to CH splits cost one memory round trip.
   constexpr int DTG = DT / NGRP;
   constexpr int CH = (DTG * 4 * kMaxFused <= 128 && NW <= 8) ? kMaxFused : (NW <= 8 ? 4 : 2);
-  constexpr int kSys = 1 | 16;  // cache policy sc0 | sc1: coherent with every agent
+  constexpr int kL2 = 1;  // cache policy sc0
+  asm volatile("buffer_inv sc0" : : : "memory");  // drop any L1 copy of the partials
   const int dt0 = grp * DTG;
   const int64_t slot0 = (int64_t)u * p.n_splits * G;  // first slot of the unit
   const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
@@ -614,7 +661,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
       const int sl = min(c0 + k, ns - 1) * G + hw;
 #pragma unroll
       for (int j = 0; j < DTG; ++j)
-        part[k][j] = __builtin_amdgcn_raw_buffer_load_b128(rs_o, (sl * DT * 64 + (dt0 + j) * 64 + lane) * 16, 0, kSys);
+        part[k][j] = __builtin_amdgcn_raw_buffer_load_b128(rs_o, (sl * DT * 64 + (dt0 + j) * 64 + lane) * 16, 0, kL2);
     }
   };
   load_chunk(0);
@@ -622,7 +669,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
 #pragma unroll
   for (int sp = 0; sp < kMaxFused; ++sp) {
     const int sl = min(sp, ns - 1) * G + hw;
-    const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rs_ml, (sl * 16 + r) * 8, 0, kSys);
+    const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rs_ml, (sl * 16 + r) * 8, 0, kL2);
     mv[sp] = sp < ns ? __uint_as_float(ml[0]) : -INFINITY;
     lv[sp] = sp < ns ? __uint_as_float(ml[1]) : 0.f;
   }
@@ -732,7 +779,7 @@ AttnPlan plan_block_attn(int batch, int n_q_heads, int n_kv_heads, int head_dim,
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 256;  // word 0: device error mask
   pl.off_cnt = off;  // per-unit arrival counters (fused merge), left at zero by every call
-  off = align(off + sizeof(uint32_t) * (size_t)units);
+  off = align(off + sizeof(uint32_t) * kCntStride * (size_t)units);
   pl.off_ml = off;
   off = align(off + sizeof(float) * 2 * 16 * (size_t)group * pl.n_splits * units);
   pl.off_o = off;
