@@ -147,25 +147,39 @@ __global__ __launch_bounds__(kThreads) void verify_argmax_kernel(VerifyParams p)
 // One workgroup per sequence: reduce the chunk keys of its 16 rows, then accept,
 // next staged token, KV-length crop, commit positions and page count.  Running
 // after the argmax kernel on the same stream, it sees every chunk key without
-// any device-wide fence.
-__global__ __launch_bounds__(kWave) void verify_accept_kernel(VerifyParams p) {
-  __shared__ int32_t s_post[kBlock];
+// any device-wide fence.  Every global load is issued up front (16 threads per
+// row over the chunk keys, the 16 block tokens, the input length), so the kernel
+// costs one memory round trip; a chain of dependent loads would cost one each.
+constexpr int kAcceptThreads = 16 * kBlock;
+__global__ __launch_bounds__(kAcceptThreads) void verify_accept_kernel(VerifyParams p) {
+  __shared__ int32_t s_post[kBlock], s_blk[kBlock];
   __shared__ int32_t s_accept, s_kvin;
   const int b = blockIdx.x, tid = threadIdx.x;
-  if (tid < kBlock) {
-    const uint64_t* pr = p.part + (int64_t)(b * kBlock + tid) * p.n_chunks;
-    uint64_t best = 0;
-    for (int c = 0; c < p.n_chunks; ++c) best = pr[c] > best ? pr[c] : best;
-    const int32_t post = (int32_t)(0xffffffffu - (uint32_t)best);
-    s_post[tid] = post;
-    p.posterior[b * kBlock + tid] = post;
-  }
+  const int row = tid >> 4, sub = tid & 15;  // 16 threads per row, rows aligned to 16 lanes
+  const uint64_t* pr = p.part + (int64_t)(b * kBlock + row) * p.n_chunks;
+  if (tid < kBlock) s_blk[tid] = p.block_tokens[b * kBlock + tid];
   if (tid == 0) s_kvin = p.kv_len_in[b];
+  uint64_t best = 0;
+#pragma unroll 4
+  for (int c = sub; c < p.n_chunks; c += 16) {
+    const uint64_t k = pr[c];
+    best = k > best ? k : best;
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)best, off), hi = __shfl_xor((uint32_t)(best >> 32), off);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    best = o > best ? o : best;
+  }
+  if (sub == 0) {
+    const int32_t post = (int32_t)(0xffffffffu - (uint32_t)best);
+    s_post[row] = post;
+    p.posterior[b * kBlock + row] = post;
+  }
   __syncthreads();
   if (tid == 0) {
-    const int32_t* blk = p.block_tokens + b * kBlock;
     int a = 0;
-    while (a < kBlock - 1 && blk[a + 1] == s_post[a]) ++a;
+    while (a < kBlock - 1 && s_blk[a + 1] == s_post[a]) ++a;
     s_accept = a;
     const int32_t kv_out = s_kvin + 1 + a;
     p.accept_len[b] = a;
@@ -183,7 +197,7 @@ __global__ __launch_bounds__(kWave) void verify_accept_kernel(VerifyParams p) {
 hipError_t launch_verify_accept(const VerifyParams& p, int batch, hipStream_t stream) {
   const int grid = batch * kBlock * p.n_chunks;
   hipLaunchKernelGGL(verify_argmax_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
-  hipLaunchKernelGGL(verify_accept_kernel, dim3(batch), dim3(kWave), 0, stream, p);
+  hipLaunchKernelGGL(verify_accept_kernel, dim3(batch), dim3(kAcceptThreads), 0, stream, p);
   return hipGetLastError();
 }
 
