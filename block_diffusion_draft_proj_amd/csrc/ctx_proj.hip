@@ -290,7 +290,6 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(PackParams p) {
   st16(p.xp + i * 8, v);
 }
 
-// C = bf16(sum over splits): 4 columns per thread; written row-major and/or packed.
 // Sum of the split partials at one float4 position, in split order.  The loads of
 // up to kSumBatch splits are all issued before the first add (the address of a
 // split past the last is clamped and its value dropped), so a reduce over 8 splits
@@ -310,6 +309,7 @@ __device__ __forceinline__ f32x4 sum_splits(const float* base, int64_t stride, i
   return s;
 }
 
+// C = bf16(sum over splits): 4 columns per thread; written row-major and/or packed.
 __global__ __launch_bounds__(256) void fc_reduce_kernel(FcReduceParams p) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
   const int64_t total = (int64_t)p.M * p.N / 4;
