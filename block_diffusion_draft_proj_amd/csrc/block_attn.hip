@@ -227,15 +227,17 @@ __device__ __forceinline__ void attend_stage(const char* stage, const bf16x8* qB
 // Split hand-off inside one L2.  Workgroup i runs on XCD i % 8 (round-robin
 // dispatch; any partition into 1, 2, 4 or 8 XCDs keeps equal i % 8 on one XCD), and
 // the decode below gives every split of a unit the same i % 8, so all of them share
-// one L2.  A split stores its partial with plain stores (the vector L1 writes
-// through; the L2 acknowledges each store once it holds the data), waits for the
-// acknowledgements, and bumps the unit's arrival counter with an atomic performed in
-// that same L2 (no device-scope bit: a device-scope atomic or write-through goes
-// past the L2 to memory and costs microseconds).  The last arrival invalidates its
-// L1 and reads the partials from the L2.  Each counter has a 128-byte line of its
-// own, so no two XCDs ever hold one counter line in a launch; across launches the
-// kernel-boundary L2 writeback and invalidate keep the counters coherent.
+// one L2.  Counter updates are atomics performed in that L2 (no device-scope bit: a
+// device-scope atomic or write-through goes past the L2 to memory and costs
+// microseconds).  A split that stores a partial uses plain stores (the vector L1
+// writes through; the L2 acknowledges each store once it holds the data) and waits
+// for the acknowledgements before it counts the partial as stored; the reader
+// invalidates its L1 and reads the partials from the L2.  Each counter has a
+// 128-byte line of its own, so no two XCDs ever hold one counter line in a launch;
+// across launches the kernel-boundary L2 writeback and invalidate keep the counters
+// coherent.
 constexpr int kCntStride = 32;  // uint32 words per arrival counter (one 128-byte line)
+constexpr int kMergeSpinLimit = 1 << 20;  // polls of the stored count (~0.5 s) before giving up
 
 // Issue this wave's share of the loads of stage pack `pk` (stages NP*pk ..
 // NP*pk + NP-1): NP * LOADS wave-wide loads dealt round-robin over the NW waves.
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   const int r = lane & 15, q = lane >> 4;
   const int h = g * G + hw;
 
-  // Start the context stream before anything else: packs 0 .. NPK-2.  Dense
+  // Start the context stream right after the Q loads: packs 0 .. NPK-2.  Dense
   // packs inside the split take the scalar-base path; the rest clamp per row.
   const int n_st = (ke - kb + TK - 1) / TK;
   const int n_pk = (n_st + NGRP - 1) / NGRP;
@@ -557,98 +559,123 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   }
 
   // Combine the wave groups in LDS (stage slots 2.. are free: every wave passed
-  // its last stage): group g > 0 hands over (m, lsum, O) per lane, group 0 folds.
-  // Lane layout of O: dims 16*dt + 4*q + v of row r.
+  // its last stage).  Each group keeps half of the dimension tiles (group k: tiles
+  // k*DTG ..): it hands the other half of its O, with its (m, lsum), to the other
+  // group and folds that group's share of its own half.  Both groups evaluate the
+  // combined (m, lsum) with one expression (group 0's terms first), so they hold
+  // identical values.  Lane layout of O: dims 16*dt + 4*q + v of row r.
+  constexpr int DTG = DT / NGRP;
+  const int dt0 = grp * DTG;
+  f32x4 oh[DTG];
   if constexpr (NGRP > 1) {
+    static_assert(NGRP == 2, "two wave groups");
     __syncthreads();
-    float* xo = reinterpret_cast<float*>(lds + 2 * GE::STAGE);          // [NGRP-1][G][DT][64][4]
-    float* xml = xo + (NGRP - 1) * G * DT * 256;                          // [NGRP-1][G][64][2]
-    if (grp > 0) {
-      float* po = xo + ((grp - 1) * G + hw) * DT * 256;
+    float* xo = reinterpret_cast<float*>(lds + 2 * GE::STAGE);  // [2][G][DTG][64][4]
+    float* xml = xo + 2 * G * DTG * 256;                         // [2][G][64][2]
+    float* give = xo + (grp * G + hw) * DTG * 256;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (dt * 64 + lane) * 4) = o[dt];
-      xml[(((grp - 1) * G + hw) * 64 + lane) * 2 + 0] = m;
-      xml[(((grp - 1) * G + hw) * 64 + lane) * 2 + 1] = lsum;
-    }
+    for (int j = 0; j < DTG; ++j)
+      *reinterpret_cast<f32x4*>(give + (j * 64 + lane) * 4) = grp ? o[j] : o[DTG + j];
+    *reinterpret_cast<float2*>(xml + ((grp * G + hw) * 64 + lane) * 2) = make_float2(m, lsum);
     __syncthreads();
-    if (grp == 0) {
+    const int oth = 1 - grp;
+    const float* take = xo + (oth * G + hw) * DTG * 256;
+    const float2 mlo = *reinterpret_cast<const float2*>(xml + ((oth * G + hw) * 64 + lane) * 2);
+    // A group that saw no key has m = -inf; one of the two always saw one (the
+    // split has a key), but guard the empty case anyway.
+    const float mn = fmaxf(m, mlo.x);
+    const bool none = mn == -INFINITY;
+    const float a_own = none ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    const float a_oth = none ? 0.f : __builtin_amdgcn_exp2f(mlo.x - mn);
+    const float l0 = grp ? mlo.y : lsum, w0 = grp ? a_oth : a_own;
+    const float l1 = grp ? lsum : mlo.y, w1 = grp ? a_own : a_oth;
+    lsum = l0 * w0 + l1 * w1;
+    m = mn;
 #pragma unroll
-      for (int k = 1; k < NGRP; ++k) {
-        const float* po = xo + ((k - 1) * G + hw) * DT * 256;
-        const float mk = xml[(((k - 1) * G + hw) * 64 + lane) * 2 + 0];
-        const float lk = xml[(((k - 1) * G + hw) * 64 + lane) * 2 + 1];
-        const float mn = fmaxf(m, mk);  // finite: group 0 always saw a key
-        const float a0 = __builtin_amdgcn_exp2f(m - mn), a1 = __builtin_amdgcn_exp2f(mk - mn);
-        lsum = lsum * a0 + lk * a1;
+    for (int j = 0; j < DTG; ++j)
+      oh[j] = (grp ? o[DTG + j] : o[j]) * a_own + *reinterpret_cast<const f32x4*>(take + (j * 64 + lane) * 4) * a_oth;
+  } else {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          o[dt] = o[dt] * a0 + *reinterpret_cast<const f32x4*>(po + (dt * 64 + lane) * 4) * a1;
-        m = mn;
-      }
-    }
+    for (int j = 0; j < DTG; ++j) oh[j] = o[j];
   }
-  // Group 0 now holds the split's (m, lsum, O) of query head hw; the other
-  // groups only help with the merge below.
+  // Every wave now holds the split's (m, lsum) for query head hw and its O for
+  // dimension tiles dt0 .. dt0 + DTG - 1.
 
   float lt = lsum + __shfl_xor(lsum, 16);
   lt += __shfl_xor(lt, 32);
 
   float* outp = p.out + (((int64_t)b * kBlock + r) * p.n_q_heads + h) * D + 4 * q;
   if (ns == 1) {
-    if (grp == 0) {
-      const float inv = 1.f / lt;
+    const float inv = 1.f / lt;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(outp + dt * 16) = o[dt] * inv;
-    }
+    for (int j = 0; j < DTG; ++j) *reinterpret_cast<f32x4*>(outp + (dt0 + j) * 16) = oh[j] * inv;
     return;
   }
 
   const int64_t slot = ((int64_t)u * p.n_splits + s) * G + hw;
   float* po = p.ws_o + slot * (DT * 256);
-  if (!p.fused) {
-    // attn_merge_kernel combines the splits after this kernel.
-    if (grp == 0) {
+  auto store_partial = [&]() {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (dt * 64 + lane) * 4) = o[dt];
-      if (q == 0) {
-        p.ws_ml[(slot * 16 + r) * 2 + 0] = m;
-        p.ws_ml[(slot * 16 + r) * 2 + 1] = lt;
-      }
-    }
+    for (int j = 0; j < DTG; ++j) *reinterpret_cast<f32x4*>(po + ((dt0 + j) * 64 + lane) * 4) = oh[j];
+    if (grp == 0 && q == 0) *reinterpret_cast<float2*>(p.ws_ml + (slot * 16 + r) * 2) = make_float2(m, lt);
+  };
+  if (!p.fused) {  // attn_merge_kernel combines the splits after this kernel
+    store_partial();
     return;
   }
 
-  // Fused merge: store the partial, count arrivals per unit; the split
-  // that arrives last combines all of them (log-sum-exp, in split order).
-  if (grp == 0) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (dt * 64 + lane) * 4) = o[dt];
-    if (q == 0) *reinterpret_cast<float2*>(p.ws_ml + (slot * 16 + r) * 2) = make_float2(m, lt);
-  }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  wait_vmcnt<0>();  // this wave's partial is in the L2
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();  // ... and every other wave's
+  // Fused merge.  The unit's counter word holds arrivals (low 16 bits) and stored
+  // partials (high 16 bits).  A split counts its arrival first: the split that
+  // arrives last keeps its own state in registers and never stores it; every other
+  // split stores its partial, waits for the L2 to acknowledge it, then counts it as
+  // stored.  The last arrival waits until the other ns - 1 partials are stored
+  // (those splits already arrived, so they are running and only storing), clears
+  // the counter for the next call and combines all ns states (log-sum-exp, in
+  // split order).
+  uint32_t* cnt = p.count + (int64_t)u * kCntStride;
+  uint32_t prev = 0;
   if (tid == 0) {
-    uint32_t* cnt = p.count + (int64_t)u * kCntStride;
-    const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const uint32_t last = prev == (uint32_t)(ns - 1) ? 1u : 0u;
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    s_last = last;
+    prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    s_last = (prev & 0xffffu) == (uint32_t)(ns - 1) ? 1u : 0u;
   }
   __syncthreads();
-  if (!__builtin_amdgcn_readfirstlane(s_last)) return;
+  if (!__builtin_amdgcn_readfirstlane(s_last)) {
+    store_partial();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    wait_vmcnt<0>();  // this wave's partial is in the L2
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();  // ... and every other wave's
+    if (tid == 0) __hip_atomic_fetch_add(cnt, 1u << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return;
+  }
+  if (tid == 0) {
+    uint32_t v = prev;
+    for (int spin = 0; (v >> 16) != (uint32_t)(ns - 1); ++spin) {
+      if (spin >= kMergeSpinLimit) {  // cannot happen while the stored splits run; never hang
+        set_dev_error(p.err, 1u << 3);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+      // Re-read the count with an atomic add of an opaque zero, performed in the L2.
+      // A load would not do: the first one brings the line into this CU's L1 and the
+      // next ones hit that stale copy (a workgroup-scope invalidate does not drop
+      // it), and the compiler turns an atomic add of a literal zero into such a load.
+      uint32_t zero;
+      asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+      v = __hip_atomic_fetch_add(cnt, zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  __syncthreads();
 
-  // The merge: every wave (all groups) takes DTG of the DT dimension tiles of its
-  // head and reads every split's partial, its own included, from the shared L2
-  // (L1 invalidated first; sc0 loads).  All loads of a chunk of CH splits, and
-  // every split's (m, l), are issued before any is used (addresses clamped to a
-  // real split), so up to CH splits cost one memory round trip.
-  constexpr int DTG = DT / NGRP;
+  // The merge: every wave combines its DTG dimension tiles of its head over all
+  // splits: its own split from registers, the others from the shared L2 (L1
+  // invalidated first; sc0 loads).  All loads of a chunk of CH splits, and every
+  // split's (m, l), are issued before any is used (addresses clamped to a real
+  // split), so up to CH splits cost one memory round trip.
   constexpr int CH = (DTG * 4 * kMaxFused <= 128 && NW <= 8) ? kMaxFused : (NW <= 8 ? 4 : 2);
   constexpr int kL2 = 1;  // cache policy sc0
   asm volatile("buffer_inv sc0" : : : "memory");  // drop any L1 copy of the partials
-  const int dt0 = grp * DTG;
   const int64_t slot0 = (int64_t)u * p.n_splits * G;  // first slot of the unit
   const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
       p.ws_o + slot0 * (DT * 256), 0, p.n_splits * G * DT * 1024, 0x00020000);
@@ -658,7 +685,9 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   auto load_chunk = [&](int c0) {
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      const int sl = min(c0 + k, ns - 1) * G + hw;
+      const int sp = min(c0 + k, ns - 1);
+      if (sp == s) continue;  // own state stays in registers
+      const int sl = sp * G + hw;
 #pragma unroll
       for (int j = 0; j < DTG; ++j)
         part[k][j] = __builtin_amdgcn_raw_buffer_load_b128(rs_o, (sl * DT * 64 + (dt0 + j) * 64 + lane) * 16, 0, kL2);
@@ -670,8 +699,8 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   for (int sp = 0; sp < kMaxFused; ++sp) {
     const int sl = min(sp, ns - 1) * G + hw;
     const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rs_ml, (sl * 16 + r) * 8, 0, kL2);
-    mv[sp] = sp < ns ? __uint_as_float(ml[0]) : -INFINITY;
-    lv[sp] = sp < ns ? __uint_as_float(ml[1]) : 0.f;
+    mv[sp] = sp < ns ? (sp == s ? m : __uint_as_float(ml[0])) : -INFINITY;
+    lv[sp] = sp < ns ? (sp == s ? lt : __uint_as_float(ml[1])) : 0.f;
   }
   float mmax = mv[0];
 #pragma unroll
@@ -691,7 +720,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
       const float wgt = __builtin_amdgcn_exp2f(mv[sp] - mmax);
       den += wgt * lv[sp];
 #pragma unroll
-      for (int j = 0; j < DTG; ++j) acc[j] += wgt * __builtin_bit_cast(f32x4, part[k][j]);
+      for (int j = 0; j < DTG; ++j) acc[j] += wgt * (sp == s ? oh[j] : __builtin_bit_cast(f32x4, part[k][j]));
     }
   }
   const float inv = 1.f / den;

@@ -82,10 +82,20 @@ __device__ __forceinline__ void lds_dma16(const void* src, char* lds_base) {
 // Same load addressed as a wave-uniform base (SGPR pair) plus a 32-bit per-lane
 // byte offset, into LDS byte address `m0` (wave-uniform): no 64-bit address math
 // per lane.
+// The base goes through readfirstlane so that it is provably wave-uniform: where the
+// compiler's uniformity analysis loses track of it, an "s" operand would otherwise be
+// handed a VGPR pair.
 __device__ __forceinline__ void lds_dma16_nt_sv(const void* sbase, uint32_t voff, uint32_t m0) {
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  // readfirstlane returns int: each half goes back to uint32 before widening, or the
+  // low half would be sign-extended into the high one.
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t u = ((uint64_t)hi << 32) | lo;
+  const void* base = (const void*)(uintptr_t)u;
   uint32_t saved;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(m0) : "memory");
+               : "=&s"(saved) : "v"(voff), "s"(base), "s"(m0) : "memory");
 }
 
 // Non-temporal global_load_lds into LDS byte address `m0` (wave-uniform).

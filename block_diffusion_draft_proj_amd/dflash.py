@@ -18,7 +18,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libdflash.so")
 
 BLOCK = 16
-DEVERR_CTX_LEN, DEVERR_PAGE_ID, DEVERR_ROW = 1, 2, 4
+DEVERR_CTX_LEN, DEVERR_PAGE_ID, DEVERR_ROW, DEVERR_MERGE = 1, 2, 4, 8
 
 _c_int, _c_i64, _c_sz, _c_f, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
 

@@ -64,6 +64,10 @@ extern "C" {
 #define DFLASH_DEVERR_CTX_LEN   1u  /* ctx_len[b] < 0 or > max_ctx_len (clamped) */
 #define DFLASH_DEVERR_PAGE_ID   2u  /* page-table entry < 0 or >= num_pages (page 0 read instead) */
 #define DFLASH_DEVERR_ROW       4u  /* row_seq / row_pos out of range (row's cache write skipped) */
+#define DFLASH_DEVERR_MERGE     8u  /* block attention: a split's partial never arrived (bounded
+                                      wait gave up; that unit's output is wrong).  Not expected:
+                                      reports a broken workspace counter, e.g. a workspace shared
+                                      by two calls in flight */
 
 /* Block of draft tokens: the staged token plus 15 mask slots
  * ("dflash-mlx", "block-diffusion draft"). */
