@@ -38,8 +38,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "4169a6e0e5fd5ede34ee03fb81917e36420b43b32353e54e26ce910d9aeea9ba",
-                "workload": "batched", "read": 278872544, "write": 10627072}
+ATTN_TRAFFIC = {"sha256": "04783979a8dc3f2c41051e6d025626aba42231ee9ddab85eb335d0a5c8d80909",
+                "workload": "batched", "read": 276767945, "write": 8506442}
 
 
 def sources_sha256(paths):
