@@ -7,11 +7,12 @@ import dataclasses
 
 import numpy as np
 import pytest
+import torch
 
 from block_diffusion_draft_proj_amd import dflash as dfl
 from block_diffusion_draft_proj_amd import synth
 from oracle import dflash_oracle as orc
-from tests.gpu_util import DEV, log, run_block_attn
+from tests.gpu_util import DEV, attn_dims, log, run_block_attn
 
 pytestmark = pytest.mark.gpu
 
@@ -117,3 +118,31 @@ def test_attn_device_error_flags_clamp_without_fault():
     out, ws = run_block_attn(cfg, pat)
     assert ws[:4].cpu().numpy().view(np.uint32)[0] & dfl.DEVERR_PAGE_ID
     assert np.all(np.isfinite(out.cpu().numpy()))
+
+
+def test_attn_merge_wait_is_bounded_and_flags_a_broken_counter():
+    # Two units of 4 splits each (L=1024, 256 keys per split).  Unit 1's counter word
+    # is pre-filled from the host with a stored count the splits can never bring to
+    # 3 (they only add to it), so its last split polls until the bounded wait gives
+    # up: the kernel still ends, DEVERR_MERGE is raised, the counter is cleared, and
+    # the merge uses the partials that were stored (all of them here).  A second call
+    # on the same workspace runs clean.
+    cfg = dataclasses.replace(synth.CONFIGS["qwen3_8b"], n_q_heads=8, n_kv_heads=2)
+    at = synth.attn_inputs(cfg, ctx_len=np.array([1024]))
+    dims = attn_dims(cfg, at)
+    ws = dfl.workspace(dfl.dflash_block_attn_workspace_size(dims, 1024), DEV)
+    cnt_unit1 = 256 + 128  # counters follow the 256-byte error area, one 128-byte line per unit
+    ws[cnt_unit1:cnt_unit1 + 4] = torch.from_numpy(np.array([0x7FFF << 16], np.uint32).view(np.uint8)).to(DEV)
+    log("attn merge: unit 1 counter pre-filled with an unreachable stored count")
+    out, ws = run_block_attn(cfg, at, ws=ws)
+    err = int(ws[:4].cpu().numpy().view(np.uint32)[0])
+    assert err & dfl.DEVERR_MERGE, err
+    assert int(ws[cnt_unit1:cnt_unit1 + 4].cpu().numpy().view(np.uint32)[0]) == 0
+    ref = orc.block_attn_ref(at.q_blk, at.k_blk, at.v_blk, at.k_cache, at.v_cache, at.ctx_len, cfg.rope_base)
+    assert np.max(np.abs(out.cpu().numpy() - ref)) <= TOL
+    ws[:4] = 0
+    out2, ws = run_block_attn(cfg, at, ws=ws)
+    assert int(ws[:4].cpu().numpy().view(np.uint32)[0]) == 0
+    err2 = float(np.max(np.abs(out2.cpu().numpy() - ref)))
+    log(f"attn merge: second call on the same workspace, max-abs err {err2:.3e}")
+    assert err2 <= TOL
