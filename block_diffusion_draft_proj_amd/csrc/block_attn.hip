@@ -357,8 +357,9 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   const int r = lane & 15, q = lane >> 4;
   const int h = g * G + hw;
 
-  // Start the context stream right after the Q loads: packs 0 .. NPK-2.  Dense
-  // packs inside the split take the scalar-base path; the rest clamp per row.
+  // Start the context stream right after the Q loads: packs 0 .. NPK-2 (part of
+  // them after the Q wait, see QF).  Dense packs inside the split take the
+  // scalar-base path; the rest clamp per row.
   const int n_st = (ke - kb + TK - 1) / TK;
   const int n_pk = (n_st + NGRP - 1) / NGRP;
   const int n_fast = PAGED ? 0 : (ke - kb) / (NGRP * TK);  // packs with every key < ke
@@ -418,16 +419,24 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
         *reinterpret_cast<u32x4*>(vz + off) = (u32x4){0u, 0u, 0u, 0u};
     }
   }
+  // Packs issued before the Q wait: Q, cos and sin compete with every CU's ring fill
+  // for HBM, so with the whole ring ahead of them they land ~4.4 us after the start,
+  // well after the ring is full; with two packs ahead they land at ~3.1 us and the
+  // rest of the ring goes out right after them (measured inside the bench step).
+  constexpr int QF = NGRP > 1 ? 2 : NPK - 1;
 #pragma unroll
-  for (int pk = 0; pk < NPK - 1; ++pk)
+  for (int pk = 0; pk < QF; ++pk)
     if (pk < n_pk) issue(pk);
 
   // Q of head h: rows at positions L + r, RoPE in fp32, rounded to bf16, as the
   // B operand of S^T = K Q^T (lane holds dims 32*ks + 8*q .. +8 of row r).
   bf16x8 qB[KS];
   if constexpr (NGRP > 1) {
-    wait_packs<LPK, NPK - 1>(n_pk);  // this wave's Q / cos / sin loads landed
+    wait_packs<LPK, QF>(n_pk);  // this wave's Q / cos / sin loads landed
     __syncthreads();                 // ... and every other wave's
+#pragma unroll
+    for (int pk = QF; pk < NPK - 1; ++pk)
+      if (pk < n_pk) issue(pk);
     const char* qrow = qst + (r * G * D + hw * D) * 2;
     const float* cr = reinterpret_cast<const float*>(qst + 32 * G * D) + r * HALF;
     const float* sr = reinterpret_cast<const float*>(qst + 32 * G * D + 32 * D) + r * HALF;
