@@ -38,8 +38,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "04783979a8dc3f2c41051e6d025626aba42231ee9ddab85eb335d0a5c8d80909",
-                "workload": "batched", "read": 276767945, "write": 8506442}
+ATTN_TRAFFIC = {"sha256": "40c069099f70c817686e7fdc1cae2b53e7a7d3b16c8a2fa545f98487572fccee",
+                "workload": "batched", "read": 276783022, "write": 8506331}
 
 
 def sources_sha256(paths):
