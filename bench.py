@@ -38,8 +38,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "40c069099f70c817686e7fdc1cae2b53e7a7d3b16c8a2fa545f98487572fccee",
-                "workload": "batched", "read": 276783022, "write": 8506331}
+ATTN_TRAFFIC = {"sha256": "a053200d3eff99c6c16dcb9184ffeb037b7ad266930b46be26d3b4b6aee5ecbb",
+                "workload": "batched", "read": 276773631, "write": 8507938}
 
 
 def sources_sha256(paths):

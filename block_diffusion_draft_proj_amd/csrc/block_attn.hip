@@ -232,7 +232,8 @@ __device__ __forceinline__ void attend_stage(const char* stage, const bf16x8* qB
 // microseconds).  A split that stores a partial uses plain stores (the vector L1
 // writes through; the L2 acknowledges each store once it holds the data) and waits
 // for the acknowledgements before it counts the partial as stored; the reader
-// invalidates its L1 and reads the partials from the L2.  Each counter has a
+// invalidates its L1 and reads the partials from the L2 (they are stored
+// write-through, which also leaves the L2 copy valid).  Each counter has a
 // 128-byte line of its own, so no two XCDs ever hold one counter line in a launch;
 // across launches the kernel-boundary L2 writeback and invalidate keep the counters
 // coherent.
@@ -623,10 +624,20 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
 
   const int64_t slot = ((int64_t)u * p.n_splits + s) * G + hw;
   float* po = p.ws_o + slot * (DT * 256);
+  // Partials are stored write-through (cache policy sc0 sc1, system scope): the L2
+  // keeps the line for the merging split, and the lines are clean by the time the
+  // kernel ends, so the end-of-kernel L2 writeback has ~6 MB less to write
+  // (-0.3 to -0.6 us per call, interleaved A/B; plain and non-temporal stores both
+  // measured slower).
+  constexpr int kWriteThrough = 1 | 16;  // sc0 | sc1
   auto store_partial = [&]() {
+    const __amdgpu_buffer_rsrc_t rs_po = __builtin_amdgcn_make_buffer_rsrc(po, 0, DT * 1024, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_pm = __builtin_amdgcn_make_buffer_rsrc(p.ws_ml + slot * 32, 0, 16 * 8, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < DTG; ++j) *reinterpret_cast<f32x4*>(po + ((dt0 + j) * 64 + lane) * 4) = oh[j];
-    if (grp == 0 && q == 0) *reinterpret_cast<float2*>(p.ws_ml + (slot * 16 + r) * 2) = make_float2(m, lt);
+    for (int j = 0; j < DTG; ++j)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, oh[j]), rs_po, ((dt0 + j) * 64 + lane) * 16, 0, kWriteThrough);
+    if (grp == 0 && q == 0)
+      __builtin_amdgcn_raw_buffer_store_b64((u32x2){__float_as_uint(m), __float_as_uint(lt)}, rs_pm, r * 8, 0, kWriteThrough);
   };
   if (!p.fused) {  // attn_merge_kernel combines the splits after this kernel
     store_partial();
