@@ -38,8 +38,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "a053200d3eff99c6c16dcb9184ffeb037b7ad266930b46be26d3b4b6aee5ecbb",
-                "workload": "batched", "read": 276773631, "write": 8507938}
+ATTN_TRAFFIC = {"sha256": "84a62eda6d7e86de80a274aef6318399461ae1327e3c435f487ee2cd6c220084",
+                "workload": "batched", "read": 276773629, "write": 8508080}
 
 
 def sources_sha256(paths):

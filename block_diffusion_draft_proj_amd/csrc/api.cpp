@@ -85,10 +85,17 @@ int dflash_rope_tables(float base, int32_t head_dim, int32_t max_pos, float* cos
 }
 
 // ------------------------------------------------------------------ verify
+// Workspace: word 0 error mask (256 bytes), chunk keys, then per-sequence arrival
+// counters (128 bytes each, 256-byte aligned).
+static size_t verify_count_offset(int32_t batch, size_t n_chunks) {
+  const size_t keys_end = 256 + sizeof(uint64_t) * (size_t)batch * DFLASH_BLOCK * n_chunks;
+  return (keys_end + 255) & ~(size_t)255;
+}
+
 size_t dflash_verify_workspace_size(int32_t batch, int32_t block, int32_t vocab) {
   if (batch < 1 || block != DFLASH_BLOCK || vocab < 1) return 0;
   const size_t n_chunks = ((size_t)vocab + kVerifyChunk - 1) / kVerifyChunk;
-  return 256 + sizeof(uint64_t) * (size_t)batch * DFLASH_BLOCK * n_chunks;
+  return verify_count_offset(batch, n_chunks) + sizeof(uint32_t) * kVerifyCntStride * (size_t)batch;
 }
 
 int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab, const void* logits, int64_t ld_logits,
@@ -125,6 +132,7 @@ int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab, const void
   p.n_pages = n_pages;
   p.page_size = page_size;
   p.part = reinterpret_cast<uint64_t*>(ws + 256);
+  p.count = reinterpret_cast<uint32_t*>(ws + verify_count_offset(batch, (size_t)n_chunks));
   return launch_status(launch_verify_accept(p, batch, stream));
 }
 

@@ -12,6 +12,7 @@ constexpr int kPlanCUs = 256;
 
 // ---------------------------------------------------------------- verify
 constexpr int kVerifyChunk = 8192;  // logits per workgroup (256 threads x 4 x 8)
+constexpr int kVerifyCntStride = 32;  // uint32 words per arrival counter (one 128-byte line)
 
 struct VerifyParams {
   const uint16_t* logits;
@@ -28,6 +29,7 @@ struct VerifyParams {
   int32_t* n_pages;     // may be null
   int32_t page_size;
   uint64_t* part;       // [batch*16*n_chunks] per-chunk keys
+  uint32_t* count;      // [batch][kVerifyCntStride] arrival counters (one-kernel form; zero between calls)
 };
 hipError_t launch_verify_accept(const VerifyParams& p, int batch, hipStream_t stream);
 

@@ -17,10 +17,14 @@
 //    held in registers, by only the threads whose own maximum matched;
 //  * each chunk publishes one 64-bit key (value key << 32 | ~index), so the row
 //    maximum with the lowest index is an order-independent max();
-//  * a second kernel (one workgroup per sequence) reduces the 16 rows and runs
-//    accept / commit / crop.  A kernel boundary is the cheapest device-wide
-//    handoff on this part: handing off inside one kernel would need an L2
-//    writeback (agent-scope release) from every workgroup.  No host round trip.
+//  * with 8 or more sequences, the last workgroup of each sequence reduces its 16
+//    rows and runs accept / commit / crop inside the same kernel: all workgroups
+//    of a sequence sit on one XCD and hand over through its L2 (arrival counted by
+//    an L2 atomic), with no device-wide fence;
+//  * with fewer sequences, a second kernel (one workgroup per sequence) does that
+//    step: a kernel boundary is then the cheapest device-wide hand-off, since
+//    handing off across XCDs inside one kernel would need an L2 writeback
+//    (agent-scope release) from every workgroup.  No host round trip.
 #include "common.h"
 #include "launch.h"
 
@@ -69,12 +73,11 @@ __device__ __forceinline__ T wg_reduce(T v, Op op, T* s_buf) {
   return r;
 }
 
-__global__ __launch_bounds__(kThreads) void verify_argmax_kernel(VerifyParams p) {
-  __shared__ uint32_t s_red[kThreads / kWave];
-
+// The chunk's 64-bit key: (order key of its maximum << 32) | ~(first index of it),
+// so the row maximum with the lowest index is an order-independent max().
+// Returned by thread 0.
+__device__ __forceinline__ uint64_t chunk_key(const VerifyParams& p, int row, int chunk, uint32_t* s_red) {
   const int tid = threadIdx.x;
-  const int row = blockIdx.x / p.n_chunks;
-  const int chunk = blockIdx.x - row * p.n_chunks;
   const uint16_t* rp = p.logits + (int64_t)row * p.ld;
   const int c0 = chunk * kVerifyChunk;
   const int c1 = min(p.vocab, c0 + kVerifyChunk);
@@ -138,10 +141,16 @@ __global__ __launch_bounds__(kThreads) void verify_argmax_kernel(VerifyParams p)
   }
   idx = wg_reduce(idx, [](uint32_t a, uint32_t c) { return min(a, c); }, s_red);
 
-  if (tid == 0) {
-    const uint64_t canon = has_nan ? 0x10000u : (zero ? 0x8000u : cmax);
-    p.part[(int64_t)row * p.n_chunks + chunk] = (canon << 32) | (uint64_t)(0xffffffffu - idx);
-  }
+  const uint64_t canon = has_nan ? 0x10000u : (zero ? 0x8000u : cmax);
+  return (canon << 32) | (uint64_t)(0xffffffffu - idx);
+}
+
+__global__ __launch_bounds__(kThreads) void verify_argmax_kernel(VerifyParams p) {
+  __shared__ uint32_t s_red[kThreads / kWave];
+  const int row = blockIdx.x / p.n_chunks;
+  const int chunk = blockIdx.x - row * p.n_chunks;
+  const uint64_t key = chunk_key(p, row, chunk, s_red);
+  if (threadIdx.x == 0) p.part[(int64_t)row * p.n_chunks + chunk] = key;
 }
 
 // One workgroup per sequence: reduce the chunk keys of its 16 rows, then accept,
@@ -151,14 +160,24 @@ __global__ __launch_bounds__(kThreads) void verify_argmax_kernel(VerifyParams p)
 // row over the chunk keys, the 16 block tokens, the input length), so the kernel
 // costs one memory round trip; a chain of dependent loads would cost one each.
 constexpr int kAcceptThreads = 16 * kBlock;
-__global__ __launch_bounds__(kAcceptThreads) void verify_accept_kernel(VerifyParams p) {
-  __shared__ int32_t s_post[kBlock], s_blk[kBlock];
-  __shared__ int32_t s_accept, s_kvin;
-  const int b = blockIdx.x, tid = threadIdx.x;
+static_assert(kAcceptThreads == kThreads, "the fused kernel runs the accept step with its own threads");
+
+struct AcceptShared {
+  int32_t post[kBlock], blk[kBlock];
+  int32_t accept, kvin;
+};
+
+// Sequence b: reduce the chunk keys of its 16 rows, then accept, next staged
+// token, KV-length crop, commit positions and page count.  256 threads.  Every
+// global load is issued up front (16 threads per row over the chunk keys, the 16
+// block tokens, the input length), so the step costs one memory round trip; a
+// chain of dependent loads would cost one each.
+__device__ __forceinline__ void accept_seq(const VerifyParams& p, int b, AcceptShared& sh) {
+  const int tid = threadIdx.x;
   const int row = tid >> 4, sub = tid & 15;  // 16 threads per row, rows aligned to 16 lanes
   const uint64_t* pr = p.part + (int64_t)(b * kBlock + row) * p.n_chunks;
-  if (tid < kBlock) s_blk[tid] = p.block_tokens[b * kBlock + tid];
-  if (tid == 0) s_kvin = p.kv_len_in[b];
+  if (tid < kBlock) sh.blk[tid] = p.block_tokens[b * kBlock + tid];
+  if (tid == 0) sh.kvin = p.kv_len_in[b];
   uint64_t best = 0;
 #pragma unroll 4
   for (int c = sub; c < p.n_chunks; c += 16) {
@@ -173,28 +192,79 @@ __global__ __launch_bounds__(kAcceptThreads) void verify_accept_kernel(VerifyPar
   }
   if (sub == 0) {
     const int32_t post = (int32_t)(0xffffffffu - (uint32_t)best);
-    s_post[row] = post;
+    sh.post[row] = post;
     p.posterior[b * kBlock + row] = post;
   }
   __syncthreads();
   if (tid == 0) {
     int a = 0;
-    while (a < kBlock - 1 && s_blk[a + 1] == s_post[a]) ++a;
-    s_accept = a;
-    const int32_t kv_out = s_kvin + 1 + a;
+    while (a < kBlock - 1 && sh.blk[a + 1] == sh.post[a]) ++a;
+    sh.accept = a;
+    const int32_t kv_out = sh.kvin + 1 + a;
     p.accept_len[b] = a;
-    p.next_token[b] = s_post[a];
+    p.next_token[b] = sh.post[a];
     p.kv_len_out[b] = kv_out;
     if (p.n_pages) p.n_pages[b] = (int32_t)(((int64_t)kv_out + p.page_size - 1) / p.page_size);
   }
   __syncthreads();
   if (p.commit_pos && tid < kBlock)
-    p.commit_pos[b * kBlock + tid] = (tid <= s_accept) ? s_kvin + tid : -1;
+    p.commit_pos[b * kBlock + tid] = (tid <= sh.accept) ? sh.kvin + tid : -1;
+}
+
+// Second kernel of the two-kernel form: one workgroup per sequence.  Running after
+// the argmax kernel on the same stream, it sees every chunk key without any
+// device-wide fence.
+__global__ __launch_bounds__(kAcceptThreads) void verify_accept_kernel(VerifyParams p) {
+  __shared__ AcceptShared sh;
+  accept_seq(p, blockIdx.x, sh);
+}
+
+// One-kernel form for batch >= 8 (every XCD holds whole sequences): workgroup i runs
+// on XCD i % 8 (round-robin dispatch) and the decode puts every workgroup of
+// sequence b on XCD b % 8, so its chunk keys and its arrival counter stay in one
+// L2.  A workgroup stores its chunk key, waits until the L2 acknowledges it, and
+// counts its arrival with an atomic performed in that L2; the last of the
+// sequence's 16 * n_chunks workgroups clears the counter and runs the accept step.
+// This saves the second launch (~5 us on this part) for ~1-2 us of tail.  Below 8
+// sequences some XCDs would sit idle, so the two-kernel form is used there.
+__global__ __launch_bounds__(kThreads) void verify_fused_kernel(VerifyParams p, int batch) {
+  __shared__ uint32_t s_red[kThreads / kWave];
+  __shared__ uint32_t s_last;
+  __shared__ AcceptShared sh;
+  const int per = kBlock * p.n_chunks;  // workgroups per sequence
+  const int xcd = blockIdx.x % kNumXcd, j = blockIdx.x / kNumXcd;
+  const int b = xcd + kNumXcd * (j / per);
+  if (b >= batch) return;
+  const int rem = j - (j / per) * per;
+  const int row_in = rem / p.n_chunks, chunk = rem - row_in * p.n_chunks;
+  const int row = b * kBlock + row_in;
+  const uint64_t key = chunk_key(p, row, chunk, s_red);
+  if (threadIdx.x == 0) {
+    p.part[(int64_t)row * p.n_chunks + chunk] = key;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    wait_vmcnt<0>();  // the key is in the L2
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    uint32_t* cnt = p.count + (int64_t)b * kVerifyCntStride;
+    const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t last = prev == (uint32_t)(per - 1) ? 1u : 0u;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(s_last)) return;
+  // Every other chunk key of the sequence was written by another CU of this XCD and
+  // never read by this one, so the loads below miss the L1 and read the L2.
+  accept_seq(p, b, sh);
 }
 
 }  // namespace
 
 hipError_t launch_verify_accept(const VerifyParams& p, int batch, hipStream_t stream) {
+  if (batch >= kNumXcd) {
+    const int grid = kNumXcd * ((batch + kNumXcd - 1) / kNumXcd) * kBlock * p.n_chunks;
+    hipLaunchKernelGGL(verify_fused_kernel, dim3(grid), dim3(kThreads), 0, stream, p, batch);
+    return hipGetLastError();
+  }
   const int grid = batch * kBlock * p.n_chunks;
   hipLaunchKernelGGL(verify_argmax_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
   hipLaunchKernelGGL(verify_accept_kernel, dim3(batch), dim3(kAcceptThreads), 0, stream, p);

@@ -49,7 +49,8 @@ def test_status_strings_and_version():
 def test_workspace_sizes():
     v = dfl.dflash_verify_workspace_size(8, 16, 151936)
     n_chunks = -(-151936 // 8192)
-    assert v == 256 + 8 * 16 * 8 * n_chunks
+    keys_end = 256 + 8 * 16 * 8 * n_chunks                      # error word, then chunk keys
+    assert v == (keys_end + 255) // 256 * 256 + 8 * 128          # then 8 arrival counters of 128 bytes
     assert dfl.dflash_verify_workspace_size(0, 16, 10) == 0
     assert dfl.dflash_verify_workspace_size(1, 15, 10) == 0
     dims = dfl.make_dims(8, 32, 8, 128, hidden=4096, kv_capacity=8208)

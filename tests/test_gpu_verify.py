@@ -55,7 +55,10 @@ def test_verify_unplanted_normal_rows_with_ties(name):
     _compare(got, ref)
 
 
-def test_verify_crafted_rows():
+# Batches of 8 or more run the one-kernel form (the accept step inside the argmax
+# kernel, sequences grouped per XCD); smaller ones the two-kernel form.
+@pytest.mark.parametrize("n_seq", [2, 10])
+def test_verify_crafted_rows(n_seq):
     V = 20000  # 3 chunks of 8192 (last partial)
     rows = np.zeros((2, 16, V), np.float32)
     rng = np.random.default_rng(3)
@@ -90,8 +93,11 @@ def test_verify_crafted_rows():
     logits[0, 11, 8999] = 0xFF81
     logits[0, 12, 16383] = 0x7F80                   # +inf at the very end of chunk 0..1 boundary
     logits[0, 12, 16384] = 0x7F80
-    blk = rng.integers(0, V, (2, 16)).astype(np.int32)
-    kv = np.array([5, 9], np.int32)
+    logits = np.tile(logits, (n_seq // 2, 1, 1))
+    blk = rng.integers(0, V, (n_seq, 16)).astype(np.int32)
+    kv = (5 + 4 * np.arange(n_seq)).astype(np.int32)
+    ref = orc.verify_accept_ref(logits, blk, kv)
+    blk[1, 1:6] = ref["post"][1, :5]                # a non-trivial accept length
     ref = orc.verify_accept_ref(logits, blk, kv)
     assert ref["post"][0, 0] == 8191 and ref["post"][0, 1] == 5 and ref["post"][0, 2] == 0
     assert ref["post"][0, 4] == 100 and ref["post"][0, 5] == 7 and ref["post"][0, 6] == 17000
@@ -100,26 +106,30 @@ def test_verify_crafted_rows():
     _compare(got, ref)
 
 
+@pytest.mark.parametrize("B", [3, 9])
 @pytest.mark.parametrize("V", [1, 2, 3, 7, 8, 9, 1001, 8191, 8192, 8193, 16385])
-def test_verify_small_and_ragged_vocab(V):
+def test_verify_small_and_ragged_vocab(V, B):
     ld = (V + 7) // 8 * 8
     rng = np.random.default_rng(V)
-    vals = rng.standard_normal((3, 16, ld)).astype(np.float32)
+    vals = rng.standard_normal((B, 16, ld)).astype(np.float32)
     logits = _bits(vals)
     logits[:, :, V:] = 0x7F80                       # +inf padding past vocab must be ignored
-    blk = rng.integers(0, V, (3, 16)).astype(np.int32)
-    post = orc.verify_accept_ref(logits[:, :, :V].copy(), blk, np.zeros(3, np.int32))["post"]
+    blk = rng.integers(0, V, (B, 16)).astype(np.int32)
+    kv = (np.arange(B) * 37 % 101).astype(np.int32)
+    post = orc.verify_accept_ref(logits[:, :, :V].copy(), blk, kv)["post"]
     blk[1, 1:8] = post[1, :7]
     blk[2, 1:16] = post[2, :15]
-    ref = orc.verify_accept_ref(logits[:, :, :V].copy(), blk, np.array([0, 3, 77], np.int32), page_size=16)
-    got, _ = run_verify(logits, blk, np.array([0, 3, 77], np.int32), page_size=16, vocab=V)
+    ref = orc.verify_accept_ref(logits[:, :, :V].copy(), blk, kv, page_size=16)
+    got, _ = run_verify(logits, blk, kv, page_size=16, vocab=V)
     _compare(got, ref, 16)
 
 
-def test_verify_workspace_reuse_and_aliasing():
+@pytest.mark.parametrize("B", [4, 12])
+def test_verify_workspace_reuse_and_aliasing(B):
+    # B = 12 also checks that the one-kernel form leaves its arrival counters at zero.
     cfg = synth.CONFIGS["qwen3_8b"]
-    vi1 = synth.verify_inputs(cfg, batch=4, seed=7)
-    vi2 = synth.verify_inputs(cfg, batch=4, seed=8)
+    vi1 = synth.verify_inputs(cfg, batch=B, seed=7)
+    vi2 = synth.verify_inputs(cfg, batch=B, seed=8)
     r1, ws = run_verify(vi1.logits, vi1.block_tokens, vi1.kv_len)
     r2, ws = run_verify(vi2.logits, vi2.block_tokens, vi2.kv_len, ws=ws)
     r3, ws = run_verify(vi1.logits, vi1.block_tokens, vi1.kv_len, ws=ws, alias_kv=True)
