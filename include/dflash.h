@@ -29,8 +29,9 @@
  *   - Workspaces are caller-owned device buffers of at least the size the
  *     matching *_workspace_size() query returns.  Zero a workspace once before
  *     its first use; every call leaves it fit for the next one (the block
- *     attention keeps per-sequence-head arrival counters in it, which each call
- *     returns to zero), so one buffer can serve any number of calls on the same
+ *     attention keeps per-sequence-head arrival counters in it, the verify with
+ *     8 or more sequences per-sequence ones, and each call returns them to
+ *     zero), so one buffer can serve any number of calls on the same
  *     stream, at any sizes up to the ones it was sized for.  Calls that run
  *     concurrently (different streams) need distinct workspaces.
  *   - Word 0 of every workspace is a sticky device-side error mask
