@@ -38,8 +38,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "84a62eda6d7e86de80a274aef6318399461ae1327e3c435f487ee2cd6c220084",
-                "workload": "batched", "read": 276773629, "write": 8508080}
+ATTN_TRAFFIC = {"sha256": "11bca090e9a936ab2612962a5c0d787901fc250b67dbd5852298cfed42e09a20",
+                "workload": "batched", "read": 276776554, "write": 8507903}
 
 
 def sources_sha256(paths):

@@ -229,14 +229,16 @@ __device__ __forceinline__ void attend_stage(const char* stage, const bf16x8* qB
 // the decode below gives every split of a unit the same i % 8, so all of them share
 // one L2.  Counter updates are atomics performed in that L2 (no device-scope bit: a
 // device-scope atomic or write-through goes past the L2 to memory and costs
-// microseconds).  A split that stores a partial uses plain stores (the vector L1
-// writes through; the L2 acknowledges each store once it holds the data) and waits
-// for the acknowledgements before it counts the partial as stored; the reader
-// invalidates its L1 and reads the partials from the L2 (they are stored
-// write-through, which also leaves the L2 copy valid).  Each counter has a
-// 128-byte line of its own, so no two XCDs ever hold one counter line in a launch;
-// across launches the kernel-boundary L2 writeback and invalidate keep the counters
-// coherent.
+// microseconds).  A split that stores a partial stores it write-through (the L2
+// acknowledges each store once it holds the data, and keeps a valid copy) and
+// waits for the acknowledgements before it counts the partial as stored.  The
+// reader's loads are served by the L2: a unit's partial slots are read once, by
+// the unit's last split, and never share a cache line with another unit's slots,
+// so no CU can hold an older copy of them in its L1 (which every launch starts
+// empty).  A workgroup-scope buffer_inv would not help here: it leaves the L1's
+// lines in place.  Each counter has a 128-byte line of its own, so no two XCDs ever
+// hold one counter line in a launch; across launches the kernel-boundary L2
+// writeback and invalidate keep the counters coherent.
 constexpr int kCntStride = 32;  // uint32 words per arrival counter (one 128-byte line)
 constexpr int kMergeSpinLimit = 1 << 20;  // polls of the stored count (~0.5 s) before giving up
 
@@ -689,13 +691,12 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   __syncthreads();
 
   // The merge: every wave combines its DTG dimension tiles of its head over all
-  // splits: its own split from registers, the others from the shared L2 (L1
-  // invalidated first; sc0 loads).  All loads of a chunk of CH splits, and every
+  // splits: its own split from registers, the others from the shared L2 (sc0
+  // loads; see the hand-off notes above).  All loads of a chunk of CH splits, and every
   // split's (m, l), are issued before any is used (addresses clamped to a real
   // split), so up to CH splits cost one memory round trip.
   constexpr int CH = (DTG * 4 * kMaxFused <= 128 && NW <= 8) ? kMaxFused : (NW <= 8 ? 4 : 2);
   constexpr int kL2 = 1;  // cache policy sc0
-  asm volatile("buffer_inv sc0" : : : "memory");  // drop any L1 copy of the partials
   const int64_t slot0 = (int64_t)u * p.n_splits * G;  // first slot of the unit
   const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
       p.ws_o + slot0 * (DT * 256), 0, p.n_splits * G * DT * 1024, 0x00020000);

@@ -252,8 +252,10 @@ __global__ __launch_bounds__(kThreads) void verify_fused_kernel(VerifyParams p, 
   }
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(s_last)) return;
-  // Every other chunk key of the sequence was written by another CU of this XCD and
-  // never read by this one, so the loads below miss the L1 and read the L2.
+  // The loads below are served by the L2: the sequence's chunk keys are read once,
+  // here, and its key block (16 rows x n_chunks x 8 bytes = 128 * n_chunks bytes
+  // from a 256-byte aligned base) shares no cache line with another sequence's, so
+  // no CU can hold an older copy of them in its L1 (which every launch starts empty).
   accept_seq(p, b, sh);
 }
 
