@@ -48,6 +48,8 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 constexpr int TK = 32;        // keys per pipeline stage
 constexpr int NST = 8;        // stages in the LDS ring
 constexpr int kMaxFused = 8;  // up to this many splits per unit merge inside the split kernel
+constexpr int kMaxSplitKeys = 8192;  // context keys per split at most
+constexpr int kMaxPtEntries = kMaxSplitKeys / 16 + 1;  // page-table slice of a split (paged caches)
 
 // Wave groups per workgroup: group k consumes stage NGRP*pack + k of every pack of
 // NGRP consecutive stages.  Two groups while the workgroup stays within 10 waves
@@ -81,11 +83,14 @@ __device__ __forceinline__ int vswz(int t) {
   else return 2 * (((t >> 1) & 1) | (((t >> 3) & 1) << 1));
 }
 
+// Paged caches: the page ids of the split come from its page-table slice in LDS
+// (`pt`, entry i = page of tokens 16*(pt0 + i) ..), so no global load precedes a
+// DMA: waiting for one would also wait for every stage load issued before it.
 template <bool PAGED>
 __device__ __forceinline__ const uint16_t* key_row(const AttnParams& p, const uint16_t* cache, int b, int g,
-                                                   int t, int D) {
+                                                   int t, int D, const int32_t LDS_AS* pt, int pt0) {
   if constexpr (PAGED) {
-    int page = p.page_table[(int64_t)b * p.capacity + (t >> 4)];
+    int page = pt[(t >> 4) - pt0];
     if ((unsigned)page >= (unsigned)p.num_pages) {
       set_dev_error(p.err, 1u << 1);
       page = 0;
@@ -101,7 +106,7 @@ __device__ __forceinline__ const uint16_t* key_row(const AttnParams& p, const ui
 // finite key row whose scores are masked, so no stale LDS data can leak in).
 template <int D, bool PAGED>
 __device__ __forceinline__ void issue_load(const AttnParams& p, uint32_t stage, int b, int g, int t0, int tend,
-                                           int li, int lane) {
+                                           int li, int lane, const int32_t LDS_AS* pt, int pt0) {
   using GE = Geo<D>;
   const int rsub = lane / GE::NCH, pch = lane % GE::NCH;
   const bool is_v = li >= GE::LOADS / 2;
@@ -110,7 +115,7 @@ __device__ __forceinline__ void issue_load(const AttnParams& p, uint32_t stage, 
   const int key = min(t0 + row, tend - 1);
   const int c = pch ^ (is_v ? vswz<D>(row) : kswz<D>(row));
   // a 1 KB load covers RPL (4 or 8) aligned rows: never crosses a 16-token page
-  const uint16_t* src = key_row<PAGED>(p, is_v ? p.v_cache : p.k_cache, b, g, key, D) + c * 8;
+  const uint16_t* src = key_row<PAGED>(p, is_v ? p.v_cache : p.k_cache, b, g, key, D, pt, pt0) + c * 8;
   lds_dma16_nt_m0(src, stage + (is_v ? GE::TILE : 0) + rb * 1024);
 }
 
@@ -248,13 +253,14 @@ constexpr int kMergeSpinLimit = 1 << 20;  // polls of the stored count (~0.5 s) 
 // past the split's last key).
 template <int D, int NW, int NP, bool PAGED>
 __device__ __forceinline__ void issue_pack(const AttnParams& p, uint32_t ring, int b, int g, int kb, int ke, int pk,
-                                           int w, int lane) {
+                                           int w, int lane, const int32_t LDS_AS* pt, int pt0) {
   using GE = Geo<D>;
 #pragma unroll
   for (int li = w; li < NP * GE::LOADS; li += NW) {
     const int sub = li / GE::LOADS;
     const int st = NP * pk + sub;
-    issue_load<D, PAGED>(p, ring + (st % NST) * GE::STAGE, b, g, kb + st * TK, ke, li - sub * GE::LOADS, lane);
+    issue_load<D, PAGED>(p, ring + (st % NST) * GE::STAGE, b, g, kb + st * TK, ke, li - sub * GE::LOADS, lane, pt,
+                         pt0);
   }
 }
 
@@ -333,6 +339,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   __shared__ __attribute__((aligned(1024))) char lds[NST * GE::STAGE + QST];
   char* const qst = lds + NST * GE::STAGE;
   __shared__ uint32_t s_last;
+  __shared__ int32_t s_pt[PAGED ? kMaxPtEntries : 1];
 
   // XCD-aware decode: WG i runs on XCD i % 8; every split of a unit shares one XCD.
   const int i_wg = blockIdx.x;
@@ -360,6 +367,17 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   const int r = lane & 15, q = lane >> 4;
   const int h = g * G + hw;
 
+  // Paged caches: the split's page ids go to LDS first, with plain loads waited for
+  // before any stage load is issued (entries of pages kb/16 .. (ke-1)/16 only: every
+  // index stays inside the sequence's page-table row, since ke <= L <= 16*capacity).
+  const int32_t LDS_AS* pt_lds = (const int32_t LDS_AS*)s_pt;
+  if constexpr (PAGED) {
+    const int n_pt = ke > kb ? ((ke - 1) >> 4) - (kb >> 4) + 1 : 0;
+    const int32_t* src = p.page_table + (int64_t)b * p.capacity + (kb >> 4);
+    for (int i = tid; i < n_pt; i += 64 * NW) s_pt[i] = src[i];
+    __syncthreads();
+  }
+
   // Start the context stream right after the Q loads: packs 0 .. NPK-2 (part of
   // them after the Q wait, see QF).  Dense packs inside the split take the
   // scalar-base path; the rest clamp per row.
@@ -377,7 +395,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
       const int64_t off = (int64_t)pk * NGRP * TK * GE::ROW;
       issue_pack_dense<D, NW, NGRP>(dpl, k_split + off, v_split + off, lds_ring, pk);
     } else {
-      issue_pack<D, NW, NGRP, PAGED>(p, lds_ring, b, g, kb, ke, pk, w, lane);
+      issue_pack<D, NW, NGRP, PAGED>(p, lds_ring, b, g, kb, ke, pk, w, lane, pt_lds, kb >> 4);
     }
   };
   constexpr int QL = G * D / 32, CL = D / 32;  // wave loads: Q rows, cos rows (sin the same)
@@ -821,8 +839,14 @@ AttnPlan plan_block_attn(int batch, int n_q_heads, int n_kv_heads, int head_dim,
   const int64_t target_wg = num_cu > 0 ? num_cu : 256;
   int64_t kps = (units * (int64_t)max_ctx + target_wg - 1) / target_wg;
   kps = ((kps + 2 * TK - 1) / (2 * TK)) * (2 * TK);
+  // At most a quarter of the longest context per split: the host does not know the
+  // lengths of a ragged batch, and its longest sequences then come in >= 4 pieces
+  // that the dispatcher spreads over the CUs (uniform batches are unaffected: there
+  // the bound above is already <= max_ctx / 4 whenever the CUs are full).
+  const int64_t quarter = ((max_ctx / 4 + 2 * TK - 1) / (2 * TK)) * (2 * TK);
+  if (kps > quarter) kps = quarter;
   if (kps < 256) kps = 256;
-  if (kps > 8192) kps = 8192;
+  if (kps > kMaxSplitKeys) kps = kMaxSplitKeys;
   pl.kps = (int)kps;
   pl.n_splits = max_ctx > 0 ? (int)((max_ctx + kps - 1) / kps) : 1;
   pl.fused = pl.n_splits <= kMaxFused;
