@@ -38,8 +38,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "fc653386ac4d1e296c3c0d1d724694639e73be8ee553b2f0866a8b12bc18e3a8",
-                "workload": "batched", "read": 276772589, "write": 8508114}
+ATTN_TRAFFIC = {"sha256": "12cc79cf2023709d45fa39d885752ee35230da1a1857e6819a2281ac7064209d",
+                "workload": "batched", "read": 276754154, "write": 8507994}
 
 
 def sources_sha256(paths):

@@ -767,28 +767,36 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   for (int j = 0; j < DTG; ++j) *reinterpret_cast<f32x4*>(outp + (dt0 + j) * 16) = acc[j] * inv;
 }
 
-// Log-sum-exp merge of the split partials: one workgroup per (unit, query head),
-// thread = (row r, 8 consecutive dims).  Partials are stored in the split
-// kernel's lane order: dims 16*dt + 4*q + v of row r at lane r + 16*q.
+// Log-sum-exp merge of the split partials (more than kMaxFused splits per unit):
+// one workgroup per (unit, query head, quarter of the dimensions: 32 dims).  Thread
+// (split group sg, row r, 8-dim chunk c) combines splits sg, sg+4, ... of its row's
+// 8 dims with all their loads issued before the first is used; the four split
+// groups are summed through LDS, in a fixed order.  Partials are stored in the
+// split kernel's lane order: dims 16*dt + 4*q + v of row r at lane r + 16*q.
+constexpr int kMergeGroups = 4;
 template <int D>
-__global__ __launch_bounds__(2 * D) void attn_merge_kernel(AttnParams p, int group) {
-  constexpr int DT = D / 16, NCH = D / 8;
-  const int u = blockIdx.x / group, w = blockIdx.x - u * group;
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int group) {
+  constexpr int DT = D / 16, NQ = D / 32;
+  __shared__ float s_acc[kMergeGroups][64][9];
+  const int dq = blockIdx.x % NQ, uh = blockIdx.x / NQ;
+  const int u = uh / group, w = uh - u * group;
   const int b = u / p.n_kv_heads, g = u - b * p.n_kv_heads;
   int L = p.ctx_len[b];
   L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
   const int ns = L > 0 ? (L + p.kps - 1) / p.kps : 1;
   if (ns == 1) return;  // written directly by the split kernel
-  const int r = threadIdx.x / NCH, c = threadIdx.x % NCH;
-  const int dt = c >> 1, q0 = 2 * (c & 1);
+  const int tid = threadIdx.x, sg = tid >> 6, rc = tid & 63;
+  const int r = rc >> 2, c = rc & 3;  // row, 8-dim chunk of the quarter
+  const int dt = 2 * dq + (c >> 1), q0 = 2 * (c & 1);
   const int h = g * group + w;
   const int64_t slot0 = (int64_t)u * p.n_splits * group + w;  // slot of split sp: slot0 + sp * group
   float mmax = -INFINITY;
+#pragma unroll 8
   for (int sp = 0; sp < ns; ++sp) mmax = fmaxf(mmax, p.ws_ml[((slot0 + (int64_t)sp * group) * 16 + r) * 2]);
   float den = 0.f;
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int sp = 0; sp < ns; ++sp) {
+#pragma unroll 8
+  for (int sp = sg; sp < ns; sp += kMergeGroups) {
     const int64_t sl = slot0 + (int64_t)sp * group;
     const float* ml = p.ws_ml + (sl * 16 + r) * 2;
     const float wgt = __builtin_amdgcn_exp2f(ml[0] - mmax);
@@ -797,8 +805,27 @@ __global__ __launch_bounds__(2 * D) void attn_merge_kernel(AttnParams p, int gro
     a0 += wgt * *reinterpret_cast<const f32x4*>(ps);
     a1 += wgt * *reinterpret_cast<const f32x4*>(ps + 64);
   }
+  float* sa = s_acc[sg][rc];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sa[e] = a0[e];
+    sa[4 + e] = a1[e];
+  }
+  sa[8] = den;
+  __syncthreads();
+  if (sg != 0) return;
+#pragma unroll
+  for (int k = 1; k < kMergeGroups; ++k) {
+    const float* o = s_acc[k][rc];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a0[e] += o[e];
+      a1[e] += o[4 + e];
+    }
+    den += o[8];
+  }
   const float inv = 1.f / den;
-  float* outp = p.out + (((int64_t)b * kBlock + r) * p.n_q_heads + h) * D + 8 * c;
+  float* outp = p.out + (((int64_t)b * kBlock + r) * p.n_q_heads + h) * D + 32 * dq + 8 * c;
   *reinterpret_cast<f32x4*>(outp) = a0 * inv;
   *reinterpret_cast<f32x4*>(outp + 4) = a1 * inv;
 }
@@ -809,7 +836,7 @@ hipError_t launch_t(const AttnParams& p, hipStream_t stream) {
   const int grid = kNumXcd * p.n_splits * groups;
   hipLaunchKernelGGL((block_attn_kernel<D, G, PAGED>), dim3(grid), dim3(64 * ngrp<G>() * G), 0, stream, p);
   if (p.n_splits > 1 && !p.fused)
-    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(p.n_units * G), dim3(2 * D), 0, stream, p, G);
+    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(p.n_units * G * (D / 32)), dim3(256), 0, stream, p, G);
   return hipGetLastError();
 }
 

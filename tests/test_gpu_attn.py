@@ -54,6 +54,7 @@ SMALL = [  # (L per sequence, Hq, Hkv, d)
     ([0], 4, 2, 64), ([1], 4, 2, 64), ([15, 16], 4, 2, 64), ([63, 64, 65], 4, 4, 128),
     ([100, 7], 8, 2, 128), ([300], 3, 1, 64), ([257, 255, 256], 5, 1, 128), ([1000, 0], 8, 1, 64),
     ([130], 6, 2, 128), ([700, 513], 7, 1, 128), ([64], 1, 1, 128), ([777, 33], 32, 8, 128),
+    ([3000, 40], 4, 2, 64),  # 12 splits of 256 keys: the separate merge kernel at d=64
 ]
 
 
