@@ -38,8 +38,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "12cc79cf2023709d45fa39d885752ee35230da1a1857e6819a2281ac7064209d",
-                "workload": "batched", "read": 276754154, "write": 8507994}
+ATTN_TRAFFIC = {"sha256": "c6340be838dd8f79366dee02cff29916ccb7f0513e88ccf3c9eaa71cba2f80b1",
+                "workload": "batched", "read": 276755258, "write": 8508272}
 
 
 def sources_sha256(paths):
