@@ -141,6 +141,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
 // Read in place, its rows would be lda apart, and that strided pattern measured
 // 2.5x slower for the whole product at 128 rows x 20480 x 4096.
 constexpr int SK_RW = 4;                     // weight-row wave groups (32 rows each)
+// Up to kSkinnyMaxRows activation rows take the skinny kernel, in chunks of up to
+// kSkinnyChunk rows (MT = 16 at 129..256 rows): every chunk streams the weights once,
+// where the tiled kernel's 128-row tiles would stream them once per 128 rows.
+constexpr int kSkinnyChunk = 256;
+constexpr int kSkinnyMaxRows = 512;
 constexpr int SK_RT = 2;                     // 16-row weight tiles per wave
 constexpr int SK_ROWS = SK_RW * SK_RT * 16;  // weight rows per workgroup (128)
 
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
   auto issue = [&](int st) {
     const int ks = st + rot < n_st ? st + rot : st + rot - n_st;
     const int k0 = kbeg + ks * BK;
-    const uint16_t* xstep = p.xp + (int64_t)(k0 / BK) * p.mp * BK;
+    const uint16_t* xstep = p.xp + ((int64_t)(k0 / BK) * p.mp + p.m_off) * BK;
     const uint32_t stage = ring + (uint32_t)((st % SG::NS) * SG::STAGE);
 #pragma unroll
     for (int i = 0; i < SG::LW; ++i) {
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt) {
       const int m = (wt * MTW + mt) * 16 + r;
-      if (m < p.M) *reinterpret_cast<f32x4*>(out + (int64_t)m * p.N + n) = acc[rt][mt];
+      if (m < p.m_rows) *reinterpret_cast<f32x4*>(out + (int64_t)(p.m_off + m) * p.N + n) = acc[rt][mt];
     }
   }
 }
@@ -425,7 +430,7 @@ ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_
   const int cus = num_cu > 0 ? num_cu : 256;
   const int target = 2 * cus;
   const int mtiles = (n_rows + GBM - 1) / GBM;
-  pl.fc_small = pl.kv_small = n_rows <= GBM;  // skinny weight-streaming kernel
+  pl.fc_small = pl.kv_small = n_rows <= kSkinnyMaxRows;  // skinny weight-streaming kernel
   if (has_fc) {
     const int sp = pl.fc_small ? skinny_splits(hidden, n_rows, k_fc, cus)
                                : split_count(mtiles * ((hidden + GBN - 1) / GBN), n_rows, k_fc, target);
@@ -444,7 +449,10 @@ ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_
   if (has_fc) off = align(off + 2 * (size_t)n_rows * hidden);
   pl.off_kv = off;
   off = align(off + sizeof(float) * (size_t)pl.kv_splits * n_rows * kv_width);
-  pl.mp = 32 * ((n_rows + 31) / 32);
+  // Rows of a packed step: every skinny chunk reads 16*MT <= 32*ceil(chunk rows / 32)
+  // rows from its offset, so with more than one chunk the steps hold whole chunks
+  // (rows past n_rows are zero in the packed activations and never stored).
+  pl.mp = n_rows <= 128 ? 32 * ((n_rows + 31) / 32) : kSkinnyChunk * ((n_rows + kSkinnyChunk - 1) / kSkinnyChunk);
   pl.off_xp = off;
   if (pl.fc_small && has_fc) off = align(off + 2 * (size_t)k_fc * pl.mp);
   pl.off_cp = off;
@@ -461,13 +469,20 @@ void launch_skinny(const GemmParams& p, int splits, hipStream_t stream) {
 
 hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStream_t stream) {
   if (small_m) {
-    // activation tiles in pairs of 16 rows (stage loads split evenly over the waves)
-    switch ((p.M + 31) / 32) {
-      case 0:
-      case 1: launch_skinny<2>(p, splits, stream); break;
-      case 2: launch_skinny<4>(p, splits, stream); break;
-      case 3: launch_skinny<6>(p, splits, stream); break;
-      default: launch_skinny<8>(p, splits, stream); break;
+    // Chunks of up to kSkinnyChunk rows, each a full pass over the weights; activation
+    // tiles in pairs of 16 rows (stage loads split evenly over the waves).
+    for (int m_off = 0; m_off < max(p.M, 1); m_off += kSkinnyChunk) {
+      GemmParams c = p;
+      c.m_off = m_off;
+      c.m_rows = min(kSkinnyChunk, p.M - m_off);
+      switch ((c.m_rows + 31) / 32) {
+        case 0:
+        case 1: launch_skinny<2>(c, splits, stream); break;
+        case 2: launch_skinny<4>(c, splits, stream); break;
+        case 3: launch_skinny<6>(c, splits, stream); break;
+        case 4: launch_skinny<8>(c, splits, stream); break;
+        default: launch_skinny<16>(c, splits, stream); break;
+      }
     }
     return hipGetLastError();
   }

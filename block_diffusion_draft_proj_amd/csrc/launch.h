@@ -88,6 +88,7 @@ struct GemmParams {
   float* out;                          // [splits][M][N] fp32 partial sums
   const uint16_t* xp;                  // skinny path: A packed as [K/64][mp][64] (64-K steps)
   int mp;                              // rows of a packed step (M rounded up to 32)
+  int m_off, m_rows;                   // skinny path: this launch's rows [m_off, m_off + m_rows) of M
 };
 struct PackParams {
   const uint16_t* a_seg[kMaxLayers];  // as GemmParams
