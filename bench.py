@@ -38,8 +38,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "c6340be838dd8f79366dee02cff29916ccb7f0513e88ccf3c9eaa71cba2f80b1",
-                "workload": "batched", "read": 276755258, "write": 8508272}
+ATTN_TRAFFIC = {"sha256": "d1e0c5f3676decc3885d3801c49532fdaeeb02c5937db54d6a9e665942137292",
+                "workload": "batched", "read": 276755249, "write": 8508045}
 
 
 def sources_sha256(paths):

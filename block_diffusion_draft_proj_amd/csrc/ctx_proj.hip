@@ -412,12 +412,15 @@ int k_per_split(int K, int splits) {
 
 // Skinny plan: one workgroup of 128 weight rows per CU, K split to fill the CUs,
 // while the fp32 partial sums (splits x M x N x 4 bytes, written and read back
-// once) stay within half the weight bytes (N x K x 2) and every split keeps >= 2
-// steps.
+// once) stay within half the weight bytes (N x K x 2; twice them above 128 rows) and
+// every split keeps >= 2 steps.
 int skinny_splits(int N, int M, int K, int num_cu) {
   const int tiles = (N + SK_ROWS - 1) / SK_ROWS;
   int splits = (num_cu + tiles - 1) / tiles;
-  splits = min(splits, max(1, (int)((int64_t)K / (4 * (int64_t)(M > 0 ? M : 1)))));
+  // fp32 partials within half the weight bytes at <= 128 rows; within twice them above,
+  // where a half-weight budget left the K/V product 2 splits (32 workgroups) at 512
+  // rows (ragged batch: 490 us per step against 523 us).
+  splits = min(splits, max(1, (int)((int64_t)K / ((M > 128 ? 1 : 4) * (int64_t)(M > 0 ? M : 1)))));
   splits = min(splits, max(1, K / (2 * BK)));
   splits = max(1, splits);
   // a divisor of 8 (1, 2, 4) or a multiple of 8, for the XCD-aware decode
