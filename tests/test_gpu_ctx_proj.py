@@ -160,13 +160,14 @@ def test_ctx_proj_ragged_paged_block_rows():
     _check(cfg, 16 * cfg.batch, seq, pos, capacity=0, table=table, num_pages=len(need), label="ragged paged")
 
 
-def test_ctx_proj_prefill_chunk_with_ragged_row_tail():
+# 300 rows: a 256-row chunk then a 44-row one; 80 rows: 6 activation tiles (MT = 6).
+@pytest.mark.parametrize("n", [300, 80])
+def test_ctx_proj_prefill_chunk_with_ragged_row_tail(n):
     cfg = dataclasses.replace(synth.CONFIGS["qwen3_8b"], n_target_layers=2)
-    n = 300
     seq = np.zeros(n, np.int32)
     pos = np.arange(n, dtype=np.int32) + 1000
     pos[::7] = -1
-    _check(cfg, n, seq, pos, capacity=1400, label="prefill 300 rows")
+    _check(cfg, n, seq, pos, capacity=1400, label=f"prefill {n} rows")
 
 
 def test_ctx_proj_without_fc():
