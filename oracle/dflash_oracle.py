@@ -292,6 +292,30 @@ def verify_accept_ref(logits: np.ndarray, block_tokens: np.ndarray, kv_len: np.n
 
 
 # --------------------------------------------------------------------------
+# Draft side of the cycle: the draft's greedy tokens at the 15 mask slots
+# (dflash-mlx page: "single-forward verify" steps 3-4 -- the draft receives the
+# block [staged, mask x 15] and one forward yields the 15 candidate tail
+# tokens; "block-diffusion draft" -- the whole block is filled in one forward.)
+# Reading: greedy drafting -- each candidate is the lowest-index maximum of the
+# draft's logits at its own slot, by the same argmax rule as the target's.
+# --------------------------------------------------------------------------
+def draft_block_ref(draft_logits: np.ndarray, staged: np.ndarray) -> np.ndarray:
+    """block_tokens [B, 16] for one cycle, as the verify step consumes them.
+
+    draft_logits [B, 16, V] bf16 bits: the draft's logits over the block
+    [staged, mask x 15]; row 0 (the staged slot) is not read.  staged [B].
+      block[b, 0] = staged[b]
+      block[b, i] = argmax_v draft_logits[b, i, v]        i = 1 .. 15
+    """
+    B = draft_logits.shape[0]
+    blk = np.empty((B, BLOCK), dtype=np.int32)
+    blk[:, 0] = np.asarray(staged, dtype=np.int32)
+    for b in range(B):                      # row-wise decode keeps memory bounded
+        blk[b, 1:] = argmax_first(bf16_to_f64(draft_logits[b, 1:]))
+    return blk
+
+
+# --------------------------------------------------------------------------
 # Brute-force twins for tiny shapes: scalar Python loops, float64 math.
 # --------------------------------------------------------------------------
 def argmax_brute(row: Sequence[float]) -> int:

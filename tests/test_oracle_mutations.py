@@ -35,6 +35,10 @@ MUTANTS = {
                       "kc, vc = k_cache[b, (g + 1) % Hkv], v_cache[b, (g + 1) % Hkv]"),
     "c_not_rounded": ("Cb = round_bf16(C)", "Cb = C"),
     "commit_positions": ("np.where(i <= accept[:, None]", "np.where(i < accept[:, None]"),
+    "draft_alignment": ("blk[b, 1:] = argmax_first(bf16_to_f64(draft_logits[b, 1:]))",
+                        "blk[b, 1:] = argmax_first(bf16_to_f64(draft_logits[b, :BLOCK - 1]))"),
+    "draft_staged_slot": ("blk[:, 0] = np.asarray(staged, dtype=np.int32)",
+                          "blk[:, 0] = argmax_first(bf16_to_f64(draft_logits[:, 0]))"),
     "rope_on_v": ("V = (Cb @ bf16_to_f64(w_v).T).reshape(M, n_kv_heads, head_dim)",
                   "V = apply_rope((Cb @ bf16_to_f64(w_v).T).reshape(M, n_kv_heads, head_dim), "
                   "np.maximum(np.asarray(row_pos), 0), base)"),

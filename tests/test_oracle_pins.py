@@ -543,3 +543,48 @@ def test_lossless_loop_with_toy_target():
         assert seq[:len(prompt) + N] == greedy[:len(prompt) + N], mode
         if mode == "perfect":
             assert cycles == math.ceil(N / 16)
+
+
+# ----------------------------------------------------------------------------- draft tokens
+def test_draft_block_matches_brute_force_and_ignores_staged_row():
+    # Small integer-valued logits force many ties; row 0 (the staged slot) holds NaN,
+    # which would win every argmax if it were read.
+    rng = np.random.default_rng(41)
+    B, V = 3, 37
+    vals = rng.integers(-3, 4, (B, 16, V)).astype(np.float32)
+    vals[:, 0, 5] = np.nan
+    vals[1, 7, 20] = np.nan                          # a NaN in a mask row does win
+    vals[2, 3, :] = -0.0
+    vals[2, 3, 11] = 0.0                             # -0 == +0: the first zero, index 0
+    staged = np.array([11, 0, 36], np.int32)
+    blk = orc.draft_block_ref(_bits(vals), staged)
+    assert blk.shape == (B, 16) and blk.dtype == np.int32
+    for b in range(B):
+        assert blk[b, 0] == staged[b]
+        for i in range(1, 16):
+            assert blk[b, i] == orc.argmax_brute(vals[b, i].tolist()), (b, i)
+    assert blk[1, 7] == 20 and blk[2, 3] == 0
+
+
+def test_draft_that_predicts_the_target_is_fully_accepted():
+    # The draft proposes the token after slot i at slot i + 1 (staged, d_1 .. d_15), and the
+    # verify compares d_{i+1} with the target's greedy token after slot i.  A draft whose
+    # logits at slot i + 1 equal the target's at slot i is therefore accepted in full, and
+    # one that is wrong first at slot j + 1 is accepted up to j.
+    rng = np.random.default_rng(42)
+    B, V = 4, 300
+    target = rng.standard_normal((B, 16, V)).astype(np.float32)
+    draft = np.empty_like(target)
+    draft[:, 0] = rng.standard_normal((B, V))
+    draft[:, 1:] = target[:, :15]
+    staged = rng.integers(0, V, B).astype(np.int32)
+    kv = np.array([0, 5, 17, 100], np.int32)
+    res = orc.verify_accept_ref(_bits(target), orc.draft_block_ref(_bits(draft), staged), kv)
+    assert np.array_equal(res["accept"], [15] * B)
+    assert np.array_equal(res["next"], orc.argmax_first(target[:, 15]))
+    for b, j in enumerate([0, 3, 9, 14]):
+        post_j = int(np.argmax(target[b, j]))
+        draft[b, j + 1] = 0.0
+        draft[b, j + 1, (post_j + 1) % V] = 1.0      # a different greedy token at slot j + 1
+    res = orc.verify_accept_ref(_bits(target), orc.draft_block_ref(_bits(draft), staged), kv)
+    assert np.array_equal(res["accept"], [0, 3, 9, 14])
