@@ -139,6 +139,11 @@ def verify_bytes(cfg, B):
     return 2 * 16 * B * cfg.vocab + 4 * 16 * B * 3 + 4 * B * 4
 
 
+def draft_bytes(cfg, B):
+    # the draft's logits at the 15 mask slots, the staged tokens in, the block out
+    return B * 15 * cfg.vocab * 2 + B * 4 + B * 16 * 4
+
+
 def proj_bytes(cfg, M, committed):
     kvw = cfg.n_kv_heads * cfg.head_dim
     return (2 * cfg.hidden * cfg.ctx_width + 2 * 2 * kvw * cfg.hidden + 2 * M * cfg.ctx_width
@@ -250,9 +255,14 @@ def main():
     # recorded event still costs the command processor a few microseconds between kernels,
     # so the verify / projection split comes from a short pass after the timed region,
     # with events after each of the three calls.
+    # The same pass times the draft-side greedy tokens (dflash_draft_argmax), the step
+    # before the verify in a decode loop; it is not part of the timed step.  It runs
+    # at the end of each pass step, on the next copy of the logits, with the verify's
+    # next_token as its staged tokens.
     N_SPLIT = 50
     tev = HipTimingEvents(2 * args.steps, torch.cuda.current_stream().cuda_stream)
-    sev = HipTimingEvents(4 * N_SPLIT, torch.cuda.current_stream().cuda_stream)
+    sev = HipTimingEvents(5 * N_SPLIT, torch.cuda.current_stream().cuda_stream)
+    dblk = z(B, 16)
 
     def step(i, ev=None, base=0, split=False):
         if ev is not None:
@@ -267,6 +277,8 @@ def main():
                             vcs[i], table, ws_p)
         if split:
             ev.record(base + 3)
+            dfl.dflash_draft_argmax(lgs[(i + 1) % R], nxt, dblk, ws_v)
+            ev.record(base + 4)
 
     for s in range(args.warmup):
         step(s % R)
@@ -277,13 +289,15 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for s in range(N_SPLIT):
-        step(s % R, sev, 4 * s, split=True)
+        step(s % R, sev, 5 * s, split=True)
     torch.cuda.synchronize()
 
     ms_step = (t1 - t0) / args.steps * 1e3
     t_attn = float(np.mean([tev.elapsed_ms(2 * s, 2 * s + 1) for s in range(args.steps)])) * 1e-3
-    t_ver = float(np.mean([sev.elapsed_ms(4 * s + 1, 4 * s + 2) for s in range(N_SPLIT)])) * 1e-3
-    t_proj = float(np.mean([sev.elapsed_ms(4 * s + 2, 4 * s + 3) for s in range(N_SPLIT)])) * 1e-3
+    t_ver = float(np.mean([sev.elapsed_ms(5 * s + 1, 5 * s + 2) for s in range(N_SPLIT)])) * 1e-3
+    t_proj = float(np.mean([sev.elapsed_ms(5 * s + 2, 5 * s + 3) for s in range(N_SPLIT)])) * 1e-3
+    t_draft = float(np.mean([sev.elapsed_ms(5 * s + 3, 5 * s + 4) for s in range(N_SPLIT)])) * 1e-3
+    d_b = draft_bytes(cfg, B)
     tev.close()
     sev.close()
     ok = bool(np.array_equal(acc.cpu().numpy(), vi.planted_accept))
@@ -307,8 +321,11 @@ def main():
                    "GB_s": round(v_b / t_ver / 1e9, 1), "bytes": v_b, "accept_matches_planted": ok},
         "ctx_proj": {"us": round(t_proj * 1e6, 2), "GB_s": round(p_b / t_proj / 1e9, 1), "bytes": p_b,
                      "rows": M, "committed_rows": committed},
-        "timing": "block_attn: HIP events around every timed call; verify and ctx_proj: events in a "
-                  "%d-step pass after the timed region" % N_SPLIT,
+        "draft_argmax": {"us": round(t_draft * 1e6, 2), "GB_s": round(d_b / t_draft / 1e9, 1),
+                         "pct_hbm_peak": round(100 * d_b / t_draft / 1e9 / HBM_PEAK_GBS, 2), "bytes": d_b,
+                         "scope": "draft-side greedy tokens at the 15 mask slots; not in the timed step"},
+        "timing": "block_attn: HIP events around every timed call; verify, ctx_proj and draft_argmax: "
+                  "events in a %d-step pass after the timed region" % N_SPLIT,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name),
                      "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": a_b},

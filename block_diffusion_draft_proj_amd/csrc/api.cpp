@@ -85,17 +85,15 @@ int dflash_rope_tables(float base, int32_t head_dim, int32_t max_pos, float* cos
 }
 
 // ------------------------------------------------------------------ verify
-// Workspace: word 0 error mask (256 bytes), chunk keys, then per-sequence arrival
-// counters (128 bytes each, 256-byte aligned).
-static size_t verify_count_offset(int32_t batch, size_t n_chunks) {
-  const size_t keys_end = 256 + sizeof(uint64_t) * (size_t)batch * DFLASH_BLOCK * n_chunks;
-  return (keys_end + 255) & ~(size_t)255;
-}
+// Workspace: word 0 error mask (256 bytes), the per-sequence arrival counters
+// (the fixed-size counter region, 128 bytes per sequence), then the chunk keys.
+constexpr size_t kVerifyKeysOffset = 256 + kCountRegionBytes;
+static_assert(sizeof(uint32_t) * kVerifyCntStride * kMaxCountSlots == kCountRegionBytes, "counter region");
 
 size_t dflash_verify_workspace_size(int32_t batch, int32_t block, int32_t vocab) {
-  if (batch < 1 || block != DFLASH_BLOCK || vocab < 1) return 0;
+  if (batch < 1 || batch > kMaxCountSlots || block != DFLASH_BLOCK || vocab < 1) return 0;
   const size_t n_chunks = ((size_t)vocab + kVerifyChunk - 1) / kVerifyChunk;
-  return verify_count_offset(batch, n_chunks) + sizeof(uint32_t) * kVerifyCntStride * (size_t)batch;
+  return kVerifyKeysOffset + sizeof(uint64_t) * (size_t)batch * DFLASH_BLOCK * n_chunks;
 }
 
 int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab, const void* logits, int64_t ld_logits,
@@ -105,7 +103,8 @@ int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab, const void
                          hipStream_t stream) {
   if (!logits || !block_tokens || !kv_len_in || !posterior || !accept_len || !next_token || !kv_len_out)
     return DFLASH_ERR_NULL;
-  if (batch < 1 || block != DFLASH_BLOCK || vocab < 1 || vocab == 0x7fffffff) return DFLASH_ERR_SHAPE;
+  if (batch < 1 || batch > kMaxCountSlots || block != DFLASH_BLOCK || vocab < 1 || vocab == 0x7fffffff)
+    return DFLASH_ERR_SHAPE;
   if (ld_logits < vocab) return DFLASH_ERR_SHAPE;
   if (page_size < 0 || (n_pages && page_size == 0)) return DFLASH_ERR_SHAPE;
   if ((ld_logits & 7) || !aligned16(logits)) return DFLASH_ERR_ALIGN;
@@ -131,14 +130,43 @@ int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab, const void
   p.commit_pos = commit_pos;
   p.n_pages = n_pages;
   p.page_size = page_size;
-  p.part = reinterpret_cast<uint64_t*>(ws + 256);
-  p.count = reinterpret_cast<uint32_t*>(ws + verify_count_offset(batch, (size_t)n_chunks));
+  p.part = reinterpret_cast<uint64_t*>(ws + kVerifyKeysOffset);
+  p.count = reinterpret_cast<uint32_t*>(ws + 256);
   return launch_status(launch_verify_accept(p, batch, stream));
+}
+
+int dflash_draft_argmax(int32_t batch, int32_t block, int32_t vocab, const void* logits, int64_t ld_logits,
+                        const int32_t* staged, int32_t* block_tokens, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  if (!logits || !block_tokens) return DFLASH_ERR_NULL;
+  if (batch < 1 || batch > kMaxCountSlots || block != DFLASH_BLOCK || vocab < 1 || vocab == 0x7fffffff)
+    return DFLASH_ERR_SHAPE;
+  if (ld_logits < vocab) return DFLASH_ERR_SHAPE;
+  if ((ld_logits & 7) || !aligned16(logits)) return DFLASH_ERR_ALIGN;
+  const int64_t n_chunks = ((int64_t)vocab + kVerifyChunk - 1) / kVerifyChunk;
+  if ((int64_t)batch * DFLASH_BLOCK * n_chunks > 0x7fffffffLL) return DFLASH_ERR_SHAPE;
+  const size_t need = dflash_verify_workspace_size(batch, block, vocab);
+  if (!workspace || workspace_bytes < need) return DFLASH_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DFLASH_ERR_ALIGN;
+  int st = check_device();
+  if (st != DFLASH_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  VerifyParams p{};
+  p.logits = static_cast<const uint16_t*>(logits);
+  p.ld = ld_logits;
+  p.vocab = vocab;
+  p.n_chunks = (int)n_chunks;
+  p.part = reinterpret_cast<uint64_t*>(ws + kVerifyKeysOffset);
+  p.count = reinterpret_cast<uint32_t*>(ws + 256);
+  p.draft_block = block_tokens;
+  p.staged = staged;
+  return launch_status(launch_draft_argmax(p, batch, stream));
 }
 
 // ------------------------------------------------------------------ block attention
 size_t dflash_block_attn_workspace_size(const dflash_dims* dims, int32_t max_ctx_len) {
   if (check_cache_dims(dims) != DFLASH_OK || max_ctx_len < 0) return 0;
+  if ((int64_t)dims->batch * dims->n_kv_heads > kMaxCountSlots) return 0;
   if (dims->n_q_heads < dims->n_kv_heads || dims->n_q_heads % dims->n_kv_heads) return 0;
   return plan_block_attn(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim, max_ctx_len, kPlanCUs)
       .ws_bytes;
@@ -154,6 +182,7 @@ int dflash_block_attn(const dflash_dims* dims, const void* q_blk, const void* k_
     return DFLASH_ERR_NULL;
   if (dims->page_size > 0 && !page_table) return DFLASH_ERR_NULL;
   if (dims->n_q_heads < dims->n_kv_heads || dims->n_q_heads % dims->n_kv_heads) return DFLASH_ERR_SHAPE;
+  if ((int64_t)dims->batch * dims->n_kv_heads > kMaxCountSlots) return DFLASH_ERR_SHAPE;
   const int group = dims->n_q_heads / dims->n_kv_heads;
   if (group > 8) return DFLASH_ERR_UNSUPPORTED;
   if (max_ctx_len < 0 || max_ctx_len > (1 << 24)) return DFLASH_ERR_SHAPE;

@@ -884,7 +884,8 @@ AttnPlan plan_block_attn(int batch, int n_q_heads, int n_kv_heads, int head_dim,
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 256;  // word 0: device error mask
   pl.off_cnt = off;  // per-unit arrival counters (fused merge), left at zero by every call
-  off = align(off + sizeof(uint32_t) * kCntStride * (size_t)units);
+  static_assert(sizeof(uint32_t) * kCntStride * kMaxCountSlots == kCountRegionBytes, "counter region");
+  off = align(off + kCountRegionBytes);
   pl.off_ml = off;
   off = align(off + sizeof(float) * 2 * 16 * (size_t)group * pl.n_splits * units);
   pl.off_o = off;

@@ -9,6 +9,14 @@ namespace dflash {
 // Split plans are made for the MI355X CU count so the workspace-size queries
 // (which run without a device) and the launches always agree.
 constexpr int kPlanCUs = 256;
+// Arrival counters live in a region of fixed size at the start of a workspace
+// (after the 256-byte error area): one 128-byte line per sequence (verify) or
+// per sequence x kv head (attention), for up to kMaxCountSlots of them.  Every
+// call's counters are a prefix of that region and no call writes anything else
+// there, so a workspace keeps its counters at zero whatever sequence of call
+// sizes it serves.
+constexpr int kMaxCountSlots = 8192;
+constexpr size_t kCountRegionBytes = 128 * (size_t)kMaxCountSlots;
 
 // ---------------------------------------------------------------- verify
 constexpr int kVerifyChunk = 8192;  // logits per workgroup (256 threads x 4 x 8)
@@ -30,8 +38,12 @@ struct VerifyParams {
   int32_t page_size;
   uint64_t* part;       // [batch*16*n_chunks] per-chunk keys
   uint32_t* count;      // [batch][kVerifyCntStride] arrival counters (one-kernel form; zero between calls)
+  // draft tokens (launch_draft_argmax only; the verify fields above stay unused there)
+  int32_t* draft_block;   // [batch][16]: slots 1..15 written, slot 0 from staged
+  const int32_t* staged;  // [batch] or null (slot 0 left as it is)
 };
 hipError_t launch_verify_accept(const VerifyParams& p, int batch, hipStream_t stream);
+hipError_t launch_draft_argmax(const VerifyParams& p, int batch, hipStream_t stream);
 
 // ---------------------------------------------------------------- RoPE tables
 hipError_t launch_rope_tables(double base, int head_dim, int max_pos, float* cos_out, float* sin_out,

@@ -25,6 +25,12 @@
 //    step: a kernel boundary is then the cheapest device-wide hand-off, since
 //    handing off across XCDs inside one kernel would need an L2 writeback
 //    (agent-scope release) from every workgroup.  No host round trip.
+//
+// The draft side of the cycle ("single-forward verify" steps 3-4: one draft
+// forward over [staged, mask x 15] yields the 15 candidate tail tokens) runs on
+// the same kernels: the greedy draft token at mask slot i is the argmax of the
+// draft's logits in row i, so only the row map (rows 1..15 of each sequence)
+// and the last step (write the tokens into the block) differ.
 #include "common.h"
 #include "launch.h"
 
@@ -145,10 +151,22 @@ __device__ __forceinline__ uint64_t chunk_key(const VerifyParams& p, int row, in
   return (canon << 32) | (uint64_t)(0xffffffffu - idx);
 }
 
+// Rows a sequence reads: all 16 for the verify, the 15 mask rows (1..15) for the
+// draft tokens.  seq_row<DRAFT>(r) is the logit row of the sequence's r-th one.
+template <bool DRAFT>
+constexpr int kRowsPerSeq = DRAFT ? kBlock - 1 : kBlock;
+template <bool DRAFT>
+__device__ __forceinline__ int seq_row(int b, int r) {
+  return b * kBlock + (DRAFT ? 1 : 0) + r;
+}
+
+template <bool DRAFT>
 __global__ __launch_bounds__(kThreads) void verify_argmax_kernel(VerifyParams p) {
   __shared__ uint32_t s_red[kThreads / kWave];
-  const int row = blockIdx.x / p.n_chunks;
-  const int chunk = blockIdx.x - row * p.n_chunks;
+  const int r = blockIdx.x / p.n_chunks;
+  const int chunk = blockIdx.x - r * p.n_chunks;
+  const int b = r / kRowsPerSeq<DRAFT>;
+  const int row = seq_row<DRAFT>(b, r - b * kRowsPerSeq<DRAFT>);
   const uint64_t key = chunk_key(p, row, chunk, s_red);
   if (threadIdx.x == 0) p.part[(int64_t)row * p.n_chunks + chunk] = key;
 }
@@ -172,15 +190,14 @@ struct AcceptShared {
 // global load is issued up front (16 threads per row over the chunk keys, the 16
 // block tokens, the input length), so the step costs one memory round trip; a
 // chain of dependent loads would cost one each.
-__device__ __forceinline__ void accept_seq(const VerifyParams& p, int b, AcceptShared& sh) {
-  const int tid = threadIdx.x;
-  const int row = tid >> 4, sub = tid & 15;  // 16 threads per row, rows aligned to 16 lanes
-  const uint64_t* pr = p.part + (int64_t)(b * kBlock + row) * p.n_chunks;
-  if (tid < kBlock) sh.blk[tid] = p.block_tokens[b * kBlock + tid];
-  if (tid == 0) sh.kvin = p.kv_len_in[b];
+// Largest chunk key of logit row `row` over its first n_chunks chunks, reduced
+// over the 16 lanes that share tid >> 4 (lane `sub` reads chunks sub, sub+16, ...).
+// Every lane of the group returns it.
+__device__ __forceinline__ uint64_t row_best(const VerifyParams& p, int row, int sub, int n_chunks) {
+  const uint64_t* pr = p.part + (int64_t)row * p.n_chunks;
   uint64_t best = 0;
 #pragma unroll 4
-  for (int c = sub; c < p.n_chunks; c += 16) {
+  for (int c = sub; c < n_chunks; c += 16) {
     const uint64_t k = pr[c];
     best = k > best ? k : best;
   }
@@ -190,8 +207,18 @@ __device__ __forceinline__ void accept_seq(const VerifyParams& p, int b, AcceptS
     const uint64_t o = ((uint64_t)hi << 32) | lo;
     best = o > best ? o : best;
   }
+  return best;
+}
+__device__ __forceinline__ int32_t key_index(uint64_t key) { return (int32_t)(0xffffffffu - (uint32_t)key); }
+
+__device__ __forceinline__ void accept_seq(const VerifyParams& p, int b, AcceptShared& sh) {
+  const int tid = threadIdx.x;
+  const int row = tid >> 4, sub = tid & 15;  // 16 threads per row, rows aligned to 16 lanes
+  if (tid < kBlock) sh.blk[tid] = p.block_tokens[b * kBlock + tid];
+  if (tid == 0) sh.kvin = p.kv_len_in[b];
+  const uint64_t best = row_best(p, b * kBlock + row, sub, p.n_chunks);
   if (sub == 0) {
-    const int32_t post = (int32_t)(0xffffffffu - (uint32_t)best);
+    const int32_t post = key_index(best);
     sh.post[row] = post;
     p.posterior[b * kBlock + row] = post;
   }
@@ -211,12 +238,26 @@ __device__ __forceinline__ void accept_seq(const VerifyParams& p, int b, AcceptS
     p.commit_pos[b * kBlock + tid] = (tid <= sh.accept) ? sh.kvin + tid : -1;
 }
 
+// Sequence b's draft tokens: the argmax of each mask row (1..15) from its chunk
+// keys, written to block[b][1..15]; slot 0 gets staged[b] when staged is given.
+// Row 0's keys are never computed, so its lanes take no chunks (they still join
+// the shuffles of their own 16-lane group, which reads no other group).
+__device__ __forceinline__ void draft_seq(const VerifyParams& p, int b) {
+  const int tid = threadIdx.x;
+  const int row = tid >> 4, sub = tid & 15;
+  const uint64_t best = row_best(p, b * kBlock + row, sub, row ? p.n_chunks : 0);
+  if (sub == 0 && row) p.draft_block[b * kBlock + row] = key_index(best);
+  if (tid == 0 && p.staged) p.draft_block[b * kBlock] = p.staged[b];
+}
+
 // Second kernel of the two-kernel form: one workgroup per sequence.  Running after
 // the argmax kernel on the same stream, it sees every chunk key without any
 // device-wide fence.
+template <bool DRAFT>
 __global__ __launch_bounds__(kAcceptThreads) void verify_accept_kernel(VerifyParams p) {
   __shared__ AcceptShared sh;
-  accept_seq(p, blockIdx.x, sh);
+  if (DRAFT) draft_seq(p, blockIdx.x);
+  else accept_seq(p, blockIdx.x, sh);
 }
 
 // One-kernel form for batch >= 8 (every XCD holds whole sequences): workgroup i runs
@@ -227,17 +268,18 @@ __global__ __launch_bounds__(kAcceptThreads) void verify_accept_kernel(VerifyPar
 // sequence's 16 * n_chunks workgroups clears the counter and runs the accept step.
 // This saves the second launch (~5 us on this part) for ~1-2 us of tail.  Below 8
 // sequences some XCDs would sit idle, so the two-kernel form is used there.
+template <bool DRAFT>
 __global__ __launch_bounds__(kThreads) void verify_fused_kernel(VerifyParams p, int batch) {
   __shared__ uint32_t s_red[kThreads / kWave];
   __shared__ uint32_t s_last;
   __shared__ AcceptShared sh;
-  const int per = kBlock * p.n_chunks;  // workgroups per sequence
+  const int per = kRowsPerSeq<DRAFT> * p.n_chunks;  // workgroups per sequence
   const int xcd = blockIdx.x % kNumXcd, j = blockIdx.x / kNumXcd;
   const int b = xcd + kNumXcd * (j / per);
   if (b >= batch) return;
   const int rem = j - (j / per) * per;
   const int row_in = rem / p.n_chunks, chunk = rem - row_in * p.n_chunks;
-  const int row = b * kBlock + row_in;
+  const int row = seq_row<DRAFT>(b, row_in);
   const uint64_t key = chunk_key(p, row, chunk, s_red);
   if (threadIdx.x == 0) {
     p.part[(int64_t)row * p.n_chunks + chunk] = key;
@@ -256,21 +298,31 @@ __global__ __launch_bounds__(kThreads) void verify_fused_kernel(VerifyParams p, 
   // here, and its key block (16 rows x n_chunks x 8 bytes = 128 * n_chunks bytes
   // from a 256-byte aligned base) shares no cache line with another sequence's, so
   // no CU can hold an older copy of them in its L1 (which every launch starts empty).
-  accept_seq(p, b, sh);
+  if (DRAFT) draft_seq(p, b);
+  else accept_seq(p, b, sh);
+}
+
+template <bool DRAFT>
+hipError_t launch_argmax_seq(const VerifyParams& p, int batch, hipStream_t stream) {
+  if (batch >= kNumXcd) {
+    const int grid = kNumXcd * ((batch + kNumXcd - 1) / kNumXcd) * kRowsPerSeq<DRAFT> * p.n_chunks;
+    hipLaunchKernelGGL(verify_fused_kernel<DRAFT>, dim3(grid), dim3(kThreads), 0, stream, p, batch);
+    return hipGetLastError();
+  }
+  const int grid = batch * kRowsPerSeq<DRAFT> * p.n_chunks;
+  hipLaunchKernelGGL(verify_argmax_kernel<DRAFT>, dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(verify_accept_kernel<DRAFT>, dim3(batch), dim3(kAcceptThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_verify_accept(const VerifyParams& p, int batch, hipStream_t stream) {
-  if (batch >= kNumXcd) {
-    const int grid = kNumXcd * ((batch + kNumXcd - 1) / kNumXcd) * kBlock * p.n_chunks;
-    hipLaunchKernelGGL(verify_fused_kernel, dim3(grid), dim3(kThreads), 0, stream, p, batch);
-    return hipGetLastError();
-  }
-  const int grid = batch * kBlock * p.n_chunks;
-  hipLaunchKernelGGL(verify_argmax_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
-  hipLaunchKernelGGL(verify_accept_kernel, dim3(batch), dim3(kAcceptThreads), 0, stream, p);
-  return hipGetLastError();
+  return launch_argmax_seq<false>(p, batch, stream);
+}
+
+hipError_t launch_draft_argmax(const VerifyParams& p, int batch, hipStream_t stream) {
+  return launch_argmax_seq<true>(p, batch, stream);
 }
 
 }  // namespace dflash

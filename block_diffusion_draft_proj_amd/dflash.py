@@ -54,6 +54,7 @@ def _load() -> ctypes.CDLL:
         "dflash_block_attn": (_c_int, [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int,
                                        _vp, _vp, _c_sz, _vp]),
         "dflash_verify_workspace_size": (_c_sz, [_c_int, _c_int, _c_int]),
+        "dflash_draft_argmax": (_c_int, [_c_int, _c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _c_sz, _vp]),
         "dflash_verify_accept": (_c_int, [_c_int, _c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _vp, _vp,
                                           _vp, _vp, _c_int, _vp, _vp, _c_sz, _vp]),
     }
@@ -70,7 +71,7 @@ LIB_PATH = _LIB_PATH
 EXPORTS = (
     "dflash_status_str", "dflash_version", "dflash_rope_tables", "dflash_ctx_proj_workspace_size",
     "dflash_ctx_proj", "dflash_block_attn_workspace_size", "dflash_block_attn",
-    "dflash_verify_workspace_size", "dflash_verify_accept",
+    "dflash_verify_workspace_size", "dflash_verify_accept", "dflash_draft_argmax",
 )
 
 
@@ -188,6 +189,20 @@ def dflash_verify_accept(logits: torch.Tensor, block_tokens: torch.Tensor, kv_le
         _dev(posterior, "posterior", (torch.int32,)), _dev(accept_len, "accept_len", (torch.int32,)),
         _dev(next_token, "next_token", (torch.int32,)), _dev(kv_len_out, "kv_len_out", (torch.int32,)),
         _dev(commit_pos, "commit_pos", (torch.int32,)), page_size, _dev(n_pages, "n_pages", (torch.int32,)),
+        _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
+
+
+def dflash_draft_argmax(logits: torch.Tensor, staged: Optional[torch.Tensor], block_tokens: torch.Tensor,
+                        workspace: torch.Tensor, vocab: Optional[int] = None, stream=None) -> None:
+    """Draft tokens: block_tokens[b, 1:16] = argmax of the draft's logits rows 1..15;
+    block_tokens[b, 0] = staged[b] when staged is given.  logits [B, 16, ld]."""
+    if logits.dim() != 3 or logits.stride(2) != 1 or logits.stride(1) != logits.shape[2] \
+            or logits.stride(0) != logits.shape[1] * logits.shape[2]:
+        raise ValueError("logits must be a contiguous [B, 16, ld] tensor")
+    B, blk, ld = (int(s) for s in logits.shape)
+    _check("dflash_draft_argmax", _lib.dflash_draft_argmax(
+        B, blk, ld if vocab is None else vocab, _dev(logits, "logits", _BF16), ld,
+        _dev(staged, "staged", (torch.int32,)), _dev(block_tokens, "block_tokens", (torch.int32,)),
         _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
 
 

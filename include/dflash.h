@@ -28,12 +28,16 @@
  *     any error nothing is enqueued and no output is touched.
  *   - Workspaces are caller-owned device buffers of at least the size the
  *     matching *_workspace_size() query returns.  Zero a workspace once before
- *     its first use; every call leaves it fit for the next one (the block
- *     attention keeps per-sequence-head arrival counters in it, the verify with
- *     8 or more sequences per-sequence ones, and each call returns them to
- *     zero), so one buffer can serve any number of calls on the same
- *     stream, at any sizes up to the ones it was sized for.  Calls that run
- *     concurrently (different streams) need distinct workspaces.
+ *     its first use; every call leaves it fit for the next one.  The block
+ *     attention keeps per-(sequence, kv head) arrival counters in it, and the
+ *     verify and the draft argmax with 8 or more sequences keep per-sequence
+ *     ones.  They sit in a region of fixed size (1 MiB after the 256-byte error
+ *     area; at most 8192 counters, hence batch <= 8192 and, for the attention,
+ *     batch * n_kv_heads <= 8192) that nothing else is written to, and each
+ *     call returns its counters to zero.  So one buffer serves any number of
+ *     calls on the same stream, in any order of sizes, as long as each call's
+ *     own *_workspace_size() fits in it.  Calls that run concurrently
+ *     (different streams) need distinct workspaces.
  *   - Word 0 of every workspace is a sticky device-side error mask
  *     (DFLASH_DEVERR_*): data-dependent faults found by the kernels (a context
  *     length, page id or row position out of range) are clamped or skipped so
@@ -184,6 +188,31 @@ int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab,
                          int32_t* next_token, int32_t* kv_len_out, int32_t* commit_pos,
                          int32_t page_size, int32_t* n_pages,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- draft-side greedy tokens (the step before the verify) ----------------
+ * One draft forward over the block [staged, mask x 15] yields the 15
+ * candidate tail tokens ("dflash-mlx: lossless speculative decoding",
+ * "single-forward verify" steps 3-4; "block-diffusion draft").  Greedy
+ * drafting: the candidate at mask slot i is the argmax of the draft's logits
+ * in row i, by the same rule as the verify's posterior.  For each b:
+ *   block_tokens[b,i] = lowest index of the maximum of logits[b,i,0:vocab],
+ *                       i = 1..15  (NaN ranks above every number; -0 == +0)
+ *   block_tokens[b,0] = staged[b]  if staged != NULL, else left unchanged
+ *
+ *   logits       [B][16][ld_logits] bf16, ld_logits >= vocab, ld_logits % 8 == 0:
+ *                the draft's logits over the block; row 0 (the staged slot) is
+ *                not read
+ *   staged       [B] int32 or NULL, e.g. the verify's next_token of the
+ *                previous cycle; must not overlap block_tokens
+ *   block_tokens [B][16] int32 output, in the layout dflash_verify_accept reads
+ * The workspace is the verify's: at least dflash_verify_workspace_size(batch,
+ * block, vocab) bytes, zeroed once; one buffer may serve both calls on one
+ * stream.  Errors as for dflash_verify_accept.  Results are bit-exact and
+ * independent of launch shape. */
+int dflash_draft_argmax(int32_t batch, int32_t block, int32_t vocab,
+                        const void* logits, int64_t ld_logits, const int32_t* staged,
+                        int32_t* block_tokens, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -80,3 +80,15 @@ def run_verify(logits: np.ndarray, block_tokens, kv_len, page_size=0, vocab=None
     if npg is not None:
         res["n_pages"] = npg.cpu().numpy()
     return res, ws
+
+
+def run_draft(logits: np.ndarray, staged, vocab=None, ws=None, init=-7):
+    """Runs dflash_draft_argmax; returns (block_tokens [B, 16] as numpy, workspace)."""
+    B, ld = logits.shape[0], logits.shape[2]
+    V = ld if vocab is None else vocab
+    if ws is None:
+        ws = dfl.workspace(dfl.dflash_verify_workspace_size(B, synth.BLOCK, V), DEV)
+    blk = torch.full((B, synth.BLOCK), init, dtype=torch.int32, device=DEV)
+    dfl.dflash_draft_argmax(u16(logits), None if staged is None else i32(staged), blk, ws, vocab=V)
+    torch.cuda.synchronize()
+    return blk.cpu().numpy(), ws

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     lib = ctypes.CDLL(dfl.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -49,13 +49,17 @@ def test_status_strings_and_version():
 def test_workspace_sizes():
     v = dfl.dflash_verify_workspace_size(8, 16, 151936)
     n_chunks = -(-151936 // 8192)
-    keys_end = 256 + 8 * 16 * 8 * n_chunks                      # error word, then chunk keys
-    assert v == (keys_end + 255) // 256 * 256 + 8 * 128          # then 8 arrival counters of 128 bytes
+    counters = 8192 * 128                                       # fixed counter region, 1 MiB
+    assert v == 256 + counters + 8 * 16 * 8 * n_chunks           # error word, counters, chunk keys
+    assert dfl.dflash_verify_workspace_size(8192, 16, 10) > 0
+    assert dfl.dflash_verify_workspace_size(8193, 16, 10) == 0
     assert dfl.dflash_verify_workspace_size(0, 16, 10) == 0
     assert dfl.dflash_verify_workspace_size(1, 15, 10) == 0
     dims = dfl.make_dims(8, 32, 8, 128, hidden=4096, kv_capacity=8208)
     a = dfl.dflash_block_attn_workspace_size(dims, 8192)
-    assert a > 8 * 8 * 4 and a % 256 == 0
+    assert a > 256 + counters + 8 * 8 * 4 and a % 256 == 0
+    assert dfl.dflash_block_attn_workspace_size(dfl.make_dims(1024, 32, 8, 128, kv_capacity=64), 64) > 0
+    assert dfl.dflash_block_attn_workspace_size(dfl.make_dims(1025, 32, 8, 128, kv_capacity=64), 64) == 0
     assert dfl.dflash_block_attn_workspace_size(dims, 16384) >= a
     bad = dfl.make_dims(8, 30, 8, 128, kv_capacity=8208)
     assert dfl.dflash_block_attn_workspace_size(bad, 8192) == 0
@@ -78,6 +82,7 @@ def test_block_attn_rejects_bad_arguments():
     good = dfl.make_dims(2, 8, 2, 64, kv_capacity=80)
     assert _attn(dfl.make_dims(0, 8, 2, 64, kv_capacity=80)) == -2
     assert _attn(dfl.make_dims(2, 8, 3, 64, kv_capacity=80)) == -2           # Hq % Hkv
+    assert _attn(dfl.make_dims(1025, 32, 8, 64, kv_capacity=80)) == -2       # units past the counter slots
     assert _attn(dfl.make_dims(2, 18, 2, 64, kv_capacity=80)) == -6          # group 9
     assert _attn(dfl.make_dims(2, 8, 2, 96, kv_capacity=80)) == -6           # head_dim
     assert _attn(dfl.make_dims(2, 8, 2, 64, page_size=8, kv_capacity=80)) == -6
@@ -99,7 +104,7 @@ def test_block_attn_rejects_bad_arguments():
 
 def _verify(**kw):
     a = dict(B=2, blk=16, V=1000, logits=FAKE, ld=1000, bt=FAKE, kvi=FAKE, post=FAKE, acc=FAKE, nxt=FAKE,
-             kvo=FAKE, cp=None, ps=0, npg=None, ws=FAKE, wsb=1 << 20)
+             kvo=FAKE, cp=None, ps=0, npg=None, ws=FAKE, wsb=1 << 22)
     a.update(kw)
     return dfl._lib.dflash_verify_accept(a["B"], a["blk"], a["V"], a["logits"], a["ld"], a["bt"], a["kvi"],
                                          a["post"], a["acc"], a["nxt"], a["kvo"], a["cp"], a["ps"], a["npg"],
@@ -109,6 +114,7 @@ def _verify(**kw):
 @no_device
 def test_verify_rejects_bad_arguments():
     assert _verify(B=0) == -2
+    assert _verify(B=8193) == -2
     assert _verify(blk=8) == -2
     assert _verify(V=0) == -2
     assert _verify(ld=999) == -2
@@ -119,6 +125,30 @@ def test_verify_rejects_bad_arguments():
     assert _verify(ws=ctypes.c_void_p(None)) == -4
     assert _verify(wsb=100) == -4
     assert _verify(ws=MIS) == -3
+
+
+def _draft(**kw):
+    a = dict(B=2, blk=16, V=1000, logits=FAKE, ld=1000, staged=None, bt=FAKE, ws=FAKE, wsb=1 << 22)
+    a.update(kw)
+    return dfl._lib.dflash_draft_argmax(a["B"], a["blk"], a["V"], a["logits"], a["ld"], a["staged"], a["bt"],
+                                        a["ws"], a["wsb"], None)
+
+
+@no_device
+def test_draft_argmax_rejects_bad_arguments():
+    assert _draft(B=0) == -2
+    assert _draft(B=8193) == -2               # more sequences than counter slots
+    assert _draft(blk=15) == -2
+    assert _draft(V=0) == -2
+    assert _draft(V=0x7fffffff, ld=0x7fffffff + 1) == -2
+    assert _draft(ld=999) == -2
+    assert _draft(ld=1004) == -3              # row stride not a multiple of 8
+    assert _draft(logits=MIS) == -3
+    assert _draft(logits=ctypes.c_void_p(None)) == -1
+    assert _draft(bt=ctypes.c_void_p(None)) == -1
+    assert _draft(ws=ctypes.c_void_p(None)) == -4
+    assert _draft(wsb=100) == -4               # the verify's workspace size is required
+    assert _draft(ws=MIS) == -3
 
 
 def _proj(dims, n_layers=2, **kw):

@@ -147,3 +147,25 @@ def test_attn_merge_wait_is_bounded_and_flags_a_broken_counter():
     err2 = float(np.max(np.abs(out2.cpu().numpy() - ref)))
     log(f"attn merge: second call on the same workspace, max-abs err {err2:.3e}")
     assert err2 <= TOL
+
+
+def test_attn_workspace_serves_growing_and_shrinking_batches():
+    # One buffer serves calls of 2, 6 and again 2 sequences, the first with a dozen splits
+    # per unit.  Each call's per-unit arrival counters are a prefix of one fixed region
+    # that no call writes anything else to, so a call with more units than the one before
+    # finds its counters at zero, not on top of the earlier call's split partials.
+    cfg = synth.CONFIGS["tiny"]
+    lens = [np.array([3000, 2500], np.int32), np.array([700, 900, 1200, 50, 1, 333], np.int32),
+            np.array([2048, 17], np.int32)]
+    ats = [synth.attn_inputs(cfg, ctx_len=L, seed=cfg.seed + 40 + i) for i, L in enumerate(lens)]
+    need = max(dfl.dflash_block_attn_workspace_size(attn_dims(cfg, at), int(at.ctx_len.max())) for at in ats)
+    ws = dfl.workspace(need, DEV)
+    for i, at in enumerate(ats):
+        out, ws = run_block_attn(cfg, at, ws=ws)
+        ref = orc.block_attn_ref(at.q_blk, at.k_blk, at.v_blk, at.k_cache, at.v_cache, at.ctx_len,
+                                 cfg.rope_base)
+        err = float(np.max(np.abs(out.cpu().numpy() - ref)))
+        log(f"attn workspace reuse, call {i} (B={len(at.ctx_len)}): max-abs err {err:.3e}")
+        assert err <= TOL, err
+        assert ws[:4].cpu().numpy().view(np.uint32)[0] == 0
+    assert not ws[256:256 + 128 * 12].any()          # every counter back at zero

@@ -8,7 +8,8 @@ import pytest
 
 from block_diffusion_draft_proj_amd import synth
 from oracle import dflash_oracle as orc
-from tests.gpu_util import log, run_verify
+from block_diffusion_draft_proj_amd import dflash as dfl
+from tests.gpu_util import DEV, log, run_draft, run_verify
 
 pytestmark = pytest.mark.gpu
 
@@ -138,3 +139,21 @@ def test_verify_workspace_reuse_and_aliasing(B):
     for k in KEYS:
         assert np.array_equal(r1[k], r3[k]), k
     assert ws[:4].cpu().numpy().view(np.uint32)[0] == 0
+
+
+def test_verify_workspace_serves_shrinking_and_growing_batches():
+    # One buffer sized for 12 sequences serves 12, 9, 3, 12 and 8 of them (both launch
+    # forms) with the draft argmax interleaved on it: the per-sequence arrival counters
+    # sit in a fixed region ahead of the chunk keys, so no call's keys land on another
+    # call's counters.
+    cfg = synth.CONFIGS["qwen3_8b"]
+    ws = dfl.workspace(dfl.dflash_verify_workspace_size(12, 16, cfg.vocab), DEV)
+    for i, B in enumerate([12, 9, 3, 12, 8]):
+        vi = synth.verify_inputs(cfg, batch=B, seed=50 + i)
+        log(f"verify workspace reuse, call {i}: B={B}")
+        got, ws = run_verify(vi.logits, vi.block_tokens, vi.kv_len, ws=ws)
+        _compare(got, orc.verify_accept_ref(vi.logits, vi.block_tokens, vi.kv_len))
+        d, ws = run_draft(vi.logits, vi.block_tokens[:, 0], ws=ws)
+        assert np.array_equal(d, orc.draft_block_ref(vi.logits, vi.block_tokens[:, 0]))
+    assert ws[:4].cpu().numpy().view(np.uint32)[0] == 0
+    assert not ws[256:256 + 128 * 12].any()          # every counter back at zero
