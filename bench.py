@@ -38,8 +38,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "d1e0c5f3676decc3885d3801c49532fdaeeb02c5937db54d6a9e665942137292",
-                "workload": "batched", "read": 276755249, "write": 8508045}
+ATTN_TRAFFIC = {"sha256": "b93be5970c4ddba204dd22150449e72965ab4b8937a64b73ac24d0436eaf2b22",
+                "workload": "batched", "read": 276755290, "write": 8508207}
 
 
 def sources_sha256(paths):
