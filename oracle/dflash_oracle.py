@@ -164,6 +164,35 @@ def ctx_proj_ref(x_layers: Sequence[np.ndarray], w_fc: np.ndarray, w_k: np.ndarr
 
 
 # --------------------------------------------------------------------------
+# The block's own q / k / v, the attention's first inputs (page "DFlash dual
+# implementations" §2: Q comes from the block tokens only, and the block's K/V
+# are the second source beside the context's).  Reading: one bias-free linear
+# map over the draft's block hidden states, nn.Linear layout, the weight rows
+# ordered q heads, then k heads, then v heads; exact products (float64), each
+# output rounded once to bf16; no RoPE here (the attention rotates Q and the
+# block K at their positions).
+# --------------------------------------------------------------------------
+def block_qkv_ref(h: np.ndarray, w_qkv: np.ndarray, n_q_heads: int, n_kv_heads: int,
+                  head_dim: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """q, k, v bf16 bits for M = 16 B block rows (sequence-major).
+
+    h [M, hidden] bf16 bits; w_qkv [(Hq + 2 Hkv) d, hidden] bf16 bits.
+      Y = h . w_qkv^T  (float64), rounded to bf16
+      q = Y[:, 0 : Hq d]              as [M, Hq, d]
+      k = Y[:, Hq d : (Hq + Hkv) d]   as [M, Hkv, d]
+      v = Y[:, (Hq + Hkv) d : ]       as [M, Hkv, d]
+    """
+    M = h.shape[0]
+    nq, nk = n_q_heads * head_dim, n_kv_heads * head_dim
+    assert w_qkv.shape[0] == nq + 2 * nk and w_qkv.shape[1] == h.shape[1]
+    Y = f64_to_bf16_bits(bf16_to_f64(h) @ bf16_to_f64(w_qkv).T)
+    q = Y[:, :nq].reshape(M, n_q_heads, head_dim)
+    k = Y[:, nq:nq + nk].reshape(M, n_kv_heads, head_dim)
+    v = Y[:, nq + nk:].reshape(M, n_kv_heads, head_dim)
+    return q, k, v
+
+
+# --------------------------------------------------------------------------
 # a4-a6: dual-source non-causal block attention
 # (page "DFlash dual implementations" §2: K/V = [ctx ; block tokens], Q from
 # the block tokens only, non-causal inside the block.)

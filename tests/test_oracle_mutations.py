@@ -39,6 +39,10 @@ MUTANTS = {
                         "blk[b, 1:] = argmax_first(bf16_to_f64(draft_logits[b, :BLOCK - 1]))"),
     "draft_staged_slot": ("blk[:, 0] = np.asarray(staged, dtype=np.int32)",
                           "blk[:, 0] = argmax_first(bf16_to_f64(draft_logits[:, 0]))"),
+    "qkv_k_v_swapped": ("k = Y[:, nq:nq + nk].reshape(M, n_kv_heads, head_dim)\n    v = Y[:, nq + nk:]",
+                        "k = Y[:, nq + nk:].reshape(M, n_kv_heads, head_dim)\n    v = Y[:, nq:nq + nk]"),
+    "qkv_not_rounded": ("Y = f64_to_bf16_bits(bf16_to_f64(h) @ bf16_to_f64(w_qkv).T)",
+                        "Y = (bf16_to_f64(h) @ bf16_to_f64(w_qkv).T).astype(np.float32).view(np.uint32) >> 16"),
     "rope_on_v": ("V = (Cb @ bf16_to_f64(w_v).T).reshape(M, n_kv_heads, head_dim)",
                   "V = apply_rope((Cb @ bf16_to_f64(w_v).T).reshape(M, n_kv_heads, head_dim), "
                   "np.maximum(np.asarray(row_pos), 0), base)"),

@@ -588,3 +588,44 @@ def test_draft_that_predicts_the_target_is_fully_accepted():
         draft[b, j + 1, (post_j + 1) % V] = 1.0      # a different greedy token at slot j + 1
     res = orc.verify_accept_ref(_bits(target), orc.draft_block_ref(_bits(draft), staged), kv)
     assert np.array_equal(res["accept"], [0, 3, 9, 14])
+
+
+# ----------------------------------------------------------------------------- block q/k/v
+def test_block_qkv_matches_scalar_brute_force():
+    rng = np.random.default_rng(43)
+    M, hidden, Hq, Hkv, d = 5, 12, 2, 1, 4
+    h = orc.f64_to_bf16_bits(rng.standard_normal((M, hidden)))
+    w = orc.f64_to_bf16_bits(rng.standard_normal(((Hq + 2 * Hkv) * d, hidden)) * 0.3)
+    q, k, v = orc.block_qkv_ref(h, w, Hq, Hkv, d)
+    hf, wf = orc.bf16_to_f64(h).tolist(), orc.bf16_to_f64(w).tolist()
+    for m in range(M):
+        for o in range((Hq + 2 * Hkv) * d):
+            acc = 0.0
+            for i in range(hidden):
+                acc += hf[m][i] * wf[o][i]
+            want = orc.f64_to_bf16_bits(np.array([acc]))[0]
+            if o < Hq * d:
+                got = q[m, o // d, o % d]
+            elif o < (Hq + Hkv) * d:
+                got = k[m, (o - Hq * d) // d, o % d]
+            else:
+                got = v[m, (o - (Hq + Hkv) * d) // d, o % d]
+            assert got == want, (m, o)
+
+
+def test_block_qkv_one_hot_weights_select_inputs_in_head_order():
+    # Weight row r picks input column perm[r]: q heads, then k heads, then v heads must
+    # come out as exact copies of the chosen columns, in that order.
+    rng = np.random.default_rng(44)
+    M, hidden, Hq, Hkv, d = 3, 64, 4, 2, 8
+    N = (Hq + 2 * Hkv) * d
+    perm = (np.arange(N) * 7 + 3) % hidden
+    h = orc.f64_to_bf16_bits(rng.standard_normal((M, hidden)))
+    w = np.zeros((N, hidden))
+    w[np.arange(N), perm] = 1.0
+    q, k, v = orc.block_qkv_ref(h, orc.f64_to_bf16_bits(w), Hq, Hkv, d)
+    sel = h[:, perm]
+    assert np.array_equal(q.reshape(M, -1), sel[:, :Hq * d])
+    assert np.array_equal(k.reshape(M, -1), sel[:, Hq * d:(Hq + Hkv) * d])
+    assert np.array_equal(v.reshape(M, -1), sel[:, (Hq + Hkv) * d:])
+    assert q.shape == (M, Hq, d) and k.shape == (M, Hkv, d) and v.shape == (M, Hkv, d)
