@@ -144,6 +144,12 @@ def draft_bytes(cfg, B):
     return B * 15 * cfg.vocab * 2 + B * 4 + B * 16 * 4
 
 
+def qkv_bytes(cfg, B):
+    # the fused q/k/v weight, the block hidden states, and q, k, v out
+    n_out = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim
+    return 2 * (n_out * cfg.hidden + 16 * B * cfg.hidden + 16 * B * n_out)
+
+
 def proj_bytes(cfg, M, committed):
     kvw = cfg.n_kv_heads * cfg.head_dim
     return (2 * cfg.hidden * cfg.ctx_width + 2 * 2 * kvw * cfg.hidden + 2 * M * cfg.ctx_width
@@ -261,8 +267,14 @@ def main():
     # next_token as its staged tokens.
     N_SPLIT = 50
     tev = HipTimingEvents(2 * args.steps, torch.cuda.current_stream().cuda_stream)
-    sev = HipTimingEvents(5 * N_SPLIT, torch.cuda.current_stream().cuda_stream)
+    sev = HipTimingEvents(6 * N_SPLIT, torch.cuda.current_stream().cuda_stream)
     dblk = z(B, 16)
+    # ... and the block's own q / k / v (dflash_block_qkv), the attention's inputs,
+    # into separate buffers so the attention's inputs stay as drawn.
+    qi = synth.block_qkv_inputs(cfg)
+    h_blk, w_qkv = u16(qi.h), u16(qi.w_qkv)
+    q2, k2, v2 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_q = dfl.workspace(dfl.dflash_block_qkv_workspace_size(dims), dev)
 
     def step(i, ev=None, base=0, split=False):
         if ev is not None:
@@ -279,6 +291,8 @@ def main():
             ev.record(base + 3)
             dfl.dflash_draft_argmax(lgs[(i + 1) % R], nxt, dblk, ws_v)
             ev.record(base + 4)
+            dfl.dflash_block_qkv(dims, h_blk, w_qkv, q2, k2, v2, ws_q)
+            ev.record(base + 5)
 
     for s in range(args.warmup):
         step(s % R)
@@ -289,15 +303,17 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for s in range(N_SPLIT):
-        step(s % R, sev, 5 * s, split=True)
+        step(s % R, sev, 6 * s, split=True)
     torch.cuda.synchronize()
 
     ms_step = (t1 - t0) / args.steps * 1e3
     t_attn = float(np.mean([tev.elapsed_ms(2 * s, 2 * s + 1) for s in range(args.steps)])) * 1e-3
-    t_ver = float(np.mean([sev.elapsed_ms(5 * s + 1, 5 * s + 2) for s in range(N_SPLIT)])) * 1e-3
-    t_proj = float(np.mean([sev.elapsed_ms(5 * s + 2, 5 * s + 3) for s in range(N_SPLIT)])) * 1e-3
-    t_draft = float(np.mean([sev.elapsed_ms(5 * s + 3, 5 * s + 4) for s in range(N_SPLIT)])) * 1e-3
+    t_ver = float(np.mean([sev.elapsed_ms(6 * s + 1, 6 * s + 2) for s in range(N_SPLIT)])) * 1e-3
+    t_proj = float(np.mean([sev.elapsed_ms(6 * s + 2, 6 * s + 3) for s in range(N_SPLIT)])) * 1e-3
+    t_draft = float(np.mean([sev.elapsed_ms(6 * s + 3, 6 * s + 4) for s in range(N_SPLIT)])) * 1e-3
+    t_qkv = float(np.mean([sev.elapsed_ms(6 * s + 4, 6 * s + 5) for s in range(N_SPLIT)])) * 1e-3
     d_b = draft_bytes(cfg, B)
+    q_b = qkv_bytes(cfg, B)
     tev.close()
     sev.close()
     ok = bool(np.array_equal(acc.cpu().numpy(), vi.planted_accept))
@@ -324,8 +340,12 @@ def main():
         "draft_argmax": {"us": round(t_draft * 1e6, 2), "GB_s": round(d_b / t_draft / 1e9, 1),
                          "pct_hbm_peak": round(100 * d_b / t_draft / 1e9 / HBM_PEAK_GBS, 2), "bytes": d_b,
                          "scope": "draft-side greedy tokens at the 15 mask slots; not in the timed step"},
-        "timing": "block_attn: HIP events around every timed call; verify, ctx_proj and draft_argmax: "
-                  "events in a %d-step pass after the timed region" % N_SPLIT,
+        "block_qkv": {"us": round(t_qkv * 1e6, 2), "GB_s": round(q_b / t_qkv / 1e9, 1),
+                      "pct_hbm_peak": round(100 * q_b / t_qkv / 1e9 / HBM_PEAK_GBS, 2), "bytes": q_b,
+                      "scope": "the block's own q/k/v (three kernels: pack, split-K GEMM, reduce); "
+                               "not in the timed step"},
+        "timing": "block_attn: HIP events around every timed call; verify, ctx_proj, draft_argmax and "
+                  "block_qkv: events in a %d-step pass after the timed region" % N_SPLIT,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name),
                      "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": a_b},

@@ -163,6 +163,81 @@ int dflash_draft_argmax(int32_t batch, int32_t block, int32_t vocab, const void*
   return launch_status(launch_draft_argmax(p, batch, stream));
 }
 
+// ------------------------------------------------------------------ block q/k/v
+static int check_qkv_dims(const dflash_dims* dims) {
+  const int st = check_cache_dims(dims);
+  if (st != DFLASH_OK) return st;
+  if (dims->n_q_heads < dims->n_kv_heads || dims->n_q_heads % dims->n_kv_heads) return DFLASH_ERR_SHAPE;
+  if (dims->n_q_heads > 1024) return DFLASH_ERR_SHAPE;
+  if (dims->hidden < 64 || dims->hidden % 64 || dims->hidden > (1 << 16)) return DFLASH_ERR_SHAPE;
+  if ((int64_t)dims->batch * DFLASH_BLOCK > (1 << 22)) return DFLASH_ERR_SHAPE;
+  return DFLASH_OK;
+}
+
+size_t dflash_block_qkv_workspace_size(const dflash_dims* dims) {
+  if (check_qkv_dims(dims) != DFLASH_OK) return 0;
+  const int n_out = (dims->n_q_heads + 2 * dims->n_kv_heads) * dims->head_dim;
+  return plan_block_qkv(dims->batch * DFLASH_BLOCK, dims->hidden, n_out, kPlanCUs).ws_bytes;
+}
+
+int dflash_block_qkv(const dflash_dims* dims, const void* h, int64_t ld_h, const void* w_qkv, void* q_blk,
+                     void* k_blk, void* v_blk, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_qkv_dims(dims);
+  if (st != DFLASH_OK) return st;
+  if (!h || !w_qkv || !q_blk || !k_blk || !v_blk) return DFLASH_ERR_NULL;
+  if (ld_h < dims->hidden) return DFLASH_ERR_SHAPE;
+  if (ld_h & 7) return DFLASH_ERR_ALIGN;
+  const void* ptrs[] = {h, w_qkv, q_blk, k_blk, v_blk};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DFLASH_ERR_ALIGN;
+  const int M = dims->batch * DFLASH_BLOCK;
+  const int nq = dims->n_q_heads * dims->head_dim, nk = dims->n_kv_heads * dims->head_dim;
+  const int n_out = nq + 2 * nk;
+  const QkvPlan pl = plan_block_qkv(M, dims->hidden, n_out, kPlanCUs);
+  if (!workspace || workspace_bytes < pl.ws_bytes) return DFLASH_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DFLASH_ERR_ALIGN;
+  st = check_device();
+  if (st != DFLASH_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  GemmParams g{};
+  g.a_seg[0] = static_cast<const uint16_t*>(h);
+  g.lda = ld_h;
+  g.seg_k = dims->hidden;
+  if (pl.small) {
+    PackParams pk{};
+    pk.a_seg[0] = g.a_seg[0];
+    pk.lda = ld_h;
+    pk.seg_k = dims->hidden;
+    pk.M = M;
+    pk.K = dims->hidden;
+    pk.mp = pl.mp;
+    pk.xp = reinterpret_cast<uint16_t*>(ws + pl.off_xp);
+    if (launch_pack_rows(pk, stream) != hipSuccess) return DFLASH_ERR_LAUNCH;
+    g.xp = pk.xp;
+    g.mp = pl.mp;
+  }
+  g.b0 = static_cast<const uint16_t*>(w_qkv);
+  g.b1 = g.b0;
+  g.n_b0 = n_out;
+  g.M = M;
+  g.N = n_out;
+  g.K = dims->hidden;
+  g.k_per_split = pl.kps;
+  g.out = reinterpret_cast<float*>(ws + pl.off_part);
+  if (launch_gemm_nt(g, pl.splits, pl.small, stream) != hipSuccess) return DFLASH_ERR_LAUNCH;
+  QkvReduceParams r{};
+  r.part = g.out;
+  r.splits = pl.splits;
+  r.M = M;
+  r.N = n_out;
+  r.nq = nq;
+  r.nk = nk;
+  r.q = static_cast<uint16_t*>(q_blk);
+  r.k = static_cast<uint16_t*>(k_blk);
+  r.v = static_cast<uint16_t*>(v_blk);
+  return launch_status(launch_qkv_reduce(r, stream));
+}
+
 // ------------------------------------------------------------------ block attention
 size_t dflash_block_attn_workspace_size(const dflash_dims* dims, int32_t max_ctx_len) {
   if (check_cache_dims(dims) != DFLASH_OK || max_ctx_len < 0) return 0;

@@ -330,6 +330,24 @@ __global__ __launch_bounds__(256) void fc_reduce_kernel(FcReduceParams p) {
   }
 }
 
+// Block q / k / v = bf16(sum over splits), 4 columns per thread.  Columns [0, nq) go
+// to q, [nq, nq + nk) to k, the rest to v, each token-major ([M][heads * d]).  nq and
+// nk are multiples of 64, so a 4-column group never straddles two outputs.
+__global__ __launch_bounds__(256) void qkv_reduce_kernel(QkvReduceParams p) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
+  const int64_t total = (int64_t)p.M * p.N / 4;
+  if (i >= total) return;
+  const f32x4 s = sum_splits(p.part + 4 * i, (int64_t)p.M * p.N, p.splits);
+  const u32x2 v = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+  const int64_t m = 4 * i / p.N;
+  const int n = (int)(4 * i - m * p.N);
+  uint16_t* dst;
+  if (n < p.nq) dst = p.q + m * p.nq + n;
+  else if (n < p.nq + p.nk) dst = p.k + m * p.nk + (n - p.nq);
+  else dst = p.v + m * p.nk + (n - p.nq - p.nk);
+  *reinterpret_cast<u32x2*>(dst) = v;
+}
+
 // K/V rows: sum splits, rotate K (pairs j, j+d/2) at the row's position, round to
 // bf16 and write into the cache.  Thread = (row, kv head, 4 consecutive j < d/2).
 __global__ __launch_bounds__(256) void kv_epilogue_kernel(KvEpilogueParams p) {
@@ -464,6 +482,28 @@ ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_
   return pl;
 }
 
+// The block q/k/v product is shaped like the fc product (many weight rows, few
+// activation rows), so it takes the same split rule and tile choice.
+QkvPlan plan_block_qkv(int n_rows, int hidden, int n_out, int num_cu) {
+  QkvPlan pl{};
+  const int cus = num_cu > 0 ? num_cu : 256;
+  const int mtiles = (n_rows + GBM - 1) / GBM;
+  pl.small = n_rows <= kSkinnyMaxRows;
+  const int sp = pl.small ? skinny_splits(n_out, n_rows, hidden, cus)
+                          : split_count(mtiles * ((n_out + GBN - 1) / GBN), n_rows, hidden, 2 * cus);
+  pl.kps = k_per_split(hidden, sp);
+  pl.splits = (hidden + pl.kps - 1) / pl.kps;
+  pl.mp = n_rows <= 128 ? 32 * ((n_rows + 31) / 32) : kSkinnyChunk * ((n_rows + kSkinnyChunk - 1) / kSkinnyChunk);
+  auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t off = 256;  // word 0: device error mask
+  pl.off_part = off;
+  off = align(off + sizeof(float) * (size_t)pl.splits * n_rows * n_out);
+  pl.off_xp = off;
+  if (pl.small) off = align(off + 2 * (size_t)hidden * pl.mp);
+  pl.ws_bytes = off;
+  return pl;
+}
+
 template <int MT>
 void launch_skinny(const GemmParams& p, int splits, hipStream_t stream) {
   dim3 grid(((p.N + SK_ROWS - 1) / SK_ROWS) * splits, 1, 1);
@@ -503,6 +543,12 @@ hipError_t launch_pack_rows(const PackParams& p, hipStream_t stream) {
 hipError_t launch_fc_reduce(const FcReduceParams& p, hipStream_t stream) {
   const int64_t n = (int64_t)p.M * p.N / 4;
   hipLaunchKernelGGL(fc_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_reduce(const QkvReduceParams& p, hipStream_t stream) {
+  const int64_t n4 = (int64_t)p.M * p.N / 4;
+  hipLaunchKernelGGL(qkv_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

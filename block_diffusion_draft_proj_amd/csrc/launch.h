@@ -131,6 +131,22 @@ struct FcReduceParams {
 };
 hipError_t launch_fc_reduce(const FcReduceParams& p, hipStream_t stream);
 
+// Block q/k/v projection: the projection's split-K GEMM over [W_q; W_k; W_v], then a
+// reduce that rounds to bf16 and splits the columns into the three outputs.
+struct QkvPlan {
+  int splits, kps;   // K split count and K elements per split (multiple of 64)
+  bool small;        // skinny weight-streaming GEMM (rows <= kSkinnyMaxRows)
+  int mp;            // skinny path: packed activation rows
+  size_t off_part, off_xp, ws_bytes;
+};
+QkvPlan plan_block_qkv(int n_rows, int hidden, int n_out, int num_cu);
+struct QkvReduceParams {
+  const float* part;   // [splits][M][N], N = nq + 2 nk
+  int splits, M, N, nq, nk;
+  uint16_t *q, *k, *v; // [M][nq], [M][nk], [M][nk] bf16
+};
+hipError_t launch_qkv_reduce(const QkvReduceParams& p, hipStream_t stream);
+
 struct KvEpilogueParams {
   const float* part;   // [splits][M][2*Hkv*d]
   int splits, M;

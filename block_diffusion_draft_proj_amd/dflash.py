@@ -55,6 +55,8 @@ def _load() -> ctypes.CDLL:
                                        _vp, _vp, _c_sz, _vp]),
         "dflash_verify_workspace_size": (_c_sz, [_c_int, _c_int, _c_int]),
         "dflash_draft_argmax": (_c_int, [_c_int, _c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _c_sz, _vp]),
+        "dflash_block_qkv_workspace_size": (_c_sz, [P]),
+        "dflash_block_qkv": (_c_int, [P, _vp, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
         "dflash_verify_accept": (_c_int, [_c_int, _c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _vp, _vp,
                                           _vp, _vp, _c_int, _vp, _vp, _c_sz, _vp]),
     }
@@ -72,6 +74,7 @@ EXPORTS = (
     "dflash_status_str", "dflash_version", "dflash_rope_tables", "dflash_ctx_proj_workspace_size",
     "dflash_ctx_proj", "dflash_block_attn_workspace_size", "dflash_block_attn",
     "dflash_verify_workspace_size", "dflash_verify_accept", "dflash_draft_argmax",
+    "dflash_block_qkv_workspace_size", "dflash_block_qkv",
 )
 
 
@@ -190,6 +193,22 @@ def dflash_verify_accept(logits: torch.Tensor, block_tokens: torch.Tensor, kv_le
         _dev(next_token, "next_token", (torch.int32,)), _dev(kv_len_out, "kv_len_out", (torch.int32,)),
         _dev(commit_pos, "commit_pos", (torch.int32,)), page_size, _dev(n_pages, "n_pages", (torch.int32,)),
         _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
+
+
+def dflash_block_qkv_workspace_size(dims: dflash_dims) -> int:
+    return int(_lib.dflash_block_qkv_workspace_size(ctypes.byref(dims)))
+
+
+def dflash_block_qkv(dims: dflash_dims, h: torch.Tensor, w_qkv: torch.Tensor, q_blk: torch.Tensor,
+                     k_blk: torch.Tensor, v_blk: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """q/k/v of the block: h [16B, ld_h] bf16 (row stride ld_h), w_qkv [(Hq+2Hkv)d, hidden]."""
+    if h.dim() != 2 or h.stride(1) != 1:
+        raise ValueError("h must be a [rows, ld_h] tensor with unit inner stride")
+    _check("dflash_block_qkv", _lib.dflash_block_qkv(
+        ctypes.byref(dims), _dev(h, "h", _BF16, contiguous=False), int(h.stride(0)),
+        _dev(w_qkv, "w_qkv", _BF16), _dev(q_blk, "q_blk", _BF16), _dev(k_blk, "k_blk", _BF16),
+        _dev(v_blk, "v_blk", _BF16), _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(),
+        _stream(stream)))
 
 
 def dflash_draft_argmax(logits: torch.Tensor, staged: Optional[torch.Tensor], block_tokens: torch.Tensor,

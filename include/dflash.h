@@ -189,6 +189,28 @@ int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab,
                          int32_t page_size, int32_t* n_pages,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- the block's own q / k / v (inputs of dflash_block_attn) ---------------
+ * Q comes from the block tokens only, and the block's K/V join the context's
+ * as the second source ("DFlash dual implementations", §2).  One bias-free
+ * linear map over the draft's block hidden states, M = 16 * batch rows:
+ *   Y = h . w_qkv^T  (fp32 accumulation of bf16 products), rounded to bf16
+ *   q_blk = Y[:, 0 : Hq*d], k_blk = Y[:, Hq*d : (Hq+Hkv)*d], v_blk = the rest
+ * No RoPE here: dflash_block_attn rotates Q and the block K.
+ *
+ *   dims       as for dflash_block_attn; uses batch, n_q_heads, n_kv_heads,
+ *              head_dim and hidden (a multiple of 64, at most 65536)
+ *   h          [16*batch][ld_h] bf16, sequence-major; ld_h >= hidden, ld_h % 8 == 0
+ *   w_qkv      [(Hq + 2*Hkv)*d][hidden] bf16, nn.Linear layout: the Hq query
+ *              heads' rows, then the Hkv key heads', then the Hkv value heads'
+ *   q_blk      [batch][16][Hq][d] bf16 output; k_blk, v_blk [batch][16][Hkv][d]
+ * The workspace holds split-K partial sums (and packed activations for up to
+ * 512 rows); it keeps no state between calls.  Results agree with the exact
+ * product rounded to bf16 to within one bf16 ulp (fp32 summation order). */
+size_t dflash_block_qkv_workspace_size(const dflash_dims* dims);
+int dflash_block_qkv(const dflash_dims* dims, const void* h, int64_t ld_h, const void* w_qkv,
+                     void* q_blk, void* k_blk, void* v_blk,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---- draft-side greedy tokens (the step before the verify) ----------------
  * One draft forward over the block [staged, mask x 15] yields the 15
  * candidate tail tokens ("dflash-mlx: lossless speculative decoding",

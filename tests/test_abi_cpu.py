@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     lib = ctypes.CDLL(dfl.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -182,3 +182,27 @@ def test_ctx_proj_rejects_bad_arguments():
     assert _proj(h) == -2                               # hidden % 64
     paged = dfl.make_dims(1, 4, 2, 64, hidden=256, page_size=16, kv_capacity=5, num_pages=4)
     assert _proj(paged) == -1                           # page table missing
+
+
+def _qkv(dims, **kw):
+    a = dict(h=FAKE, ld=256, w=FAKE, q=FAKE, k=FAKE, v=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return dfl._lib.dflash_block_qkv(ctypes.byref(dims), a["h"], a["ld"], a["w"], a["q"], a["k"], a["v"],
+                                     a["ws"], a["wsb"], None)
+
+
+@no_device
+def test_block_qkv_rejects_bad_arguments():
+    good = dfl.make_dims(2, 8, 2, 64, hidden=256, kv_capacity=80)
+    assert dfl.dflash_block_qkv_workspace_size(good) > 256
+    assert dfl.dflash_block_qkv_workspace_size(dfl.make_dims(2, 8, 2, 64, hidden=200, kv_capacity=80)) == 0
+    assert _qkv(dfl.make_dims(2, 8, 2, 64, hidden=200, kv_capacity=80), ld=200) == -2    # hidden % 64
+    assert _qkv(dfl.make_dims(2, 8, 3, 64, hidden=256, kv_capacity=80)) == -2            # Hq % Hkv
+    assert _qkv(dfl.make_dims(2, 8, 2, 96, hidden=256, kv_capacity=80)) == -6            # head_dim
+    assert _qkv(good, ld=128) == -2
+    assert _qkv(good, ld=260) == -3
+    assert _qkv(good, h=ctypes.c_void_p(None)) == -1
+    assert _qkv(good, v=ctypes.c_void_p(None)) == -1
+    assert _qkv(good, w=MIS) == -3
+    assert _qkv(good, ws=ctypes.c_void_p(None)) == -4
+    assert _qkv(good, wsb=300) == -4
