@@ -38,8 +38,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "b93be5970c4ddba204dd22150449e72965ab4b8937a64b73ac24d0436eaf2b22",
-                "workload": "batched", "read": 276755290, "write": 8508207}
+ATTN_TRAFFIC = {"sha256": "070f0b20b2368bba8983deb7afb088b48a986d9a21a8a2100b0a426a95919bb0",
+                "workload": "batched", "read": 276755286, "write": 8508354}
 
 
 def sources_sha256(paths):
