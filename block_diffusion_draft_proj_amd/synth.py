@@ -259,11 +259,12 @@ class BlockQkvInputs:
     w_qkv: np.ndarray           # [(Hq + 2 Hkv) d, hidden] bf16 bits: q heads, k heads, v heads
 
 
-def block_qkv_inputs(cfg: Config, batch: Optional[int] = None, seed: Optional[int] = None) -> BlockQkvInputs:
-    """Block hidden states N(0, 1) and a fused q/k/v weight N(0, 0.02^2), bf16."""
+def block_qkv_inputs(cfg: Config, batch: Optional[int] = None, seed: Optional[int] = None,
+                     w_std: float = 0.02) -> BlockQkvInputs:
+    """Block hidden states N(0, 1) and a fused q/k/v weight N(0, w_std^2), bf16."""
     rngs = streams(cfg.seed if seed is None else seed)
     B = cfg.batch if batch is None else batch
     n_out = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim
     h = normal_bf16(rngs["x_blk"], (B * BLOCK, cfg.hidden), 1.0)
-    w = normal_bf16(rngs["w_q"], (n_out, cfg.hidden), 0.02)
+    w = normal_bf16(rngs["w_q"], (n_out, cfg.hidden), w_std)
     return BlockQkvInputs(cfg, h, w)

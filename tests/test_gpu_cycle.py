@@ -1,0 +1,146 @@
+"""Two decode cycles on the device, chained through the C ABI with no host round
+trip, against the oracle's own chain of the same steps:
+
+  block q/k/v -> block attention -> draft tokens -> verify -> context projection
+  of the committed rows (at the verify's commit positions) -> the next cycle's
+  q/k/v and attention at the verify's new lengths.
+
+The draft's logits equal the target's one slot later except at one slot per
+sequence, so the accept lengths differ.  Token results are compared bit for
+bit. The committed cache rows use the projection's tolerance (one bf16 ulp +
+6e-3 rms). Cache rows that nothing committed must be untouched.
+
+The attention's tolerance here adds a term for its inputs. The device's q/k/v
+may differ from the oracle's by one bf16 ulp, in about 1 % of the elements
+(the projection's own bound). A one-ulp change of a block V entry passes
+through with the weight of its key, which can be close to 1. So the bound is
+the attention's 2e-2 for identical inputs, plus twice the largest change that
+moving 1 % of the q/k/v elements by one ulp (random elements and directions,
+three draws) causes in the oracle.  That term comes from the oracle alone."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_draft_proj_amd import dflash as dfl
+from block_diffusion_draft_proj_amd import synth
+from oracle import dflash_oracle as orc
+from tests.gpu_util import DEV, host_u16, i32, log, rope_tables, u16
+
+pytestmark = pytest.mark.gpu
+
+
+def ulp_bf16(x):
+    a = np.abs(np.asarray(x, np.float64))
+    return 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 7)
+
+
+def one_ulp_allowance(qkv, k_cache, v_cache, ctx_len, base, seed, frac=0.01, draws=3):
+    """Twice the largest change of the oracle attention over `draws` random draws in
+    which each q/k/v element moves one ulp with probability `frac` (the share of
+    elements the projection's own test lets differ)."""
+    rng = np.random.default_rng(seed)
+    a = orc.block_attn_ref(*qkv, k_cache, v_cache, ctx_len, base)
+    worst = 0.0
+    for _ in range(draws):
+        moved = []
+        for x in qkv:
+            f = orc.bf16_to_f64(x)
+            step = rng.choice([-1.0, 1.0], f.shape) * (rng.random(f.shape) < frac)
+            moved.append(orc.f64_to_bf16_bits(f + step * ulp_bf16(f)))
+        b = orc.block_attn_ref(*moved, k_cache, v_cache, ctx_len, base)
+        worst = max(worst, float(np.max(np.abs(a - b))))
+    return 2.0 * worst
+
+
+@pytest.mark.parametrize("name,lens", [("tiny", [40, 77, 130]), ("qwen3_8b", [300, 17, 1000, 512])])
+def test_two_cycles_on_device(name, lens):
+    cfg = synth.CONFIGS[name]
+    L0 = np.array(lens, np.int32)
+    B, Hq, Hkv, d = len(L0), cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    at = synth.attn_inputs(cfg, ctx_len=L0, seed=cfg.seed + 70)
+    dims = dfl.make_dims(B, Hq, Hkv, d, hidden=cfg.hidden, kv_capacity=at.capacity)
+    cos, sin = rope_tables(d, at.capacity + 32, cfg.rope_base)
+    # q/k/v weight std 0.005 (q/k/v std ~0.32 at hidden 4096): the attention stays soft, so
+    # one-ulp input differences move it little and its bound keeps its teeth.  Peaked
+    # attention is the subject of the attention's own tests, on identical inputs.
+    qis = [synth.block_qkv_inputs(cfg, batch=B, seed=cfg.seed + 71 + c, w_std=0.005) for c in range(2)]
+    target = synth.verify_inputs(cfg, batch=B, spike=False, seed=cfg.seed + 73).logits
+    draft = synth.verify_inputs(cfg, batch=B, spike=False, seed=cfg.seed + 74).logits
+    wrong = [(5 * b + 2) % 16 for b in range(B)]     # first wrong draft slot (15: none)
+    draft_ok = draft.copy()
+    draft_ok[:, 1:] = target[:, :15]
+    for b, j in enumerate(wrong):
+        if j < 15:
+            draft_ok[b, j + 1] = draft[b, j + 1]
+    staged = (np.arange(B) * 101 + 7).astype(np.int32) % cfg.vocab
+    pj = synth.ctx_proj_inputs(cfg, 16 * B, seed=cfg.seed + 75)
+    row_seq = np.repeat(np.arange(B), 16).astype(np.int32)
+
+    # ---- device chain
+    kc, vc = u16(at.k_cache), u16(at.v_cache)
+    kv = i32(L0)
+    ws_q = dfl.workspace(dfl.dflash_block_qkv_workspace_size(dims), DEV)
+    ws_a = dfl.workspace(max(dfl.dflash_block_attn_workspace_size(dims, int(L0.max()) + 16 * c)
+                             for c in range(2)), DEV)
+    ws_v = dfl.workspace(dfl.dflash_verify_workspace_size(B, 16, cfg.vocab), DEV)
+    ws_p = dfl.workspace(dfl.dflash_ctx_proj_workspace_size(dims, 16 * B, cfg.n_target_layers,
+                                                            cfg.target_hidden), DEV)
+    z = lambda *s: torch.full(s, -7, dtype=torch.int32, device=DEV)
+    blk, post, acc, nxt, cp = z(B, 16), z(B, 16), z(B), z(B), z(B, 16)
+    outs = []
+    for c in range(2):
+        q = torch.empty(B, 16, Hq, d, dtype=torch.int16, device=DEV)
+        k = torch.empty(B, 16, Hkv, d, dtype=torch.int16, device=DEV)
+        v = torch.empty_like(k)
+        dfl.dflash_block_qkv(dims, u16(qis[c].h), u16(qis[c].w_qkv), q, k, v, ws_q)
+        out = torch.empty(B, 16, Hq, d, dtype=torch.float32, device=DEV)
+        max_ctx = int(L0.max()) + (16 if c else 0)
+        dfl.dflash_block_attn(dims, q, k, v, kc, vc, None, kv, max_ctx, cos, sin, out, ws_a)
+        outs.append(out)
+        if c == 0:
+            dfl.dflash_draft_argmax(u16(draft_ok), i32(staged), blk, ws_v)
+            dfl.dflash_verify_accept(u16(target), blk, kv, post, acc, nxt, kv, cp, 0, None, ws_v)
+            dfl.dflash_ctx_proj(dims, [u16(x) for x in pj.x_layers], i32(row_seq), cp.view(-1), u16(pj.w_fc),
+                                u16(pj.w_k), u16(pj.w_v), cos, sin, None, kc, vc, None, ws_p)
+    torch.cuda.synchronize()
+
+    # ---- oracle chain
+    def qkv_ref(qi):
+        return [x.reshape(B, 16, *x.shape[1:]) for x in orc.block_qkv_ref(qi.h, qi.w_qkv, Hq, Hkv, d)]
+
+    out_ref = [orc.block_attn_ref(*qkv_ref(qis[0]), at.k_cache, at.v_cache, L0, cfg.rope_base)]
+    slack = [one_ulp_allowance(qkv_ref(qis[0]), at.k_cache, at.v_cache, L0, cfg.rope_base, 1)]
+    blk_ref = orc.draft_block_ref(draft_ok, staged)
+    vref = orc.verify_accept_ref(target, blk_ref, L0)
+    log(f"cycle {name}: accept {vref['accept'].tolist()}")
+    pos = vref["commit_pos"].reshape(-1)
+    pr = orc.ctx_proj_ref(pj.x_layers, pj.w_fc, pj.w_k, pj.w_v, pos, Hkv, d, cfg.rope_base)
+    kc_ref, vc_ref = at.k_cache.copy(), at.v_cache.copy()
+    for r in np.nonzero(pos >= 0)[0]:
+        kc_ref[row_seq[r], :, pos[r]] = orc.f64_to_bf16_bits(pr["Kb"][r])
+        vc_ref[row_seq[r], :, pos[r]] = orc.f64_to_bf16_bits(pr["Vb"][r])
+    out_ref.append(orc.block_attn_ref(*qkv_ref(qis[1]), kc_ref, vc_ref, vref["kv_len"], cfg.rope_base))
+    slack.append(one_ulp_allowance(qkv_ref(qis[1]), kc_ref, vc_ref, vref["kv_len"], cfg.rope_base, 2))
+
+    # ---- compare
+    assert np.array_equal(blk.cpu().numpy(), blk_ref)
+    assert np.array_equal(acc.cpu().numpy(), vref["accept"])
+    assert np.array_equal(acc.cpu().numpy(), [min(j, 15) for j in wrong])
+    assert np.array_equal(nxt.cpu().numpy(), vref["next"])
+    assert np.array_equal(kv.cpu().numpy(), vref["kv_len"])
+    kc_g, vc_g = host_u16(kc), host_u16(vc)
+    committed = np.zeros(kc_g.shape[::2][:1] + (kc_g.shape[2],), bool)   # [B, cap]
+    for r in np.nonzero(pos >= 0)[0]:
+        committed[row_seq[r], pos[r]] = True
+    for g, want, orig in ((kc_g, kc_ref, at.k_cache), (vc_g, vc_ref, at.v_cache)):
+        gm, wm = orc.bf16_to_f64(g), orc.bf16_to_f64(want)
+        rms = float(np.sqrt(np.mean(wm.transpose(0, 2, 1, 3)[committed] ** 2)))
+        diff = np.abs(gm - wm).transpose(0, 2, 1, 3)[committed]
+        assert np.all(diff <= ulp_bf16(wm.transpose(0, 2, 1, 3)[committed]) + 6e-3 * rms)
+        assert np.array_equal(g.transpose(0, 2, 1, 3)[~committed], orig.transpose(0, 2, 1, 3)[~committed])
+    for c in range(2):
+        err = float(np.max(np.abs(outs[c].cpu().numpy() - out_ref[c])))
+        log(f"  cycle {c} attention max-abs err {err:.3e} (allowance for one-ulp inputs {slack[c]:.3e})")
+        assert err <= 2e-2 + slack[c], (c, err, slack[c])
+    for ws in (ws_q, ws_a, ws_v, ws_p):
+        assert ws[:4].cpu().numpy().view(np.uint32)[0] == 0
