@@ -7,7 +7,9 @@ One step = one pass of the whole hot path over one batch, in cycle order:
                           next staged token, commit positions, KV-length crop
   3. dflash_ctx_proj     projection of the committed rows' target hidden states into
                           the context cache (fc + K/V + RoPE + scatter)
-on seeded synthetic inputs of the batched-serving workload (B=8, L=8192, 32q/8kv,
+A pass after the timed steps also times the rest of a cycle that runs on the device
+(dflash_draft_argmax and dflash_block_qkv), reported beside the step, not in it.
+Everything runs on seeded synthetic inputs of the batched-serving workload (B=8, L=8192, 32q/8kv,
 d=128, 5x4096 target features, V=151936).  Inputs are resident in HBM and rotated
 over several copies so the bytes touched between two uses of one copy exceed 2 GiB
 (4x the 256 MB Infinity Cache): the numbers are cold-cache numbers.

@@ -14,7 +14,10 @@
  *   - greedy verify: target argmax at the 16 block positions, accepted prefix
  *     length sum(cumprod(draft == posterior)), next staged token, commit of
  *     1 + accept tokens and crop of the KV length ("dflash-mlx", "single-forward
- *     verify" steps 6-9 and guarantees 2-3; "DFlash dual implementations", §3).
+ *     verify" steps 6-9 and guarantees 2-3; "DFlash dual implementations", §3);
+ *   - around them, the rest of a cycle on the device: the block's own q / k / v
+ *     (the attention's inputs, same §2) and the draft-side greedy tokens at the
+ *     15 mask slots ("dflash-mlx", "single-forward verify" steps 3-4).
  *
  * Conventions shared by every entry point:
  *   - All tensor arguments are DEVICE pointers owned by the caller unless a
