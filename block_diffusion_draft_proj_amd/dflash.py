@@ -204,6 +204,14 @@ def dflash_block_qkv(dims: dflash_dims, h: torch.Tensor, w_qkv: torch.Tensor, q_
     """q/k/v of the block: h [16B, ld_h] bf16 (row stride ld_h), w_qkv [(Hq+2Hkv)d, hidden]."""
     if h.dim() != 2 or h.stride(1) != 1:
         raise ValueError("h must be a [rows, ld_h] tensor with unit inner stride")
+    B, Hq, Hkv, d = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    if h.shape[0] != BLOCK * B or h.shape[1] < dims.hidden:
+        raise ValueError(f"h must hold {BLOCK * B} rows of at least {dims.hidden} features")
+    if tuple(w_qkv.shape) != ((Hq + 2 * Hkv) * d, dims.hidden):
+        raise ValueError(f"w_qkv must be [{(Hq + 2 * Hkv) * d}, {dims.hidden}]")
+    for name, t, heads in (("q_blk", q_blk, Hq), ("k_blk", k_blk, Hkv), ("v_blk", v_blk, Hkv)):
+        if t.numel() != B * BLOCK * heads * d:
+            raise ValueError(f"{name} must hold [{B}, {BLOCK}, {heads}, {d}] elements")
     _check("dflash_block_qkv", _lib.dflash_block_qkv(
         ctypes.byref(dims), _dev(h, "h", _BF16, contiguous=False), int(h.stride(0)),
         _dev(w_qkv, "w_qkv", _BF16), _dev(q_blk, "q_blk", _BF16), _dev(k_blk, "k_blk", _BF16),
@@ -219,6 +227,8 @@ def dflash_draft_argmax(logits: torch.Tensor, staged: Optional[torch.Tensor], bl
             or logits.stride(0) != logits.shape[1] * logits.shape[2]:
         raise ValueError("logits must be a contiguous [B, 16, ld] tensor")
     B, blk, ld = (int(s) for s in logits.shape)
+    if block_tokens.numel() != B * blk or (staged is not None and staged.numel() < B):
+        raise ValueError(f"block_tokens must be [{B}, {blk}] and staged hold {B} tokens")
     _check("dflash_draft_argmax", _lib.dflash_draft_argmax(
         B, blk, ld if vocab is None else vocab, _dev(logits, "logits", _BF16), ld,
         _dev(staged, "staged", (torch.int32,)), _dev(block_tokens, "block_tokens", (torch.int32,)),
