@@ -1,5 +1,5 @@
 """Two decode cycles on the device, chained through the C ABI with no host round
-trip, against the oracle's own chain of the same steps:
+trip, against the oracle's own chain of the same steps (dense and paged caches):
 
   block q/k/v -> block attention -> draft tokens -> verify -> context projection
   of the committed rows (at the verify's commit positions) -> the next cycle's
@@ -34,12 +34,12 @@ def ulp_bf16(x):
     return 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 7)
 
 
-def one_ulp_allowance(qkv, k_cache, v_cache, ctx_len, base, seed, frac=0.01, draws=3):
+def one_ulp_allowance(qkv, k_cache, v_cache, ctx_len, base, seed, table=None, frac=0.01, draws=3):
     """Twice the largest change of the oracle attention over `draws` random draws in
     which each q/k/v element moves one ulp with probability `frac` (the share of
     elements the projection's own test lets differ)."""
     rng = np.random.default_rng(seed)
-    a = orc.block_attn_ref(*qkv, k_cache, v_cache, ctx_len, base)
+    a = orc.block_attn_ref(*qkv, k_cache, v_cache, ctx_len, base, page_table=table)
     worst = 0.0
     for _ in range(draws):
         moved = []
@@ -47,19 +47,27 @@ def one_ulp_allowance(qkv, k_cache, v_cache, ctx_len, base, seed, frac=0.01, dra
             f = orc.bf16_to_f64(x)
             step = rng.choice([-1.0, 1.0], f.shape) * (rng.random(f.shape) < frac)
             moved.append(orc.f64_to_bf16_bits(f + step * ulp_bf16(f)))
-        b = orc.block_attn_ref(*moved, k_cache, v_cache, ctx_len, base)
+        b = orc.block_attn_ref(*moved, k_cache, v_cache, ctx_len, base, page_table=table)
         worst = max(worst, float(np.max(np.abs(a - b))))
     return 2.0 * worst
 
 
-@pytest.mark.parametrize("name,lens", [("tiny", [40, 77, 130]), ("qwen3_8b", [300, 17, 1000, 512])])
-def test_two_cycles_on_device(name, lens):
+@pytest.mark.parametrize("name,lens,paged", [("tiny", [40, 77, 130], False), ("qwen3_8b", [300, 17, 1000, 512], False),
+                                             ("tiny", [33, 64, 200], True), ("qwen3_8b", [511, 90, 1024], True)])
+def test_two_cycles_on_device(name, lens, paged):
     cfg = synth.CONFIGS[name]
     L0 = np.array(lens, np.int32)
     B, Hq, Hkv, d = len(L0), cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
-    at = synth.attn_inputs(cfg, ctx_len=L0, seed=cfg.seed + 70)
-    dims = dfl.make_dims(B, Hq, Hkv, d, hidden=cfg.hidden, kv_capacity=at.capacity)
-    cos, sin = rope_tables(d, at.capacity + 32, cfg.rope_base)
+    at = synth.attn_inputs(cfg, ctx_len=L0, seed=cfg.seed + 70, page_size=16 if paged else 0)
+    table = at.page_table
+    dims = dfl.make_dims(B, Hq, Hkv, d, hidden=cfg.hidden, page_size=16 if paged else 0, kv_capacity=at.capacity,
+                         num_pages=at.num_pages)
+    cos, sin = rope_tables(d, at.capacity * (16 if paged else 1) + 32, cfg.rope_base)
+    tbl = None if table is None else i32(table)
+
+    def slot(b, p):
+        """(first, third) index of token p of sequence b in a [*, Hkv, *, d] cache."""
+        return (int(table[b, p // 16]), p % 16) if paged else (b, p)
     # q/k/v weight std 0.005 (q/k/v std ~0.32 at hidden 4096): the attention stays soft, so
     # one-ulp input differences move it little and its bound keeps its teeth.  Peaked
     # attention is the subject of the attention's own tests, on identical inputs.
@@ -95,21 +103,21 @@ def test_two_cycles_on_device(name, lens):
         dfl.dflash_block_qkv(dims, u16(qis[c].h), u16(qis[c].w_qkv), q, k, v, ws_q)
         out = torch.empty(B, 16, Hq, d, dtype=torch.float32, device=DEV)
         max_ctx = int(L0.max()) + (16 if c else 0)
-        dfl.dflash_block_attn(dims, q, k, v, kc, vc, None, kv, max_ctx, cos, sin, out, ws_a)
+        dfl.dflash_block_attn(dims, q, k, v, kc, vc, tbl, kv, max_ctx, cos, sin, out, ws_a)
         outs.append(out)
         if c == 0:
             dfl.dflash_draft_argmax(u16(draft_ok), i32(staged), blk, ws_v)
             dfl.dflash_verify_accept(u16(target), blk, kv, post, acc, nxt, kv, cp, 0, None, ws_v)
             dfl.dflash_ctx_proj(dims, [u16(x) for x in pj.x_layers], i32(row_seq), cp.view(-1), u16(pj.w_fc),
-                                u16(pj.w_k), u16(pj.w_v), cos, sin, None, kc, vc, None, ws_p)
+                                u16(pj.w_k), u16(pj.w_v), cos, sin, None, kc, vc, tbl, ws_p)
     torch.cuda.synchronize()
 
     # ---- oracle chain
     def qkv_ref(qi):
         return [x.reshape(B, 16, *x.shape[1:]) for x in orc.block_qkv_ref(qi.h, qi.w_qkv, Hq, Hkv, d)]
 
-    out_ref = [orc.block_attn_ref(*qkv_ref(qis[0]), at.k_cache, at.v_cache, L0, cfg.rope_base)]
-    slack = [one_ulp_allowance(qkv_ref(qis[0]), at.k_cache, at.v_cache, L0, cfg.rope_base, 1)]
+    out_ref = [orc.block_attn_ref(*qkv_ref(qis[0]), at.k_cache, at.v_cache, L0, cfg.rope_base, page_table=table)]
+    slack = [one_ulp_allowance(qkv_ref(qis[0]), at.k_cache, at.v_cache, L0, cfg.rope_base, 1, table)]
     blk_ref = orc.draft_block_ref(draft_ok, staged)
     vref = orc.verify_accept_ref(target, blk_ref, L0)
     log(f"cycle {name}: accept {vref['accept'].tolist()}")
@@ -117,10 +125,12 @@ def test_two_cycles_on_device(name, lens):
     pr = orc.ctx_proj_ref(pj.x_layers, pj.w_fc, pj.w_k, pj.w_v, pos, Hkv, d, cfg.rope_base)
     kc_ref, vc_ref = at.k_cache.copy(), at.v_cache.copy()
     for r in np.nonzero(pos >= 0)[0]:
-        kc_ref[row_seq[r], :, pos[r]] = orc.f64_to_bf16_bits(pr["Kb"][r])
-        vc_ref[row_seq[r], :, pos[r]] = orc.f64_to_bf16_bits(pr["Vb"][r])
-    out_ref.append(orc.block_attn_ref(*qkv_ref(qis[1]), kc_ref, vc_ref, vref["kv_len"], cfg.rope_base))
-    slack.append(one_ulp_allowance(qkv_ref(qis[1]), kc_ref, vc_ref, vref["kv_len"], cfg.rope_base, 2))
+        x, y = slot(row_seq[r], pos[r])
+        kc_ref[x, :, y] = orc.f64_to_bf16_bits(pr["Kb"][r])
+        vc_ref[x, :, y] = orc.f64_to_bf16_bits(pr["Vb"][r])
+    out_ref.append(orc.block_attn_ref(*qkv_ref(qis[1]), kc_ref, vc_ref, vref["kv_len"], cfg.rope_base,
+                                      page_table=table))
+    slack.append(one_ulp_allowance(qkv_ref(qis[1]), kc_ref, vc_ref, vref["kv_len"], cfg.rope_base, 2, table))
 
     # ---- compare
     assert np.array_equal(blk.cpu().numpy(), blk_ref)
@@ -129,9 +139,9 @@ def test_two_cycles_on_device(name, lens):
     assert np.array_equal(nxt.cpu().numpy(), vref["next"])
     assert np.array_equal(kv.cpu().numpy(), vref["kv_len"])
     kc_g, vc_g = host_u16(kc), host_u16(vc)
-    committed = np.zeros(kc_g.shape[::2][:1] + (kc_g.shape[2],), bool)   # [B, cap]
+    committed = np.zeros((kc_g.shape[0], kc_g.shape[2]), bool)   # [B, cap] dense, [pages, 16] paged
     for r in np.nonzero(pos >= 0)[0]:
-        committed[row_seq[r], pos[r]] = True
+        committed[slot(row_seq[r], pos[r])] = True
     for g, want, orig in ((kc_g, kc_ref, at.k_cache), (vc_g, vc_ref, at.v_cache)):
         gm, wm = orc.bf16_to_f64(g), orc.bf16_to_f64(want)
         rms = float(np.sqrt(np.mean(wm.transpose(0, 2, 1, 3)[committed] ** 2)))
