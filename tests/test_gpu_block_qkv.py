@@ -72,3 +72,15 @@ def test_block_qkv_padded_rows_and_tiled_path():
     _check(cfg, synth.block_qkv_inputs(cfg, batch=40, seed=62), 40, "tiny 640 rows")
     cfg = synth.CONFIGS["qwen3_8b"]
     _check(cfg, synth.block_qkv_inputs(cfg, batch=40, seed=63), 40, "qwen3_8b 640 rows")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,hidden", [
+    (1, 1, 1, 64, 64),       # one head of each kind, the smallest hidden: 192 outputs < one weight tile
+    (2, 2, 2, 128, 128),     # group size 1
+    (33, 8, 1, 128, 192),    # 528 rows (just past the skinny path), one kv head, hidden 3 x 64
+    (5, 12, 4, 64, 320),     # group 3
+])
+def test_block_qkv_degenerate_shapes(B, Hq, Hkv, d, hidden):
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, hidden=hidden)
+    _check(cfg, synth.block_qkv_inputs(cfg, batch=B, seed=64 + B), B, f"{Hq}q/{Hkv}kv d={d} hidden={hidden}")
