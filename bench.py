@@ -40,8 +40,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "070f0b20b2368bba8983deb7afb088b48a986d9a21a8a2100b0a426a95919bb0",
-                "workload": "batched", "read": 276755286, "write": 8508354}
+ATTN_TRAFFIC = {"sha256": "a4db4b94c4a7804e7438cc2e02e70d9ee5af73aeec0dbf694795d1db3431b1c4",
+                "workload": "batched", "read": 276755255, "write": 8508250}
 
 
 def sources_sha256(paths):
@@ -344,7 +344,7 @@ def main():
                          "scope": "draft-side greedy tokens at the 15 mask slots; not in the timed step"},
         "block_qkv": {"us": round(t_qkv * 1e6, 2), "GB_s": round(q_b / t_qkv / 1e9, 1),
                       "pct_hbm_peak": round(100 * q_b / t_qkv / 1e9 / HBM_PEAK_GBS, 2), "bytes": q_b,
-                      "scope": "the block's own q/k/v (three kernels: pack, split-K GEMM, reduce); "
+                      "scope": "the block's own q/k/v (two kernels: split-K GEMM, reduce); "
                                "not in the timed step"},
         "timing": "block_attn: HIP events around every timed call; verify, ctx_proj, draft_argmax and "
                   "block_qkv: events in a %d-step pass after the timed region" % N_SPLIT,

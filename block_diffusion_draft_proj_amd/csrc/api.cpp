@@ -203,19 +203,7 @@ int dflash_block_qkv(const dflash_dims* dims, const void* h, int64_t ld_h, const
   g.a_seg[0] = static_cast<const uint16_t*>(h);
   g.lda = ld_h;
   g.seg_k = dims->hidden;
-  if (pl.small) {
-    PackParams pk{};
-    pk.a_seg[0] = g.a_seg[0];
-    pk.lda = ld_h;
-    pk.seg_k = dims->hidden;
-    pk.M = M;
-    pk.K = dims->hidden;
-    pk.mp = pl.mp;
-    pk.xp = reinterpret_cast<uint16_t*>(ws + pl.off_xp);
-    if (launch_pack_rows(pk, stream) != hipSuccess) return DFLASH_ERR_LAUNCH;
-    g.xp = pk.xp;
-    g.mp = pl.mp;
-  }
+  // g.xp stays null: the skinny product reads h in place (one segment, rows ld_h apart)
   g.b0 = static_cast<const uint16_t*>(w_qkv);
   g.b1 = g.b0;
   g.n_b0 = n_out;

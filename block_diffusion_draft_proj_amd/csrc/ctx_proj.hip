@@ -167,7 +167,9 @@ struct SkGeo {
   static_assert(NS >= 3, "two stages in flight");
 };
 
-template <int MT>
+// PACKED: activations come packed as [K/64][mp][64] steps (pack_rows_kernel); else
+// they are read in place from the single segment a_seg[0] ([M][lda], K <= lda).
+template <int MT, bool PACKED>
 __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(GemmParams p) {
   using SG = SkGeo<MT>;
   __shared__ __attribute__((aligned(1024))) char lds[SG::NS * SG::STAGE];
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
   auto issue = [&](int st) {
     const int ks = st + rot < n_st ? st + rot : st + rot - n_st;
     const int k0 = kbeg + ks * BK;
-    const uint16_t* xstep = p.xp + ((int64_t)(k0 / BK) * p.mp + p.m_off) * BK;
+    const uint16_t* xstep = PACKED ? p.xp + ((int64_t)(k0 / BK) * p.mp + p.m_off) * BK : nullptr;
     const uint32_t stage = ring + (uint32_t)((st % SG::NS) * SG::STAGE);
 #pragma unroll
     for (int i = 0; i < SG::LW; ++i) {
@@ -216,9 +218,17 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
         const uint16_t* brow = n < p.n_b0 ? p.b0 + (int64_t)n * p.K : p.b1 + (int64_t)(n - p.n_b0) * p.K;
         lds_dma16_nt_m0(brow + k0 + ((pch ^ ((row >> 1) & 7)) << 3), stage + li * 1024);
       } else {
-        // packed activations: the 16*MT rows of step ks are one contiguous block
         const int row = (li - SG::W_TILE / 1024) * 8 + lrow;
-        lds_dma16_m0(xstep + row * BK + ((pch ^ ((row >> 1) & 7)) << 3), stage + li * 1024);
+        const int sw = (pch ^ ((row >> 1) & 7)) << 3;
+        if (PACKED) {
+          // packed activations: the 16*MT rows of step ks are one contiguous block
+          lds_dma16_m0(xstep + row * BK + sw, stage + li * 1024);
+        } else {
+          // in place: 128 bytes of row m_off + row (clamped to the last real row, whose
+          // extra results are never stored), columns k0 .. k0 + 63
+          const int m = min(p.m_off + row, p.M - 1);
+          lds_dma16_m0(p.a_seg[0] + (int64_t)m * p.lda + k0 + sw, stage + li * 1024);
+        }
       }
     }
   };
@@ -498,16 +508,28 @@ QkvPlan plan_block_qkv(int n_rows, int hidden, int n_out, int num_cu) {
   size_t off = 256;  // word 0: device error mask
   pl.off_part = off;
   off = align(off + sizeof(float) * (size_t)pl.splits * n_rows * n_out);
-  pl.off_xp = off;
-  if (pl.small) off = align(off + 2 * (size_t)hidden * pl.mp);
+  pl.off_xp = off;  // unused: the q/k/v product reads its activations in place
   pl.ws_bytes = off;
   return pl;
 }
 
-template <int MT>
+template <int MT, bool PACKED>
 void launch_skinny(const GemmParams& p, int splits, hipStream_t stream) {
   dim3 grid(((p.N + SK_ROWS - 1) / SK_ROWS) * splits, 1, 1);
-  hipLaunchKernelGGL((gemm_skinny_kernel<MT>), grid, dim3(SkGeo<MT>::WAVES * 64), 0, stream, p);
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT, PACKED>), grid, dim3(SkGeo<MT>::WAVES * 64), 0, stream, p);
+}
+
+// One chunk of up to kSkinnyChunk rows; activation tiles in pairs of 16 rows.
+template <bool PACKED>
+void launch_skinny_chunk(const GemmParams& c, int splits, hipStream_t stream) {
+  switch ((c.m_rows + 31) / 32) {
+    case 0:
+    case 1: launch_skinny<2, PACKED>(c, splits, stream); break;
+    case 2: launch_skinny<4, PACKED>(c, splits, stream); break;
+    case 3: launch_skinny<6, PACKED>(c, splits, stream); break;
+    case 4: launch_skinny<8, PACKED>(c, splits, stream); break;
+    default: launch_skinny<16, PACKED>(c, splits, stream); break;
+  }
 }
 
 hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStream_t stream) {
@@ -518,14 +540,8 @@ hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStre
       GemmParams c = p;
       c.m_off = m_off;
       c.m_rows = min(kSkinnyChunk, p.M - m_off);
-      switch ((c.m_rows + 31) / 32) {
-        case 0:
-        case 1: launch_skinny<2>(c, splits, stream); break;
-        case 2: launch_skinny<4>(c, splits, stream); break;
-        case 3: launch_skinny<6>(c, splits, stream); break;
-        case 4: launch_skinny<8>(c, splits, stream); break;
-        default: launch_skinny<16>(c, splits, stream); break;
-      }
+      if (p.xp) launch_skinny_chunk<true>(c, splits, stream);
+      else launch_skinny_chunk<false>(c, splits, stream);
     }
     return hipGetLastError();
   }
