@@ -40,8 +40,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "a4db4b94c4a7804e7438cc2e02e70d9ee5af73aeec0dbf694795d1db3431b1c4",
-                "workload": "batched", "read": 276755255, "write": 8508250}
+ATTN_TRAFFIC = {"sha256": "683788db56ffb7ee2483cfbf4f8a3d03bf4794cff45b4ea0afe602a5713e569f",
+                "workload": "batched", "read": 276755249, "write": 8508114}
 
 
 def sources_sha256(paths):

@@ -349,20 +349,7 @@ int dflash_ctx_proj(const dflash_dims* dims, int32_t n_rows, const void* const* 
     for (int l = 0; l < n_layers; ++l) g.a_seg[l] = static_cast<const uint16_t*>(x_layers[l]);
     g.lda = ld_x;
     g.seg_k = d_target;
-    if (pl.fc_small) {
-      // the skinny product reads its activations packed step by step
-      PackParams pk{};
-      for (int l = 0; l < n_layers; ++l) pk.a_seg[l] = g.a_seg[l];
-      pk.lda = ld_x;
-      pk.seg_k = d_target;
-      pk.M = n_rows;
-      pk.K = k_fc;
-      pk.mp = pl.mp;
-      pk.xp = reinterpret_cast<uint16_t*>(ws + pl.off_xp);
-      if (launch_pack_rows(pk, stream) != hipSuccess) return DFLASH_ERR_LAUNCH;
-      g.xp = pk.xp;
-      g.mp = pl.mp;
-    }
+    // g.xp stays null: the skinny product reads the layers' rows in place
     g.b0 = static_cast<const uint16_t*>(w_fc);
     g.b1 = g.b0;
     g.n_b0 = dims->hidden;

@@ -167,8 +167,9 @@ struct SkGeo {
   static_assert(NS >= 3, "two stages in flight");
 };
 
-// PACKED: activations come packed as [K/64][mp][64] steps (pack_rows_kernel); else
-// they are read in place from the single segment a_seg[0] ([M][lda], K <= lda).
+// PACKED: activations come packed as [K/64][mp][64] steps (written by
+// fc_reduce_kernel for the K/V product); else they are read in place from the
+// segments a_seg[] ([M][lda] each, seg_k columns of K per segment).
 template <int MT, bool PACKED>
 __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(GemmParams p) {
   using SG = SkGeo<MT>;
@@ -204,6 +205,20 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
   // Column tiles walk their K range from different starting steps, so the
   // activation steps read at one time are spread over the range.
   const int rot = n_st > 0 ? col % n_st : 0;
+  // In-place reads: the segment bases, made wave-uniform register values once, so
+  // the per-stage choice below is a chain of scalar selects.  (Indexing a_seg[] at
+  // run time instead puts a scalar load in every stage, whose wait counter also
+  // counts LDS reads.)
+  static_assert(kMaxLayers == 8, "one register value per segment below");
+  auto uniform_ptr = [&](int l) -> uint64_t {
+    if (PACKED) return 0;
+    const uint64_t a = (uint64_t)(uintptr_t)p.a_seg[l];
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    return ((uint64_t)hi << 32) | lo;
+  };
+  const uint64_t sb0 = uniform_ptr(0), sb1 = uniform_ptr(1), sb2 = uniform_ptr(2), sb3 = uniform_ptr(3);
+  const uint64_t sb4 = uniform_ptr(4), sb5 = uniform_ptr(5), sb6 = uniform_ptr(6), sb7 = uniform_ptr(7);
   auto issue = [&](int st) {
     const int ks = st + rot < n_st ? st + rot : st + rot - n_st;
     const int k0 = kbeg + ks * BK;
@@ -225,9 +240,14 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
           lds_dma16_m0(xstep + row * BK + sw, stage + li * 1024);
         } else {
           // in place: 128 bytes of row m_off + row (clamped to the last real row, whose
-          // extra results are never stored), columns k0 .. k0 + 63
+          // extra results are never stored), columns k0 .. k0 + 63 of A, which lie in
+          // one segment (seg_k is a multiple of 64)
           const int m = min(p.m_off + row, p.M - 1);
-          lds_dma16_m0(p.a_seg[0] + (int64_t)m * p.lda + k0 + sw, stage + li * 1024);
+          const int seg = k0 / p.seg_k;  // wave-uniform
+          const uint64_t base = seg == 0 ? sb0 : seg == 1 ? sb1 : seg == 2 ? sb2 : seg == 3 ? sb3
+                              : seg == 4 ? sb4 : seg == 5 ? sb5 : seg == 6 ? sb6 : sb7;
+          const uint16_t* src = reinterpret_cast<const uint16_t*>((uintptr_t)base);
+          lds_dma16_m0(src + (int64_t)m * p.lda + (k0 - seg * p.seg_k) + sw, stage + li * 1024);
         }
       }
     }
@@ -484,8 +504,7 @@ ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_
   // rows from its offset, so with more than one chunk the steps hold whole chunks
   // (rows past n_rows are zero in the packed activations and never stored).
   pl.mp = n_rows <= 128 ? 32 * ((n_rows + 31) / 32) : kSkinnyChunk * ((n_rows + kSkinnyChunk - 1) / kSkinnyChunk);
-  pl.off_xp = off;
-  if (pl.fc_small && has_fc) off = align(off + 2 * (size_t)k_fc * pl.mp);
+  pl.off_xp = off;  // unused: the skinny fc product reads the layers' rows in place
   pl.off_cp = off;
   if (pl.kv_small) off = align(off + 2 * (size_t)hidden * pl.mp);
   pl.ws_bytes = off;
