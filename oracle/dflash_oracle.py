@@ -29,9 +29,8 @@ feature C held in bf16; rotate-half RoPE with base 1e6 applied to Q and K
 only; softmax scale d^-1/2; q head h uses kv head floor(h/G); block Q and K are
 rounded to bf16 after RoPE, ctx K/V are bf16 in the cache; argmax takes the
 lowest index among equal maxima, NaN ranks above everything, -0 == +0.
-The bf16 rounding of the rotated block Q / K is a quantisation decision and is
-taken in the kernel's precision (float32 tables, float32 products and sums, no
-fused multiply-add); everything else is float64.
+The rotated block Q / K are rounded to bf16 once, from the exact rotation with
+the float32 cos / sin tables; everything else is float64.
 
 Parity note: the projection/norm/RoPE structure of the real draft model is not
 fixed by the pages; the oracle pins the method *under the readings above*.
@@ -39,6 +38,7 @@ fixed by the pages; the oracle pins the method *under the readings above*.
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -112,23 +112,50 @@ def apply_rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
 
 
-def rope_to_bf16(x_bits: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+def rope_tables_f32(pos: np.ndarray, head_dim: int, base: float) -> Tuple[np.ndarray, np.ndarray]:
+    """cos / sin of the RoPE angles at ``pos`` [n]: computed in float64 and rounded
+    to float32 (the tables every side of the path reads), returned as float64 [n, d/2]."""
+    th = rope_angles(pos, head_dim, base)
+    return (np.cos(th).astype(np.float32).astype(np.float64),
+            np.sin(th).astype(np.float32).astype(np.float64))
+
+
+def round_bf16_sum(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """bf16 nearest-even rounding of the EXACT sum a + b of float64 arrays.
+
+    s = fl64(a + b) and its rounding error e (error-free two-sum) hold the exact
+    value s + e.  Rounding s to bf16 gives the same answer as rounding s + e,
+    except when s lies exactly halfway between two bf16 neighbours and e != 0:
+    then the exact value is off the midpoint, on the side of e's sign.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    s = a + b
+    bb = s - a
+    e = (a - (s - bb)) + (b - bb)
+    r = round_bf16(s)
+    _, ex = np.frexp(s)
+    half = np.ldexp(1.0, (np.maximum(ex, -125) - 9).astype(np.int64))   # half a bf16 step at |s|
+    tie = (np.abs(s - r) == half) & (e != 0) & np.isfinite(s)
+    r[tie] = s[tie] + np.sign(e[tie]) * half[tie]
+    return r
+
+
+def rope_bf16(x_bits: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     """bf16(RoPE(x)) for bf16 inputs x[..., n, H, d], as float64 values.
 
-    Rounding to bf16 is a quantisation decision, so it is taken in the precision
-    the kernel computes it in: cos / sin of the float64 angle rounded to float32,
-    then, per pair, fl32(fl32(x_j c) - fl32(x_{j+d/2} s)) and
-    fl32(fl32(x_{j+d/2} c) + fl32(x_j s)) -- every product and sum rounded to
-    float32, no fused multiply-add -- then round-to-nearest-even to bf16.
+    The plain definition: rotate each pair with the float32 cos / sin tables,
+      y_j = x_j c - x_{j+d/2} s,   y_{j+d/2} = x_{j+d/2} c + x_j s,
+    and round each exact y once to bf16 (nearest even).  A bf16 value times a
+    float32 value is exact in float64 (8 + 24 significant bits), and the sum of
+    the two products is rounded from its exact value (``round_bf16_sum``).
     """
-    x = bf16_to_f64(x_bits).astype(np.float32)   # exact
+    x = bf16_to_f64(x_bits)
     d = x.shape[-1]
-    th = rope_angles(pos, d, base)
-    c = np.cos(th).astype(np.float32)[:, None, :]
-    s = np.sin(th).astype(np.float32)[:, None, :]
+    c, s = rope_tables_f32(pos, d, base)
+    c, s = c[:, None, :], s[:, None, :]
     lo, hi = x[..., : d // 2], x[..., d // 2:]
-    y = np.concatenate([(lo * c) - (hi * s), (hi * c) + (lo * s)], axis=-1)  # float32 ops
-    return round_bf16(y.astype(np.float64))
+    return np.concatenate([round_bf16_sum(lo * c, -(hi * s)), round_bf16_sum(hi * c, lo * s)], axis=-1)
 
 
 # --------------------------------------------------------------------------
@@ -218,8 +245,8 @@ def block_attn_unit_ref(q_b: np.ndarray, k_b: np.ndarray, v_b: np.ndarray,
       Keys  = [K_ctx[0:L] ; bf16(RoPE(k_blk[:, g]))] [L+16, d]
       Vals  = [V_ctx[0:L] ; v_blk[:, g]]
       S = Q_h Keys^T * scale,  P = softmax over all L+16 keys (no mask),  O = P Vals.
-    The bf16 roundings of the rotated block rows follow ``rope_to_bf16``; the
-    rest is float64.  Returns O [16, group, d] (and P [group, 16, L+16] if asked).
+    The rotated block rows are rounded once from their exact values
+    (``rope_bf16``); the rest is float64.  Returns O [16, group, d] (and P [group, 16, L+16] if asked).
     """
     d = q_b.shape[-1]
     if scale is None:
@@ -227,8 +254,8 @@ def block_attn_unit_ref(q_b: np.ndarray, k_b: np.ndarray, v_b: np.ndarray,
     L = int(ctx_len)
     pos = L + np.arange(BLOCK)
     hs = slice(g * group, (g + 1) * group)
-    Q = rope_to_bf16(q_b[:, hs, :], pos, base)                                   # [16, G, d]
-    Kblk = rope_to_bf16(k_b[:, g:g + 1, :], pos, base)[:, 0, :]
+    Q = rope_bf16(q_b[:, hs, :], pos, base)                                      # [16, G, d]
+    Kblk = rope_bf16(k_b[:, g:g + 1, :], pos, base)[:, 0, :]
     Keys = np.concatenate([bf16_to_f64(k_ctx[:L]), Kblk], axis=0)
     Vals = np.concatenate([bf16_to_f64(v_ctx[:L]), bf16_to_f64(v_b[:, g, :])], axis=0)
     out = np.empty((BLOCK, group, d))
@@ -378,19 +405,40 @@ def rope_brute(vec: Sequence[float], pos: int, base: float) -> List[float]:
     return out
 
 
+def bf16_round_fraction(v: Fraction) -> float:
+    """Nearest-even bf16 value of an exact rational (finite range), by integer arithmetic."""
+    if v == 0:
+        return 0.0
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^e <= a < 2^(e+2)
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)                                               # subnormal grid below 2^-126
+    step = Fraction(2) ** (e - 7)
+    q, rem = divmod(a, step)                                       # a = q * step + rem
+    if rem * 2 > step or (rem * 2 == step and q % 2 == 1):
+        q += 1
+    return sign * float(q * step)
+
+
 def rope_brute_bf16(vec: Sequence[float], pos: int, base: float) -> List[float]:
-    """Scalar twin of ``rope_to_bf16`` for one bf16-valued vector: float32 scalar steps."""
+    """Scalar twin of ``rope_bf16`` for one bf16-valued vector, in exact rational
+    arithmetic: float32 cos / sin of the float64 angle, exact rotation, one
+    nearest-even rounding to bf16."""
     d = len(vec)
     h = d // 2
-    f32 = np.float32
     out = [0.0] * d
     for j in range(h):
         th = pos * base ** (-2.0 * j / d)
-        c, s = f32(math.cos(th)), f32(math.sin(th))
-        a, b = f32(vec[j]), f32(vec[j + h])
-        out[j] = float(f32(f32(a * c) - f32(b * s)))
-        out[j + h] = float(f32(f32(b * c) + f32(a * s)))
-    return [float(v) for v in round_bf16(np.array(out))]
+        c = Fraction(float(np.float32(math.cos(th))))
+        s = Fraction(float(np.float32(math.sin(th))))
+        a, b = Fraction(float(vec[j])), Fraction(float(vec[j + h]))
+        out[j] = bf16_round_fraction(a * c - b * s)
+        out[j + h] = bf16_round_fraction(b * c + a * s)
+    return out
 
 
 def block_attn_brute(q_b, k_b, v_b, k_ctx, v_ctx, ctx_len: int, g: int, group: int,

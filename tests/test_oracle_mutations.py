@@ -20,8 +20,13 @@ MUTANTS = {
     "rope_sign": ("return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)",
                   "return np.concatenate([lo * c + hi * s, hi * c - lo * s], axis=-1)"),
     "rope_freq": ("inv_freq = base ** (-2.0 * j / head_dim)", "inv_freq = base ** (-1.0 * j / head_dim)"),
-    "q_not_rounded": ("Q = rope_to_bf16(q_b[:, hs, :], pos, base)",
+    "q_not_rounded": ("Q = rope_bf16(q_b[:, hs, :], pos, base)",
                       "Q = apply_rope(bf16_to_f64(q_b[:, hs, :]), pos, base)"),
+    "rope_f64_tables": ("return (np.cos(th).astype(np.float32).astype(np.float64),\n"
+                        "            np.sin(th).astype(np.float32).astype(np.float64))",
+                        "return (np.cos(th), np.sin(th))"),
+    "rope_no_two_sum": ("r[tie] = s[tie] + np.sign(e[tie]) * half[tie]", "r[tie] = r[tie]"),
+    "rope_sum_sign": ("round_bf16_sum(lo * c, -(hi * s))", "round_bf16_sum(lo * c, hi * s)"),
     "drop_block_keys": ("Keys = np.concatenate([bf16_to_f64(k_ctx[:L]), Kblk], axis=0)\n"
                         "    Vals = np.concatenate([bf16_to_f64(v_ctx[:L]), bf16_to_f64(v_b[:, g, :])], axis=0)",
                         "Keys = bf16_to_f64(k_ctx[:L+16])\n    Vals = bf16_to_f64(v_ctx[:L+16])"),

@@ -7,6 +7,7 @@ an independent library routine (torch's float64 scaled-dot-product attention).
 import json
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -144,56 +145,109 @@ def test_rope_matches_scalar_brute_force():
             assert np.allclose(got[n, h], orc.rope_brute(list(x[n, h]), int(pos[n]), 1e6), atol=1e-12)
 
 
-def test_rope_to_bf16_matches_scalar_twin():
+def _exact_rope_bf16(x, pos, j, d, base):
+    """bf16(exact rotation) of coordinate j (< d) of the bf16-valued vector x, with the
+    float32 tables, by exact rational arithmetic (an independent route)."""
+    h = d // 2
+    jj = j % h
+    th = pos * base ** (-2.0 * jj / d)
+    c = Fraction(float(np.float32(math.cos(th))))
+    s = Fraction(float(np.float32(math.sin(th))))
+    a, b = Fraction(float(x[jj])), Fraction(float(x[jj + h]))
+    return orc.bf16_round_fraction(a * c - b * s if j < h else b * c + a * s)
+
+
+def test_bf16_round_fraction_by_hand():
+    F = Fraction
+    assert orc.bf16_round_fraction(F(1) + F(1, 2 ** 8)) == 1.0                         # tie -> even
+    assert orc.bf16_round_fraction(F(1) + F(3, 2 ** 8)) == 1.0 + 2 ** -6               # tie -> even (up)
+    assert orc.bf16_round_fraction(F(1) + F(1, 2 ** 8) + F(1, 2 ** 80)) == 1.0 + 2 ** -7
+    assert orc.bf16_round_fraction(-(F(1) + F(1, 2 ** 8) - F(1, 2 ** 80))) == -1.0
+    assert orc.bf16_round_fraction(F(3, 7)) == float(orc.round_bf16(np.array([3 / 7]))[0])
+    assert orc.bf16_round_fraction(F(1, 2 ** 140)) == 0.0                              # below half the subnormal step
+    assert orc.bf16_round_fraction(F(3, 2 ** 134)) == 2.0 ** -132                      # subnormal tie -> even
+
+
+def test_round_bf16_sum_is_rounding_of_the_exact_sum():
+    # fl64(a + b) lands exactly on a bf16 midpoint while the exact sum is just off it:
+    # only the two-sum correction rounds the exact value.
+    mid = 1.0 + 2.0 ** -8                       # halfway between 1 and 1 + 2^-7
+    for a, b, want in [(mid, 2.0 ** -70, 1.0 + 2.0 ** -7), (mid, -(2.0 ** -70), 1.0),
+                       (-mid, 2.0 ** -70, -1.0), (1.0 + 3 * 2.0 ** -8, -(2.0 ** -80), 1.0 + 2.0 ** -7),
+                       (mid, 0.0, 1.0), (2.0, -1.0, 1.0)]:
+        got = orc.round_bf16_sum(np.array([a]), np.array([b]))[0]
+        assert got == want == orc.bf16_round_fraction(Fraction(a) + Fraction(b))
+    rng = np.random.default_rng(32)
+    a = rng.standard_normal(3000) * np.exp(rng.uniform(-5, 5, 3000))
+    b = rng.standard_normal(3000) * np.exp(rng.uniform(-40, 5, 3000))
+    got = orc.round_bf16_sum(a, b)
+    for i in range(0, 3000, 7):
+        assert got[i] == orc.bf16_round_fraction(Fraction(float(a[i])) + Fraction(float(b[i])))
+
+
+def test_rope_bf16_equals_exact_rational_rounding():
     rng = np.random.default_rng(30)
-    xb = orc.f64_to_bf16_bits(rng.standard_normal((5, 2, 32)) * 2.0)
+    d = 32
+    xb = orc.f64_to_bf16_bits(rng.standard_normal((5, 2, d)) * 2.0)
     pos = np.array([0, 3, 999, 8191, 32767])
-    got = orc.rope_to_bf16(xb, pos, 1e6)
+    got = orc.rope_bf16(xb, pos, 1e6)
+    x = orc.bf16_to_f64(xb)
     for n in range(5):
-        for h in range(2):
-            assert np.array_equal(got[n, h], orc.rope_brute_bf16(list(orc.bf16_to_f64(xb[n, h])), int(pos[n]), 1e6))
+        for hh in range(2):
+            assert got[n, hh].tolist() == orc.rope_brute_bf16(list(x[n, hh]), int(pos[n]), 1e6)
+            for j in range(d):
+                assert got[n, hh, j] == _exact_rope_bf16(x[n, hh], int(pos[n]), j, d, 1e6)
+
+
+def test_rope_bf16_on_rounding_sensitive_elements():
+    # Elements whose bf16 rounding changes with float64 instead of float32 tables, or with
+    # float32 evaluation of the rotation, are the ones closest to a rounding midpoint:
+    # exactly where an oracle mistake in the tables or the final rounding would show.
+    rng = np.random.default_rng(33)
+    d = 128
+    xb = orc.f64_to_bf16_bits(rng.standard_normal((3000, 4, d)) * 1.3)
+    pos = rng.integers(0, 40000, 3000)
+    got = orc.rope_bf16(xb, pos, 1e6)
+    x = orc.bf16_to_f64(xb)
+    f64_tables = orc.round_bf16(orc.apply_rope(x, pos, 1e6))
+    th = orc.rope_angles(pos, d, 1e6)[:, None, :]
+    c32, s32 = np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
+    x32 = x.astype(np.float32)
+    lo, hi = x32[..., :d // 2], x32[..., d // 2:]
+    f32_eval = orc.round_bf16(np.concatenate([lo * c32 - hi * s32, hi * c32 + lo * s32], -1).astype(np.float64))
+    sens = np.argwhere((f64_tables != got) | (f32_eval != got) | (f64_tables != f32_eval))
+    assert 5 <= len(sens) <= 4000, len(sens)
+    for n, hh, j in sens[:400]:
+        assert got[n, hh, j] == _exact_rope_bf16(x[n, hh], int(pos[n]), int(j), d, 1e6)
 
 
 @pytest.mark.parametrize("case", _golden("rope_cases.txt"), ids=lambda c: f"d{c['d']}p{c['pos']}j{c['j']}")
-def test_rope_to_bf16_closed_form_golden(case):
+def test_rope_bf16_closed_form_golden(case):
     d, j, pos = case["d"], case["j"], case["pos"]
     e = np.zeros((1, 1, d), np.uint16)
     e[0, 0, j] = 0x3F80                                   # unit vector e_j
-    got = orc.rope_to_bf16(e, np.array([pos]), case["base"])[0, 0]
+    got = orc.rope_bf16(e, np.array([pos]), case["base"])[0, 0]
     want = np.zeros(d)
     want[j] = orc.round_bf16(np.array([float(np.float32(math.cos(case["theta"])))]))[0]
     want[j + d // 2] = orc.round_bf16(np.array([float(np.float32(math.sin(case["theta"])))]))[0]
     assert np.allclose(got, want, atol=1e-15, rtol=0)
 
 
-def test_rope_to_bf16_differs_from_exact_rounding_only_at_midpoints():
-    # The kernel-precision rounding equals bf16(exact RoPE) except where the exact
-    # value lies within float32 resolution of a bf16 rounding midpoint; there the
-    # two choices are adjacent bf16 values.
+def test_rope_bf16_within_half_a_step_of_the_exact_rotation():
     rng = np.random.default_rng(31)
     xb = orc.f64_to_bf16_bits(rng.standard_normal((400, 8, 128)) * 1.3)
     pos = rng.integers(0, 33000, 400)
-    a = orc.rope_to_bf16(xb, pos, 1e6)
+    a = orc.rope_bf16(xb, pos, 1e6)
     x = orc.bf16_to_f64(xb)
-    exact = orc.apply_rope(x, pos, 1e6)
-    b = orc.round_bf16(exact)
-    # float32 evaluation error scales with the summed product magnitudes |x_j c| + |x_j' s|
+    exact = orc.apply_rope(x, pos, 1e6)                         # float64 tables
+    half_step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(a), 2.0 ** -126))) - 8)
+    # float32 tables move each product by at most 2^-24 of itself
     th = orc.rope_angles(pos, 128, 1e6)[:, None, :]
     lo, hi = np.abs(x[..., :64]), np.abs(x[..., 64:])
     c, s = np.abs(np.cos(th)), np.abs(np.sin(th))
     mag = np.concatenate([lo * c + hi * s, hi * c + lo * s], axis=-1)
-    diff = a != b
-    assert 0 < diff.sum() and diff.mean() < 1e-3
-    # everywhere: a is a bf16 value within half a bf16 step (of a) plus float32
-    # evaluation error of the exact rotation
-    half_step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(a), 2.0 ** -126))) - 8)
-    assert np.all(np.abs(a - exact) <= half_step + 2.0 ** -22 * mag)
-    # where the two roundings disagree, the exact value sits within float32 error of
-    # the boundary between them
-    ex, av, bv, mg = exact[diff], a[diff], b[diff], mag[diff]
-    boundary = np.where(np.abs(ex - av) < np.abs(ex - bv), av, bv)
-    assert np.all(np.abs(ex - (av + bv) / 2) <= 2.0 ** -22 * mg + np.abs(av - bv) / 2)
-    assert np.all(np.abs(ex - boundary) <= np.abs(av - bv))
+    assert np.all(np.abs(a - exact) <= half_step + 2.0 ** -24 * mag)
+    assert np.array_equal(orc.rope_bf16(xb, np.zeros(400, np.int64), 1e6), orc.bf16_to_f64(xb))   # identity at 0
 
 
 # ----------------------------------------------------------------------------- ctx projection
@@ -371,8 +425,8 @@ def test_attn_matches_torch_sdpa_float64(L, G, Hkv, d):
     for b in range(B):
         Lb = int(ctx[b])
         pos = Lb + np.arange(16)
-        Q = orc.rope_to_bf16(q[b], pos, 1e6)          # rotation rounding is pinned separately
-        Kb = orc.rope_to_bf16(k[b], pos, 1e6)
+        Q = orc.rope_bf16(q[b], pos, 1e6)             # rotation rounding is pinned separately
+        Kb = orc.rope_bf16(k[b], pos, 1e6)
         K = np.concatenate([orc.bf16_to_f64(kc[b][:, :Lb]), Kb.transpose(1, 0, 2)], axis=1)
         Vv = np.concatenate([orc.bf16_to_f64(vc[b][:, :Lb]), orc.bf16_to_f64(v[b]).transpose(1, 0, 2)], axis=1)
         ref = torch.nn.functional.scaled_dot_product_attention(
