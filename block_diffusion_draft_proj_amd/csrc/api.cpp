@@ -17,13 +17,19 @@ using namespace dflash;
 namespace {
 
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+// Per device: 0 unknown, 2 unsupported, else 1 + the partition's XCD count
+// (1, 2, 4 or 8) in the bits above bit 0.
+std::atomic<int> g_arch_state[kMaxDevices];
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Current device must be a gfx950 (MI355X class) part: the kernels use its MFMA
-// and bf16 conversion instructions.
-int check_device() {
+// and bf16 conversion instructions.  On success *xcc_mask is the partition's XCD
+// count - 1 (count 1, 2, 4 or 8; 8 if the runtime reports anything else).  With
+// round-robin dispatch workgroup i runs on XCD i & xcc_mask, so equal i mod 8 share
+// a die; the one-launch hand-offs count arrivals in that die's L2, and their
+// kernels check their die against this mask (DFLASH_DEVERR_XCD).
+int check_device(uint32_t* xcc_mask = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return DFLASH_ERR_UNSUPPORTED;
   if (dev < 0 || dev >= kMaxDevices) return DFLASH_ERR_UNSUPPORTED;
@@ -31,10 +37,15 @@ int check_device() {
   if (st == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DFLASH_ERR_UNSUPPORTED;
-    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    int n_xcc = 0;
+    if (hipDeviceGetAttribute(&n_xcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess) n_xcc = 0;
+    if (n_xcc != 1 && n_xcc != 2 && n_xcc != 4 && n_xcc != 8) n_xcc = 8;
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 + 2 * n_xcc : 2;
     g_arch_state[dev].store(st, std::memory_order_relaxed);
   }
-  return st == 1 ? DFLASH_OK : DFLASH_ERR_UNSUPPORTED;
+  if (st == 2) return DFLASH_ERR_UNSUPPORTED;
+  if (xcc_mask) *xcc_mask = (uint32_t)(st >> 1) - 1u;
+  return DFLASH_OK;
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_LAUNCH; }
@@ -113,10 +124,13 @@ int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab, const void
   const size_t need = dflash_verify_workspace_size(batch, block, vocab);
   if (!workspace || workspace_bytes < need) return DFLASH_ERR_WORKSPACE;
   if (!aligned16(workspace)) return DFLASH_ERR_ALIGN;
-  int st = check_device();
+  uint32_t xcc_mask = 0;
+  int st = check_device(&xcc_mask);
   if (st != DFLASH_OK) return st;
   char* ws = static_cast<char*>(workspace);
   VerifyParams p{};
+  p.err = reinterpret_cast<uint32_t*>(ws);
+  p.xcc_mask = xcc_mask;
   p.logits = static_cast<const uint16_t*>(logits);
   p.ld = ld_logits;
   p.vocab = vocab;
@@ -148,10 +162,13 @@ int dflash_draft_argmax(int32_t batch, int32_t block, int32_t vocab, const void*
   const size_t need = dflash_verify_workspace_size(batch, block, vocab);
   if (!workspace || workspace_bytes < need) return DFLASH_ERR_WORKSPACE;
   if (!aligned16(workspace)) return DFLASH_ERR_ALIGN;
-  int st = check_device();
+  uint32_t xcc_mask = 0;
+  int st = check_device(&xcc_mask);
   if (st != DFLASH_OK) return st;
   char* ws = static_cast<char*>(workspace);
   VerifyParams p{};
+  p.err = reinterpret_cast<uint32_t*>(ws);
+  p.xcc_mask = xcc_mask;
   p.logits = static_cast<const uint16_t*>(logits);
   p.ld = ld_logits;
   p.vocab = vocab;
@@ -262,10 +279,12 @@ int dflash_block_attn(const dflash_dims* dims, const void* q_blk, const void* k_
   if (!aligned16(workspace)) return DFLASH_ERR_ALIGN;
   const int64_t grid = (int64_t)8 * pl.n_splits * (((int64_t)dims->batch * dims->n_kv_heads + 7) / 8);
   if (grid > 0x7fffffffLL) return DFLASH_ERR_SHAPE;
-  st = check_device();
+  uint32_t xcc_mask = 0;
+  st = check_device(&xcc_mask);
   if (st != DFLASH_OK) return st;
   char* ws = static_cast<char*>(workspace);
   AttnParams p{};
+  p.xcc_mask = xcc_mask;
   p.q_blk = static_cast<const uint16_t*>(q_blk);
   p.k_blk = static_cast<const uint16_t*>(k_blk);
   p.v_blk = static_cast<const uint16_t*>(v_blk);

@@ -92,7 +92,7 @@ __device__ __forceinline__ const uint16_t* key_row(const AttnParams& p, const ui
   if constexpr (PAGED) {
     int page = pt[(t >> 4) - pt0];
     if ((unsigned)page >= (unsigned)p.num_pages) {
-      set_dev_error(p.err, 1u << 1);
+      set_dev_error(p.err, kDevErrPageId);
       page = 0;
     }
     return cache + (((int64_t)page * p.n_kv_heads + g) * 16 + (t & 15)) * D;
@@ -342,7 +342,12 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   __shared__ int32_t s_pt[PAGED ? kMaxPtEntries : 1];
 
   // XCD-aware decode: WG i runs on XCD i % 8; every split of a unit shares one XCD.
+  // The merge's hand-off through one XCD's L2 depends on it, so a workgroup that finds
+  // itself elsewhere raises DEVERR_XCD (with 2 or 4 XCDs per partition, i % 8 still
+  // fixes the die: checked modulo the partition's XCD count).
   const int i_wg = blockIdx.x;
+  if (p.fused && threadIdx.x == 0 && ((xcc_id() ^ (uint32_t)i_wg) & p.xcc_mask) != 0)
+    set_dev_error(p.err, kDevErrXcd);
   const int xcd = i_wg % kNumXcd;
   const int jj = i_wg / kNumXcd;
   const int s = jj % p.n_splits;
@@ -352,7 +357,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
 
   int L = p.ctx_len[b];
   if (L < 0 || L > p.max_ctx) {
-    if (threadIdx.x == 0 && s == 0) set_dev_error(p.err, 1u);
+    if (threadIdx.x == 0 && s == 0) set_dev_error(p.err, kDevErrCtxLen);
     L = L < 0 ? 0 : p.max_ctx;
   }
   const int ns = L > 0 ? (L + p.kps - 1) / p.kps : 1;
@@ -449,7 +454,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   for (int pk = 0; pk < QF; ++pk)
     if (pk < n_pk) issue(pk);
 
-  // Q of head h: rows at positions L + r, RoPE in fp32, rounded to bf16, as the
+  // Q of head h: rows at positions L + r, rotated exactly and rounded once to bf16, as the
   // B operand of S^T = K Q^T (lane holds dims 32*ks + 8*q .. +8 of row r).
   bf16x8 qB[KS];
   if constexpr (NGRP > 1) {
@@ -476,10 +481,10 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
         const float hi = (e & 1) ? bf16_hi(wh) : bf16_lo(wh);
         const float c = e < 4 ? c0[e] : c1[e - 4];
         const float sn = e < 4 ? s0[e] : s1[e - 4];
-        float ylo, yhi;
-        rope_pair(lo, hi, c, sn, ylo, yhi);
-        qB[ks][e] = static_cast<__bf16>(ylo);
-        qB[ks + KS / 2][e] = static_cast<__bf16>(yhi);
+        uint16_t ylo, yhi;
+        rope_pair_bf16(lo, hi, c, sn, ylo, yhi);
+        qB[ks][e] = __builtin_bit_cast(__bf16, ylo);
+        qB[ks + KS / 2][e] = __builtin_bit_cast(__bf16, yhi);
       }
     }
   } else {
@@ -501,10 +506,10 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
         const float hi = (e & 1) ? bf16_hi(wh) : bf16_lo(wh);
         const float c = e < 4 ? c0[e] : c1[e - 4];
         const float sn = e < 4 ? s0[e] : s1[e - 4];
-        float ylo, yhi;
-        rope_pair(lo, hi, c, sn, ylo, yhi);
-        qB[ks][e] = static_cast<__bf16>(ylo);
-        qB[ks + KS / 2][e] = static_cast<__bf16>(yhi);
+        uint16_t ylo, yhi;
+        rope_pair_bf16(lo, hi, c, sn, ylo, yhi);
+        qB[ks][e] = __builtin_bit_cast(__bf16, ylo);
+        qB[ks + KS / 2][e] = __builtin_bit_cast(__bf16, yhi);
       }
     }
   }
@@ -530,16 +535,16 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
         u32x4 ylo, yhi;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          float y[2][2];
+          uint16_t y[2][2];
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) {
             const int j = 8 * c + 2 * e2 + hb;
             const float xl = hb ? bf16_hi(lo[e2]) : bf16_lo(lo[e2]);
             const float xh = hb ? bf16_hi(hi[e2]) : bf16_lo(hi[e2]);
-            rope_pair(xl, xh, cq[t * HALF + j], sq[t * HALF + j], y[0][hb], y[1][hb]);
+            rope_pair_bf16(xl, xh, cq[t * HALF + j], sq[t * HALF + j], y[0][hb], y[1][hb]);
           }
-          ylo[e2] = (uint32_t)f32_to_bf16(y[0][0]) | ((uint32_t)f32_to_bf16(y[0][1]) << 16);
-          yhi[e2] = (uint32_t)f32_to_bf16(y[1][0]) | ((uint32_t)f32_to_bf16(y[1][1]) << 16);
+          ylo[e2] = (uint32_t)y[0][0] | ((uint32_t)y[0][1] << 16);
+          yhi[e2] = (uint32_t)y[1][0] | ((uint32_t)y[1][1] << 16);
         }
         *reinterpret_cast<u32x4*>(kt + t * GE::ROW + ((c ^ kswz<D>(t)) << 4)) = ylo;
         *reinterpret_cast<u32x4*>(kt + t * GE::ROW + (((c + HC) ^ kswz<D>(t)) << 4)) = yhi;
@@ -576,11 +581,11 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
       const uint16_t* vr = p.v_blk + rowoff;
       const float c = p.rope_cos[(int64_t)(L + t) * HALF + j];
       const float sn = p.rope_sin[(int64_t)(L + t) * HALF + j];
-      float y0, y1;
-      rope_pair(bf16_to_f32(kr[j]), bf16_to_f32(kr[j + HALF]), c, sn, y0, y1);
+      uint16_t y0, y1;
+      rope_pair_bf16(bf16_to_f32(kr[j]), bf16_to_f32(kr[j + HALF]), c, sn, y0, y1);
       const int j2 = j + HALF;
-      *reinterpret_cast<uint16_t*>(kt + t * GE::ROW + (((j >> 3) ^ kswz<D>(t)) << 4) + 2 * (j & 7)) = f32_to_bf16(y0);
-      *reinterpret_cast<uint16_t*>(kt + t * GE::ROW + (((j2 >> 3) ^ kswz<D>(t)) << 4) + 2 * (j2 & 7)) = f32_to_bf16(y1);
+      *reinterpret_cast<uint16_t*>(kt + t * GE::ROW + (((j >> 3) ^ kswz<D>(t)) << 4) + 2 * (j & 7)) = y0;
+      *reinterpret_cast<uint16_t*>(kt + t * GE::ROW + (((j2 >> 3) ^ kswz<D>(t)) << 4) + 2 * (j2 & 7)) = y1;
       *reinterpret_cast<uint16_t*>(vt + t * GE::ROW + (((j >> 3) ^ vswz<D>(t)) << 4) + 2 * (j & 7)) = vr[j];
       *reinterpret_cast<uint16_t*>(vt + t * GE::ROW + (((j2 >> 3) ^ vswz<D>(t)) << 4) + 2 * (j2 & 7)) = vr[j2];
     }
@@ -692,7 +697,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
     uint32_t v = prev;
     for (int spin = 0; (v >> 16) != (uint32_t)(ns - 1); ++spin) {
       if (spin >= kMergeSpinLimit) {  // cannot happen while the stored splits run; never hang
-        set_dev_error(p.err, 1u << 3);
+        set_dev_error(p.err, kDevErrMerge);
         break;
       }
       __builtin_amdgcn_s_sleep(2);

@@ -45,13 +45,37 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// One rotate-half RoPE pair in fp32, every product and sum rounded on its own
-// (no fused multiply-add), so the bf16 rounding that follows is reproducible
-// bit for bit by any IEEE fp32 evaluation of the same expression.
-__device__ __forceinline__ void rope_pair(float lo, float hi, float c, float s, float& ylo, float& yhi) {
+// bf16 (nearest even) of the exact sum a + b of two fp64 values, rounded once.
+// The fp64 sum s and its rounding error e (two-sum) hold the exact value.  It is
+// narrowed to fp32 by round-to-odd -- truncate toward zero, then set the last bit
+// if anything was dropped -- which keeps enough of the discarded part that the
+// fp32 -> bf16 nearest-even step (16 bits narrower) equals a direct rounding of
+// the exact value.  s is a double (not float) so no step rounds on its own.
+__device__ __forceinline__ uint16_t bf16_of_exact_sum(double a, double b) {
 #pragma clang fp contract(off)
-  ylo = lo * c - hi * s;
-  yhi = hi * c + lo * s;
+  const double s = a + b;
+  const double bb = s - a;
+  const double e = (a - (s - bb)) + (b - bb);
+  const float f = (float)s;
+  uint32_t u = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != s) {
+    if (fabs(back) > fabs(s)) u -= 1u;   // f was rounded away from zero: step back
+    u |= 1u;
+  } else if (e != 0.0) {                 // s is an fp32 value; the exact sum is just off it
+    if ((e < 0.0) != (f < 0.0)) u -= 1u; // ... on the side of zero
+    u |= 1u;
+  }
+  return f32_to_bf16(__uint_as_float(u));
+}
+
+// One rotate-half RoPE pair (lo = x_j, hi = x_{j+d/2}) with fp32 cos / sin: each
+// output is the exact rotation rounded once to bf16.  The product of two fp32
+// values (24 significant bits each) is exact in fp64.
+__device__ __forceinline__ void rope_pair_bf16(float lo, float hi, float c, float s, uint16_t& ylo,
+                                               uint16_t& yhi) {
+  ylo = bf16_of_exact_sum((double)lo * (double)c, -((double)hi * (double)s));
+  yhi = bf16_of_exact_sum((double)hi * (double)c, (double)lo * (double)s);
 }
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -128,6 +152,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+
+// Accelerator die (XCD) the wave runs on: HW_REG_XCC_ID (hardware register 20),
+// bits 3:0, on gfx950.
+__device__ __forceinline__ uint32_t xcc_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20);
+}
+
+// Device-side error bits (workspace word 0), as declared in the public header.
+constexpr uint32_t kDevErrCtxLen = 1u, kDevErrPageId = 2u, kDevErrRow = 4u, kDevErrMerge = 8u,
+                   kDevErrXcd = 16u;
 
 __device__ __forceinline__ void set_dev_error(uint32_t* err_word, uint32_t bit) {
   __hip_atomic_fetch_or(err_word, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -378,8 +378,8 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(QkvReduceParams p) {
   *reinterpret_cast<u32x2*>(dst) = v;
 }
 
-// K/V rows: sum splits, rotate K (pairs j, j+d/2) at the row's position, round to
-// bf16 and write into the cache.  Thread = (row, kv head, 4 consecutive j < d/2).
+// K/V rows: sum splits, rotate K (pairs j, j+d/2) at the row's position (exactly,
+// one rounding to bf16) and write into the cache.  Thread = (row, kv head, 4 consecutive j < d/2).
 __global__ __launch_bounds__(256) void kv_epilogue_kernel(KvEpilogueParams p) {
   const int half = p.head_dim / 2;
   const int per_row = p.n_kv_heads * (half / 4);
@@ -406,14 +406,14 @@ __global__ __launch_bounds__(256) void kv_epilogue_kernel(KvEpilogueParams p) {
   const bool bad = (unsigned)seq >= (unsigned)p.batch || pos >= p.max_pos ||
                    (paged ? (pos >> 4) >= p.capacity : pos >= p.capacity);
   if (bad) {
-    set_dev_error(p.err, 4u);
+    set_dev_error(p.err, kDevErrRow);
     return;
   }
   int64_t row_off;
   if (paged) {
     const int page = p.page_table[(int64_t)seq * p.capacity + (pos >> 4)];
     if ((unsigned)page >= (unsigned)p.num_pages) {
-      set_dev_error(p.err, 2u);
+      set_dev_error(p.err, kDevErrPageId);
       return;
     }
     row_off = (((int64_t)page * p.n_kv_heads + hh) * 16 + (pos & 15)) * p.head_dim;
@@ -422,18 +422,13 @@ __global__ __launch_bounds__(256) void kv_epilogue_kernel(KvEpilogueParams p) {
   }
   const f32x4 c = *reinterpret_cast<const f32x4*>(p.rope_cos + (int64_t)pos * half + j);
   const f32x4 s = *reinterpret_cast<const f32x4*>(p.rope_sin + (int64_t)pos * half + j);
-  f32x4 y0, y1;
+  uint16_t y0[4], y1[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float a, b;
-    rope_pair(k0[e], k1[e], c[e], s[e], a, b);
-    y0[e] = a;
-    y1[e] = b;
-  }
+  for (int e = 0; e < 4; ++e) rope_pair_bf16(k0[e], k1[e], c[e], s[e], y0[e], y1[e]);
   uint16_t* kd = p.k_cache + row_off;
   uint16_t* vd = p.v_cache + row_off;
-  *reinterpret_cast<u32x2*>(kd + j) = (u32x2){pack_bf16x2(y0[0], y0[1]), pack_bf16x2(y0[2], y0[3])};
-  *reinterpret_cast<u32x2*>(kd + j + half) = (u32x2){pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3])};
+  *reinterpret_cast<u32x2*>(kd + j) = (u32x2){y0[0] | ((uint32_t)y0[1] << 16), y0[2] | ((uint32_t)y0[3] << 16)};
+  *reinterpret_cast<u32x2*>(kd + j + half) = (u32x2){y1[0] | ((uint32_t)y1[1] << 16), y1[2] | ((uint32_t)y1[3] << 16)};
   *reinterpret_cast<u32x2*>(vd + j) = (u32x2){pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3])};
   *reinterpret_cast<u32x2*>(vd + j + half) = (u32x2){pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
 }

@@ -38,6 +38,8 @@ struct VerifyParams {
   int32_t page_size;
   uint64_t* part;       // [batch*16*n_chunks] per-chunk keys
   uint32_t* count;      // [batch][kVerifyCntStride] arrival counters (one-kernel form; zero between calls)
+  uint32_t* err;        // sticky device error word (workspace word 0)
+  uint32_t xcc_mask;    // XCDs of the partition - 1: workgroup i must run on XCD i & xcc_mask
   // draft tokens (launch_draft_argmax only; the verify fields above stay unused there)
   int32_t* draft_block;   // [batch][16]: slots 1..15 written, slot 0 from staged
   const int32_t* staged;  // [batch] or null (slot 0 left as it is)
@@ -66,6 +68,7 @@ struct AttnParams {
   uint32_t* err;    // sticky device error word
   uint32_t* count;  // [units] arrival counters of the fused merge (zero between calls)
   int fused;        // 1: the last split of a unit merges; 0: attn_merge_kernel does
+  uint32_t xcc_mask; // XCDs of the partition - 1: workgroup i must run on XCD i & xcc_mask
   int batch, n_q_heads, n_kv_heads;
   int capacity;     // dense rows per (seq, head) | page-table columns
   int num_pages;

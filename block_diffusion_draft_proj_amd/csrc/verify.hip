@@ -274,6 +274,9 @@ __global__ __launch_bounds__(kThreads) void verify_fused_kernel(VerifyParams p, 
   __shared__ uint32_t s_last;
   __shared__ AcceptShared sh;
   const int per = kRowsPerSeq<DRAFT> * p.n_chunks;  // workgroups per sequence
+  // A workgroup off the expected die would count its arrival in another L2, and the
+  // sequence's accept step would never run: raise DEVERR_XCD instead of staying silent.
+  if (threadIdx.x == 0 && ((xcc_id() ^ blockIdx.x) & p.xcc_mask) != 0) set_dev_error(p.err, kDevErrXcd);
   const int xcd = blockIdx.x % kNumXcd, j = blockIdx.x / kNumXcd;
   const int b = xcd + kNumXcd * (j / per);
   if (b >= batch) return;

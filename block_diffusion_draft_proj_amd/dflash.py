@@ -18,7 +18,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libdflash.so")
 
 BLOCK = 16
-DEVERR_CTX_LEN, DEVERR_PAGE_ID, DEVERR_ROW, DEVERR_MERGE = 1, 2, 4, 8
+DEVERR_CTX_LEN, DEVERR_PAGE_ID, DEVERR_ROW, DEVERR_MERGE, DEVERR_XCD = 1, 2, 4, 8, 16
 
 _c_int, _c_i64, _c_sz, _c_f, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
 
@@ -104,6 +104,26 @@ def _dev(t: Optional[torch.Tensor], name: str, dtypes, contiguous: bool = True) 
     return _vp(t.data_ptr())
 
 
+def _numel(t: Optional[torch.Tensor], want: int, name: str, at_least: bool = False) -> None:
+    """Size check before a pointer is handed over: the kernels trust these sizes."""
+    if t is None:
+        return
+    n = t.numel()
+    if (n < want) if at_least else (n != want):
+        raise ValueError(f"{name} holds {n} elements, {'at least ' if at_least else ''}{want} needed")
+
+
+def _cache_numel(dims: "dflash_dims") -> int:
+    if dims.page_size > 0:
+        return dims.num_pages * dims.n_kv_heads * dims.page_size * dims.head_dim
+    return dims.batch * dims.n_kv_heads * dims.kv_capacity * dims.head_dim
+
+
+def _check_rope(rope_cos: torch.Tensor, rope_sin: torch.Tensor, head_dim: int) -> None:
+    if rope_cos.dim() != 2 or rope_cos.shape[1] != head_dim // 2 or tuple(rope_sin.shape) != tuple(rope_cos.shape):
+        raise ValueError(f"rope_cos / rope_sin must both be [max_pos, {head_dim // 2}]")
+
+
 def make_dims(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, hidden: int = 0,
               page_size: int = 0, kv_capacity: int = 0, num_pages: int = 0,
               softmax_scale: float = 0.0) -> dflash_dims:
@@ -121,6 +141,8 @@ def dflash_version() -> int:
 
 def dflash_rope_tables(base: float, head_dim: int, max_pos: int, cos_out: torch.Tensor,
                        sin_out: torch.Tensor, stream=None) -> None:
+    _numel(cos_out, max_pos * (head_dim // 2), "cos_out", at_least=True)
+    _numel(sin_out, max_pos * (head_dim // 2), "sin_out", at_least=True)
     _check("dflash_rope_tables", _lib.dflash_rope_tables(
         base, head_dim, max_pos, _dev(cos_out, "cos_out", (torch.float32,)),
         _dev(sin_out, "sin_out", (torch.float32,)), _stream(stream)))
@@ -141,6 +163,19 @@ def dflash_ctx_proj(dims: dflash_dims, x_layers: Sequence[torch.Tensor], row_seq
     for i, x in enumerate(x_layers):
         if x.dim() != 2 or x.stride(1) != 1 or tuple(x.shape) != (n_rows, d_target) or x.stride(0) != ld:
             raise ValueError(f"x_layers[{i}] must be [n_rows, d_target] with unit inner stride and a common row stride")
+    D, kvw = dims.hidden, dims.n_kv_heads * dims.head_dim
+    _numel(row_seq, n_rows, "row_seq")
+    _numel(row_pos, n_rows, "row_pos")
+    _numel(w_fc, D * len(x_layers) * d_target, "w_fc")
+    _numel(w_k, kvw * D, "w_k")
+    _numel(w_v, kvw * D, "w_v")
+    _numel(c_out, n_rows * D, "c_out", at_least=True)
+    _numel(k_cache, _cache_numel(dims), "k_cache")
+    _numel(v_cache, _cache_numel(dims), "v_cache")
+    if dims.page_size > 0:
+        _numel(page_table, dims.batch * dims.kv_capacity, "page_table")
+    _check_rope(rope_cos, rope_sin, dims.head_dim)
+    for i, x in enumerate(x_layers):
         _dev(x, f"x_layers[{i}]", _BF16, contiguous=False)
     arr = (_vp * len(x_layers))(*[x.data_ptr() for x in x_layers])
     _check("dflash_ctx_proj", _lib.dflash_ctx_proj(
@@ -162,6 +197,17 @@ def dflash_block_attn(dims: dflash_dims, q_blk: torch.Tensor, k_blk: torch.Tenso
                       ctx_len: torch.Tensor, max_ctx_len: int, rope_cos: torch.Tensor,
                       rope_sin: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
                       stream=None) -> None:
+    B, Hq, Hkv, d = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    _numel(q_blk, B * BLOCK * Hq * d, "q_blk")
+    _numel(k_blk, B * BLOCK * Hkv * d, "k_blk")
+    _numel(v_blk, B * BLOCK * Hkv * d, "v_blk")
+    _numel(k_cache, _cache_numel(dims), "k_cache")
+    _numel(v_cache, _cache_numel(dims), "v_cache")
+    if dims.page_size > 0:
+        _numel(page_table, B * dims.kv_capacity, "page_table")
+    _numel(ctx_len, B, "ctx_len")
+    _numel(out, B * BLOCK * Hq * d, "out")
+    _check_rope(rope_cos, rope_sin, d)
     _check("dflash_block_attn", _lib.dflash_block_attn(
         ctypes.byref(dims), _dev(q_blk, "q_blk", _BF16), _dev(k_blk, "k_blk", _BF16),
         _dev(v_blk, "v_blk", _BF16), _dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16),
@@ -186,6 +232,11 @@ def dflash_verify_accept(logits: torch.Tensor, block_tokens: torch.Tensor, kv_le
             or logits.stride(0) != logits.shape[1] * logits.shape[2]:
         raise ValueError("logits must be a contiguous [B, 16, ld] tensor")
     B, blk, ld = (int(s) for s in logits.shape)
+    for name, t, n in (("block_tokens", block_tokens, B * blk), ("kv_len_in", kv_len_in, B),
+                       ("posterior", posterior, B * blk), ("accept_len", accept_len, B),
+                       ("next_token", next_token, B), ("kv_len_out", kv_len_out, B),
+                       ("commit_pos", commit_pos, B * blk), ("n_pages", n_pages, B)):
+        _numel(t, n, name)
     _check("dflash_verify_accept", _lib.dflash_verify_accept(
         B, blk, ld if vocab is None else vocab, _dev(logits, "logits", _BF16), ld,
         _dev(block_tokens, "block_tokens", (torch.int32,)), _dev(kv_len_in, "kv_len_in", (torch.int32,)),

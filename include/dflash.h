@@ -76,6 +76,12 @@ extern "C" {
                                       wait gave up; that unit's output is wrong).  Not expected:
                                       reports a broken workspace counter, e.g. a workspace shared
                                       by two calls in flight */
+#define DFLASH_DEVERR_XCD      16u  /* a workgroup of a one-launch hand-off (block attention's split
+                                      merge, the verify's or draft argmax's accept step at batch >= 8)
+                                      ran on another accelerator die (XCD) than the dispatch order
+                                      the hand-off relies on.  That call's outputs may be wrong or
+                                      stale and its arrival counters may be left non-zero: zero the
+                                      whole workspace before reusing it.  Not expected on MI355X */
 
 /* Block of draft tokens: the staged token plus 15 mask slots
  * ("dflash-mlx", "block-diffusion draft"). */

@@ -75,6 +75,7 @@ def run_verify(logits: np.ndarray, block_tokens, kv_len, page_size=0, vocab=None
     dfl.dflash_verify_accept(u16(logits), i32(block_tokens), kvi, post, acc, nxt, kvo, cp, page_size, npg, ws,
                              vocab=V)
     torch.cuda.synchronize()
+    assert int(ws[:4].cpu().numpy().view(np.uint32)[0]) == 0, "device error word set"
     res = {"post": post.cpu().numpy(), "accept": acc.cpu().numpy(), "next": nxt.cpu().numpy(),
            "kv_len": kvo.cpu().numpy(), "commit_pos": cp.cpu().numpy()}
     if npg is not None:
@@ -91,4 +92,5 @@ def run_draft(logits: np.ndarray, staged, vocab=None, ws=None, init=-7):
     blk = torch.full((B, synth.BLOCK), init, dtype=torch.int32, device=DEV)
     dfl.dflash_draft_argmax(u16(logits), None if staged is None else i32(staged), blk, ws, vocab=V)
     torch.cuda.synchronize()
+    assert int(ws[:4].cpu().numpy().view(np.uint32)[0]) == 0, "device error word set"
     return blk.cpu().numpy(), ws

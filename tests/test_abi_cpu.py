@@ -206,3 +206,109 @@ def test_block_qkv_rejects_bad_arguments():
     assert _qkv(good, w=MIS) == -3
     assert _qkv(good, ws=ctypes.c_void_p(None)) == -4
     assert _qkv(good, wsb=300) == -4
+
+
+# ---------------------------------------------------------------- binding size checks
+# The Python wrappers check every tensor's size against the dims before any pointer
+# is handed over (the kernels trust those sizes).  Host tensors of the right sizes get
+# past the size checks and stop at the device check; wrong sizes stop earlier.
+def _t(*shape, dtype=torch.int16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _attn_args(B=2, Hq=8, Hkv=2, d=64, cap=80, **kw):
+    dims = dfl.make_dims(B, Hq, Hkv, d, kv_capacity=cap)
+    a = dict(q=_t(B, 16, Hq, d), k=_t(B, 16, Hkv, d), v=_t(B, 16, Hkv, d), kc=_t(B, Hkv, cap, d),
+             vc=_t(B, Hkv, cap, d), pt=None, ctx=_t(B, dtype=torch.int32), cos=_t(100, d // 2, dtype=torch.float32),
+             sin=_t(100, d // 2, dtype=torch.float32), out=_t(B, 16, Hq, d, dtype=torch.float32),
+             ws=_t(1024, dtype=torch.uint8))
+    a.update(kw)
+    return dims, a
+
+
+def _call_attn(dims, a):
+    dfl.dflash_block_attn(dims, a["q"], a["k"], a["v"], a["kc"], a["vc"], a["pt"], a["ctx"], 64, a["cos"],
+                          a["sin"], a["out"], a["ws"])
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("q", _t(2, 16, 8, 32)), ("k", _t(2, 16, 1, 64)), ("v", _t(1, 16, 2, 64)), ("kc", _t(2, 2, 79, 64)),
+    ("vc", _t(2, 2, 81, 64)), ("ctx", _t(1, dtype=torch.int32)), ("out", _t(2, 16, 8, 63, dtype=torch.float32)),
+    ("cos", _t(100, 64, dtype=torch.float32)), ("sin", _t(99, 32, dtype=torch.float32)),
+])
+def test_binding_block_attn_checks_sizes(name, bad):
+    dims, a = _attn_args(**{name: bad})
+    with pytest.raises(ValueError, match="elements|rope_cos"):
+        _call_attn(dims, a)
+    dims, a = _attn_args()
+    with pytest.raises(ValueError, match="device tensor"):
+        _call_attn(dims, a)
+
+
+def test_binding_block_attn_checks_page_table_size():
+    dims = dfl.make_dims(2, 8, 2, 64, page_size=16, kv_capacity=5, num_pages=10)
+    _, a = _attn_args(kc=_t(10, 2, 16, 64), vc=_t(10, 2, 16, 64), pt=_t(2, 4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="page_table"):
+        _call_attn(dims, a)
+
+
+def _proj_args(n=32, nl=2, dt=256, D=256, Hkv=2, d=64, cap=80, **kw):
+    dims = dfl.make_dims(1, 4, Hkv, d, hidden=D, kv_capacity=cap)
+    a = dict(xs=[_t(n, dt) for _ in range(nl)], seq=_t(n, dtype=torch.int32), pos=_t(n, dtype=torch.int32),
+             wfc=_t(D, nl * dt), wk=_t(Hkv * d, D), wv=_t(Hkv * d, D), cos=_t(100, d // 2, dtype=torch.float32),
+             sin=_t(100, d // 2, dtype=torch.float32), cout=None, kc=_t(1, Hkv, cap, d), vc=_t(1, Hkv, cap, d),
+             pt=None, ws=_t(1024, dtype=torch.uint8))
+    a.update(kw)
+    return dims, a
+
+
+def _call_proj(dims, a):
+    dfl.dflash_ctx_proj(dims, a["xs"], a["seq"], a["pos"], a["wfc"], a["wk"], a["wv"], a["cos"], a["sin"],
+                        a["cout"], a["kc"], a["vc"], a["pt"], a["ws"])
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("seq", _t(31, dtype=torch.int32)), ("pos", _t(33, dtype=torch.int32)), ("wfc", _t(256, 256)),
+    ("wk", _t(64, 256)), ("wv", _t(128, 255)), ("cout", _t(31, 256)), ("kc", _t(1, 2, 79, 64)),
+    ("vc", _t(2, 2, 80, 64)), ("cos", _t(100, 16, dtype=torch.float32)),
+])
+def test_binding_ctx_proj_checks_sizes(name, bad):
+    dims, a = _proj_args(**{name: bad})
+    with pytest.raises(ValueError, match="elements|rope_cos"):
+        _call_proj(dims, a)
+    dims, a = _proj_args()
+    with pytest.raises(ValueError, match="device tensor"):
+        _call_proj(dims, a)
+
+
+def _verify_args(B=3, **kw):
+    i = lambda *s: _t(*s, dtype=torch.int32)
+    a = dict(logits=_t(B, 16, 1000), bt=i(B, 16), kvi=i(B), post=i(B, 16), acc=i(B), nxt=i(B), kvo=i(B),
+             cp=i(B, 16), npg=i(B))
+    a.update(kw)
+    return a
+
+
+def _call_verify(a):
+    dfl.dflash_verify_accept(a["logits"], a["bt"], a["kvi"], a["post"], a["acc"], a["nxt"], a["kvo"], a["cp"], 16,
+                             a["npg"], _t(1024, dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("name", ["bt", "kvi", "post", "acc", "nxt", "kvo", "cp", "npg"])
+def test_binding_verify_checks_sizes(name):
+    a = _verify_args()
+    a[name] = torch.zeros(a[name].numel() - 1, dtype=torch.int32)
+    with pytest.raises(ValueError, match=name.replace("bt", "block_tokens").replace("kvi", "kv_len_in")
+                       .replace("post", "posterior").replace("acc", "accept_len").replace("nxt", "next_token")
+                       .replace("kvo", "kv_len_out").replace("cp", "commit_pos").replace("npg", "n_pages")):
+        _call_verify(a)
+    with pytest.raises(ValueError, match="device tensor"):
+        _call_verify(_verify_args())
+
+
+def test_deverr_bits_match_the_header():
+    text = open(HEADER).read()
+    bits = dict(re.findall(r"#define DFLASH_DEVERR_(\w+)\s+(\d+)u", text))
+    assert {k: int(v) for k, v in bits.items()} == {
+        "CTX_LEN": dfl.DEVERR_CTX_LEN, "PAGE_ID": dfl.DEVERR_PAGE_ID, "ROW": dfl.DEVERR_ROW,
+        "MERGE": dfl.DEVERR_MERGE, "XCD": dfl.DEVERR_XCD}

@@ -58,7 +58,7 @@ def _commit_positions(kv_len, rng):
 
 
 def _run(cfg, n_rows, row_seq, row_pos, capacity, paged_table=None, num_pages=0, with_fc=True,
-         c_out=True, seed=None):
+         c_out=True, seed=None, ld_pad=0):
     pj = synth.ctx_proj_inputs(cfg, n_rows, seed=seed)
     Hkv, d, D = cfg.n_kv_heads, cfg.head_dim, cfg.hidden
     B = cfg.batch
@@ -79,8 +79,14 @@ def _run(cfg, n_rows, row_seq, row_pos, capacity, paged_table=None, num_pages=0,
         wfc, n_layers, dt = None, 1, D
     ws = dfl.workspace(dfl.dflash_ctx_proj_workspace_size(dims, n_rows, n_layers, dt), DEV)
     cbuf = torch.zeros(n_rows, D, dtype=torch.int16, device=DEV) if (c_out and with_fc) else None
-    log(f"ctx_proj {cfg.name}: M={n_rows} K={n_layers * dt} D={D} paged={paged_table is not None}")
-    dfl.dflash_ctx_proj(dims, [u16(x) for x in xs], i32(row_seq), i32(row_pos),
+    log(f"ctx_proj {cfg.name}: M={n_rows} K={n_layers * dt} D={D} paged={paged_table is not None} "
+        f"ld_x={dt + ld_pad}")
+    if ld_pad:   # each layer's rows lie ld_x = d_target + ld_pad elements apart (a strided view)
+        dev_x = [torch.cat([u16(x), torch.full((n_rows, ld_pad), 0x7FC0, dtype=torch.int16, device=DEV)],
+                           dim=1)[:, :dt] for x in xs]
+    else:
+        dev_x = [u16(x) for x in xs]
+    dfl.dflash_ctx_proj(dims, dev_x, i32(row_seq), i32(row_pos),
                         None if wfc is None else u16(wfc), u16(pj.w_k), u16(pj.w_v), cos, sin, cbuf, kc, vc,
                         None if paged_table is None else i32(paged_table), ws)
     torch.cuda.synchronize()
@@ -103,8 +109,9 @@ def _gather_rows(cache, row_seq, row_pos, table=None):
     return live, orc.bf16_to_f64(np.stack(rows))
 
 
-def _check(cfg, n_rows, row_seq, row_pos, capacity, table=None, num_pages=0, with_fc=True, label=""):
-    ref, kc, vc, cb, err = _run(cfg, n_rows, row_seq, row_pos, capacity, table, num_pages, with_fc)
+def _check(cfg, n_rows, row_seq, row_pos, capacity, table=None, num_pages=0, with_fc=True, label="", ld_pad=0):
+    ref, kc, vc, cb, err = _run(cfg, n_rows, row_seq, row_pos, capacity, table, num_pages, with_fc,
+                                ld_pad=ld_pad)
     assert err == 0
     live, k = _gather_rows(kc, row_seq, row_pos, table)
     _, v = _gather_rows(vc, row_seq, row_pos, table)
@@ -187,3 +194,47 @@ def test_ctx_proj_bad_rows_flagged_and_skipped():
     ref, kc, vc, cb, err = _run(cfg, n, seq, pos, capacity=80)
     assert err & dfl.DEVERR_ROW
     assert np.count_nonzero(np.any(kc != 0, axis=-1)) == 7 * cfg.n_kv_heads
+
+
+# Above 512 rows (prefill chunks) the projection takes the tiled MFMA GEMM, whose A
+# operand walks the layers' row pointers at run time and whose C is row-major.
+def test_ctx_proj_qwen3_8b_full_prefill_2048_rows():
+    cfg = synth.CONFIGS["qwen3_8b"]
+    n = 2048
+    seq = np.zeros(n, np.int32)
+    pos = np.arange(n, dtype=np.int32)
+    _check(cfg, n, seq, pos, capacity=n + 16, label="qwen3_8b prefill 2048 rows x 5 layers")
+
+
+def test_ctx_proj_ragged_prefill_1000_rows_strided_layers():
+    # Two sequences' rows interleaved in runs, every ninth row uncommitted, and layer rows
+    # 64 elements wider than the layer (ld_x > d_target; the padding holds NaN).
+    cfg = dataclasses.replace(synth.CONFIGS["qwen3_8b"], batch=2, n_target_layers=3)
+    n = 1000
+    seq = (np.arange(n) // 37 % 2).astype(np.int32)
+    pos = np.zeros(n, np.int32)
+    for b in range(2):
+        rows = np.nonzero(seq == b)[0]
+        pos[rows] = 100 + 3 * b + np.arange(len(rows))
+    pos[::9] = -1
+    _check(cfg, n, seq, pos, capacity=700, label="ragged prefill 1000 rows, ld_x > d_target", ld_pad=64)
+
+
+def test_ctx_proj_paged_prefill_700_rows():
+    cfg = dataclasses.replace(synth.CONFIGS["qwen3_8b"], n_target_layers=2)
+    n = 700
+    seq = np.zeros(n, np.int32)
+    pos = np.arange(n, dtype=np.int32) + 5
+    width = (n + 5 + 15) // 16
+    table = np.random.default_rng(3).permutation(width).astype(np.int32)[None, :]
+    _check(cfg, n, seq, pos, capacity=0, table=table, num_pages=width, label="paged prefill 700 rows")
+
+
+def test_ctx_proj_skinny_rows_strided_layers():
+    # Per-cycle rows (<= 512) read the layers in place too: layer rows ld_x > d_target apart.
+    cfg = synth.CONFIGS["batched"]
+    n = 128
+    seq = np.repeat(np.arange(cfg.batch, dtype=np.int32), 16)
+    pos = np.tile(np.arange(16, dtype=np.int32), cfg.batch) + 200
+    pos[5::16] = -1
+    _check(cfg, n, seq, pos, capacity=240, label="batched block rows, ld_x > d_target", ld_pad=128)
