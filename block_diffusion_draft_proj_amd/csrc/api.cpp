@@ -252,10 +252,16 @@ size_t dflash_block_attn_workspace_size(const dflash_dims* dims, int32_t max_ctx
       .ws_bytes;
 }
 
-int dflash_block_attn(const dflash_dims* dims, const void* q_blk, const void* k_blk, const void* v_blk,
-                      const void* k_cache, const void* v_cache, const int32_t* page_table, const int32_t* ctx_len,
-                      int32_t max_ctx_len, const float* rope_cos, const float* rope_sin, int32_t max_pos,
-                      float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation, planning and launch of the block attention on workspace `ws` of
+// `ws_bytes` bytes; `err` is the device error word (word 0 of ws when null).
+int block_attn_run(const dflash_dims* dims, const void* q_blk, const void* k_blk, const void* v_blk,
+                   const void* k_cache, const void* v_cache, const int32_t* page_table, const int32_t* ctx_len,
+                   int32_t max_ctx_len, const float* rope_cos, const float* rope_sin, int32_t max_pos, float* out,
+                   char* ws, size_t ws_bytes, uint32_t* err, char* (*scratch_of_device)(), hipStream_t stream) {
   int st = check_cache_dims(dims);
   if (st != DFLASH_OK) return st;
   if (!q_blk || !k_blk || !v_blk || !k_cache || !v_cache || !ctx_len || !rope_cos || !rope_sin || !out)
@@ -273,16 +279,20 @@ int dflash_block_attn(const dflash_dims* dims, const void* q_blk, const void* k_
   const void* ptrs[] = {q_blk, k_blk, v_blk, k_cache, v_cache, rope_cos, rope_sin, out};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return DFLASH_ERR_ALIGN;
+  if (err && (reinterpret_cast<uintptr_t>(err) & 3u)) return DFLASH_ERR_ALIGN;
   const AttnPlan pl =
       plan_block_attn(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim, max_ctx_len, kPlanCUs);
-  if (!workspace || workspace_bytes < pl.ws_bytes) return DFLASH_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return DFLASH_ERR_ALIGN;
+  if ((!ws && !scratch_of_device) || ws_bytes < pl.ws_bytes) return DFLASH_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return DFLASH_ERR_ALIGN;
   const int64_t grid = (int64_t)8 * pl.n_splits * (((int64_t)dims->batch * dims->n_kv_heads + 7) / 8);
   if (grid > 0x7fffffffLL) return DFLASH_ERR_SHAPE;
   uint32_t xcc_mask = 0;
   st = check_device(&xcc_mask);
   if (st != DFLASH_OK) return st;
-  char* ws = static_cast<char*>(workspace);
+  if (!ws) {
+    ws = scratch_of_device();
+    if (!ws) return DFLASH_ERR_LAUNCH;
+  }
   AttnParams p{};
   p.xcc_mask = xcc_mask;
   p.q_blk = static_cast<const uint16_t*>(q_blk);
@@ -297,7 +307,7 @@ int dflash_block_attn(const dflash_dims* dims, const void* q_blk, const void* k_
   p.out = out;
   p.ws_o = reinterpret_cast<float*>(ws + pl.off_o);
   p.ws_ml = reinterpret_cast<float*>(ws + pl.off_ml);
-  p.err = reinterpret_cast<uint32_t*>(ws);
+  p.err = err ? err : reinterpret_cast<uint32_t*>(ws);
   p.count = reinterpret_cast<uint32_t*>(ws + pl.off_cnt);
   p.fused = pl.fused ? 1 : 0;
   p.batch = dims->batch;
@@ -312,6 +322,51 @@ int dflash_block_attn(const dflash_dims* dims, const void* q_blk, const void* k_
   const double scale = dims->softmax_scale > 0.f ? (double)dims->softmax_scale : 1.0 / sqrt((double)dims->head_dim);
   p.scale_log2 = (float)(scale * 1.4426950408889634);
   return launch_status(launch_block_attn(p, dims->head_dim, group, dims->page_size > 0, stream));
+}
+
+// Scratch of the allocation-free attention entry point: one array per device,
+// zero at load (the arrival counters must start at zero; every call leaves them
+// at zero), held until the process ends.  In host code `scratch` only names the
+// symbol: its device address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = DFLASH_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+std::atomic<char*> g_scratch_ptr[kMaxDevices];
+
+char* scratch_of_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  char* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+    ptr = static_cast<char*>(addr);
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);  // same value from any racing thread
+  }
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_block_attn(const dflash_dims* dims, const void* q_blk, const void* k_blk, const void* v_blk,
+                      const void* k_cache, const void* v_cache, const int32_t* page_table, const int32_t* ctx_len,
+                      int32_t max_ctx_len, const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                      float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return block_attn_run(dims, q_blk, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, max_ctx_len, rope_cos,
+                        rope_sin, max_pos, out, static_cast<char*>(workspace), workspace_bytes, nullptr, nullptr,
+                        stream);
+}
+
+int dflash_block_attn_noalloc(const dflash_dims* dims, const void* q_blk, const void* k_blk, const void* v_blk,
+                              const void* k_cache, const void* v_cache, const int32_t* page_table,
+                              const int32_t* ctx_len, int32_t max_ctx_len, const float* rope_cos,
+                              const float* rope_sin, int32_t max_pos, float* out, uint32_t* dev_err,
+                              hipStream_t stream) {
+  return block_attn_run(dims, q_blk, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len, max_ctx_len, rope_cos,
+                        rope_sin, max_pos, out, nullptr, kNoAllocScratchBytes, dev_err, scratch_of_current_device,
+                        stream);
 }
 
 // ------------------------------------------------------------------ context projection

@@ -53,6 +53,8 @@ def _load() -> ctypes.CDLL:
         "dflash_block_attn_workspace_size": (_c_sz, [P, _c_int]),
         "dflash_block_attn": (_c_int, [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int,
                                        _vp, _vp, _c_sz, _vp]),
+        "dflash_block_attn_noalloc": (_c_int, [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int,
+                                               _vp, _vp, _vp]),
         "dflash_verify_workspace_size": (_c_sz, [_c_int, _c_int, _c_int]),
         "dflash_draft_argmax": (_c_int, [_c_int, _c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _c_sz, _vp]),
         "dflash_block_qkv_workspace_size": (_c_sz, [P]),
@@ -74,8 +76,9 @@ EXPORTS = (
     "dflash_status_str", "dflash_version", "dflash_rope_tables", "dflash_ctx_proj_workspace_size",
     "dflash_ctx_proj", "dflash_block_attn_workspace_size", "dflash_block_attn",
     "dflash_verify_workspace_size", "dflash_verify_accept", "dflash_draft_argmax",
-    "dflash_block_qkv_workspace_size", "dflash_block_qkv",
+    "dflash_block_qkv_workspace_size", "dflash_block_qkv", "dflash_block_attn_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def _check(fn: str, code: int) -> None:
@@ -216,6 +219,34 @@ def dflash_block_attn(dims: dflash_dims, q_blk: torch.Tensor, k_blk: torch.Tenso
         _dev(rope_sin, "rope_sin", (torch.float32,)), int(rope_cos.shape[0]),
         _dev(out, "out", (torch.float32,)), _dev(workspace, "workspace", (torch.uint8,)),
         workspace.numel(), _stream(stream)))
+
+
+def dflash_block_attn_noalloc(dims: dflash_dims, q_blk: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor,
+                              k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: Optional[torch.Tensor],
+                              ctx_len: torch.Tensor, max_ctx_len: int, rope_cos: torch.Tensor,
+                              rope_sin: torch.Tensor, out: torch.Tensor, dev_err: Optional[torch.Tensor] = None,
+                              stream=None) -> None:
+    """dflash_block_attn on the library's static scratch (no workspace); the device
+    error bits go to dev_err (one int32 on the device) when given."""
+    B, Hq, Hkv, d = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    _numel(q_blk, B * BLOCK * Hq * d, "q_blk")
+    _numel(k_blk, B * BLOCK * Hkv * d, "k_blk")
+    _numel(v_blk, B * BLOCK * Hkv * d, "v_blk")
+    _numel(k_cache, _cache_numel(dims), "k_cache")
+    _numel(v_cache, _cache_numel(dims), "v_cache")
+    if dims.page_size > 0:
+        _numel(page_table, B * dims.kv_capacity, "page_table")
+    _numel(ctx_len, B, "ctx_len")
+    _numel(out, B * BLOCK * Hq * d, "out")
+    _numel(dev_err, 1, "dev_err", at_least=True)
+    _check_rope(rope_cos, rope_sin, d)
+    _check("dflash_block_attn_noalloc", _lib.dflash_block_attn_noalloc(
+        ctypes.byref(dims), _dev(q_blk, "q_blk", _BF16), _dev(k_blk, "k_blk", _BF16),
+        _dev(v_blk, "v_blk", _BF16), _dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16),
+        _dev(page_table, "page_table", (torch.int32,)), _dev(ctx_len, "ctx_len", (torch.int32,)),
+        max_ctx_len, _dev(rope_cos, "rope_cos", (torch.float32,)),
+        _dev(rope_sin, "rope_sin", (torch.float32,)), int(rope_cos.shape[0]),
+        _dev(out, "out", (torch.float32,)), _dev(dev_err, "dev_err", (torch.int32,)), _stream(stream)))
 
 
 def dflash_verify_workspace_size(batch: int, block: int, vocab: int) -> int:

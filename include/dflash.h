@@ -174,6 +174,31 @@ int dflash_block_attn(const dflash_dims* dims, const void* q_blk, const void* k_
                       const float* rope_cos, const float* rope_sin, int32_t max_pos,
                       float* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- block attention without a workspace ----------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): dflash_block_attn with
+ * the workspace replaced by a library-owned scratch array of
+ * DFLASH_NOALLOC_SCRATCH_BYTES per device (a static device array, zero at load,
+ * held until the process ends).  Same arguments, results and errors as
+ * dflash_block_attn, except:
+ *   - no workspace arguments; a call whose dflash_block_attn_workspace_size()
+ *     exceeds DFLASH_NOALLOC_SCRATCH_BYTES returns DFLASH_ERR_WORKSPACE and
+ *     launches nothing (the batched 8 x 8192 and long 32768-token shapes fit;
+ *     a ragged batch of 32 x 16384 does not);
+ *   - dev_err: optional device pointer to a uint32 (4-byte aligned) into which the
+ *     DFLASH_DEVERR_* bits are OR-ed; NULL leaves them in the scratch, unreported;
+ *   - the call allocates nothing (no hipMalloc / hipFree, no allocating library
+ *     routine).  The first call on a device looks the scratch's address up once.
+ * Every call on a device shares that device's scratch: calls that overlap in time
+ * on one device (different streams, or threads) race and give wrong results.
+ * Serialise them, e.g. on one stream. */
+#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int dflash_block_attn_noalloc(const dflash_dims* dims, const void* q_blk, const void* k_blk,
+                              const void* v_blk, const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, const int32_t* ctx_len,
+                              int32_t max_ctx_len, const float* rope_cos, const float* rope_sin,
+                              int32_t max_pos, float* out, uint32_t* dev_err, hipStream_t stream);
+
 /* ---- greedy verify, accept, commit and crop (a7-a9) ----------------------
  * For each sequence b (block == 16):
  *   posterior[b,i] = lowest index of the maximum of logits[b,i,0:vocab]

@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     lib = ctypes.CDLL(dfl.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -312,3 +312,18 @@ def test_deverr_bits_match_the_header():
     assert {k: int(v) for k, v in bits.items()} == {
         "CTX_LEN": dfl.DEVERR_CTX_LEN, "PAGE_ID": dfl.DEVERR_PAGE_ID, "ROW": dfl.DEVERR_ROW,
         "MERGE": dfl.DEVERR_MERGE, "XCD": dfl.DEVERR_XCD}
+
+
+@no_device
+def test_block_attn_noalloc_refuses_sizes_beyond_its_scratch():
+    # A ragged batch of 32 x 16384 tokens needs more split partials than the scratch holds.
+    dims = dfl.make_dims(32, 32, 8, 128, page_size=16, kv_capacity=1100, num_pages=40000)
+    assert dfl.dflash_block_attn_workspace_size(dims, 16384) > dfl.NOALLOC_SCRATCH_BYTES
+    rc = dfl._lib.dflash_block_attn_noalloc(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16384,
+                                            FAKE, FAKE, 16400, FAKE, None, None)
+    assert rc == -4
+    assert dfl._lib.dflash_block_attn_noalloc(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                              16384, FAKE, FAKE, 16400, FAKE, ctypes.c_void_p(0x100002), None) == -3
+    text = open(HEADER).read()
+    assert "#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in text
+    assert dfl.NOALLOC_SCRATCH_BYTES == 32 << 20
