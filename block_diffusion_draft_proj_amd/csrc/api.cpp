@@ -60,7 +60,19 @@ int check_cache_dims(const dflash_dims* d) {
   if (d->page_size != 0 && d->page_size != 16) return DFLASH_ERR_UNSUPPORTED;
   if (d->kv_capacity < 1) return DFLASH_ERR_SHAPE;
   if (d->page_size > 0 && d->num_pages < 1) return DFLASH_ERR_SHAPE;
+  // Sliding window: a ring of `window` rows per (sequence, kv head) inside the
+  // capacity; paged rings hold whole pages.
+  if (d->window < 0) return DFLASH_ERR_SHAPE;
+  if (d->window > 0) {
+    if (d->page_size > 0 ? (d->window % 16 || d->window / 16 > d->kv_capacity) : d->window > d->kv_capacity)
+      return DFLASH_ERR_CAPACITY;
+  }
   return DFLASH_OK;
+}
+
+// Context keys a call attends per sequence at most: the window bounds them.
+int32_t attended_keys(const dflash_dims* d, int32_t max_ctx_len) {
+  return d->window > 0 && d->window < max_ctx_len ? d->window : max_ctx_len;
 }
 
 }  // namespace
@@ -248,7 +260,8 @@ size_t dflash_block_attn_workspace_size(const dflash_dims* dims, int32_t max_ctx
   if (check_cache_dims(dims) != DFLASH_OK || max_ctx_len < 0) return 0;
   if ((int64_t)dims->batch * dims->n_kv_heads > kMaxCountSlots) return 0;
   if (dims->n_q_heads < dims->n_kv_heads || dims->n_q_heads % dims->n_kv_heads) return 0;
-  return plan_block_attn(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim, max_ctx_len, kPlanCUs)
+  return plan_block_attn(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
+                         attended_keys(dims, max_ctx_len), kPlanCUs)
       .ws_bytes;
 }
 
@@ -274,14 +287,14 @@ int block_attn_run(const dflash_dims* dims, const void* q_blk, const void* k_blk
   if (max_ctx_len < 0 || max_ctx_len > (1 << 24)) return DFLASH_ERR_SHAPE;
   const int64_t cap_tokens =
       dims->page_size > 0 ? (int64_t)dims->kv_capacity * dims->page_size : (int64_t)dims->kv_capacity;
-  if (max_ctx_len > cap_tokens) return DFLASH_ERR_CAPACITY;
+  if (dims->window == 0 && max_ctx_len > cap_tokens) return DFLASH_ERR_CAPACITY;
   if ((int64_t)max_pos < (int64_t)max_ctx_len + DFLASH_BLOCK) return DFLASH_ERR_CAPACITY;
   const void* ptrs[] = {q_blk, k_blk, v_blk, k_cache, v_cache, rope_cos, rope_sin, out};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return DFLASH_ERR_ALIGN;
   if (err && (reinterpret_cast<uintptr_t>(err) & 3u)) return DFLASH_ERR_ALIGN;
-  const AttnPlan pl =
-      plan_block_attn(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim, max_ctx_len, kPlanCUs);
+  const AttnPlan pl = plan_block_attn(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
+                                      attended_keys(dims, max_ctx_len), kPlanCUs);
   if ((!ws && !scratch_of_device) || ws_bytes < pl.ws_bytes) return DFLASH_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return DFLASH_ERR_ALIGN;
   const int64_t grid = (int64_t)8 * pl.n_splits * (((int64_t)dims->batch * dims->n_kv_heads + 7) / 8);
@@ -316,6 +329,7 @@ int block_attn_run(const dflash_dims* dims, const void* q_blk, const void* k_blk
   p.capacity = dims->kv_capacity;
   p.num_pages = dims->page_size > 0 ? dims->num_pages : 0;
   p.max_ctx = max_ctx_len;
+  p.window = dims->window;
   p.kps = pl.kps;
   p.n_splits = pl.n_splits;
   p.n_units = dims->batch * dims->n_kv_heads;
@@ -496,6 +510,7 @@ int dflash_ctx_proj(const dflash_dims* dims, int32_t n_rows, const void* const* 
   k.page_size = dims->page_size;
   k.capacity = dims->kv_capacity;
   k.num_pages = dims->page_size > 0 ? dims->num_pages : 0;
+  k.window = dims->window;
   k.err = reinterpret_cast<uint32_t*>(ws);
   return launch_status(launch_kv_epilogue(k, stream));
 }

@@ -83,9 +83,13 @@ __device__ __forceinline__ int vswz(int t) {
   else return 2 * (((t >> 1) & 1) | (((t >> 3) & 1) << 1));
 }
 
-// Paged caches: the page ids of the split come from its page-table slice in LDS
-// (`pt`, entry i = page of tokens 16*(pt0 + i) ..), so no global load precedes a
-// DMA: waiting for one would also wait for every stage load issued before it.
+// Cache row of a key.  `t` is the key's row in the unit's storage order, unwrapped:
+// without a window it is the key's position; with a sliding window of W rows it runs
+// past W where the ring wraps (row t - W), and t < 2W.  Paged caches: the page ids
+// of the split come from its page-table slice in LDS (`pt`, entry i = page of rows
+// 16*(pt0 + i) .. in the same unwrapped order; W is a multiple of 16, so t & 15 is
+// the row in the page), so no global load precedes a DMA: waiting for one would
+// also wait for every stage load issued before it.
 template <bool PAGED>
 __device__ __forceinline__ const uint16_t* key_row(const AttnParams& p, const uint16_t* cache, int b, int g,
                                                    int t, int D, const int32_t LDS_AS* pt, int pt0) {
@@ -97,16 +101,18 @@ __device__ __forceinline__ const uint16_t* key_row(const AttnParams& p, const ui
     }
     return cache + (((int64_t)page * p.n_kv_heads + g) * 16 + (t & 15)) * D;
   } else {
+    if (p.window > 0 && t >= p.window) t -= p.window;
     return cache + (((int64_t)b * p.n_kv_heads + g) * p.capacity + t) * D;
   }
 }
 
 // One wave-wide 1 KB load (index li of the stage's LOADS) of the stage holding keys
 // [t0, t0+TK) of unit (b, g), clamped to tend-1 (rows past the range hold a real,
-// finite key row whose scores are masked, so no stale LDS data can leak in).
+// finite key row whose scores are masked, so no stale LDS data can leak in).  Key t
+// sits in storage row t + roff (unwrapped, see key_row).
 template <int D, bool PAGED>
 __device__ __forceinline__ void issue_load(const AttnParams& p, uint32_t stage, int b, int g, int t0, int tend,
-                                           int li, int lane, const int32_t LDS_AS* pt, int pt0) {
+                                           int li, int lane, const int32_t LDS_AS* pt, int pt0, int roff) {
   using GE = Geo<D>;
   const int rsub = lane / GE::NCH, pch = lane % GE::NCH;
   const bool is_v = li >= GE::LOADS / 2;
@@ -115,7 +121,7 @@ __device__ __forceinline__ void issue_load(const AttnParams& p, uint32_t stage, 
   const int key = min(t0 + row, tend - 1);
   const int c = pch ^ (is_v ? vswz<D>(row) : kswz<D>(row));
   // a 1 KB load covers RPL (4 or 8) aligned rows: never crosses a 16-token page
-  const uint16_t* src = key_row<PAGED>(p, is_v ? p.v_cache : p.k_cache, b, g, key, D, pt, pt0) + c * 8;
+  const uint16_t* src = key_row<PAGED>(p, is_v ? p.v_cache : p.k_cache, b, g, key + roff, D, pt, pt0) + c * 8;
   lds_dma16_nt_m0(src, stage + (is_v ? GE::TILE : 0) + rb * 1024);
 }
 
@@ -253,14 +259,14 @@ constexpr int kMergeSpinLimit = 1 << 20;  // polls of the stored count (~0.5 s) 
 // past the split's last key).
 template <int D, int NW, int NP, bool PAGED>
 __device__ __forceinline__ void issue_pack(const AttnParams& p, uint32_t ring, int b, int g, int kb, int ke, int pk,
-                                           int w, int lane, const int32_t LDS_AS* pt, int pt0) {
+                                           int w, int lane, const int32_t LDS_AS* pt, int pt0, int roff) {
   using GE = Geo<D>;
 #pragma unroll
   for (int li = w; li < NP * GE::LOADS; li += NW) {
     const int sub = li / GE::LOADS;
     const int st = NP * pk + sub;
     issue_load<D, PAGED>(p, ring + (st % NST) * GE::STAGE, b, g, kb + st * TK, ke, li - sub * GE::LOADS, lane, pt,
-                         pt0);
+                         pt0, roff);
   }
 }
 
@@ -360,11 +366,19 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
     if (threadIdx.x == 0 && s == 0) set_dev_error(p.err, kDevErrCtxLen);
     L = L < 0 ? 0 : p.max_ctx;
   }
-  const int ns = L > 0 ? (L + p.kps - 1) / p.kps : 1;
+  // Context keys: the last Lw = min(L, W) positions under a sliding window of W,
+  // else all L.  Key j (0 <= j < Lw) is position L - Lw + j.
+  const int Lw = p.window > 0 ? min(L, p.window) : L;
+  const int ns = Lw > 0 ? (Lw + p.kps - 1) / p.kps : 1;
   if (s >= ns) return;
   const int kb = s * p.kps;
-  const int ke = min(L, kb + p.kps);
+  const int ke = min(Lw, kb + p.kps);
   const bool last_split = (s == ns - 1);
+  // Storage row of key kb: its position, or with a window the position mod W (the
+  // cache is a ring of W rows).  Rows of the split run on from there, unwrapped
+  // (key t in row t + roff, wrapping at W; see key_row).
+  const int sr = p.window > 0 ? (L - Lw + kb) % p.window : kb;
+  const int roff = sr - kb;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -373,13 +387,20 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   const int h = g * G + hw;
 
   // Paged caches: the split's page ids go to LDS first, with plain loads waited for
-  // before any stage load is issued (entries of pages kb/16 .. (ke-1)/16 only: every
-  // index stays inside the sequence's page-table row, since ke <= L <= 16*capacity).
+  // before any stage load is issued: entries of the pages holding rows sr ..
+  // sr + (ke - kb) - 1 only.  Every index stays inside the sequence's page-table row:
+  // without a window the rows are keys < L <= 16*capacity; with one, the column
+  // wraps at W/16 <= capacity (W a multiple of 16, checked on the host).
   const int32_t LDS_AS* pt_lds = (const int32_t LDS_AS*)s_pt;
   if constexpr (PAGED) {
-    const int n_pt = ke > kb ? ((ke - 1) >> 4) - (kb >> 4) + 1 : 0;
-    const int32_t* src = p.page_table + (int64_t)b * p.capacity + (kb >> 4);
-    for (int i = tid; i < n_pt; i += 64 * NW) s_pt[i] = src[i];
+    const int n_pt = ke > kb ? ((sr + (ke - kb) - 1) >> 4) - (sr >> 4) + 1 : 0;
+    const int32_t* src = p.page_table + (int64_t)b * p.capacity;
+    const int wcols = p.window >> 4;
+    for (int i = tid; i < n_pt; i += 64 * NW) {
+      int col = (sr >> 4) + i;
+      if (wcols > 0 && col >= wcols) col -= wcols;
+      s_pt[i] = src[col];
+    }
     __syncthreads();
   }
 
@@ -388,11 +409,12 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   // scalar-base path; the rest clamp per row.
   const int n_st = (ke - kb + TK - 1) / TK;
   const int n_pk = (n_st + NGRP - 1) / NGRP;
-  const int n_fast = PAGED ? 0 : (ke - kb) / (NGRP * TK);  // packs with every key < ke
+  // packs with every key < ke (and, in a ring, every row before the wrap)
+  const int n_fast = PAGED ? 0 : (p.window > 0 ? min(ke - kb, p.window - sr) : ke - kb) / (NGRP * TK);
   const DensePlan<D, NW, NGRP> dpl = dense_plan<D, NW, NGRP>(w, lane);
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(LDS_AS char*)lds;
   const uint32_t qst_lds = lds_ring + NST * GE::STAGE;
-  const int64_t unit_row0 = ((int64_t)b * p.n_kv_heads + g) * p.capacity + kb;  // dense: row of key kb
+  const int64_t unit_row0 = ((int64_t)b * p.n_kv_heads + g) * p.capacity + sr;  // dense: row of key kb
   const char* k_split = reinterpret_cast<const char*>(p.k_cache) + unit_row0 * GE::ROW;
   const char* v_split = reinterpret_cast<const char*>(p.v_cache) + unit_row0 * GE::ROW;
   auto issue = [&](int pk) {
@@ -400,7 +422,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
       const int64_t off = (int64_t)pk * NGRP * TK * GE::ROW;
       issue_pack_dense<D, NW, NGRP>(dpl, k_split + off, v_split + off, lds_ring, pk);
     } else {
-      issue_pack<D, NW, NGRP, PAGED>(p, lds_ring, b, g, kb, ke, pk, w, lane, pt_lds, kb >> 4);
+      issue_pack<D, NW, NGRP, PAGED>(p, lds_ring, b, g, kb, ke, pk, w, lane, pt_lds, sr >> 4, roff);
     }
   };
   constexpr int QL = G * D / 32, CL = D / 32;  // wave loads: Q rows, cos rows (sin the same)
@@ -788,7 +810,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int group
   const int b = u / p.n_kv_heads, g = u - b * p.n_kv_heads;
   int L = p.ctx_len[b];
   L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
-  const int ns = L > 0 ? (L + p.kps - 1) / p.kps : 1;
+  const int Lw = p.window > 0 ? min(L, p.window) : L;
+  const int ns = Lw > 0 ? (Lw + p.kps - 1) / p.kps : 1;
   if (ns == 1) return;  // written directly by the split kernel
   const int tid = threadIdx.x, sg = tid >> 6, rc = tid & 63;
   const int r = rc >> 2, c = rc & 3;  // row, 8-dim chunk of the quarter

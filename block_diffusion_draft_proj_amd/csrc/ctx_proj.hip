@@ -403,22 +403,25 @@ __global__ __launch_bounds__(256) void kv_epilogue_kernel(KvEpilogueParams p) {
   if (pos < 0) return;  // uncommitted block slot
   const int seq = p.row_seq[m];
   const bool paged = p.page_size > 0;
+  // Storage row: the position, or with a sliding window of W rows the position mod W
+  // (a ring; the host checked W against the capacity).
+  const int row = p.window > 0 ? pos % p.window : pos;
   const bool bad = (unsigned)seq >= (unsigned)p.batch || pos >= p.max_pos ||
-                   (paged ? (pos >> 4) >= p.capacity : pos >= p.capacity);
+                   (paged ? (row >> 4) >= p.capacity : row >= p.capacity);
   if (bad) {
     set_dev_error(p.err, kDevErrRow);
     return;
   }
   int64_t row_off;
   if (paged) {
-    const int page = p.page_table[(int64_t)seq * p.capacity + (pos >> 4)];
+    const int page = p.page_table[(int64_t)seq * p.capacity + (row >> 4)];
     if ((unsigned)page >= (unsigned)p.num_pages) {
       set_dev_error(p.err, kDevErrPageId);
       return;
     }
-    row_off = (((int64_t)page * p.n_kv_heads + hh) * 16 + (pos & 15)) * p.head_dim;
+    row_off = (((int64_t)page * p.n_kv_heads + hh) * 16 + (row & 15)) * p.head_dim;
   } else {
-    row_off = (((int64_t)seq * p.n_kv_heads + hh) * p.capacity + pos) * p.head_dim;
+    row_off = (((int64_t)seq * p.n_kv_heads + hh) * p.capacity + row) * p.head_dim;
   }
   const f32x4 c = *reinterpret_cast<const f32x4*>(p.rope_cos + (int64_t)pos * half + j);
   const f32x4 s = *reinterpret_cast<const f32x4*>(p.rope_sin + (int64_t)pos * half + j);

@@ -73,6 +73,7 @@ struct AttnParams {
   int capacity;     // dense rows per (seq, head) | page-table columns
   int num_pages;
   int max_ctx;
+  int window;       // > 0: sliding window of this many positions, cache a ring of that many rows
   int kps;          // context keys per split (multiple of 64)
   int n_splits;     // splits per unit at max_ctx
   int n_units;      // batch * n_kv_heads
@@ -163,6 +164,7 @@ struct KvEpilogueParams {
   uint16_t* v_cache;
   const int32_t* page_table;
   int batch, page_size, capacity, num_pages;
+  int window;          // > 0: position p goes to ring row p mod window
   uint32_t* err;
 };
 hipError_t launch_kv_epilogue(const KvEpilogueParams& p, hipStream_t stream);

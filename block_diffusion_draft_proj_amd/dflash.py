@@ -27,7 +27,7 @@ class dflash_dims(ctypes.Structure):
     _fields_ = [
         ("batch", _c_int), ("block", _c_int), ("n_q_heads", _c_int), ("n_kv_heads", _c_int),
         ("head_dim", _c_int), ("hidden", _c_int), ("page_size", _c_int), ("kv_capacity", _c_int),
-        ("num_pages", _c_int), ("softmax_scale", _c_f),
+        ("num_pages", _c_int), ("softmax_scale", _c_f), ("window", _c_int),
     ]
 
 
@@ -129,9 +129,9 @@ def _check_rope(rope_cos: torch.Tensor, rope_sin: torch.Tensor, head_dim: int) -
 
 def make_dims(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, hidden: int = 0,
               page_size: int = 0, kv_capacity: int = 0, num_pages: int = 0,
-              softmax_scale: float = 0.0) -> dflash_dims:
+              softmax_scale: float = 0.0, window: int = 0) -> dflash_dims:
     return dflash_dims(batch, BLOCK, n_q_heads, n_kv_heads, head_dim, hidden, page_size, kv_capacity,
-                       num_pages, softmax_scale)
+                       num_pages, softmax_scale, window)
 
 
 def dflash_status_str(code: int) -> str:

@@ -104,6 +104,15 @@ typedef struct dflash_dims {
                               paged: page-table columns per sequence             */
     int32_t num_pages;     /* paged: pages in the pool; dense: ignored           */
     float   softmax_scale; /* <= 0 selects 1/sqrt(head_dim)                      */
+    int32_t window;        /* 0: the context is every committed position.  W > 0:
+                              sliding window -- the context is the last min(L, W)
+                              positions and the cache is a ring of W rows per
+                              (sequence, kv head): position p lives in row p mod W
+                              (dense: W <= kv_capacity; paged: W % 16 == 0 and
+                              W / 16 <= kv_capacity, the page table then holding
+                              the ring's W / 16 pages).  Violations return
+                              DFLASH_ERR_CAPACITY.  "DFlash dual
+                              implementations" §3: RotatingKVCache               */
 } dflash_dims;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -126,8 +135,11 @@ int dflash_rope_tables(float base, int32_t head_dim, int32_t max_pos,
  *   C[r]     = bf16(X_cat[r] W_fc^T)                               (hidden)
  *   K[r]     = bf16(RoPE(C[r] W_k^T, row_pos[r])),  V[r] = bf16(C[r] W_v^T)
  * and K[r], V[r] (n_kv_heads x head_dim each) are written to the context cache
- * of sequence row_seq[r] at token position row_pos[r].  Rows with row_pos < 0
- * are computed but not written (uncommitted block slots).  fp32 accumulation.
+ * of sequence row_seq[r] at token position row_pos[r] (with a sliding window W:
+ * ring row row_pos[r] mod W; a call must then not commit two positions of one
+ * sequence W or more apart, whose rows would collide).  Rows with row_pos < 0
+ * are computed but not written (uncommitted block slots).  fp32 accumulation;
+ * K is the bf16 value nearest to the exact rotation of the fp32 product.
  *
  *   x_layers   HOST array of n_layers (1..8) device pointers, each [n_rows][ld_x] bf16
  *   d_target   width of each target layer (multiple of 64); ld_x >= d_target, % 8 == 0
@@ -158,13 +170,17 @@ int dflash_ctx_proj(const dflash_dims* dims, int32_t n_rows,
  *   Keys= [ K_cache[b,g,0:L] ; bf16(RoPE(k_blk[b,:,g])) ]          [L+16, d]
  *   Vals= [ V_cache[b,g,0:L] ; v_blk[b,:,g] ]
  *   out[b,i,h,:] = softmax(Q Keys^T * scale) Vals   over all L+16 keys, no mask.
- * bf16 operands, fp32 accumulation, fp32 output.
+ * bf16 operands, fp32 accumulation, fp32 output.  The rotated Q and block K are
+ * the bf16 values nearest to the exact rotation with the fp32 tables.  With a
+ * sliding window W (dims->window) the context rows are the last Lw = min(L, W)
+ * positions L-Lw .. L-1, read from ring rows (position mod W); the block still
+ * sits at L .. L+15.
  *
  *   q_blk   [B][16][Hq][d] bf16, before RoPE
  *   k_blk   [B][16][Hkv][d] bf16, before RoPE;  v_blk [B][16][Hkv][d] bf16
  *   k_cache, v_cache, page_table: context cache (K already rotated), see dims
  *   ctx_len [B] int32 device; max_ctx_len: host bound >= every ctx_len[b]
- *           (dense: <= kv_capacity; paged: <= kv_capacity*page_size)
+ *           (without a window: dense <= kv_capacity, paged <= kv_capacity*page_size)
  *   rope_*  tables with max_pos >= max_ctx_len + 16
  *   out     [B][16][Hq][d] fp32 */
 size_t dflash_block_attn_workspace_size(const dflash_dims* dims, int32_t max_ctx_len);

@@ -226,21 +226,31 @@ def block_qkv_ref(h: np.ndarray, w_qkv: np.ndarray, n_q_heads: int, n_kv_heads: 
 # --------------------------------------------------------------------------
 def gather_pages(cache: np.ndarray, page_table: np.ndarray, b: int, length: int) -> np.ndarray:
     """Dense [Hkv, length, d] view of sequence b from a paged [P, Hkv, ps, d] cache."""
+    return gather_rows(cache, page_table, b, np.arange(length))
+
+
+def gather_rows(cache: np.ndarray, page_table: Optional[np.ndarray], b: int, rows: np.ndarray) -> np.ndarray:
+    """Storage rows ``rows`` of sequence b as [Hkv, len(rows), d]: from a dense
+    [B, Hkv, cap, d] cache, or through the page table of a paged [P, Hkv, ps, d] one."""
+    rows = np.asarray(rows, dtype=np.int64)
+    if page_table is None:
+        return cache[b][:, rows, :]
     ps = cache.shape[2]
-    t = np.arange(length)
-    pages = page_table[b, t // ps]
-    return np.transpose(cache[pages, :, t % ps, :], (1, 0, 2))
+    pages = page_table[b, rows // ps]
+    return np.transpose(cache[pages, :, rows % ps, :], (1, 0, 2))
 
 
 def block_attn_unit_ref(q_b: np.ndarray, k_b: np.ndarray, v_b: np.ndarray,
                         k_ctx: np.ndarray, v_ctx: np.ndarray, ctx_len: int, g: int,
                         group: int, base: float, scale: Optional[float] = None,
-                        return_probs: bool = False):
+                        return_probs: bool = False, block_pos: Optional[int] = None):
     """Attention of one (sequence, kv head g) unit.
 
     q_b [16, Hq, d], k_b / v_b [16, Hkv, d] bf16 bits (q, k pre-RoPE);
-    k_ctx / v_ctx [>=ctx_len, d] bf16 bits of kv head g (K already rotated).
-    Block positions are ctx_len .. ctx_len+15.  For each q head h of the group:
+    k_ctx / v_ctx [>=ctx_len, d] bf16 bits of kv head g (K already rotated): the
+    first ctx_len rows are the context keys, in position order.  Block positions
+    are block_pos .. block_pos+15 (block_pos defaults to ctx_len; a sliding window
+    passes fewer context rows than the block's position).  For each q head h:
       Q_h   = bf16(RoPE(q_h))                        [16, d]
       Keys  = [K_ctx[0:L] ; bf16(RoPE(k_blk[:, g]))] [L+16, d]
       Vals  = [V_ctx[0:L] ; v_blk[:, g]]
@@ -252,7 +262,7 @@ def block_attn_unit_ref(q_b: np.ndarray, k_b: np.ndarray, v_b: np.ndarray,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     L = int(ctx_len)
-    pos = L + np.arange(BLOCK)
+    pos = (L if block_pos is None else int(block_pos)) + np.arange(BLOCK)
     hs = slice(g * group, (g + 1) * group)
     Q = rope_bf16(q_b[:, hs, :], pos, base)                                      # [16, G, d]
     Kblk = rope_bf16(k_b[:, g:g + 1, :], pos, base)[:, 0, :]
@@ -274,12 +284,19 @@ def block_attn_ref(q_blk: np.ndarray, k_blk: np.ndarray, v_blk: np.ndarray,
                    k_cache: np.ndarray, v_cache: np.ndarray, ctx_len: np.ndarray,
                    base: float, page_table: Optional[np.ndarray] = None,
                    scale: Optional[float] = None,
-                   units: Optional[Sequence[Tuple[int, int]]] = None) -> np.ndarray:
+                   units: Optional[Sequence[Tuple[int, int]]] = None,
+                   window: int = 0) -> np.ndarray:
     """O [B, 16, Hq, d] float64 for every (b, kv head) unit, or only ``units``.
 
     k_cache / v_cache: dense [B, Hkv, cap, d] or, with ``page_table``, paged
     [P, Hkv, page, d]; the oracle gathers pages itself.  Entries of units not
     computed are NaN.
+
+    Sliding window (page "DFlash dual implementations" §3: the MLX side trims a
+    rotating cache).  Reading: with window W > 0 the cache keeps the last W
+    committed positions in a ring of W rows (position t in row t mod W), and the
+    context of sequence b is positions max(0, L-W) .. L-1; the block stays at
+    positions L .. L+15.
     """
     B, _, Hq, d = q_blk.shape
     Hkv = k_blk.shape[2]
@@ -288,13 +305,13 @@ def block_attn_ref(q_blk: np.ndarray, k_blk: np.ndarray, v_blk: np.ndarray,
     todo = units if units is not None else [(b, g) for b in range(B) for g in range(Hkv)]
     for b, g in todo:
         L = int(ctx_len[b])
-        if page_table is None:
-            kc, vc = k_cache[b, g], v_cache[b, g]
-        else:
-            kc = gather_pages(k_cache, page_table, b, L)[g]
-            vc = gather_pages(v_cache, page_table, b, L)[g]
+        first = max(0, L - window) if window > 0 else 0
+        t = np.arange(first, L)                               # context positions
+        rows = t % window if window > 0 else t                # their storage rows
+        kc = gather_rows(k_cache, page_table, b, rows)[g]
+        vc = gather_rows(v_cache, page_table, b, rows)[g]
         out[b, :, g * G:(g + 1) * G, :] = block_attn_unit_ref(
-            q_blk[b], k_blk[b], v_blk[b], kc, vc, L, g, G, base, scale)
+            q_blk[b], k_blk[b], v_blk[b], kc, vc, L - first, g, G, base, scale, block_pos=L)
     return out
 
 
@@ -442,14 +459,16 @@ def rope_brute_bf16(vec: Sequence[float], pos: int, base: float) -> List[float]:
 
 
 def block_attn_brute(q_b, k_b, v_b, k_ctx, v_ctx, ctx_len: int, g: int, group: int,
-                     base: float, scale: Optional[float] = None) -> np.ndarray:
-    """Scalar-loop twin of ``block_attn_unit_ref`` (same arguments), for tiny shapes."""
+                     base: float, scale: Optional[float] = None, first: int = 0) -> np.ndarray:
+    """Scalar-loop twin of ``block_attn_unit_ref`` for tiny shapes: k_ctx / v_ctx
+    hold the rows of positions 0 .. ctx_len-1 in order, and the context keys are
+    positions first .. ctx_len-1 (first > 0: a sliding window)."""
     d = q_b.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     L = int(ctx_len)
     f = lambda a: [float(t) for t in bf16_to_f64(a)]
     keys, vals = [], []
-    for t in range(L):
+    for t in range(first, L):
         keys.append(f(k_ctx[t]))
         vals.append(f(v_ctx[t]))
     for i in range(BLOCK):

@@ -35,18 +35,18 @@ def rope_tables(head_dim: int, max_pos: int, base: float = 1.0e6):
     return cos, sin
 
 
-def attn_dims(cfg: synth.Config, at: "synth.AttnInputs") -> "dfl.dflash_dims":
+def attn_dims(cfg: synth.Config, at: "synth.AttnInputs", window: int = 0) -> "dfl.dflash_dims":
     return dfl.make_dims(len(at.ctx_len), cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, hidden=cfg.hidden,
                          page_size=16 if at.page_table is not None else 0, kv_capacity=at.capacity,
-                         num_pages=at.num_pages)
+                         num_pages=at.num_pages, window=window)
 
 
 def run_block_attn(cfg: synth.Config, at: "synth.AttnInputs", max_ctx=None, ws=None, cos_sin=None,
-                   ctx_len_override=None):
+                   ctx_len_override=None, window=0):
     """Runs dflash_block_attn on device copies of ``at``; returns (out, workspace)."""
     B = len(at.ctx_len)
     max_ctx = int(at.ctx_len.max()) if max_ctx is None else max_ctx
-    dims = attn_dims(cfg, at)
+    dims = attn_dims(cfg, at, window)
     cos, sin = cos_sin if cos_sin is not None else rope_tables(cfg.head_dim, max_ctx + 2 * synth.BLOCK,
                                                               cfg.rope_base)
     if ws is None:

@@ -327,3 +327,19 @@ def test_block_attn_noalloc_refuses_sizes_beyond_its_scratch():
     text = open(HEADER).read()
     assert "#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in text
     assert dfl.NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
+@no_device
+def test_window_validation():
+    d = dfl.make_dims(2, 8, 2, 64, kv_capacity=80, window=81)
+    assert _attn(d) == -5                                   # dense ring wider than the capacity
+    assert _attn(dfl.make_dims(2, 8, 2, 64, kv_capacity=80, window=-1)) == -2
+    p = dfl.make_dims(2, 8, 2, 64, page_size=16, kv_capacity=5, num_pages=10, window=72)
+    assert _attn(p, pt=FAKE) == -5                          # paged ring not whole pages
+    p = dfl.make_dims(2, 8, 2, 64, page_size=16, kv_capacity=5, num_pages=10, window=96)
+    assert _attn(p, pt=FAKE) == -5                          # 6 pages > 5 table columns
+    # with a window the context may exceed the capacity (the ring keeps the last W rows)
+    w = dfl.make_dims(2, 8, 2, 64, kv_capacity=80, window=64)
+    assert dfl.dflash_block_attn_workspace_size(w, 100000) == dfl.dflash_block_attn_workspace_size(w, 64)
+    assert _attn(w, maxc=100000, maxpos=100016, wsb=16) == -4   # past the capacity check, stops at the workspace
+    assert _proj(dfl.make_dims(1, 4, 2, 64, hidden=256, kv_capacity=80, window=100)) == -5

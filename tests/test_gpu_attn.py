@@ -36,11 +36,11 @@ def _paged_copy(at: synth.AttnInputs, seed=0) -> synth.AttnInputs:
                                num_pages=B * width)
 
 
-def _check(cfg, at, units=None, tol=TOL, label=""):
-    out, ws = run_block_attn(cfg, at)
+def _check(cfg, at, units=None, tol=TOL, label="", window=0):
+    out, ws = run_block_attn(cfg, at, window=window)
     got = out.cpu().numpy()
     ref = orc.block_attn_ref(at.q_blk, at.k_blk, at.v_blk, at.k_cache, at.v_cache, at.ctx_len, cfg.rope_base,
-                             page_table=at.page_table, units=units)
+                             page_table=at.page_table, units=units, window=window)
     mask = ~np.isnan(ref)
     err = float(np.max(np.abs(got[mask] - ref[mask])))
     log(f"attn {label}: max-abs err {err:.3e}")
@@ -169,3 +169,37 @@ def test_attn_workspace_serves_growing_and_shrinking_batches():
         assert err <= TOL, err
         assert ws[:4].cpu().numpy().view(np.uint32)[0] == 0
     assert not ws[256:256 + 128 * 12].any()          # every counter back at zero
+
+
+# Sliding window (ring of W rows per unit, position t in row t mod W): the context is
+# the last min(L, W) positions.  Cases: the ring wraps inside a split, sequences shorter
+# than W, W == L, a window smaller than one 64-key pack, several splits, and more than
+# 8 splits (the separate merge kernel).  The caches hold unrelated values in every row,
+# so a wrong ring row shows up as a wrong result.
+WINDOW = [  # (L per sequence, W, Hq, Hkv, d)
+    ([3000, 700], 1008, 8, 2, 128), ([5000, 4100], 4096, 32, 8, 128), ([64, 17, 200], 48, 4, 2, 64),
+    ([1000], 1000, 4, 4, 128), ([2100, 33], 112, 8, 1, 64),
+]
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("case", WINDOW, ids=lambda c: f"L{c[0]}_W{c[1]}_h{c[2]}x{c[3]}_d{c[4]}")
+def test_attn_sliding_window(case, paged):
+    lens, W, hq, hkv, d = case
+    if paged:
+        W = (W + 15) // 16 * 16
+    cfg = dataclasses.replace(synth.CONFIGS["qwen3_8b"], n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                              seed=hash((tuple(lens), W, hq, d)) & 0xFFFF)
+    at = synth.attn_inputs(cfg, ctx_len=np.array(lens), page_size=0)
+    assert at.capacity >= W
+    if paged:
+        at = _paged_copy(at, seed=W)
+    _check(cfg, at, label=f"window {case} paged={paged}", window=W)
+
+
+def test_attn_sliding_window_many_splits():
+    # 32768-key window over a 40000-token context at B=1: 32 splits, merged by the
+    # separate kernel; the ring wraps at 40000 mod 32768 = 7232.
+    cfg = synth.CONFIGS["long_ctx"]
+    at = synth.attn_inputs(cfg, ctx_len=np.array([40000]))
+    _check(cfg, at, label="long context, window 32768 of 40000", window=32768)

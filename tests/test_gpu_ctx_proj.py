@@ -58,17 +58,17 @@ def _commit_positions(kv_len, rng):
 
 
 def _run(cfg, n_rows, row_seq, row_pos, capacity, paged_table=None, num_pages=0, with_fc=True,
-         c_out=True, seed=None, ld_pad=0):
+         c_out=True, seed=None, ld_pad=0, window=0):
     pj = synth.ctx_proj_inputs(cfg, n_rows, seed=seed)
     Hkv, d, D = cfg.n_kv_heads, cfg.head_dim, cfg.hidden
     B = cfg.batch
     if paged_table is None:
         kc = torch.zeros(B, Hkv, capacity, d, dtype=torch.int16, device=DEV)
-        dims = dfl.make_dims(B, cfg.n_q_heads, Hkv, d, hidden=D, kv_capacity=capacity)
+        dims = dfl.make_dims(B, cfg.n_q_heads, Hkv, d, hidden=D, kv_capacity=capacity, window=window)
     else:
         kc = torch.zeros(num_pages, Hkv, 16, d, dtype=torch.int16, device=DEV)
         dims = dfl.make_dims(B, cfg.n_q_heads, Hkv, d, hidden=D, page_size=16,
-                             kv_capacity=paged_table.shape[1], num_pages=num_pages)
+                             kv_capacity=paged_table.shape[1], num_pages=num_pages, window=window)
     vc = torch.zeros_like(kc)
     max_pos = int(max(np.max(row_pos), 0)) + 32
     cos, sin = rope_tables(d, max_pos, cfg.rope_base)
@@ -99,22 +99,26 @@ def _run(cfg, n_rows, row_seq, row_pos, capacity, paged_table=None, num_pages=0,
     return ref, host_u16(kc), host_u16(vc), (None if cbuf is None else host_u16(cbuf)), err
 
 
-def _gather_rows(cache, row_seq, row_pos, table=None):
-    """[n_live, Hkv, d] cache rows at the committed (seq, pos) of each live row."""
+def _gather_rows(cache, row_seq, row_pos, table=None, window=0):
+    """[n_live, Hkv, d] cache rows at the committed (seq, pos) of each live row (ring row
+    pos mod window under a sliding window)."""
     live = np.nonzero(row_pos >= 0)[0]
     rows = []
     for m in live:
         s, p = int(row_seq[m]), int(row_pos[m])
+        if window:
+            p %= window
         rows.append(cache[s, :, p] if table is None else cache[table[s, p // 16], :, p % 16])
     return live, orc.bf16_to_f64(np.stack(rows))
 
 
-def _check(cfg, n_rows, row_seq, row_pos, capacity, table=None, num_pages=0, with_fc=True, label="", ld_pad=0):
+def _check(cfg, n_rows, row_seq, row_pos, capacity, table=None, num_pages=0, with_fc=True, label="", ld_pad=0,
+           window=0):
     ref, kc, vc, cb, err = _run(cfg, n_rows, row_seq, row_pos, capacity, table, num_pages, with_fc,
-                                ld_pad=ld_pad)
+                                ld_pad=ld_pad, window=window)
     assert err == 0
-    live, k = _gather_rows(kc, row_seq, row_pos, table)
-    _, v = _gather_rows(vc, row_seq, row_pos, table)
+    live, k = _gather_rows(kc, row_seq, row_pos, table, window)
+    _, v = _gather_rows(vc, row_seq, row_pos, table, window)
     _close(k, ref["K"][live], label + " K")
     _close(v, ref["V"][live], label + " V")
     # only committed rows were written
@@ -238,3 +242,20 @@ def test_ctx_proj_skinny_rows_strided_layers():
     pos = np.tile(np.arange(16, dtype=np.int32), cfg.batch) + 200
     pos[5::16] = -1
     _check(cfg, n, seq, pos, capacity=240, label="batched block rows, ld_x > d_target", ld_pad=128)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_ctx_proj_sliding_window_ring_rows(paged):
+    # Committed rows of 8 sequences straddle the ring's wrap (window 96 rows): position
+    # p goes to row p mod 96, and nothing else in the ring is written.
+    cfg = synth.CONFIGS["batched"]
+    W = 96
+    kv_len = np.array([90, 85, 95, 96, 1000, 190, 5, 300], np.int32)
+    pos = _commit_positions(kv_len, np.random.default_rng(4))
+    seq = np.repeat(np.arange(cfg.batch, dtype=np.int32), 16)
+    if paged:
+        table = np.random.default_rng(5).permutation(cfg.batch * W // 16).astype(np.int32).reshape(cfg.batch, -1)
+        _check(cfg, 16 * cfg.batch, seq, pos, capacity=0, table=table, num_pages=cfg.batch * W // 16,
+               label="window 96, paged ring", window=W)
+    else:
+        _check(cfg, 16 * cfg.batch, seq, pos, capacity=W, label="window 96, dense ring", window=W)

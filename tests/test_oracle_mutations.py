@@ -27,6 +27,10 @@ MUTANTS = {
                         "return (np.cos(th), np.sin(th))"),
     "rope_no_two_sum": ("r[tie] = s[tie] + np.sign(e[tie]) * half[tie]", "r[tie] = r[tie]"),
     "rope_sum_sign": ("round_bf16_sum(lo * c, -(hi * s))", "round_bf16_sum(lo * c, hi * s)"),
+    "window_first": ("first = max(0, L - window) if window > 0 else 0",
+                     "first = max(0, L - window + 1) if window > 0 else 0"),
+    "window_ring_rows": ("rows = t % window if window > 0 else t", "rows = t"),
+    "window_block_pos": ("L - first, g, G, base, scale, block_pos=L)", "L - first, g, G, base, scale)"),
     "drop_block_keys": ("Keys = np.concatenate([bf16_to_f64(k_ctx[:L]), Kblk], axis=0)\n"
                         "    Vals = np.concatenate([bf16_to_f64(v_ctx[:L]), bf16_to_f64(v_b[:, g, :])], axis=0)",
                         "Keys = bf16_to_f64(k_ctx[:L+16])\n    Vals = bf16_to_f64(v_ctx[:L+16])"),
@@ -35,9 +39,10 @@ MUTANTS = {
     "accept_alignment": ("matches = (blk[:, 1:] == post[:, :BLOCK - 1])",
                          "matches = (blk[:, :BLOCK - 1] == post[:, :BLOCK - 1])"),
     "commit_count": ("kv_out = (kv_in + 1 + accept)", "kv_out = (kv_in + accept)"),
-    "block_positions": ("pos = L + np.arange(BLOCK)\n    hs", "pos = L + 1 + np.arange(BLOCK)\n    hs"),
-    "wrong_kv_head": ("kc, vc = k_cache[b, g], v_cache[b, g]",
-                      "kc, vc = k_cache[b, (g + 1) % Hkv], v_cache[b, (g + 1) % Hkv]"),
+    "block_positions": ("pos = (L if block_pos is None else int(block_pos)) + np.arange(BLOCK)",
+                        "pos = (L if block_pos is None else int(block_pos)) + 1 + np.arange(BLOCK)"),
+    "wrong_kv_head": ("kc = gather_rows(k_cache, page_table, b, rows)[g]\n        vc = gather_rows(v_cache, page_table, b, rows)[g]",
+                      "kc = gather_rows(k_cache, page_table, b, rows)[(g + 1) % Hkv]\n        vc = gather_rows(v_cache, page_table, b, rows)[(g + 1) % Hkv]"),
     "c_not_rounded": ("Cb = round_bf16(C)", "Cb = C"),
     "commit_positions": ("np.where(i <= accept[:, None]", "np.where(i < accept[:, None]"),
     "draft_alignment": ("blk[b, 1:] = argmax_first(bf16_to_f64(draft_logits[b, 1:]))",

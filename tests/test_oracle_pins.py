@@ -470,6 +470,68 @@ def test_attn_paged_equals_dense():
     assert np.array_equal(a, b)
 
 
+def _ring(linear: np.ndarray, W: int) -> np.ndarray:
+    """[W, d] ring holding positions 0..n-1 written in order (later ones overwrite)."""
+    ring = np.full((W,) + linear.shape[1:], 0x7FC0, np.uint16)      # NaN where never written
+    for t in range(linear.shape[0]):
+        ring[t % W] = linear[t]
+    return ring
+
+
+@pytest.mark.parametrize("L,W", [(9, 4), (20, 7), (5, 5), (3, 8), (0, 4), (33, 16)])
+def test_attn_window_ring_equals_brute_force_on_the_last_w_positions(L, W):
+    # Rows written position by position into a ring of W rows; the windowed oracle must
+    # equal a scalar brute force that takes positions max(0, L-W) .. L-1 from the linear
+    # history directly.
+    rng = np.random.default_rng(18 + L + W)
+    G, d, Hkv = 2, 8, 1
+    enc = orc.f64_to_bf16_bits
+    q = enc(rng.standard_normal((16, G, d)))
+    k = enc(rng.standard_normal((16, Hkv, d)))
+    v = enc(rng.standard_normal((16, Hkv, d)))
+    kl = enc(rng.standard_normal((L, d)) * 2)
+    vl = enc(rng.standard_normal((L, d)) * 2)
+    kc = _ring(kl, W)[None, None]
+    vc = _ring(vl, W)[None, None]
+    got = orc.block_attn_ref(q[None], k[None], v[None], kc, vc, np.array([L]), 1e6, window=W)[0]
+    want = orc.block_attn_brute(q, k, v, kl, vl, L, 0, G, 1e6, first=max(0, L - W))
+    assert np.allclose(got, want, atol=1e-12)
+
+
+def test_attn_window_at_least_the_context_changes_nothing():
+    cfg = synth.CONFIGS["tiny"]
+    at = synth.attn_inputs(cfg, ctx_len=np.array([37, 64, 3]))
+    base = orc.block_attn_ref(at.q_blk, at.k_blk, at.v_blk, at.k_cache, at.v_cache, at.ctx_len, 1e6)
+    for W in (64, at.k_cache.shape[2]):
+        win = orc.block_attn_ref(at.q_blk, at.k_blk, at.v_blk, at.k_cache, at.v_cache, at.ctx_len, 1e6, window=W)
+        assert np.array_equal(win, base)
+    short = orc.block_attn_ref(at.q_blk, at.k_blk, at.v_blk, at.k_cache, at.v_cache, at.ctx_len, 1e6, window=20)
+    assert np.array_equal(short[2], base[2])            # L = 3 <= 20: unchanged
+    assert not np.allclose(short[0], base[0])           # L = 37 > 20: fewer keys
+
+
+def test_attn_window_paged_ring_equals_dense_ring():
+    rng = np.random.default_rng(19)
+    B, Hkv, G, d, W = 2, 2, 2, 16, 48
+    enc = orc.f64_to_bf16_bits
+    q = enc(rng.standard_normal((B, 16, Hkv * G, d)))
+    k = enc(rng.standard_normal((B, 16, Hkv, d)))
+    v = enc(rng.standard_normal((B, 16, Hkv, d)))
+    kc = enc(rng.standard_normal((B, Hkv, W, d)))
+    vc = enc(rng.standard_normal((B, Hkv, W, d)))
+    ctx = np.array([100, 30])
+    table = rng.permutation(B * W // 16).reshape(B, W // 16).astype(np.int32)
+    kp = np.zeros((B * W // 16, Hkv, 16, d), np.uint16)
+    vp = np.zeros_like(kp)
+    for b in range(B):
+        for r in range(W):
+            kp[table[b, r // 16], :, r % 16] = kc[b, :, r]
+            vp[table[b, r // 16], :, r % 16] = vc[b, :, r]
+    a = orc.block_attn_ref(q, k, v, kc, vc, ctx, 1e6, window=W)
+    b_ = orc.block_attn_ref(q, k, v, kp, vp, ctx, 1e6, page_table=table, window=W)
+    assert np.array_equal(a, b_)
+
+
 # ----------------------------------------------------------------------------- verify / accept
 @pytest.mark.parametrize("case", _golden("accept_cases.txt"), ids=lambda c: c["name"])
 def test_accept_golden_cases(case):
