@@ -389,6 +389,58 @@ def draft_block_ref(draft_logits: np.ndarray, staged: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# The rest of a draft layer around the attention (page "DFlash dual
+# implementations", §1 model definition: the draft model reuses Qwen3's RMSNorm,
+# MLP and rotary embedding; §2: the attention).  Reading: a pre-norm residual
+# decoder layer --
+#   n1 = RMSNorm(x; w_in)                       -> the block q/k/v projection
+#   x1 = x + bf16(attn) W_o^T                   (o_proj, residual add)
+#   n2 = RMSNorm(x1; w_post)
+#   x2 = x1 + (silu(n2 W_gate^T) * (n2 W_up^T)) W_down^T    (SwiGLU MLP)
+# with RMSNorm(x; w) = x / sqrt(mean(x^2) + eps) * w, silu(g) = g / (1 + e^-g),
+# no biases, and every tensor a bf16 model stores between the steps (attn
+# output, x1, n1 / n2, the MLP activation, x2) rounded once to bf16; all
+# arithmetic in between is float64 here.
+# --------------------------------------------------------------------------
+def rmsnorm_ref(x: np.ndarray, w_bits: np.ndarray, eps: float) -> np.ndarray:
+    """bf16(x / sqrt(mean(x^2) + eps) * w) per row of float64 values x [M, D], as float64."""
+    x = np.asarray(x, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return round_bf16(x * r * bf16_to_f64(w_bits))
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    return g / (1.0 + np.exp(-g))
+
+
+def draft_layer_post_ref(x_bits: np.ndarray, attn: np.ndarray, w_o: np.ndarray, w_post: np.ndarray,
+                         w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, eps: float) -> dict:
+    """The layer after the attention, for M = 16 B block rows.
+
+    x_bits [M, D] bf16 bits (the layer's input, the residual); attn [M, Hq*d] the
+    attention output (float values, rounded to bf16 here); weights bf16 bits in
+    nn.Linear layout: w_o [D, Hq*d], w_gate / w_up [I, D], w_down [D, I]; w_post [D].
+    Returns float64 arrays: a, x1, n2, g, u, act, x2_exact, x2 (= bf16(x2_exact)).
+    """
+    a = round_bf16(np.asarray(attn, dtype=np.float64))
+    x1 = round_bf16(bf16_to_f64(x_bits) + a @ bf16_to_f64(w_o).T)
+    n2 = rmsnorm_ref(x1, w_post, eps)
+    g = n2 @ bf16_to_f64(w_gate).T
+    u = n2 @ bf16_to_f64(w_up).T
+    act = round_bf16(silu(g) * u)
+    x2 = x1 + act @ bf16_to_f64(w_down).T
+    return {"a": a, "x1": x1, "n2": n2, "g": g, "u": u, "act": act, "x2_exact": x2, "x2": round_bf16(x2)}
+
+
+def rmsnorm_brute(row: Sequence[float], w: Sequence[float], eps: float) -> List[float]:
+    """Scalar twin of ``rmsnorm_ref`` for one row (exact rational sum of squares)."""
+    ss = sum(Fraction(float(v)) ** 2 for v in row)
+    ms = float(ss / len(row)) + eps
+    r = 1.0 / math.sqrt(ms)
+    return [float(round_bf16(np.array([float(v) * r * float(wj)]))[0]) for v, wj in zip(row, w)]
+
+
+# --------------------------------------------------------------------------
 # Brute-force twins for tiny shapes: scalar Python loops, float64 math.
 # --------------------------------------------------------------------------
 def argmax_brute(row: Sequence[float]) -> int:

@@ -31,6 +31,17 @@ MUTANTS = {
                      "first = max(0, L - window + 1) if window > 0 else 0"),
     "window_ring_rows": ("rows = t % window if window > 0 else t", "rows = t"),
     "window_block_pos": ("L - first, g, G, base, scale, block_pos=L)", "L - first, g, G, base, scale)"),
+    "rms_no_square": ("r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
+                      "r = 1.0 / np.sqrt(np.mean(np.abs(x), axis=-1, keepdims=True) + eps)"),
+    "rms_no_eps": ("r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
+                   "r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True))"),
+    "silu_sign": ("return g / (1.0 + np.exp(-g))", "return g / (1.0 + np.exp(g))"),
+    "layer_no_residual": ("x1 = round_bf16(bf16_to_f64(x_bits) + a @ bf16_to_f64(w_o).T)",
+                          "x1 = round_bf16(a @ bf16_to_f64(w_o).T)"),
+    "layer_gate_up_swapped": ("act = round_bf16(silu(g) * u)", "act = round_bf16(silu(u) * g)"),
+    "layer_act_not_rounded": ("act = round_bf16(silu(g) * u)", "act = silu(g) * u"),
+    "layer_w_o_transposed": ("x1 = round_bf16(bf16_to_f64(x_bits) + a @ bf16_to_f64(w_o).T)",
+                             "x1 = round_bf16(bf16_to_f64(x_bits) + a @ bf16_to_f64(w_o))"),
     "drop_block_keys": ("Keys = np.concatenate([bf16_to_f64(k_ctx[:L]), Kblk], axis=0)\n"
                         "    Vals = np.concatenate([bf16_to_f64(v_ctx[:L]), bf16_to_f64(v_b[:, g, :])], axis=0)",
                         "Keys = bf16_to_f64(k_ctx[:L+16])\n    Vals = bf16_to_f64(v_ctx[:L+16])"),

@@ -532,6 +532,115 @@ def test_attn_window_paged_ring_equals_dense_ring():
     assert np.array_equal(a, b_)
 
 
+# ----------------------------------------------------------------------------- draft layer
+def test_rmsnorm_constant_rows_closed_form():
+    w = orc.f64_to_bf16_bits(np.ones(64))
+    for c in (2.0, -0.75, 1e-3):
+        x = np.full((1, 64), c)
+        got = orc.rmsnorm_ref(x, w, 0.0)
+        assert np.all(got == np.sign(c))                       # c / |c| exactly
+        eps = 1e-6
+        want = float(orc.round_bf16(np.array([c / math.sqrt(c * c + eps)]))[0])
+        assert np.all(orc.rmsnorm_ref(x, w, eps) == want)
+    assert float(orc.round_bf16(np.array([1e-3 / math.sqrt(1e-6 + 1e-6)]))[0]) == \
+        orc.rmsnorm_ref(np.full((1, 64), 1e-3), w, 1e-6)[0, 0]  # eps matters at small rms
+
+
+def test_rmsnorm_scale_invariant_and_unit_rms():
+    rng = np.random.default_rng(40)
+    x = orc.round_bf16(rng.standard_normal((7, 256)) * 3)
+    w = orc.f64_to_bf16_bits(np.ones(256))
+    y = orc.rmsnorm_ref(x, w, 0.0)
+    for alpha in (0.25, 8.0, 2.0 ** -20):
+        assert np.array_equal(orc.rmsnorm_ref(x * alpha, w, 0.0), y)
+    assert np.all(np.abs(np.sqrt(np.mean(y * y, axis=1)) - 1) < 2 ** -8)
+
+
+def test_rmsnorm_matches_scalar_brute_force_with_weights():
+    rng = np.random.default_rng(41)
+    x = orc.round_bf16(rng.standard_normal((3, 48)))
+    wb = orc.f64_to_bf16_bits(1 + 0.1 * rng.standard_normal(48))
+    got = orc.rmsnorm_ref(x, wb, 1e-6)
+    w = orc.bf16_to_f64(wb)
+    for i in range(3):
+        assert got[i].tolist() == orc.rmsnorm_brute(list(x[i]), list(w), 1e-6)
+
+
+def test_silu_closed_forms():
+    x = np.array([0.0, 1.0, -1.0, 30.0, -30.0, 2.5])
+    y = orc.silu(x)
+    assert y[0] == 0.0
+    assert abs(y[1] - 1 / (1 + math.exp(-1))) < 1e-15
+    assert np.allclose(orc.silu(x) - orc.silu(-x), x, atol=1e-14)   # silu(x) - silu(-x) = x
+    assert abs(y[3] - 30.0) < 1e-11 and abs(y[4]) < 1e-11
+
+
+def _layer_inputs(rng, M=16, D=64, Hd=48, I=96, wstd=0.1):
+    enc = orc.f64_to_bf16_bits
+    return dict(x=enc(rng.standard_normal((M, D))), attn=rng.standard_normal((M, Hd)) * 0.5,
+                w_o=enc(rng.standard_normal((D, Hd)) * wstd), w_post=enc(1 + 0.1 * rng.standard_normal(D)),
+                w_gate=enc(rng.standard_normal((I, D)) * wstd), w_up=enc(rng.standard_normal((I, D)) * wstd),
+                w_down=enc(rng.standard_normal((D, I)) * wstd))
+
+
+def test_draft_layer_post_zero_attention_and_zero_down_is_identity():
+    rng = np.random.default_rng(42)
+    li = _layer_inputs(rng)
+    li["attn"] = np.zeros_like(li["attn"])
+    li["w_down"] = np.zeros_like(li["w_down"])
+    r = orc.draft_layer_post_ref(li["x"], li["attn"], li["w_o"], li["w_post"], li["w_gate"], li["w_up"],
+                                 li["w_down"], 1e-6)
+    assert np.array_equal(r["x1"], orc.bf16_to_f64(li["x"]))
+    assert np.array_equal(r["x2"], orc.bf16_to_f64(li["x"]))
+
+
+def test_draft_layer_post_identity_weights_closed_form():
+    # W_o = W_gate = W_up = W_down = I (D = Hq*d = I): x1 = bf16(x + bf16(a)),
+    # x2 = bf16(x1 + bf16(silu(n2) * n2)) with n2 = RMSNorm(x1)
+    rng = np.random.default_rng(43)
+    D = 32
+    eye = orc.f64_to_bf16_bits(np.eye(D))
+    li = _layer_inputs(rng, D=D, Hd=D, I=D)
+    r = orc.draft_layer_post_ref(li["x"], li["attn"], eye, li["w_post"], eye, eye, eye, 1e-6)
+    x = orc.bf16_to_f64(li["x"])
+    a = orc.round_bf16(li["attn"])
+    w = orc.bf16_to_f64(li["w_post"])
+    for i in range(4):
+        x1 = [float(orc.round_bf16(np.array([x[i, j] + a[i, j]]))[0]) for j in range(D)]
+        n2 = orc.rmsnorm_brute(x1, list(w), 1e-6)
+        act = [float(orc.round_bf16(np.array([v / (1 + math.exp(-v)) * v]))[0]) for v in n2]
+        x2 = [float(orc.round_bf16(np.array([x1[j] + act[j]]))[0]) for j in range(D)]
+        assert r["x1"][i].tolist() == x1 and r["x2"][i].tolist() == x2
+
+
+def test_draft_layer_post_mlp_increment_is_linear_in_w_down_and_swiglu_order():
+    rng = np.random.default_rng(44)
+    li = _layer_inputs(rng)
+    args = [li["x"], li["attn"], li["w_o"], li["w_post"], li["w_gate"], li["w_up"]]
+    r1 = orc.draft_layer_post_ref(*args, li["w_down"], 1e-6)
+    w2 = orc.f64_to_bf16_bits(orc.bf16_to_f64(li["w_down"]) * 2)      # exact doubling
+    r2 = orc.draft_layer_post_ref(*args, w2, 1e-6)
+    assert np.allclose(r2["x2_exact"] - r2["x1"], 2 * (r1["x2_exact"] - r1["x1"]), rtol=1e-12, atol=1e-12)
+    # the gate goes through silu, the up projection does not: swapping them changes the result
+    r3 = orc.draft_layer_post_ref(li["x"], li["attn"], li["w_o"], li["w_post"], li["w_up"], li["w_gate"],
+                                  li["w_down"], 1e-6)
+    assert not np.allclose(r3["act"], r1["act"])
+    # scalar check of one MLP output element
+    n2, wg, wu, wd = r1["n2"], orc.bf16_to_f64(li["w_gate"]), orc.bf16_to_f64(li["w_up"]), orc.bf16_to_f64(li["w_down"])
+    i, j = 3, 5
+    acts = []
+    for k in range(wg.shape[0]):
+        g = sum(n2[i, t] * wg[k, t] for t in range(n2.shape[1]))
+        u = sum(n2[i, t] * wu[k, t] for t in range(n2.shape[1]))
+        acts.append(float(orc.round_bf16(np.array([g / (1 + math.exp(-g)) * u]))[0]))
+    want = r1["x1"][i, j] + sum(acts[k] * wd[j, k] for k in range(len(acts)))
+    assert abs(r1["x2_exact"][i, j] - want) < 1e-12
+    # ... and of one o_proj output: x1[i, j] = bf16(x[i, j] + sum_t bf16(a[i, t]) W_o[j, t])
+    a, wo = orc.round_bf16(li["attn"]), orc.bf16_to_f64(li["w_o"])
+    x1 = orc.bf16_to_f64(li["x"])[i, j] + sum(a[i, t] * wo[j, t] for t in range(a.shape[1]))
+    assert r1["x1"][i, j] == float(orc.round_bf16(np.array([x1]))[0])
+
+
 # ----------------------------------------------------------------------------- verify / accept
 @pytest.mark.parametrize("case", _golden("accept_cases.txt"), ids=lambda c: c["name"])
 def test_accept_golden_cases(case):
