@@ -515,4 +515,89 @@ int dflash_ctx_proj(const dflash_dims* dims, int32_t n_rows, const void* const* 
   return launch_status(launch_kv_epilogue(k, stream));
 }
 
+// ------------------------------------------------------------------ draft layer around the attention
+int dflash_rmsnorm(int32_t rows, int32_t hidden, const void* x, int64_t ld_x, const void* weight, float eps,
+                   void* out, int64_t ld_out, hipStream_t stream) {
+  if (!x || !weight || !out) return DFLASH_ERR_NULL;
+  if (rows < 0 || rows > (1 << 24) || hidden < 8 || hidden % 8 || hidden > (1 << 20)) return DFLASH_ERR_SHAPE;
+  if (ld_x < hidden || ld_out < hidden || !(eps >= 0.f) || !isfinite(eps)) return DFLASH_ERR_SHAPE;
+  if ((ld_x & 7) || (ld_out & 7) || !aligned16(x) || !aligned16(weight) || !aligned16(out)) return DFLASH_ERR_ALIGN;
+  if (rows == 0) return DFLASH_OK;
+  const int st = check_device();
+  if (st != DFLASH_OK) return st;
+  RmsNormParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.ld_x = ld_x;
+  p.w = static_cast<const uint16_t*>(weight);
+  p.eps = eps;
+  p.out = static_cast<uint16_t*>(out);
+  p.ld_out = ld_out;
+  p.rows = rows;
+  p.cols = hidden;
+  return launch_status(launch_rmsnorm(p, stream));
+}
+
+static int check_layer_dims(const dflash_dims* dims, int32_t intermediate) {
+  if (!dims) return DFLASH_ERR_NULL;
+  if (dims->batch < 1 || (int64_t)dims->batch * DFLASH_BLOCK > (1 << 22) || dims->block != DFLASH_BLOCK)
+    return DFLASH_ERR_SHAPE;
+  if (dims->n_q_heads < 1 || dims->n_q_heads > 1024) return DFLASH_ERR_SHAPE;
+  if (dims->head_dim != 64 && dims->head_dim != 128) return DFLASH_ERR_UNSUPPORTED;
+  if (dims->hidden < 64 || dims->hidden % 64 || dims->hidden > 16384) return DFLASH_ERR_SHAPE;
+  if (intermediate < 64 || intermediate % 64 || intermediate > (1 << 17)) return DFLASH_ERR_SHAPE;
+  return DFLASH_OK;
+}
+
+size_t dflash_draft_layer_post_workspace_size(const dflash_dims* dims, int32_t intermediate) {
+  if (check_layer_dims(dims, intermediate) != DFLASH_OK) return 0;
+  return plan_draft_layer_post(dims->batch * DFLASH_BLOCK, dims->hidden, dims->n_q_heads * dims->head_dim,
+                               intermediate, kPlanCUs)
+      .ws_bytes;
+}
+
+int dflash_draft_layer_post(const dflash_dims* dims, int32_t intermediate, const void* x, const float* attn_out,
+                            const void* w_o, const void* w_post_norm, const void* w_gate, const void* w_up,
+                            const void* w_down, float eps, void* x_out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  int st = check_layer_dims(dims, intermediate);
+  if (st != DFLASH_OK) return st;
+  if (!x || !attn_out || !w_o || !w_post_norm || !w_gate || !w_up || !w_down || !x_out) return DFLASH_ERR_NULL;
+  if (!(eps >= 0.f) || !isfinite(eps)) return DFLASH_ERR_SHAPE;
+  const void* ptrs[] = {x, attn_out, w_o, w_post_norm, w_gate, w_up, w_down, x_out};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DFLASH_ERR_ALIGN;
+  const int M = dims->batch * DFLASH_BLOCK, D = dims->hidden, A = dims->n_q_heads * dims->head_dim;
+  const LayerPlan pl = plan_draft_layer_post(M, D, A, intermediate, kPlanCUs);
+  if (!workspace || workspace_bytes < pl.ws_bytes) return DFLASH_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DFLASH_ERR_ALIGN;
+  st = check_device();
+  if (st != DFLASH_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  LayerPostParams p{};
+  p.M = M;
+  p.hidden = D;
+  p.attn_cols = A;
+  p.inter = intermediate;
+  p.eps = eps;
+  p.x = static_cast<const uint16_t*>(x);
+  p.attn = attn_out;
+  p.w_o = static_cast<const uint16_t*>(w_o);
+  p.w_post = static_cast<const uint16_t*>(w_post_norm);
+  p.w_gate = static_cast<const uint16_t*>(w_gate);
+  p.w_up = static_cast<const uint16_t*>(w_up);
+  p.w_down = static_cast<const uint16_t*>(w_down);
+  p.x_out = static_cast<uint16_t*>(x_out);
+  p.a_bf16 = reinterpret_cast<uint16_t*>(ws + pl.off_a);
+  p.part_o = reinterpret_cast<float*>(ws + pl.off_po);
+  p.x1 = reinterpret_cast<uint16_t*>(ws + pl.off_x1);
+  p.n2 = reinterpret_cast<uint16_t*>(ws + pl.off_n2);
+  p.part_gu = reinterpret_cast<float*>(ws + pl.off_pgu);
+  p.act = reinterpret_cast<uint16_t*>(ws + pl.off_act);
+  p.part_d = reinterpret_cast<float*>(ws + pl.off_pd);
+  p.splits_o = pl.o.splits;
+  p.splits_gu = pl.gu.splits;
+  p.splits_d = pl.dn.splits;
+  return launch_status(launch_draft_layer_post(p, pl, stream));
+}
+
 }  // extern "C"

@@ -169,4 +169,44 @@ struct KvEpilogueParams {
 };
 hipError_t launch_kv_epilogue(const KvEpilogueParams& p, hipStream_t stream);
 
+// ---------------------------------------------------------------- draft layer around the attention
+struct RmsNormParams {
+  const uint16_t* x;
+  int64_t ld_x;
+  const uint16_t* w;
+  float eps;
+  uint16_t* out;
+  int64_t ld_out;
+  int rows, cols;
+};
+hipError_t launch_rmsnorm(const RmsNormParams& p, hipStream_t stream);
+
+struct LayerPostParams {
+  int M, hidden, attn_cols, inter;  // rows (16 B), D, Hq*d, I
+  float eps;
+  const uint16_t* x;        // [M][D] layer input (residual)
+  const float* attn;        // [M][attn_cols] attention output
+  const uint16_t* w_o;      // [D][attn_cols]
+  const uint16_t* w_post;   // [D]
+  const uint16_t* w_gate;   // [I][D]
+  const uint16_t* w_up;     // [I][D]
+  const uint16_t* w_down;   // [D][I]
+  uint16_t* x_out;          // [M][D]
+  // workspace pieces
+  uint16_t* a_bf16;         // [M][attn_cols]
+  float* part_o;            // [splits_o][M][D]
+  uint16_t* x1;             // [M][D]
+  uint16_t* n2;             // [M][D]
+  float* part_gu;           // [splits_gu][M][2I]
+  uint16_t* act;            // [M][I]
+  float* part_d;            // [splits_d][M][D]
+  int splits_o, splits_gu, splits_d;
+};
+struct LayerPlan {
+  QkvPlan o, gu, dn;        // split plans of the three products
+  size_t off_a, off_po, off_x1, off_n2, off_pgu, off_act, off_pd, ws_bytes;
+};
+LayerPlan plan_draft_layer_post(int rows, int hidden, int attn_cols, int inter, int num_cu);
+hipError_t launch_draft_layer_post(const LayerPostParams& p, const LayerPlan& pl, hipStream_t stream);
+
 }  // namespace dflash

@@ -55,6 +55,10 @@ def _load() -> ctypes.CDLL:
                                        _vp, _vp, _c_sz, _vp]),
         "dflash_block_attn_noalloc": (_c_int, [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int,
                                                _vp, _vp, _vp]),
+        "dflash_rmsnorm": (_c_int, [_c_int, _c_int, _vp, _c_i64, _vp, _c_f, _vp, _c_i64, _vp]),
+        "dflash_draft_layer_post_workspace_size": (_c_sz, [P, _c_int]),
+        "dflash_draft_layer_post": (_c_int, [P, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_f, _vp, _vp, _c_sz,
+                                             _vp]),
         "dflash_verify_workspace_size": (_c_sz, [_c_int, _c_int, _c_int]),
         "dflash_draft_argmax": (_c_int, [_c_int, _c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _c_sz, _vp]),
         "dflash_block_qkv_workspace_size": (_c_sz, [P]),
@@ -77,6 +81,7 @@ EXPORTS = (
     "dflash_ctx_proj", "dflash_block_attn_workspace_size", "dflash_block_attn",
     "dflash_verify_workspace_size", "dflash_verify_accept", "dflash_draft_argmax",
     "dflash_block_qkv_workspace_size", "dflash_block_qkv", "dflash_block_attn_noalloc",
+    "dflash_rmsnorm", "dflash_draft_layer_post_workspace_size", "dflash_draft_layer_post",
 )
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -314,6 +319,40 @@ def dflash_draft_argmax(logits: torch.Tensor, staged: Optional[torch.Tensor], bl
     _check("dflash_draft_argmax", _lib.dflash_draft_argmax(
         B, blk, ld if vocab is None else vocab, _dev(logits, "logits", _BF16), ld,
         _dev(staged, "staged", (torch.int32,)), _dev(block_tokens, "block_tokens", (torch.int32,)),
+        _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
+
+
+def dflash_rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, out: torch.Tensor, stream=None) -> None:
+    """out[r] = bf16(RMSNorm(x[r]; weight)): x, out [rows, >= hidden] with unit inner stride."""
+    if x.dim() != 2 or out.dim() != 2 or x.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("x and out must be [rows, ld] tensors with unit inner stride")
+    rows, hidden = int(x.shape[0]), int(weight.numel())
+    if x.shape[1] < hidden or tuple(out.shape) != (rows, int(out.shape[1])) or out.shape[1] < hidden \
+            or out.shape[0] != rows:
+        raise ValueError(f"x and out must hold {rows} rows of at least {hidden} features")
+    _check("dflash_rmsnorm", _lib.dflash_rmsnorm(
+        rows, hidden, _dev(x, "x", _BF16, contiguous=False), int(x.stride(0)), _dev(weight, "weight", _BF16),
+        float(eps), _dev(out, "out", _BF16, contiguous=False), int(out.stride(0)), _stream(stream)))
+
+
+def dflash_draft_layer_post_workspace_size(dims: dflash_dims, intermediate: int) -> int:
+    return int(_lib.dflash_draft_layer_post_workspace_size(ctypes.byref(dims), intermediate))
+
+
+def dflash_draft_layer_post(dims: dflash_dims, intermediate: int, x: torch.Tensor, attn_out: torch.Tensor,
+                            w_o: torch.Tensor, w_post_norm: torch.Tensor, w_gate: torch.Tensor,
+                            w_up: torch.Tensor, w_down: torch.Tensor, eps: float, x_out: torch.Tensor,
+                            workspace: torch.Tensor, stream=None) -> None:
+    """o_proj + residual, RMSNorm, SwiGLU MLP + residual over the 16*batch block rows."""
+    M, D, A, I = BLOCK * dims.batch, dims.hidden, dims.n_q_heads * dims.head_dim, intermediate
+    for name, t, n in (("x", x, M * D), ("attn_out", attn_out, M * A), ("w_o", w_o, D * A),
+                       ("w_post_norm", w_post_norm, D), ("w_gate", w_gate, I * D), ("w_up", w_up, I * D),
+                       ("w_down", w_down, D * I), ("x_out", x_out, M * D)):
+        _numel(t, n, name)
+    _check("dflash_draft_layer_post", _lib.dflash_draft_layer_post(
+        ctypes.byref(dims), I, _dev(x, "x", _BF16), _dev(attn_out, "attn_out", (torch.float32,)),
+        _dev(w_o, "w_o", _BF16), _dev(w_post_norm, "w_post_norm", _BF16), _dev(w_gate, "w_gate", _BF16),
+        _dev(w_up, "w_up", _BF16), _dev(w_down, "w_down", _BF16), float(eps), _dev(x_out, "x_out", _BF16),
         _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
 
 

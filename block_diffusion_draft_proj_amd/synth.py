@@ -58,6 +58,11 @@ class Config:
     page_size: int                # 0 = dense cache, 16 = paged
     seed: int
     rope_base: float = 1.0e6
+    intermediate: int = 0         # draft MLP width I (0: 3 x hidden)
+
+    @property
+    def inter(self) -> int:
+        return self.intermediate or 3 * self.hidden
 
     @property
     def group(self) -> int:
@@ -80,10 +85,14 @@ class Config:
 
 CONFIGS: Dict[str, Config] = {
     "tiny": Config("tiny", 1, 64, None, 256, 4, 2, 64, 2, 256, 1024, 0.15, 0, 1001),
-    "qwen3_8b": Config("qwen3_8b", 1, 2048, None, 4096, 32, 8, 128, 5, 4096, 151936, 0.10, 0, 1002),
-    "batched": Config("batched", 8, 8192, None, 4096, 32, 8, 128, 5, 4096, 151936, 0.10, 0, 1003),
-    "long_ctx": Config("long_ctx", 1, 32768, None, 5120, 40, 8, 128, 5, 5120, 151936, 0.10, 0, 1004),
-    "ragged": Config("ragged", 32, None, (512, 16384), 4096, 32, 8, 128, 5, 4096, 151936, 0.10, 16, 1005),
+    "qwen3_8b": Config("qwen3_8b", 1, 2048, None, 4096, 32, 8, 128, 5, 4096, 151936, 0.10, 0, 1002,
+                       intermediate=12288),
+    "batched": Config("batched", 8, 8192, None, 4096, 32, 8, 128, 5, 4096, 151936, 0.10, 0, 1003,
+                      intermediate=12288),
+    "long_ctx": Config("long_ctx", 1, 32768, None, 5120, 40, 8, 128, 5, 5120, 151936, 0.10, 0, 1004,
+                       intermediate=17408),
+    "ragged": Config("ragged", 32, None, (512, 16384), 4096, 32, 8, 128, 5, 4096, 151936, 0.10, 16, 1005,
+                     intermediate=12288),
 }
 
 
@@ -268,3 +277,37 @@ def block_qkv_inputs(cfg: Config, batch: Optional[int] = None, seed: Optional[in
     h = normal_bf16(rngs["x_blk"], (B * BLOCK, cfg.hidden), 1.0)
     w = normal_bf16(rngs["w_q"], (n_out, cfg.hidden), w_std)
     return BlockQkvInputs(cfg, h, w)
+
+
+@dataclasses.dataclass
+class DraftLayerInputs:
+    cfg: Config
+    x: np.ndarray               # [16 B, D] bf16 bits: the layer's input (the residual stream)
+    attn: np.ndarray            # [16 B, Hq d] float32: an attention output
+    w_in: np.ndarray            # [D] bf16 bits: input RMSNorm weight
+    w_o: np.ndarray             # [D, Hq d]
+    w_post: np.ndarray          # [D]: post-attention RMSNorm weight
+    w_gate: np.ndarray          # [I, D]
+    w_up: np.ndarray            # [I, D]
+    w_down: np.ndarray          # [D, I]
+    eps: float = 1e-6
+
+
+def draft_layer_inputs(cfg: Config, batch: Optional[int] = None, seed: Optional[int] = None,
+                       attn_std: float = 0.5) -> DraftLayerInputs:
+    """Random weights of a Qwen3-shaped draft layer: projections N(0, 0.02^2), norm
+    weights N(1, 0.05^2); the layer input N(0, 1) and an attention output
+    N(0, attn_std^2) in float32 (a weighted mean of value rows is narrower than
+    the rows themselves)."""
+    rngs = streams((cfg.seed if seed is None else seed) + 77)
+    B = cfg.batch if batch is None else batch
+    M, D, A, I = B * BLOCK, cfg.hidden, cfg.n_q_heads * cfg.head_dim, cfg.inter
+    x = normal_bf16(rngs["x_blk"], (M, D), 1.0)
+    attn = rngs["tail"].standard_normal((M, A), dtype=np.float32) * np.float32(attn_std)
+    w_in = f32_to_bf16_bits(1 + 0.05 * rngs["w_k"].standard_normal(D, dtype=np.float32))
+    w_post = f32_to_bf16_bits(1 + 0.05 * rngs["w_k"].standard_normal(D, dtype=np.float32))
+    w_o = normal_bf16(rngs["w_q"], (D, A), 0.02)
+    w_gate = normal_bf16(rngs["w_fc"], (I, D), 0.02)
+    w_up = normal_bf16(rngs["w_fc"], (I, D), 0.02)
+    w_down = normal_bf16(rngs["w_v"], (D, I), 0.02)
+    return DraftLayerInputs(cfg, x, attn, w_in, w_o, w_post, w_gate, w_up, w_down)

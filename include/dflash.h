@@ -286,6 +286,41 @@ int dflash_draft_argmax(int32_t batch, int32_t block, int32_t vocab,
                         int32_t* block_tokens, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
+/* ---- the rest of a draft layer around the attention ------------------------
+ * The draft model reuses Qwen3's RMSNorm and MLP around its attention ("DFlash
+ * dual implementations", §1 model definition).  A pre-norm residual layer over
+ * the M = 16 * batch block rows (sequence-major), x the layer's input:
+ *   n1 = RMSNorm(x; w_in)                 -> dflash_rmsnorm, then dflash_block_qkv
+ *   attn = dflash_block_attn(q, k, v, ...)
+ *   x1 = x + bf16(attn) W_o^T,  n2 = RMSNorm(x1; w_post)
+ *   x_out = x1 + bf16(silu(n2 W_gate^T) * (n2 W_up^T)) W_down^T
+ * RMSNorm(x; w) = x / sqrt(mean(x^2) + eps) * w;  silu(g) = g / (1 + exp(-g)).
+ * No biases.  Every stored tensor is bf16 (rounded to nearest even), products
+ * accumulate in fp32, the RMSNorm factor is computed in fp64. */
+
+/* out[r] = bf16(RMSNorm(x[r]; weight)) for r < rows.
+ *   x [rows][ld_x] bf16, weight [hidden] bf16, out [rows][ld_out] bf16;
+ *   hidden % 8 == 0, ld_x, ld_out >= hidden and % 8 == 0; eps >= 0.
+ * No workspace.  out may equal x only if ld_out == ld_x (rows are independent). */
+int dflash_rmsnorm(int32_t rows, int32_t hidden, const void* x, int64_t ld_x, const void* weight,
+                   float eps, void* out, int64_t ld_out, hipStream_t stream);
+
+/* o_proj + residual, RMSNorm, SwiGLU MLP + residual (the layer after the attention).
+ *   dims          uses batch, n_q_heads, head_dim, hidden (a multiple of 64, <= 16384)
+ *   intermediate  I, the MLP width (a multiple of 64, <= 131072)
+ *   x             [16*batch][hidden] bf16, the layer's input (the residual)
+ *   attn_out      [batch][16][n_q_heads][head_dim] fp32, dflash_block_attn's output
+ *   w_o           [hidden][n_q_heads*head_dim] bf16;  w_post_norm [hidden] bf16
+ *   w_gate, w_up  [I][hidden] bf16;  w_down [hidden][I] bf16 (nn.Linear layouts)
+ *   x_out         [16*batch][hidden] bf16 (must not overlap x)
+ * The workspace holds the intermediate tensors and split-K partial sums; it keeps
+ * no state between calls. */
+size_t dflash_draft_layer_post_workspace_size(const dflash_dims* dims, int32_t intermediate);
+int dflash_draft_layer_post(const dflash_dims* dims, int32_t intermediate, const void* x,
+                            const float* attn_out, const void* w_o, const void* w_post_norm,
+                            const void* w_gate, const void* w_up, const void* w_down, float eps,
+                            void* x_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
