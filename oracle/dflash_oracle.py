@@ -441,6 +441,72 @@ def rmsnorm_brute(row: Sequence[float], w: Sequence[float], eps: float) -> List[
 
 
 # --------------------------------------------------------------------------
+# Rollback of recurrent (GatedDeltaNet) state by tape replay (page "dflash-mlx:
+# lossless speculative decoding", guarantee 3: verifying the block advances the
+# recurrent state by all 16 candidate steps; the state cannot be cropped, so
+# during the verify an "innovation tape" of per-step k, g and increments is
+# recorded, and after acceptance only the accepted steps are replayed onto the
+# state saved before the block; page "DFlash dual implementations" §7: the state
+# is rolled back along the accepted prefix).
+# Reading: the gated delta rule of Gated DeltaNet (Yang, Kautz, Hatamizadeh,
+# "Gated Delta Networks", ICLR 2025), per head, state S [d_v, d_k]:
+#   alpha_t = exp(g_t),  delta_t = beta_t (v_t - alpha_t S_{t-1} k_t)   (innovation)
+#   S_t = alpha_t S_{t-1} + delta_t k_t^T
+# The tape holds (k_t, g_t, delta_t); replay of the committed steps t = 0..a
+# (the staged token and a accepted drafts) needs no S k product.
+# --------------------------------------------------------------------------
+def gdn_block_ref(S0: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray,
+                  beta: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """The verify's pass over the 16 block steps of one head, float64.
+
+    S0 [d_v, d_k]; k [16, d_k]; v [16, d_v]; g, beta [16].  Returns the states
+    after each step [16, d_v, d_k] and the innovations delta [16, d_v]."""
+    S = np.asarray(S0, dtype=np.float64).copy()
+    states, delta = [], []
+    for t in range(k.shape[0]):
+        alpha = math.exp(float(g[t]))
+        d = float(beta[t]) * (v[t] - alpha * (S @ k[t]))
+        S = alpha * S + np.outer(d, k[t])
+        states.append(S.copy())
+        delta.append(d)
+    return np.stack(states), np.stack(delta)
+
+
+def gdn_replay_ref(S0: np.ndarray, k_tape: np.ndarray, g_tape: np.ndarray, delta_tape: np.ndarray,
+                   accept: np.ndarray) -> np.ndarray:
+    """Rolled-back states [B, H, d_v, d_k]: S = S0[b, h], then for t = 0..accept[b]:
+    S = exp(g[b, t, h]) S + delta[b, t, h] k[b, t, h]^T.
+
+    S0 [B, H, d_v, d_k] float; k_tape [B, 16, H, d_k] bf16 bits; g_tape [B, 16, H] and
+    delta_tape [B, 16, H, d_v] float; accept [B] in [0, 15]."""
+    out = np.array(S0, dtype=np.float64)
+    k = bf16_to_f64(k_tape)
+    B = out.shape[0]
+    for b in range(B):
+        for t in range(int(accept[b]) + 1):
+            alpha = np.exp(np.asarray(g_tape[b, t], dtype=np.float64))          # [H]
+            d = np.asarray(delta_tape[b, t], dtype=np.float64)                  # [H, d_v]
+            out[b] = alpha[:, None, None] * out[b] + d[:, :, None] * k[b, t][:, None, :]
+    return out
+
+
+def gdn_block_brute(S0, k, v, g, beta) -> List[np.ndarray]:
+    """Scalar twin of ``gdn_block_ref`` in the delta rule's matrix form,
+    S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T, with loops."""
+    dv, dk = len(S0), len(S0[0])
+    S = [[float(S0[i][j]) for j in range(dk)] for i in range(dv)]
+    out = []
+    for t in range(len(k)):
+        a, bt = math.exp(float(g[t])), float(beta[t])
+        P = [[a * ((1.0 if r == c else 0.0) - bt * float(k[t][r]) * float(k[t][c])) for c in range(dk)]
+             for r in range(dk)]
+        S = [[sum(S[i][r] * P[r][j] for r in range(dk)) + bt * float(v[t][i]) * float(k[t][j])
+              for j in range(dk)] for i in range(dv)]
+        out.append(np.array(S))
+    return out
+
+
+# --------------------------------------------------------------------------
 # Brute-force twins for tiny shapes: scalar Python loops, float64 math.
 # --------------------------------------------------------------------------
 def argmax_brute(row: Sequence[float]) -> int:

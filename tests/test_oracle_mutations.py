@@ -42,6 +42,14 @@ MUTANTS = {
     "layer_act_not_rounded": ("act = round_bf16(silu(g) * u)", "act = silu(g) * u"),
     "layer_w_o_transposed": ("x1 = round_bf16(bf16_to_f64(x_bits) + a @ bf16_to_f64(w_o).T)",
                              "x1 = round_bf16(bf16_to_f64(x_bits) + a @ bf16_to_f64(w_o))"),
+    "replay_off_by_one": ("for t in range(int(accept[b]) + 1):", "for t in range(int(accept[b])):"),
+    "replay_no_decay": ("out[b] = alpha[:, None, None] * out[b] + d[:, :, None] * k[b, t][:, None, :]",
+                        "out[b] = out[b] + d[:, :, None] * k[b, t][:, None, :]"),
+    "replay_outer_transposed": ("out[b] = alpha[:, None, None] * out[b] + d[:, :, None] * k[b, t][:, None, :]",
+                                "out[b] = alpha[:, None, None] * out[b] + (d[:, :, None] * k[b, t][:, None, :])"
+                                "[:, ::-1, ::-1]"),
+    "gdn_innovation_no_alpha": ("d = float(beta[t]) * (v[t] - alpha * (S @ k[t]))",
+                                "d = float(beta[t]) * (v[t] - (S @ k[t]))"),
     "drop_block_keys": ("Keys = np.concatenate([bf16_to_f64(k_ctx[:L]), Kblk], axis=0)\n"
                         "    Vals = np.concatenate([bf16_to_f64(v_ctx[:L]), bf16_to_f64(v_b[:, g, :])], axis=0)",
                         "Keys = bf16_to_f64(k_ctx[:L+16])\n    Vals = bf16_to_f64(v_ctx[:L+16])"),

@@ -641,6 +641,83 @@ def test_draft_layer_post_mlp_increment_is_linear_in_w_down_and_swiglu_order():
     assert r1["x1"][i, j] == float(orc.round_bf16(np.array([x1]))[0])
 
 
+# ----------------------------------------------------------------------------- recurrent-state tape replay
+def _gdn_head(rng, dk=6, dv=5, T=16):
+    k = rng.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)          # Gated DeltaNet normalises its keys
+    v = rng.standard_normal((T, dv))
+    g = -np.abs(rng.standard_normal(T)) * 0.3              # log-gates < 0: alpha in (0, 1)
+    beta = 1 / (1 + np.exp(-rng.standard_normal(T)))       # write strength in (0, 1)
+    return rng.standard_normal((dv, dk)), k, v, g, beta
+
+
+def test_gdn_block_matches_matrix_form_brute_force():
+    rng = np.random.default_rng(50)
+    S0, k, v, g, beta = _gdn_head(rng)
+    states, _ = orc.gdn_block_ref(S0, k, v, g, beta)
+    brute = orc.gdn_block_brute(S0.tolist(), k.tolist(), v.tolist(), g, beta)
+    for t in range(16):
+        assert np.allclose(states[t], brute[t], atol=1e-12, rtol=1e-12)
+
+
+def test_gdn_replay_of_the_accepted_steps_equals_the_state_after_them():
+    # Tape recorded by the block pass; replaying steps 0..a from the saved state must
+    # give the block pass's own state after step a, for every a (matrix-form twin).
+    rng = np.random.default_rng(51)
+    B, H, dk, dv = 3, 2, 6, 5
+    S0 = np.zeros((B, H, dv, dk))
+    ks = np.zeros((B, 16, H, dk), np.uint16)
+    gs = np.zeros((B, 16, H))
+    ds = np.zeros((B, 16, H, dv))
+    want = np.zeros((B, 16, H, dv, dk))
+    for b in range(B):
+        for h in range(H):
+            S, k, v, g, beta = _gdn_head(rng, dk, dv)
+            kb = orc.f64_to_bf16_bits(k)                    # the tape stores k in bf16
+            k = orc.bf16_to_f64(kb)
+            states, delta = orc.gdn_block_ref(S, k, v, g, beta)
+            brute = orc.gdn_block_brute(S.tolist(), k.tolist(), v.tolist(), g, beta)
+            S0[b, h], ks[b, :, h], gs[b, :, h], ds[b, :, h] = S, kb, g, delta
+            want[b, :, h] = np.stack(brute)
+    for a in range(16):
+        got = orc.gdn_replay_ref(S0, ks, gs, ds, np.full(B, a))
+        assert np.allclose(got, want[:, a], atol=1e-11)
+    mixed = orc.gdn_replay_ref(S0, ks, gs, ds, np.array([0, 15, 7]))
+    assert np.allclose(mixed, np.stack([want[0, 0], want[1, 15], want[2, 7]]), atol=1e-11)
+
+
+def test_gdn_delta_rule_memorises_orthonormal_keys():
+    # alpha = 1, beta = 1, orthonormal keys: after the writes, S k_t = v_t for every
+    # written key (each write replaces the value stored under its key).
+    rng = np.random.default_rng(52)
+    dk = dv = 16
+    Q, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Q.T                                               # 16 orthonormal keys
+    v = rng.standard_normal((16, dv))
+    states, _ = orc.gdn_block_ref(rng.standard_normal((dv, dk)), k, v, np.zeros(16), np.ones(16))
+    for a in (0, 5, 15):
+        for t in range(a + 1):
+            assert np.allclose(states[a] @ k[t], v[t], atol=1e-12)
+
+
+def test_gdn_zero_gate_forgets_everything_before():
+    # alpha_t = 0 at step 4 erases the earlier state: replaying from two different saved
+    # states gives the same result from step 4 on.
+    rng = np.random.default_rng(53)
+    _, k, v, g, beta = _gdn_head(rng, 4, 3)
+    g[4] = -np.inf
+    kb = orc.f64_to_bf16_bits(k)[None, :, None]
+    ga = np.asarray(g)[None, :, None]
+    _, delta = orc.gdn_block_ref(np.zeros((3, 4)), orc.bf16_to_f64(kb[0, :, 0]), v, g, beta)
+    da = delta[None, :, None]
+    s1 = orc.gdn_replay_ref(rng.standard_normal((1, 1, 3, 4)), kb, ga, da, np.array([9]))
+    s2 = orc.gdn_replay_ref(rng.standard_normal((1, 1, 3, 4)), kb, ga, da, np.array([9]))
+    assert np.array_equal(s1, s2)
+    s3 = orc.gdn_replay_ref(rng.standard_normal((1, 1, 3, 4)), kb, ga, da, np.array([3]))
+    s4 = orc.gdn_replay_ref(rng.standard_normal((1, 1, 3, 4)), kb, ga, da, np.array([3]))
+    assert not np.allclose(s3, s4)
+
+
 # ----------------------------------------------------------------------------- verify / accept
 @pytest.mark.parametrize("case", _golden("accept_cases.txt"), ids=lambda c: c["name"])
 def test_accept_golden_cases(case):
