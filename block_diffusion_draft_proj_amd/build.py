@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "lib", "libdflash.so")
 
-SOURCES = ["api.cpp", "verify.hip", "rope.hip", "block_attn.hip", "ctx_proj.hip", "draft_layer.hip"]
+SOURCES = ["api.cpp", "verify.hip", "rope.hip", "block_attn.hip", "ctx_proj.hip", "draft_layer.hip", "gdn_replay.hip"]
 
 # Packed fp32 VALU forms are kept out of generated code (see the design notes).
 HIP_FLAGS = [

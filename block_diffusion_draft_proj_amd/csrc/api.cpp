@@ -600,4 +600,38 @@ int dflash_draft_layer_post(const dflash_dims* dims, int32_t intermediate, const
   return launch_status(launch_draft_layer_post(p, pl, stream));
 }
 
+// ------------------------------------------------------------------ recurrent-state tape replay
+int dflash_gdn_tape_replay(int32_t batch, int32_t n_heads, int32_t d_k, int32_t d_v, const float* state_in,
+                           float* state_out, const void* k_tape, const float* g_tape, const float* delta_tape,
+                           const int32_t* accept_len, uint32_t* dev_err, hipStream_t stream) {
+  if (!state_in || !state_out || !k_tape || !g_tape || !delta_tape || !accept_len) return DFLASH_ERR_NULL;
+  if (batch < 1 || n_heads < 1 || (int64_t)batch * n_heads > (1 << 24)) return DFLASH_ERR_SHAPE;
+  if (d_k < 4 || d_k > 256 || d_k % 4 || d_v < 1 || d_v > 4096) return DFLASH_ERR_SHAPE;
+  const void* ptrs[] = {state_in, state_out, k_tape, g_tape, delta_tape};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return DFLASH_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(accept_len) & 3u) || (reinterpret_cast<uintptr_t>(dev_err) & 3u))
+    return DFLASH_ERR_ALIGN;
+  // The state is replayed in place when state_out == state_in; partial overlap is not allowed.
+  const size_t state_bytes = sizeof(float) * (size_t)batch * n_heads * d_v * d_k;
+  const char* si = reinterpret_cast<const char*>(state_in);
+  const char* so = reinterpret_cast<const char*>(state_out);
+  if (si != so && si < so + state_bytes && so < si + state_bytes) return DFLASH_ERR_SHAPE;
+  const int st = check_device();
+  if (st != DFLASH_OK) return st;
+  GdnReplayParams p{};
+  p.batch = batch;
+  p.n_heads = n_heads;
+  p.dk = d_k;
+  p.dv = d_v;
+  p.state_in = state_in;
+  p.state_out = state_out;
+  p.k_tape = static_cast<const uint16_t*>(k_tape);
+  p.g_tape = g_tape;
+  p.delta_tape = delta_tape;
+  p.accept_len = accept_len;
+  p.err = dev_err;
+  return launch_status(launch_gdn_replay(p, stream));
+}
+
 }  // extern "C"

@@ -161,7 +161,7 @@ __device__ __forceinline__ uint32_t xcc_id() {
 
 // Device-side error bits (workspace word 0), as declared in the public header.
 constexpr uint32_t kDevErrCtxLen = 1u, kDevErrPageId = 2u, kDevErrRow = 4u, kDevErrMerge = 8u,
-                   kDevErrXcd = 16u;
+                   kDevErrXcd = 16u, kDevErrAccept = 32u;
 
 __device__ __forceinline__ void set_dev_error(uint32_t* err_word, uint32_t bit) {
   __hip_atomic_fetch_or(err_word, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -209,4 +209,17 @@ struct LayerPlan {
 LayerPlan plan_draft_layer_post(int rows, int hidden, int attn_cols, int inter, int num_cu);
 hipError_t launch_draft_layer_post(const LayerPostParams& p, const LayerPlan& pl, hipStream_t stream);
 
+// ---------------------------------------------------------------- recurrent-state tape replay
+struct GdnReplayParams {
+  int batch, n_heads, dk, dv;
+  const float* state_in;     // [B][H][dv][dk] fp32
+  float* state_out;          // same layout; may alias state_in
+  const uint16_t* k_tape;    // [B][16][H][dk] bf16
+  const float* g_tape;       // [B][16][H]
+  const float* delta_tape;   // [B][16][H][dv]
+  const int32_t* accept_len; // [B]
+  uint32_t* err;             // optional sticky error word
+};
+hipError_t launch_gdn_replay(const GdnReplayParams& p, hipStream_t stream);
+
 }  // namespace dflash

@@ -18,7 +18,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libdflash.so")
 
 BLOCK = 16
-DEVERR_CTX_LEN, DEVERR_PAGE_ID, DEVERR_ROW, DEVERR_MERGE, DEVERR_XCD = 1, 2, 4, 8, 16
+DEVERR_CTX_LEN, DEVERR_PAGE_ID, DEVERR_ROW, DEVERR_MERGE, DEVERR_XCD, DEVERR_ACCEPT = 1, 2, 4, 8, 16, 32
 
 _c_int, _c_i64, _c_sz, _c_f, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
 
@@ -59,6 +59,7 @@ def _load() -> ctypes.CDLL:
         "dflash_draft_layer_post_workspace_size": (_c_sz, [P, _c_int]),
         "dflash_draft_layer_post": (_c_int, [P, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_f, _vp, _vp, _c_sz,
                                              _vp]),
+        "dflash_gdn_tape_replay": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
         "dflash_verify_workspace_size": (_c_sz, [_c_int, _c_int, _c_int]),
         "dflash_draft_argmax": (_c_int, [_c_int, _c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _c_sz, _vp]),
         "dflash_block_qkv_workspace_size": (_c_sz, [P]),
@@ -82,6 +83,7 @@ EXPORTS = (
     "dflash_verify_workspace_size", "dflash_verify_accept", "dflash_draft_argmax",
     "dflash_block_qkv_workspace_size", "dflash_block_qkv", "dflash_block_attn_noalloc",
     "dflash_rmsnorm", "dflash_draft_layer_post_workspace_size", "dflash_draft_layer_post",
+    "dflash_gdn_tape_replay",
 )
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -354,6 +356,26 @@ def dflash_draft_layer_post(dims: dflash_dims, intermediate: int, x: torch.Tenso
         _dev(w_o, "w_o", _BF16), _dev(w_post_norm, "w_post_norm", _BF16), _dev(w_gate, "w_gate", _BF16),
         _dev(w_up, "w_up", _BF16), _dev(w_down, "w_down", _BF16), float(eps), _dev(x_out, "x_out", _BF16),
         _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
+
+
+def dflash_gdn_tape_replay(state_in: torch.Tensor, state_out: torch.Tensor, k_tape: torch.Tensor,
+                           g_tape: torch.Tensor, delta_tape: torch.Tensor, accept_len: torch.Tensor,
+                           dev_err: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Recurrent state after the accepted steps: state [B, H, d_v, d_k] fp32 (out may be in),
+    k_tape [B, 16, H, d_k] bf16, g_tape [B, 16, H] fp32, delta_tape [B, 16, H, d_v] fp32."""
+    if state_in.dim() != 4:
+        raise ValueError("state_in must be [batch, n_heads, d_v, d_k]")
+    B, H, dv, dk = (int(x) for x in state_in.shape)
+    for name, t, n in (("state_out", state_out, B * H * dv * dk), ("k_tape", k_tape, B * BLOCK * H * dk),
+                       ("g_tape", g_tape, B * BLOCK * H), ("delta_tape", delta_tape, B * BLOCK * H * dv),
+                       ("accept_len", accept_len, B)):
+        _numel(t, n, name)
+    _numel(dev_err, 1, "dev_err", at_least=True)
+    _check("dflash_gdn_tape_replay", _lib.dflash_gdn_tape_replay(
+        B, H, dk, dv, _dev(state_in, "state_in", (torch.float32,)), _dev(state_out, "state_out", (torch.float32,)),
+        _dev(k_tape, "k_tape", _BF16), _dev(g_tape, "g_tape", (torch.float32,)),
+        _dev(delta_tape, "delta_tape", (torch.float32,)), _dev(accept_len, "accept_len", (torch.int32,)),
+        _dev(dev_err, "dev_err", (torch.int32,)), _stream(stream)))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

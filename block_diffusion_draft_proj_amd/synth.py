@@ -311,3 +311,27 @@ def draft_layer_inputs(cfg: Config, batch: Optional[int] = None, seed: Optional[
     w_up = normal_bf16(rngs["w_fc"], (I, D), 0.02)
     w_down = normal_bf16(rngs["w_v"], (D, I), 0.02)
     return DraftLayerInputs(cfg, x, attn, w_in, w_o, w_post, w_gate, w_up, w_down)
+
+
+@dataclasses.dataclass
+class GdnTapeInputs:
+    state: np.ndarray           # [B, H, d_v, d_k] float32: recurrent state saved before the block
+    k_tape: np.ndarray          # [B, 16, H, d_k] bf16 bits: unit-norm keys
+    g_tape: np.ndarray          # [B, 16, H] float32: log-gates (< 0)
+    delta_tape: np.ndarray      # [B, 16, H, d_v] float32: innovations
+    accept: np.ndarray          # [B] int32 accept lengths
+
+
+def gdn_tape_inputs(batch: int, n_heads: int, d_k: int, d_v: int, accept_p: float = 0.1,
+                    seed: int = 2024) -> GdnTapeInputs:
+    """A saved recurrent state N(0, 0.05^2), keys uniform on the unit sphere, gates
+    alpha = exp(g) uniform in [0.9, 1), innovations N(0, 0.1^2), and planted accept
+    lengths min(15, Geometric(accept_p) - 1)."""
+    rngs = streams(seed)
+    state = rngs["kv_ctx"].standard_normal((batch, n_heads, d_v, d_k), dtype=np.float32) * np.float32(0.05)
+    k = rngs["x_blk"].standard_normal((batch, BLOCK, n_heads, d_k))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    g = np.log(rngs["tail"].uniform(0.9, 1.0, (batch, BLOCK, n_heads))).astype(np.float32)
+    delta = rngs["w_v"].standard_normal((batch, BLOCK, n_heads, d_v), dtype=np.float32) * np.float32(0.1)
+    accept = np.minimum(BLOCK - 1, rngs["accept"].geometric(accept_p, batch) - 1).astype(np.int32)
+    return GdnTapeInputs(state, f32_to_bf16_bits(k.astype(np.float32)), g, delta, accept)

@@ -82,6 +82,7 @@ extern "C" {
                                       the hand-off relies on.  That call's outputs may be wrong or
                                       stale and its arrival counters may be left non-zero: zero the
                                       whole workspace before reusing it.  Not expected on MI355X */
+#define DFLASH_DEVERR_ACCEPT   32u  /* recurrent-state replay: accept_len[b] outside [0, 15] (clamped) */
 
 /* Block of draft tokens: the staged token plus 15 mask slots
  * ("dflash-mlx", "block-diffusion draft"). */
@@ -320,6 +321,33 @@ int dflash_draft_layer_post(const dflash_dims* dims, int32_t intermediate, const
                             const float* attn_out, const void* w_o, const void* w_post_norm,
                             const void* w_gate, const void* w_up, const void* w_down, float eps,
                             void* x_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- rollback of recurrent state by tape replay ----------------------------
+ * Verifying the block advances a recurrent (GatedDeltaNet) layer's state by all
+ * 16 candidate steps; it cannot be cropped like an attention cache.  During the
+ * verify a tape of per-step keys, gates and increments is recorded, and after
+ * acceptance only the accepted steps are replayed onto the state saved before
+ * the block ("dflash-mlx: lossless speculative decoding", guarantee 3;
+ * "DFlash dual implementations", §7).  With the gated delta rule (per head,
+ * state S [d_v][d_k], S_t = exp(g_t) S_{t-1} + delta_t k_t^T, where the tape's
+ * innovation is delta_t = beta_t (v_t - exp(g_t) S_{t-1} k_t)), for each b, h:
+ *   S = state_in[b,h];  for t = 0 .. accept_len[b]:
+ *       S = exp(g_tape[b,t,h]) * S + delta_tape[b,t,h,:] (x) k_tape[b,t,h,:]
+ *   state_out[b,h] = S
+ * i.e. the state after the staged token and the accepted drafts (1 + accept_len
+ * steps).  fp32 arithmetic.
+ *   state_in, state_out [batch][n_heads][d_v][d_k] fp32; state_out == state_in
+ *               replays in place (any other overlap is refused)
+ *   k_tape      [batch][16][n_heads][d_k] bf16;  g_tape [batch][16][n_heads] fp32
+ *   delta_tape  [batch][16][n_heads][d_v] fp32;  accept_len [batch] int32, e.g.
+ *               dflash_verify_accept's output
+ *   dev_err     optional uint32 (device): DFLASH_DEVERR_ACCEPT is OR-ed in when an
+ *               accept_len lies outside [0, 15] (it is clamped)
+ * d_k a multiple of 4 in [4, 256], d_v in [1, 4096].  No workspace. */
+int dflash_gdn_tape_replay(int32_t batch, int32_t n_heads, int32_t d_k, int32_t d_v,
+                           const float* state_in, float* state_out, const void* k_tape,
+                           const float* g_tape, const float* delta_tape, const int32_t* accept_len,
+                           uint32_t* dev_err, hipStream_t stream);
 
 #ifdef __cplusplus
 }

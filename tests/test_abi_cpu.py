@@ -30,7 +30,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = ctypes.CDLL(dfl.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -311,7 +311,7 @@ def test_deverr_bits_match_the_header():
     bits = dict(re.findall(r"#define DFLASH_DEVERR_(\w+)\s+(\d+)u", text))
     assert {k: int(v) for k, v in bits.items()} == {
         "CTX_LEN": dfl.DEVERR_CTX_LEN, "PAGE_ID": dfl.DEVERR_PAGE_ID, "ROW": dfl.DEVERR_ROW,
-        "MERGE": dfl.DEVERR_MERGE, "XCD": dfl.DEVERR_XCD}
+        "MERGE": dfl.DEVERR_MERGE, "XCD": dfl.DEVERR_XCD, "ACCEPT": dfl.DEVERR_ACCEPT}
 
 
 @no_device
@@ -343,3 +343,19 @@ def test_window_validation():
     assert dfl.dflash_block_attn_workspace_size(w, 100000) == dfl.dflash_block_attn_workspace_size(w, 64)
     assert _attn(w, maxc=100000, maxpos=100016, wsb=16) == -4   # past the capacity check, stops at the workspace
     assert _proj(dfl.make_dims(1, 4, 2, 64, hidden=256, kv_capacity=80, window=100)) == -5
+
+
+@no_device
+def test_gdn_tape_replay_rejects_bad_arguments():
+    def call(B=2, H=4, dk=128, dv=128, si=FAKE, so=ctypes.c_void_p(0x200000), k=FAKE, g=FAKE, d=FAKE, a=FAKE,
+             err=None):
+        return dfl._lib.dflash_gdn_tape_replay(B, H, dk, dv, si, so, k, g, d, a, err, None)
+    assert call(si=ctypes.c_void_p(None)) == -1
+    assert call(a=ctypes.c_void_p(None)) == -1
+    assert call(B=0) == -2
+    assert call(dk=130) == -2                     # d_k % 4
+    assert call(dk=260) == -2
+    assert call(dv=0) == -2
+    assert call(k=MIS) == -3
+    assert call(err=ctypes.c_void_p(0x100002)) == -3
+    assert call(so=ctypes.c_void_p(0x100000 + 4096)) == -2   # partial overlap with state_in
