@@ -26,6 +26,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -154,6 +156,22 @@ def qkv_bytes(cfg, B):
     return 2 * (n_out * cfg.hidden + 16 * B * cfg.hidden + 16 * B * n_out)
 
 
+def layer_bytes(cfg, B):
+    # the draft layer around the attention: input RMSNorm (x in, n1 out, weight) and the
+    # post-attention part (o_proj, gate/up, down weights; x and the fp32 attention output
+    # in, x_out out; the post-norm weight)
+    M, D, A, I = 16 * B, cfg.hidden, cfg.n_q_heads * cfg.head_dim, cfg.inter
+    norm = 2 * M * D * 2 + 2 * D
+    post = 2 * (D * A + 2 * I * D + D * I) + 4 * M * A + 2 * M * D * 2 + 2 * D
+    return norm, post
+
+
+def replay_bytes(B, H, dk, dv, accept):
+    # the fp32 state in and out, and the accepted steps of the tape (k bf16, delta fp32, g)
+    steps = int((accept.astype(np.int64) + 1).sum())
+    return 2 * 4 * B * H * dv * dk + steps * H * (2 * dk + 4 * dv + 4) + 4 * B
+
+
 def proj_bytes(cfg, M, committed):
     kvw = cfg.n_kv_heads * cfg.head_dim
     return (2 * cfg.hidden * cfg.ctx_width + 2 * 2 * kvw * cfg.hidden + 2 * M * cfg.ctx_width
@@ -277,8 +295,9 @@ def main():
     # at the end of each pass step, on the next copy of the logits, with the verify's
     # next_token as its staged tokens.
     N_SPLIT = 50
+    NEV = 9
     tev = HipTimingEvents(2 * args.steps, torch.cuda.current_stream().cuda_stream)
-    sev = HipTimingEvents(6 * N_SPLIT, torch.cuda.current_stream().cuda_stream)
+    sev = HipTimingEvents(NEV * N_SPLIT, torch.cuda.current_stream().cuda_stream)
     dblk = z(B, 16)
     # ... and the block's own q / k / v (dflash_block_qkv), the attention's inputs,
     # into separate buffers so the attention's inputs stay as drawn.
@@ -286,6 +305,20 @@ def main():
     h_blk, w_qkv = u16(qi.h), u16(qi.w_qkv)
     q2, k2, v2 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_q = dfl.workspace(dfl.dflash_block_qkv_workspace_size(dims), dev)
+    # ... the draft layer around the attention (input RMSNorm; o_proj, post-norm, MLP),
+    # on the attention output of the step, with random Qwen3-shaped weights ...
+    li = synth.draft_layer_inputs(cfg, batch=B)
+    lx, lw_in, lw_o, lw_post = u16(li.x), u16(li.w_in), u16(li.w_o), u16(li.w_post)
+    lw_gate, lw_up, lw_down = u16(li.w_gate), u16(li.w_up), u16(li.w_down)
+    n1 = torch.empty_like(lx)
+    lx_out = torch.empty_like(lx)
+    ws_l = dfl.workspace(dfl.dflash_draft_layer_post_workspace_size(dims, cfg.inter), dev)
+    # ... and the rollback of a recurrent layer's state to the accepted prefix, with the
+    # verify's accept lengths (32 heads of 128 x 128 state per sequence)
+    GH, GD = 32, 128
+    gi = synth.gdn_tape_inputs(B, GH, GD, GD, seed=cfg.seed)
+    g_state, g_out = torch.from_numpy(gi.state).to(dev), torch.empty(B, GH, GD, GD, dtype=torch.float32, device=dev)
+    g_k, g_g, g_d = u16(gi.k_tape), torch.from_numpy(gi.g_tape).to(dev), torch.from_numpy(gi.delta_tape).to(dev)
 
     def step(i, ev=None, base=0, split=False):
         if ev is not None:
@@ -304,6 +337,13 @@ def main():
             ev.record(base + 4)
             dfl.dflash_block_qkv(dims, h_blk, w_qkv, q2, k2, v2, ws_q)
             ev.record(base + 5)
+            dfl.dflash_rmsnorm(lx, lw_in, li.eps, n1)
+            ev.record(base + 6)
+            dfl.dflash_draft_layer_post(dims, cfg.inter, lx, out, lw_o, lw_post, lw_gate, lw_up, lw_down, li.eps,
+                                        lx_out, ws_l)
+            ev.record(base + 7)
+            dfl.dflash_gdn_tape_replay(g_state, g_out, g_k, g_g, g_d, acc)
+            ev.record(base + 8)
 
     n_settle = 0
     t_settle = time.perf_counter()
@@ -322,15 +362,16 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for s in range(N_SPLIT):
-        step(s % R, sev, 6 * s, split=True)
+        step(s % R, sev, NEV * s, split=True)
     torch.cuda.synchronize()
 
     ms_step = (t1 - t0) / args.steps * 1e3
     t_attn = float(np.mean([tev.elapsed_ms(2 * s, 2 * s + 1) for s in range(args.steps)])) * 1e-3
-    t_ver = float(np.mean([sev.elapsed_ms(6 * s + 1, 6 * s + 2) for s in range(N_SPLIT)])) * 1e-3
-    t_proj = float(np.mean([sev.elapsed_ms(6 * s + 2, 6 * s + 3) for s in range(N_SPLIT)])) * 1e-3
-    t_draft = float(np.mean([sev.elapsed_ms(6 * s + 3, 6 * s + 4) for s in range(N_SPLIT)])) * 1e-3
-    t_qkv = float(np.mean([sev.elapsed_ms(6 * s + 4, 6 * s + 5) for s in range(N_SPLIT)])) * 1e-3
+    span = lambda i, j: float(np.mean([sev.elapsed_ms(NEV * s + i, NEV * s + j) for s in range(N_SPLIT)])) * 1e-3
+    t_ver, t_proj, t_draft, t_qkv = span(1, 2), span(2, 3), span(3, 4), span(4, 5)
+    t_norm, t_post, t_replay = span(5, 6), span(6, 7), span(7, 8)
+    nb, pb = layer_bytes(cfg, B)
+    rb = replay_bytes(B, GH, GD, GD, acc.cpu().numpy())
     d_b = draft_bytes(cfg, B)
     q_b = qkv_bytes(cfg, B)
     tev.close()
@@ -365,8 +406,21 @@ def main():
                       "pct_hbm_peak": round(100 * q_b / t_qkv / 1e9 / HBM_PEAK_GBS, 2), "bytes": q_b,
                       "scope": "the block's own q/k/v (two kernels: split-K GEMM, reduce); "
                                "not in the timed step"},
-        "timing": "block_attn: HIP events around every timed call; verify, ctx_proj, draft_argmax and "
-                  "block_qkv: events in a %d-step pass after the timed region" % N_SPLIT,
+        "draft_layer": {"rmsnorm_us": round(t_norm * 1e6, 2), "post_us": round(t_post * 1e6, 2),
+                        "post_GB_s": round(pb / t_post / 1e9, 1),
+                        "post_pct_hbm_peak": round(100 * pb / t_post / 1e9 / HBM_PEAK_GBS, 2),
+                        "bytes": {"rmsnorm": nb, "post": pb}, "intermediate": cfg.inter,
+                        "forward_us": round((t_norm + t_qkv + t_attn + t_post) * 1e6, 2),
+                        "scope": "one random-weight draft layer around the step's attention: input RMSNorm, "
+                                 "then (after q/k/v and the attention) o_proj + residual, RMSNorm, SwiGLU MLP + "
+                                 "residual; forward_us = rmsnorm + block_qkv + block_attn + post; not in the "
+                                 "timed step"},
+        "gdn_replay": {"us": round(t_replay * 1e6, 2), "GB_s": round(rb / t_replay / 1e9, 1),
+                       "pct_hbm_peak": round(100 * rb / t_replay / 1e9 / HBM_PEAK_GBS, 2), "bytes": rb,
+                       "shape": f"B={B}, 32 heads, 128x128 fp32 state, the verify's accept lengths",
+                       "scope": "rollback of recurrent state to the accepted prefix; not in the timed step"},
+        "timing": "block_attn: HIP events around every timed call; the other calls: events in a %d-step "
+                  "pass after the timed region" % N_SPLIT,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name),
                      "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": a_b},
