@@ -69,13 +69,31 @@ __device__ __forceinline__ uint16_t bf16_of_exact_sum(double a, double b) {
   return f32_to_bf16(__uint_as_float(u));
 }
 
+// bf16 (nearest even) of the exact value a*c + b*d of fp32 inputs, rounded once.
+// Fast path: y = fma(a, c, fl(b*d)) is within 2^-24 (|b d| + |y|) of the exact value
+// (one product rounding, one fma rounding); whenever y lies farther than twice that
+// from the midpoint of its bf16 interval, the exact value rounds to the same bf16 as
+// y (it cannot cross that midpoint, nor reach the midpoints of the neighbouring
+// intervals, half a step away).  Otherwise (rare: within ~2^-15 of a step around the
+// midpoint) the exact value is rounded through fp64 (bf16_of_exact_sum; products of
+// two fp32 values are exact in fp64).
+__device__ __forceinline__ uint16_t bf16_of_exact_dot2(float a, float c, float b, float d) {
+  const float bd = b * d;
+  const float y = __builtin_fmaf(a, c, bd);
+  const uint32_t u = __float_as_uint(y);
+  const float mid = __uint_as_float((u & 0xffff0000u) | 0x8000u);  // same sign and binade as y
+  const float dist = fabsf(y - mid);                               // exact (same binade)
+  const float err = (fabsf(bd) + fabsf(y)) * 0x1p-23f + 0x1p-140f;
+  if (dist > err && (u & 0x7f800000u) != 0x7f800000u) return f32_to_bf16(y);
+  return bf16_of_exact_sum((double)a * (double)c, (double)b * (double)d);
+}
+
 // One rotate-half RoPE pair (lo = x_j, hi = x_{j+d/2}) with fp32 cos / sin: each
-// output is the exact rotation rounded once to bf16.  The product of two fp32
-// values (24 significant bits each) is exact in fp64.
+// output is the exact rotation rounded once to bf16.
 __device__ __forceinline__ void rope_pair_bf16(float lo, float hi, float c, float s, uint16_t& ylo,
                                                uint16_t& yhi) {
-  ylo = bf16_of_exact_sum((double)lo * (double)c, -((double)hi * (double)s));
-  yhi = bf16_of_exact_sum((double)hi * (double)c, (double)lo * (double)s);
+  ylo = bf16_of_exact_dot2(lo, c, hi, -s);
+  yhi = bf16_of_exact_dot2(hi, c, lo, s);
 }
 
 #define LDS_AS __attribute__((address_space(3)))
