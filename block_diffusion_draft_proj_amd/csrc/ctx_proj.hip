@@ -136,10 +136,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
 // Per stage a wave reads its own 32 weight rows (4 KB) and its activation tiles
 // from LDS and does 2 x MTW x 2 MFMAs; each weight byte crosses LDS 1 + TG times
 // and each activation byte five times (vs. thirteen for a square-tile GEMM).
-// The activations come pre-packed step by step ([K/64][16*MT rows][64], see
-// pack_rows_kernel): a step's tile is one contiguous 16*MT x 128-byte block.
-// Read in place, its rows would be lda apart, and that strided pattern measured
-// 2.5x slower for the whole product at 128 rows x 20480 x 4096.
+// The activations either come packed step by step ([K/64][16*MT rows][64]: the K/V
+// product reads C packed by fc_reduce_kernel, or by pack_rows_kernel when the rows
+// already are C), a step's tile then being one contiguous 16*MT x 128-byte block, or
+// are read in place from their rows (the fc product walks the target layers' rows,
+// the q/k/v and draft-layer products their activation rows), see PACKED below.
 constexpr int SK_RW = 4;                     // weight-row wave groups (32 rows each)
 // Up to kSkinnyMaxRows activation rows take the skinny kernel, in chunks of up to
 // kSkinnyChunk rows (MT = 16 at 129..256 rows): every chunk streams the weights once,
@@ -499,10 +500,11 @@ ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_
   pl.off_kv = off;
   off = align(off + sizeof(float) * (size_t)pl.kv_splits * n_rows * kv_width);
   // Rows of a packed step: every skinny chunk reads 16*MT <= 32*ceil(chunk rows / 32)
-  // rows from its offset, so with more than one chunk the steps hold whole chunks
-  // (rows past n_rows are zero in the packed activations and never stored).
+  // rows from its offset, so with more than one chunk the steps hold whole chunks.
+  // Rows past n_rows hold whatever the workspace held (zero from pack_rows_kernel);
+  // an MFMA output row depends on its own activation row only, and the products of
+  // those rows are never stored.
   pl.mp = n_rows <= 128 ? 32 * ((n_rows + 31) / 32) : kSkinnyChunk * ((n_rows + kSkinnyChunk - 1) / kSkinnyChunk);
-  pl.off_xp = off;  // unused: the skinny fc product reads the layers' rows in place
   pl.off_cp = off;
   if (pl.kv_small) off = align(off + 2 * (size_t)hidden * pl.mp);
   pl.ws_bytes = off;
@@ -525,8 +527,7 @@ QkvPlan plan_block_qkv(int n_rows, int hidden, int n_out, int num_cu) {
   size_t off = 256;  // word 0: device error mask
   pl.off_part = off;
   off = align(off + sizeof(float) * (size_t)pl.splits * n_rows * n_out);
-  pl.off_xp = off;  // unused: the q/k/v product reads its activations in place
-  pl.ws_bytes = off;
+  pl.ws_bytes = off;  // the product reads its activations in place: no packed copy
   return pl;
 }
 

@@ -120,7 +120,7 @@ struct ProjPlan {
   size_t ws_bytes;
   size_t off_fc, off_c, off_kv;
   int mp;                   // skinny path: packed activation rows (M rounded up to 32)
-  size_t off_xp, off_cp;    // skinny path: packed fc input, packed C
+  size_t off_cp;            // skinny path: packed C (the K/V product's activations)
 };
 ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_fc, int num_cu);
 hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStream_t stream);
@@ -141,7 +141,7 @@ struct QkvPlan {
   int splits, kps;   // K split count and K elements per split (multiple of 64)
   bool small;        // skinny weight-streaming GEMM (rows <= kSkinnyMaxRows)
   int mp;            // skinny path: packed activation rows
-  size_t off_part, off_xp, ws_bytes;
+  size_t off_part, ws_bytes;
 };
 QkvPlan plan_block_qkv(int n_rows, int hidden, int n_out, int num_cu);
 struct QkvReduceParams {

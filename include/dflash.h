@@ -254,8 +254,8 @@ int dflash_verify_accept(int32_t batch, int32_t block, int32_t vocab,
  *   w_qkv      [(Hq + 2*Hkv)*d][hidden] bf16, nn.Linear layout: the Hq query
  *              heads' rows, then the Hkv key heads', then the Hkv value heads'
  *   q_blk      [batch][16][Hq][d] bf16 output; k_blk, v_blk [batch][16][Hkv][d]
- * The workspace holds split-K partial sums (and packed activations for up to
- * 512 rows); it keeps no state between calls.  Results agree with the exact
+ * The workspace holds split-K partial sums (h is read in place); it keeps no
+ * state between calls.  Results agree with the exact
  * product rounded to bf16 to within one bf16 ulp (fp32 summation order). */
 size_t dflash_block_qkv_workspace_size(const dflash_dims* dims);
 int dflash_block_qkv(const dflash_dims* dims, const void* h, int64_t ld_h, const void* w_qkv,
