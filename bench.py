@@ -127,6 +127,10 @@ def parse():
     ap.add_argument("--config", default="batched")
     ap.add_argument("--rotate", type=int, default=0, help="input copies (0 = enough for >= 2 GiB between reuses)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-rows", type=int, default=0,
+                    help="instead of the step, time dflash_ctx_proj over one prefill chunk of this many rows "
+                         "(qwen3_8b-shaped: 5 x 4096 target features -> 4096 -> 8 x 128 K/V) and print its "
+                         "TFLOP/s against the bf16 MFMA peak")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the step, copy a buffer of this many MiB device to device 5 times: the "
                          "yardstick that converts the HBM byte counters of a profiler into bytes")
@@ -221,6 +225,48 @@ def cpu_baseline(cfg, at, vi, pj, row_pos, t_budget=20.0, repeats=3):
                       f"{repeats} ({t_step:.2f} s/step: attn {t_attn:.2f}, verify {t_ver:.2f}, proj {t_proj:.2f})"}
 
 
+def prefill(rows, steps, warmup):
+    """One prefill chunk of the context projection (fc + K/V + RoPE + scatter), timed with
+    HIP events per call; flops = 2 M (n_t D_t D + 2 D Hkv d)."""
+    import torch
+    from block_diffusion_draft_proj_amd import dflash as dfl
+    from block_diffusion_draft_proj_amd import synth
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS["qwen3_8b"]
+    u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    pj = synth.ctx_proj_inputs(cfg, 0, weights_only=True)
+    Dt, nt, D, Hkv, d = cfg.target_hidden, cfg.n_target_layers, cfg.hidden, cfg.n_kv_heads, cfg.head_dim
+    xs = [(torch.randn(rows, Dt, device=dev) * 1.0).to(torch.bfloat16).view(torch.int16) for _ in range(nt)]
+    dims = dfl.make_dims(1, cfg.n_q_heads, Hkv, d, hidden=D, kv_capacity=rows + 16)
+    kc = torch.zeros(1, Hkv, rows + 16, d, dtype=torch.int16, device=dev)
+    vc = torch.zeros_like(kc)
+    cos = torch.empty(rows + 32, d // 2, dtype=torch.float32, device=dev)
+    sin = torch.empty_like(cos)
+    dfl.dflash_rope_tables(cfg.rope_base, d, rows + 32, cos, sin)
+    seq = torch.zeros(rows, dtype=torch.int32, device=dev)
+    pos = torch.arange(rows, dtype=torch.int32, device=dev)
+    ws = dfl.workspace(dfl.dflash_ctx_proj_workspace_size(dims, rows, nt, Dt), dev)
+    wfc, wk, wv = u16(pj.w_fc), u16(pj.w_k), u16(pj.w_v)
+    call = lambda: dfl.dflash_ctx_proj(dims, xs, seq, pos, wfc, wk, wv, cos, sin, None, kc, vc, None, ws)
+    for _ in range(warmup):
+        call()
+    ev = HipTimingEvents(2 * steps, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        ev.record(2 * s)
+        call()
+        ev.record(2 * s + 1)
+    torch.cuda.synchronize()
+    t = float(np.mean([ev.elapsed_ms(2 * s, 2 * s + 1) for s in range(steps)])) * 1e-3
+    ev.close()
+    flops = 2.0 * rows * (nt * Dt * D + 2 * D * Hkv * d)
+    print(json.dumps({"prefill": {"rows": rows, "us": round(t * 1e6, 1), "flops": flops,
+                                  "TFLOP_s": round(flops / t / 1e12, 1),
+                                  "pct_bf16_mfma_peak": round(100 * flops / t / 2.5e15, 2),
+                                  "workload": "qwen3_8b-shaped context projection, one chunk: "
+                                              f"{rows} x {nt * Dt} -> {D} -> {2 * Hkv * d}"}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -229,6 +275,9 @@ def main():
         sys.exit(2)
     if args.copy_mib:
         copy_yardstick(args.copy_mib)
+        return
+    if args.prefill_rows:
+        prefill(args.prefill_rows, max(1, min(args.steps, 20)), max(1, min(args.warmup, 5)))
         return
     import numpy as np
     import torch
@@ -320,10 +369,17 @@ def main():
     g_state, g_out = torch.from_numpy(gi.state).to(dev), torch.empty(B, GH, GD, GD, dtype=torch.float32, device=dev)
     g_k, g_g, g_d = u16(gi.k_tape), torch.from_numpy(gi.g_tape).to(dev), torch.from_numpy(gi.delta_tape).to(dev)
 
+    # The attention calls are prepared once per input copy (checks and argument conversion
+    # done here), so the event before a call is followed at once by the launch: with an
+    # idle GPU (the first timed step) the span would otherwise include the host's
+    # marshalling time.
+    attn_calls = [dfl.bind_block_attn(dims, q, k, v, kcs[i], vcs[i], table, ctx, max_ctx, cos, sin, out, ws_a)
+                  for i in range(R)]
+
     def step(i, ev=None, base=0, split=False):
         if ev is not None:
             ev.record(base)
-        dfl.dflash_block_attn(dims, q, k, v, kcs[i], vcs[i], table, ctx, max_ctx, cos, sin, out, ws_a)
+        attn_calls[i]()
         if ev is not None:
             ev.record(base + 1)
         dfl.dflash_verify_accept(lgs[i], blk, kv_in, post, acc, nxt, kv_out, commit, 0, None, ws_v)

@@ -228,6 +228,41 @@ def dflash_block_attn(dims: dflash_dims, q_blk: torch.Tensor, k_blk: torch.Tenso
         workspace.numel(), _stream(stream)))
 
 
+def bind_block_attn(dims: dflash_dims, q_blk: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor,
+                    k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: Optional[torch.Tensor],
+                    ctx_len: torch.Tensor, max_ctx_len: int, rope_cos: torch.Tensor, rope_sin: torch.Tensor,
+                    out: torch.Tensor, workspace: torch.Tensor, stream=None):
+    """dflash_block_attn with every check and argument conversion done once, now: returns
+    a function of no arguments that only calls the entry point (and raises on a non-zero
+    status).  For loops that call the attention many times on the same buffers; the
+    tensors must stay alive and in place while the function is used."""
+    B, Hq, Hkv, d = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    _numel(q_blk, B * BLOCK * Hq * d, "q_blk")
+    _numel(k_blk, B * BLOCK * Hkv * d, "k_blk")
+    _numel(v_blk, B * BLOCK * Hkv * d, "v_blk")
+    _numel(k_cache, _cache_numel(dims), "k_cache")
+    _numel(v_cache, _cache_numel(dims), "v_cache")
+    if dims.page_size > 0:
+        _numel(page_table, B * dims.kv_capacity, "page_table")
+    _numel(ctx_len, B, "ctx_len")
+    _numel(out, B * BLOCK * Hq * d, "out")
+    _check_rope(rope_cos, rope_sin, d)
+    args = (ctypes.byref(dims), _dev(q_blk, "q_blk", _BF16), _dev(k_blk, "k_blk", _BF16),
+            _dev(v_blk, "v_blk", _BF16), _dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16),
+            _dev(page_table, "page_table", (torch.int32,)), _dev(ctx_len, "ctx_len", (torch.int32,)),
+            max_ctx_len, _dev(rope_cos, "rope_cos", (torch.float32,)),
+            _dev(rope_sin, "rope_sin", (torch.float32,)), int(rope_cos.shape[0]),
+            _dev(out, "out", (torch.float32,)), _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(),
+            _stream(stream))
+    fn = _lib.dflash_block_attn
+
+    def call() -> None:
+        code = fn(*args)
+        if code != 0:
+            _check("dflash_block_attn", code)
+    return call
+
+
 def dflash_block_attn_noalloc(dims: dflash_dims, q_blk: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor,
                               k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: Optional[torch.Tensor],
                               ctx_len: torch.Tensor, max_ctx_len: int, rope_cos: torch.Tensor,

@@ -359,3 +359,14 @@ def test_gdn_tape_replay_rejects_bad_arguments():
     assert call(k=MIS) == -3
     assert call(err=ctypes.c_void_p(0x100002)) == -3
     assert call(so=ctypes.c_void_p(0x100000 + 4096)) == -2   # partial overlap with state_in
+
+
+def test_binding_prepared_attention_call_checks_sizes_once():
+    dims, a = _attn_args(q=_t(2, 16, 8, 32))
+    with pytest.raises(ValueError, match="q_blk"):
+        dfl.bind_block_attn(dims, a["q"], a["k"], a["v"], a["kc"], a["vc"], a["pt"], a["ctx"], 64, a["cos"],
+                            a["sin"], a["out"], a["ws"])
+    dims, a = _attn_args()
+    with pytest.raises(ValueError, match="device tensor"):
+        dfl.bind_block_attn(dims, a["q"], a["k"], a["v"], a["kc"], a["vc"], a["pt"], a["ctx"], 64, a["cos"],
+                            a["sin"], a["out"], a["ws"])
