@@ -316,6 +316,65 @@ def block_attn_ref(q_blk: np.ndarray, k_blk: np.ndarray, v_blk: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# The block's q/k/v and the attention as one step (page "DFlash dual
+# implementations", §2: Q comes from the block tokens only, the block's K/V are
+# the second source).  Reading: the products are exact; the rotated Q enters the
+# attention unrounded (no bf16 storage of q between the two steps); the rotated
+# block K and the block V are rounded once to bf16 from their exact values, as
+# they sit beside the bf16 context cache.  The rotation uses the float32 tables.
+# --------------------------------------------------------------------------
+def attend_ref(Q: np.ndarray, Keys: np.ndarray, Vals: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(Q Keys^T scale) Vals over all keys (no mask), float64; Q [n, d]."""
+    s = (Q @ Keys.T) * scale
+    s = s - s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return (e / e.sum(axis=1, keepdims=True)) @ Vals
+
+
+def block_qkv_attn_ref(h: np.ndarray, w_qkv: np.ndarray, n_q_heads: int, n_kv_heads: int,
+                       k_cache: np.ndarray, v_cache: np.ndarray, ctx_len: np.ndarray, base: float,
+                       page_table: Optional[np.ndarray] = None, scale: Optional[float] = None,
+                       units: Optional[Sequence[Tuple[int, int]]] = None, window: int = 0) -> np.ndarray:
+    """O [B, 16, Hq, d] float64 for the block hidden states h [16 B, hidden] (bf16 bits).
+
+      Y = h w_qkv^T (exact), split into q [B,16,Hq,d], k, v [B,16,Hkv,d]
+      Q      = RoPE(q) at positions L .. L+15               (not rounded)
+      K_blk  = bf16(RoPE(k)),  V_blk = bf16(v)              (rounded once)
+      O      = attention over [context ; block] as in block_attn_ref (window W > 0: the
+               last min(L, W) context positions, from ring rows).
+    """
+    Hq, Hkv = n_q_heads, n_kv_heads
+    M = h.shape[0]
+    B = M // BLOCK
+    d = w_qkv.shape[0] // (Hq + 2 * Hkv)
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    Y = bf16_to_f64(h) @ bf16_to_f64(w_qkv).T
+    q = Y[:, :Hq * d].reshape(B, BLOCK, Hq, d)
+    k = Y[:, Hq * d:(Hq + Hkv) * d].reshape(B, BLOCK, Hkv, d)
+    v = Y[:, (Hq + Hkv) * d:].reshape(B, BLOCK, Hkv, d)
+    out = np.full((B, BLOCK, Hq, d), np.nan)
+    todo = units if units is not None else [(b, g) for b in range(B) for g in range(Hkv)]
+    for b, g in todo:
+        L = int(ctx_len[b])
+        pos = L + np.arange(BLOCK)
+        c, s_ = rope_tables_f32(pos, d, base)
+        rot = lambda x: np.concatenate([x[:, :d // 2] * c - x[:, d // 2:] * s_,
+                                        x[:, d // 2:] * c + x[:, :d // 2] * s_], axis=1)
+        first = max(0, L - window) if window > 0 else 0
+        t = np.arange(first, L)
+        rows = t % window if window > 0 else t
+        Keys = np.concatenate([bf16_to_f64(gather_rows(k_cache, page_table, b, rows)[g]),
+                               round_bf16(rot(k[b, :, g]))], axis=0)
+        Vals = np.concatenate([bf16_to_f64(gather_rows(v_cache, page_table, b, rows)[g]),
+                               round_bf16(v[b, :, g])], axis=0)
+        for hh in range(G):
+            hd = g * G + hh
+            out[b, :, hd, :] = attend_ref(rot(q[b, :, hd]), Keys, Vals, scale)
+    return out
+
+
+# --------------------------------------------------------------------------
 # a7-a9: greedy verify, prefix acceptance, commit and crop
 # (dflash-mlx page: "what is lossless" -- emitted tokens are the target's
 # greedy argmax; "single-forward verify" steps 6-9; guarantee 2 -- the

@@ -27,9 +27,10 @@ MUTANTS = {
                         "return (np.cos(th), np.sin(th))"),
     "rope_no_two_sum": ("r[tie] = s[tie] + np.sign(e[tie]) * half[tie]", "r[tie] = r[tie]"),
     "rope_sum_sign": ("round_bf16_sum(lo * c, -(hi * s))", "round_bf16_sum(lo * c, hi * s)"),
-    "window_first": ("first = max(0, L - window) if window > 0 else 0",
-                     "first = max(0, L - window + 1) if window > 0 else 0"),
-    "window_ring_rows": ("rows = t % window if window > 0 else t", "rows = t"),
+    "window_first": ("first = max(0, L - window) if window > 0 else 0\n        t = np.arange(first, L)  ",
+                     "first = max(0, L - window + 1) if window > 0 else 0\n        t = np.arange(first, L)  "),
+    "window_ring_rows": ("rows = t % window if window > 0 else t                # their storage rows",
+                         "rows = t                # their storage rows"),
     "window_block_pos": ("L - first, g, G, base, scale, block_pos=L)", "L - first, g, G, base, scale)"),
     "rms_no_square": ("r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
                       "r = 1.0 / np.sqrt(np.mean(np.abs(x), axis=-1, keepdims=True) + eps)"),
@@ -50,6 +51,11 @@ MUTANTS = {
                                 "[:, ::-1, ::-1]"),
     "gdn_innovation_no_alpha": ("d = float(beta[t]) * (v[t] - alpha * (S @ k[t]))",
                                 "d = float(beta[t]) * (v[t] - (S @ k[t]))"),
+    "fused_q_rounded": ("out[b, :, hd, :] = attend_ref(rot(q[b, :, hd]), Keys, Vals, scale)",
+                        "out[b, :, hd, :] = attend_ref(round_bf16(rot(q[b, :, hd])), Keys, Vals, scale)"),
+    "fused_k_not_rotated": ("round_bf16(rot(k[b, :, g]))], axis=0)", "round_bf16(k[b, :, g])], axis=0)"),
+    "fused_v_slice": ("v = Y[:, (Hq + Hkv) * d:].reshape(B, BLOCK, Hkv, d)",
+                      "v = Y[:, Hq * d:(Hq + Hkv) * d].reshape(B, BLOCK, Hkv, d)"),
     "drop_block_keys": ("Keys = np.concatenate([bf16_to_f64(k_ctx[:L]), Kblk], axis=0)\n"
                         "    Vals = np.concatenate([bf16_to_f64(v_ctx[:L]), bf16_to_f64(v_b[:, g, :])], axis=0)",
                         "Keys = bf16_to_f64(k_ctx[:L+16])\n    Vals = bf16_to_f64(v_ctx[:L+16])"),

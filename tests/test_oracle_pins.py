@@ -718,6 +718,77 @@ def test_gdn_zero_gate_forgets_everything_before():
     assert not np.allclose(s3, s4)
 
 
+# ----------------------------------------------------------------------------- q/k/v and attention as one step
+def _fused_inputs(rng, B=2, Hq=4, Hkv=2, d=16, D=32, L=(20, 7), cap=24):
+    enc = orc.f64_to_bf16_bits
+    h = enc(rng.standard_normal((16 * B, D)))
+    w = enc(rng.standard_normal(((Hq + 2 * Hkv) * d, D)) * 0.2)
+    kc = enc(rng.standard_normal((B, Hkv, cap, d)) * 1.5)
+    vc = enc(rng.standard_normal((B, Hkv, cap, d)) * 1.5)
+    return h, w, kc, vc, np.array(L)
+
+
+def test_block_qkv_attn_matches_torch_sdpa_on_the_exact_operands():
+    # Independent route: float64 q/k/v by a torch matmul, rotation written out with the
+    # float32 tables, block K / V rounded to bf16, then torch's float64 SDPA (GQA).
+    rng = np.random.default_rng(60)
+    Hq, Hkv, d = 4, 2, 16
+    h, w, kc, vc, ctx = _fused_inputs(rng, Hq=Hq, Hkv=Hkv, d=d)
+    got = orc.block_qkv_attn_ref(h, w, Hq, Hkv, kc, vc, ctx, 1e6)
+    Y = (torch.from_numpy(orc.bf16_to_f64(h)) @ torch.from_numpy(orc.bf16_to_f64(w)).T).numpy()
+    for b in range(2):
+        Lb = int(ctx[b])
+        th = np.arange(Lb, Lb + 16)[:, None] * 1e6 ** (-2.0 * np.arange(d // 2) / d)
+        c = np.cos(th).astype(np.float32).astype(np.float64)
+        s_ = np.sin(th).astype(np.float32).astype(np.float64)
+        yb = Y[16 * b:16 * b + 16]
+        q = yb[:, :Hq * d].reshape(16, Hq, d)
+        k = yb[:, Hq * d:(Hq + Hkv) * d].reshape(16, Hkv, d)
+        v = yb[:, (Hq + Hkv) * d:].reshape(16, Hkv, d)
+        def rot(x):
+            lo, hi = x[..., :d // 2], x[..., d // 2:]
+            return np.concatenate([lo * c[:, None] - hi * s_[:, None], hi * c[:, None] + lo * s_[:, None]], -1)
+        Q = rot(q)
+        K = np.concatenate([orc.bf16_to_f64(kc[b][:, :Lb]), orc.round_bf16(rot(k)).transpose(1, 0, 2)], axis=1)
+        V = np.concatenate([orc.bf16_to_f64(vc[b][:, :Lb]), orc.round_bf16(v).transpose(1, 0, 2)], axis=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q.transpose(1, 0, 2))[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+            enable_gqa=True)[0].numpy().transpose(1, 0, 2)
+        assert np.allclose(got[b], ref, atol=1e-11, rtol=1e-11)
+
+
+def test_block_qkv_attn_close_to_the_two_step_chain():
+    # The same step through bf16 q/k/v (block_qkv_ref, then block_attn_ref) differs only
+    # by those roundings: a few bf16 steps of q move the output far less than its spread.
+    rng = np.random.default_rng(61)
+    Hq, Hkv, d = 4, 2, 16
+    h, w, kc, vc, ctx = _fused_inputs(rng, Hq=Hq, Hkv=Hkv, d=d)
+    one = orc.block_qkv_attn_ref(h, w, Hq, Hkv, kc, vc, ctx, 1e6)
+    q, k, v = orc.block_qkv_ref(h, w, Hq, Hkv, d)
+    B = 2
+    two = orc.block_attn_ref(q.reshape(B, 16, Hq, d), k.reshape(B, 16, Hkv, d), v.reshape(B, 16, Hkv, d), kc, vc,
+                             ctx, 1e6)
+    diff = np.max(np.abs(one - two))
+    assert 0 < diff < 0.05 * np.std(two)
+
+
+def test_block_qkv_attn_window_and_paged_agree_with_dense():
+    rng = np.random.default_rng(62)
+    h, w, kc, vc, ctx = _fused_inputs(rng, L=(40, 9), cap=48)
+    dense = orc.block_qkv_attn_ref(h, w, 4, 2, kc, vc, ctx, 1e6)
+    wide = orc.block_qkv_attn_ref(h, w, 4, 2, kc, vc, ctx, 1e6, window=48)
+    assert np.array_equal(dense, wide)
+    table = rng.permutation(6).reshape(2, 3).astype(np.int32)
+    kp = np.zeros((6, 2, 16, 16), np.uint16)
+    vp = np.zeros_like(kp)
+    for b in range(2):
+        for t in range(48):
+            kp[table[b, t // 16], :, t % 16] = kc[b, :, t]
+            vp[table[b, t // 16], :, t % 16] = vc[b, :, t]
+    paged = orc.block_qkv_attn_ref(h, w, 4, 2, kp, vp, ctx, 1e6, page_table=table)
+    assert np.array_equal(dense, paged)
+
+
 # ----------------------------------------------------------------------------- verify / accept
 @pytest.mark.parametrize("case", _golden("accept_cases.txt"), ids=lambda c: c["name"])
 def test_accept_golden_cases(case):
