@@ -147,9 +147,11 @@ __device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, u
 // Keys [0, nvalid) of the stage are real (nvalid >= 1), the rest are masked out.
 // Scores stay unscaled until the exponent: p = exp2(s * scale_log2 - m), with the
 // running max m kept in scaled units (scale > 0, so max and scaling commute).
-template <int D>
-__device__ __forceinline__ void attend_stage(const char* stage, const bf16x8* qB, f32x4* o, float& m,
-                                             float& lsum, int lane, int nvalid, float scale_log2) {
+// QHL: Q comes as a bf16 pair (qB = hi, qL = lo, Q = hi + lo), so S^T takes two MFMAs
+// per K step.
+template <int D, bool QHL = false>
+__device__ __forceinline__ void attend_stage(const char* stage, const bf16x8* qB, const bf16x8* qL, f32x4* o,
+                                             float& m, float& lsum, int lane, int nvalid, float scale_log2) {
   using GE = Geo<D>;
   static_assert(TK == 32, "one 32-key MFMA step per stage");
   constexpr int KS = D / 32, DT = D / 16;
@@ -173,6 +175,10 @@ __device__ __forceinline__ void attend_stage(const char* stage, const bf16x8* qB
   for (int ks = 0; ks < KS; ++ks) {
     s0 = mfma16x16x32(ka[0][ks], qB[ks], s0);
     s1 = mfma16x16x32(ka[1][ks], qB[ks], s1);
+    if constexpr (QHL) {
+      s0 = mfma16x16x32(ka[0][ks], qL[ks], s0);
+      s1 = mfma16x16x32(ka[1][ks], qL[ks], s1);
+    }
   }
   float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};  // key 8q + e
   if (nvalid < TK) {
@@ -328,7 +334,9 @@ __device__ __forceinline__ void wait_packs(int after) {
   }
 }
 
-template <int D, int G, bool PAGED>
+// QHL: the q / k inputs come already rotated by the fused q/k/v product: Q as a bf16
+// hi/lo pair (q_blk = hi, q_lo = lo; no RoPE here), the block K rotated and rounded.
+template <int D, int G, bool PAGED, bool QHL>
 __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnParams p) {
   using GE = Geo<D>;
   constexpr int NGRP = ngrp<G>();
@@ -432,8 +440,23 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
     const char* qsrc = reinterpret_cast<const char*>(p.q_blk + (((int64_t)b * kBlock) * p.n_q_heads + g * G) * D);
     const char* csrc = reinterpret_cast<const char*>(p.rope_cos + (int64_t)L * HALF);
     const char* ssrc = reinterpret_cast<const char*>(p.rope_sin + (int64_t)L * HALF);
+    if constexpr (QHL) {
+      // Q hi into the Q area; Q lo into the rest of it (the cos / sin part, 2*CL loads)
+      // and then the ring slot of stage NST-2, which the context stream first fills
+      // inside the loop (Q is in registers by then).
+      const char* lsrc = reinterpret_cast<const char*>(p.q_lo + (((int64_t)b * kBlock) * p.n_q_heads + g * G) * D);
 #pragma unroll
-    for (int li = w; li < QL + 2 * CL; li += NW) {
+      for (int li = w; li < 2 * QL; li += NW) {
+        const int lo = li >= QL, l = li - lo * QL;
+        const int ci = l * 64 + lane, row = ci / qrow_chunks, col = ci - row * qrow_chunks;
+        const uint32_t dst = !lo ? qst_lds + l * 1024
+                                 : (l < 2 * CL ? qst_lds + (QL + l) * 1024
+                                               : lds_ring + (NST - 2) * GE::STAGE + (l - 2 * CL) * 1024);
+        lds_dma16_m0((lo ? lsrc : qsrc) + ((int64_t)row * p.n_q_heads * D + col * 8) * 2, dst);
+      }
+    }
+#pragma unroll
+    for (int li = w; li < (QHL ? 0 : QL + 2 * CL); li += NW) {
       if (li < QL) {
         const int ci = li * 64 + lane, row = ci / qrow_chunks, col = ci - row * qrow_chunks;
         lds_dma16_m0(qsrc + ((int64_t)row * p.n_q_heads * D + col * 8) * 2, qst_lds + li * 1024);
@@ -459,6 +482,8 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
         const uint16_t* src = (is_v ? p.v_blk : p.k_blk) + brow0 + t * bstride;
         if (is_v)
           lds_dma16_m0(src + ((pch ^ vswz<D>(t)) << 3), bslot + GE::TILE + (li - BL) * 1024);
+        else if (QHL)  // already rotated: straight into its swizzled place
+          lds_dma16_m0(src + ((pch ^ kswz<D>(t)) << 3), bslot + li * 1024);
         else
           lds_dma16_m0(src + (pch << 3), bslot + kBlock * GE::ROW + li * 1024);
       }
@@ -478,8 +503,23 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
 
   // Q of head h: rows at positions L + r, rotated exactly and rounded once to bf16, as the
   // B operand of S^T = K Q^T (lane holds dims 32*ks + 8*q .. +8 of row r).
-  bf16x8 qB[KS];
-  if constexpr (NGRP > 1) {
+  bf16x8 qB[KS], qL[QHL ? KS : 1];
+  if constexpr (NGRP > 1 && QHL) {
+    wait_packs<LPK, QF>(n_pk);  // this wave's Q loads landed
+    __syncthreads();                 // ... and every other wave's
+#pragma unroll
+    for (int pk = QF; pk < NPK - 1; ++pk)
+      if (pk < n_pk) issue(pk);
+    const int off0 = (r * G * D + hw * D + 8 * q) * 2;  // byte offset of this lane's row chunk in a Q blob
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = off0 + 64 * ks, blk = off >> 10;
+      qB[ks] = *reinterpret_cast<const bf16x8*>(qst + off);
+      const char* lsrc = blk < 2 * CL ? qst + (QL + blk) * 1024
+                                      : lds + (NST - 2) * GE::STAGE + (blk - 2 * CL) * 1024;
+      qL[ks] = *reinterpret_cast<const bf16x8*>(lsrc + (off & 1023));
+    }
+  } else if constexpr (NGRP > 1) {
     wait_packs<LPK, QF>(n_pk);  // this wave's Q / cos / sin loads landed
     __syncthreads();                 // ... and every other wave's
 #pragma unroll
@@ -508,6 +548,13 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
         qB[ks][e] = __builtin_bit_cast(__bf16, ylo);
         qB[ks + KS / 2][e] = __builtin_bit_cast(__bf16, yhi);
       }
+    }
+  } else if constexpr (QHL) {
+    const int64_t qo = (((int64_t)b * kBlock + r) * p.n_q_heads + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qB[ks] = __builtin_bit_cast(bf16x8, ld16(p.q_blk + qo + 32 * ks + 8 * q));
+      qL[ks] = __builtin_bit_cast(bf16x8, ld16(p.q_lo + qo + 32 * ks + 8 * q));
     }
   } else {
     const uint16_t* qrow = p.q_blk + (((int64_t)b * kBlock + r) * p.n_q_heads + h) * D;
@@ -546,11 +593,12 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
       // The block tile first (its loads landed with Q): rotate the raw K rows with
       // the cos / sin rows of the same positions, one 8-dim chunk pair per thread,
       // then wave group 0 attends to the 16 block keys while the context streams in.
+      // (QHL: the block K came rotated, straight into its place.)
       char* kt = lds + (NST - 1) * GE::STAGE;
       const float* cq = reinterpret_cast<const float*>(qst + 32 * G * D);
       const float* sq = reinterpret_cast<const float*>(qst + 32 * G * D + 32 * D);
       constexpr int HC = HALF / 8;  // chunks per half row
-      for (int it = tid; it < kBlock * HC; it += 64 * NW) {
+      for (int it = tid; it < (QHL ? 0 : kBlock * HC); it += 64 * NW) {
         const int t = it / HC, c = it - t * HC;
         const u32x4 lo = *reinterpret_cast<const u32x4*>(kt + (kBlock + t) * GE::ROW + c * 16);
         const u32x4 hi = *reinterpret_cast<const u32x4*>(kt + (kBlock + t) * GE::ROW + (c + HC) * 16);
@@ -572,7 +620,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
         *reinterpret_cast<u32x4*>(kt + t * GE::ROW + (((c + HC) ^ kswz<D>(t)) << 4)) = yhi;
       }
       __syncthreads();
-      if (grp == 0) attend_stage<D>(kt, qB, o, m, lsum, lane, kBlock, p.scale_log2);
+      if (grp == 0) attend_stage<D, QHL>(kt, qB, qL, o, m, lsum, lane, kBlock, p.scale_log2);
     }
   }
 
@@ -583,8 +631,8 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
     if (pk + NPK - 1 < n_pk) issue(pk + NPK - 1);
     const int st = NGRP * pk + grp;
     if (st < n_st)
-      attend_stage<D>(lds + (st % NST) * GE::STAGE, qB, o, m, lsum, lane, min(TK, ke - kb - st * TK),
-                            p.scale_log2);
+      attend_stage<D, QHL>(lds + (st % NST) * GE::STAGE, qB, qL, o, m, lsum, lane, min(TK, ke - kb - st * TK),
+                           p.scale_log2);
   }
 
   // One wave group: block keys (positions L .. L+15) after the context, in the
@@ -601,10 +649,12 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
       const int64_t rowoff = (((int64_t)b * kBlock + t) * p.n_kv_heads + g) * D;
       const uint16_t* kr = p.k_blk + rowoff;
       const uint16_t* vr = p.v_blk + rowoff;
-      const float c = p.rope_cos[(int64_t)(L + t) * HALF + j];
-      const float sn = p.rope_sin[(int64_t)(L + t) * HALF + j];
-      uint16_t y0, y1;
-      rope_pair_bf16(bf16_to_f32(kr[j]), bf16_to_f32(kr[j + HALF]), c, sn, y0, y1);
+      uint16_t y0 = kr[j], y1 = kr[j + HALF];  // QHL: already rotated
+      if (!QHL) {
+        const float c = p.rope_cos[(int64_t)(L + t) * HALF + j];
+        const float sn = p.rope_sin[(int64_t)(L + t) * HALF + j];
+        rope_pair_bf16(bf16_to_f32(kr[j]), bf16_to_f32(kr[j + HALF]), c, sn, y0, y1);
+      }
       const int j2 = j + HALF;
       *reinterpret_cast<uint16_t*>(kt + t * GE::ROW + (((j >> 3) ^ kswz<D>(t)) << 4) + 2 * (j & 7)) = y0;
       *reinterpret_cast<uint16_t*>(kt + t * GE::ROW + (((j2 >> 3) ^ kswz<D>(t)) << 4) + 2 * (j2 & 7)) = y1;
@@ -612,7 +662,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
       *reinterpret_cast<uint16_t*>(vt + t * GE::ROW + (((j2 >> 3) ^ vswz<D>(t)) << 4) + 2 * (j2 & 7)) = vr[j2];
     }
     __syncthreads();
-    if (grp == 0) attend_stage<D>(lds, qB, o, m, lsum, lane, kBlock, p.scale_log2);
+    if (grp == 0) attend_stage<D, QHL>(lds, qB, qL, o, m, lsum, lane, kBlock, p.scale_log2);
   }
 
   // Combine the wave groups in LDS (stage slots 2.. are free: every wave passed
@@ -862,7 +912,10 @@ template <int D, int G, bool PAGED>
 hipError_t launch_t(const AttnParams& p, hipStream_t stream) {
   const int groups = (p.n_units + kNumXcd - 1) / kNumXcd;
   const int grid = kNumXcd * p.n_splits * groups;
-  hipLaunchKernelGGL((block_attn_kernel<D, G, PAGED>), dim3(grid), dim3(64 * ngrp<G>() * G), 0, stream, p);
+  if (p.q_lo)
+    hipLaunchKernelGGL((block_attn_kernel<D, G, PAGED, true>), dim3(grid), dim3(64 * ngrp<G>() * G), 0, stream, p);
+  else
+    hipLaunchKernelGGL((block_attn_kernel<D, G, PAGED, false>), dim3(grid), dim3(64 * ngrp<G>() * G), 0, stream, p);
   if (p.n_splits > 1 && !p.fused)
     hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(p.n_units * G * (D / 32)), dim3(256), 0, stream, p, G);
   return hipGetLastError();

@@ -54,6 +54,8 @@ hipError_t launch_rope_tables(double base, int head_dim, int max_pos, float* cos
 // ---------------------------------------------------------------- block attention
 struct AttnParams {
   const uint16_t* q_blk;
+  const uint16_t* q_lo;     // null: q_blk is the pre-RoPE q; else q_blk / q_lo are the rotated Q's
+                            // bf16 hi / lo parts and k_blk the rotated block K (fused q/k/v path)
   const uint16_t* k_blk;
   const uint16_t* v_blk;
   const uint16_t* k_cache;
@@ -105,7 +107,25 @@ struct GemmParams {
   const uint16_t* xp;                  // skinny path: A packed as [K/64][mp][64] (64-K steps)
   int mp;                              // rows of a packed step (M rounded up to 32)
   int m_off, m_rows;                   // skinny path: this launch's rows [m_off, m_off + m_rows) of M
+  // Fused q/k/v epilogue (the block's q/k/v feeding the attention directly): the K
+  // splits of a 128-column tile hand their partial tiles over inside one XCD's L2 and
+  // the last one writes the rotated Q as a bf16 hi/lo pair, the rotated block K and V.
+  uint32_t* cnt;                       // [ncols][32] arrival counters, zero between calls
+  float* tile;                         // [ncols][splits][tile_rows][128] partial tiles
+  int tile_rows;                       // rows of a tile slot (>= 16 * MT of every chunk)
+  const int32_t* ctx_len;              // [B] committed lengths: block row i at position L + i
+  int max_ctx;
+  const float* rope_cos;
+  const float* rope_sin;
+  int head_dim, nq, nk;                // nq = Hq d, nk = Hkv d; N = nq + 2 nk
+  uint16_t* q_hi;                      // [M][nq] bf16: the rotated q, rounded
+  uint16_t* q_lo;                      // [M][nq] bf16: what the rounding left
+  uint16_t* k_out;                     // [M][nk] bf16: the rotated k
+  uint16_t* v_out;                     // [M][nk] bf16
+  uint32_t* err;
+  uint32_t xcc_mask;
 };
+hipError_t launch_qkv_fused(const GemmParams& p, int splits, hipStream_t stream);
 struct PackParams {
   const uint16_t* a_seg[kMaxLayers];  // as GemmParams
   int64_t lda;

@@ -60,6 +60,9 @@ def _load() -> ctypes.CDLL:
         "dflash_draft_layer_post": (_c_int, [P, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_f, _vp, _vp, _c_sz,
                                              _vp]),
         "dflash_gdn_tape_replay": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+        "dflash_block_qkv_attn_workspace_size": (_c_sz, [P, _c_int]),
+        "dflash_block_qkv_attn": (_c_int, [P, _vp, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp,
+                                           _vp, _c_sz, _vp]),
         "dflash_verify_workspace_size": (_c_sz, [_c_int, _c_int, _c_int]),
         "dflash_draft_argmax": (_c_int, [_c_int, _c_int, _c_int, _vp, _c_i64, _vp, _vp, _vp, _c_sz, _vp]),
         "dflash_block_qkv_workspace_size": (_c_sz, [P]),
@@ -83,7 +86,7 @@ EXPORTS = (
     "dflash_verify_workspace_size", "dflash_verify_accept", "dflash_draft_argmax",
     "dflash_block_qkv_workspace_size", "dflash_block_qkv", "dflash_block_attn_noalloc",
     "dflash_rmsnorm", "dflash_draft_layer_post_workspace_size", "dflash_draft_layer_post",
-    "dflash_gdn_tape_replay",
+    "dflash_gdn_tape_replay", "dflash_block_qkv_attn_workspace_size", "dflash_block_qkv_attn",
 )
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -341,6 +344,37 @@ def dflash_block_qkv(dims: dflash_dims, h: torch.Tensor, w_qkv: torch.Tensor, q_
         _dev(w_qkv, "w_qkv", _BF16), _dev(q_blk, "q_blk", _BF16), _dev(k_blk, "k_blk", _BF16),
         _dev(v_blk, "v_blk", _BF16), _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(),
         _stream(stream)))
+
+
+def dflash_block_qkv_attn_workspace_size(dims: dflash_dims, max_ctx_len: int) -> int:
+    return int(_lib.dflash_block_qkv_attn_workspace_size(ctypes.byref(dims), max_ctx_len))
+
+
+def dflash_block_qkv_attn(dims: dflash_dims, h: torch.Tensor, w_qkv: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, page_table: Optional[torch.Tensor], ctx_len: torch.Tensor,
+                          max_ctx_len: int, rope_cos: torch.Tensor, rope_sin: torch.Tensor, out: torch.Tensor,
+                          workspace: torch.Tensor, stream=None) -> None:
+    """The block's q/k/v and the attention in one call: h [16B, ld_h] bf16, w_qkv [(Hq+2Hkv)d, hidden]."""
+    if h.dim() != 2 or h.stride(1) != 1:
+        raise ValueError("h must be a [rows, ld_h] tensor with unit inner stride")
+    B, Hq, Hkv, d = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    if h.shape[0] != BLOCK * B or h.shape[1] < dims.hidden:
+        raise ValueError(f"h must hold {BLOCK * B} rows of at least {dims.hidden} features")
+    _numel(w_qkv, (Hq + 2 * Hkv) * d * dims.hidden, "w_qkv")
+    _numel(k_cache, _cache_numel(dims), "k_cache")
+    _numel(v_cache, _cache_numel(dims), "v_cache")
+    if dims.page_size > 0:
+        _numel(page_table, B * dims.kv_capacity, "page_table")
+    _numel(ctx_len, B, "ctx_len")
+    _numel(out, B * BLOCK * Hq * d, "out")
+    _check_rope(rope_cos, rope_sin, d)
+    _check("dflash_block_qkv_attn", _lib.dflash_block_qkv_attn(
+        ctypes.byref(dims), _dev(h, "h", _BF16, contiguous=False), int(h.stride(0)), _dev(w_qkv, "w_qkv", _BF16),
+        _dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16),
+        _dev(page_table, "page_table", (torch.int32,)), _dev(ctx_len, "ctx_len", (torch.int32,)), max_ctx_len,
+        _dev(rope_cos, "rope_cos", (torch.float32,)), _dev(rope_sin, "rope_sin", (torch.float32,)),
+        int(rope_cos.shape[0]), _dev(out, "out", (torch.float32,)), _dev(workspace, "workspace", (torch.uint8,)),
+        workspace.numel(), _stream(stream)))
 
 
 def dflash_draft_argmax(logits: torch.Tensor, staged: Optional[torch.Tensor], block_tokens: torch.Tensor,

@@ -262,6 +262,32 @@ int dflash_block_qkv(const dflash_dims* dims, const void* h, int64_t ld_h, const
                      void* q_blk, void* k_blk, void* v_blk,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- the block's q/k/v and the attention in one call ------------------------
+ * dflash_block_qkv followed by dflash_block_attn, with the hand-off between them
+ * fused ("DFlash dual implementations", §2: Q from the block tokens only, the
+ * block's K/V as the second source).  Per sequence b, block row i at position
+ * L + i (L = ctx_len[b]):
+ *   q, k, v = h[b,i] . w_qkv^T                     (fp32 accumulation, not rounded)
+ *   Q      = RoPE(q)                               (carried as a bf16 pair hi + lo,
+ *                                                    ~16 significant bits: no bf16
+ *                                                    rounding of q or Q on the way)
+ *   K_blk  = bf16(RoPE(k)),  V_blk = bf16(v)       (rounded once)
+ *   out    = the attention of dflash_block_attn over [context ; block] (dims->window
+ *            honoured), fp32.
+ * The q/k/v product's K splits of each 128-column tile hand their partial tiles over
+ * inside one XCD's L2; the last split rotates and rounds them into the attention's
+ * inputs, so no separate reduce kernel runs.  Arguments as for dflash_block_qkv (h,
+ * ld_h, w_qkv; batch <= 32, i.e. at most 512 block rows: DFLASH_ERR_UNSUPPORTED above)
+ * and dflash_block_attn (cache, ctx_len, max_ctx_len, rope tables, out).  The
+ * workspace (dflash_block_qkv_attn_workspace_size) also holds the q/k/v outputs; zero
+ * it once before first use, as for the attention. */
+size_t dflash_block_qkv_attn_workspace_size(const dflash_dims* dims, int32_t max_ctx_len);
+int dflash_block_qkv_attn(const dflash_dims* dims, const void* h, int64_t ld_h, const void* w_qkv,
+                          const void* k_cache, const void* v_cache, const int32_t* page_table,
+                          const int32_t* ctx_len, int32_t max_ctx_len, const float* rope_cos,
+                          const float* rope_sin, int32_t max_pos, float* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* ---- draft-side greedy tokens (the step before the verify) ----------------
  * One draft forward over the block [staged, mask x 15] yields the 15
  * candidate tail tokens ("dflash-mlx: lossless speculative decoding",
