@@ -160,6 +160,17 @@ def qkv_bytes(cfg, B):
     return 2 * (n_out * cfg.hidden + 16 * B * cfg.hidden + 16 * B * n_out)
 
 
+def fused_bytes(cfg, ctx_len):
+    # the fused q/k/v weight and the block hidden states in, the context K/V cache read,
+    # the fp32 attention output out (the block's q/k/v never leave the call)
+    B, Hq, Hkv, d = len(ctx_len), cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    n_out = (Hq + 2 * Hkv) * d
+    b = 2 * (n_out * cfg.hidden + 16 * B * cfg.hidden) + 4 * Hkv * d * int(ctx_len.sum()) + 4 * 16 * B * Hq * d + 4 * B
+    if cfg.page_size:
+        b += 4 * int(((ctx_len + 15) // 16).sum())
+    return b
+
+
 def layer_bytes(cfg, B):
     # the draft layer around the attention: input RMSNorm (x in, n1 out, weight) and the
     # post-attention part (o_proj, gate/up, down weights; x and the fp32 attention output
@@ -344,7 +355,7 @@ def main():
     # at the end of each pass step, on the next copy of the logits, with the verify's
     # next_token as its staged tokens.
     N_SPLIT = 50
-    NEV = 9
+    NEV = 10
     tev = HipTimingEvents(2 * args.steps, torch.cuda.current_stream().cuda_stream)
     sev = HipTimingEvents(NEV * N_SPLIT, torch.cuda.current_stream().cuda_stream)
     dblk = z(B, 16)
@@ -368,6 +379,10 @@ def main():
     gi = synth.gdn_tape_inputs(B, GH, GD, GD, seed=cfg.seed)
     g_state, g_out = torch.from_numpy(gi.state).to(dev), torch.empty(B, GH, GD, GD, dtype=torch.float32, device=dev)
     g_k, g_g, g_d = u16(gi.k_tape), torch.from_numpy(gi.g_tape).to(dev), torch.from_numpy(gi.delta_tape).to(dev)
+    # ... and the block's q/k/v with the attention in one call (dflash_block_qkv_attn), on
+    # the same hidden states and weight as dflash_block_qkv, into its own output
+    ws_f = dfl.workspace(dfl.dflash_block_qkv_attn_workspace_size(dims, max_ctx), dev)
+    out_f = torch.empty_like(out)
 
     # The attention calls are prepared once per input copy (checks and argument conversion
     # done here), so the event before a call is followed at once by the launch: with an
@@ -400,6 +415,8 @@ def main():
             ev.record(base + 7)
             dfl.dflash_gdn_tape_replay(g_state, g_out, g_k, g_g, g_d, acc)
             ev.record(base + 8)
+            dfl.dflash_block_qkv_attn(dims, h_blk, w_qkv, kcs[i], vcs[i], table, ctx, max_ctx, cos, sin, out_f, ws_f)
+            ev.record(base + 9)
 
     n_settle = 0
     t_settle = time.perf_counter()
@@ -425,7 +442,8 @@ def main():
     t_attn = float(np.mean([tev.elapsed_ms(2 * s, 2 * s + 1) for s in range(args.steps)])) * 1e-3
     span = lambda i, j: float(np.mean([sev.elapsed_ms(NEV * s + i, NEV * s + j) for s in range(N_SPLIT)])) * 1e-3
     t_ver, t_proj, t_draft, t_qkv = span(1, 2), span(2, 3), span(3, 4), span(4, 5)
-    t_norm, t_post, t_replay = span(5, 6), span(6, 7), span(7, 8)
+    t_norm, t_post, t_replay, t_fused = span(5, 6), span(6, 7), span(7, 8), span(8, 9)
+    f_b = fused_bytes(cfg, at.ctx_len)
     nb, pb = layer_bytes(cfg, B)
     rb = replay_bytes(B, GH, GD, GD, acc.cpu().numpy())
     d_b = draft_bytes(cfg, B)
@@ -475,6 +493,12 @@ def main():
                        "pct_hbm_peak": round(100 * rb / t_replay / 1e9 / HBM_PEAK_GBS, 2), "bytes": rb,
                        "shape": f"B={B}, 32 heads, 128x128 fp32 state, the verify's accept lengths",
                        "scope": "rollback of recurrent state to the accepted prefix; not in the timed step"},
+        "block_qkv_attn": {"us": round(t_fused * 1e6, 2), "GB_s": round(f_b / t_fused / 1e9, 1),
+                            "pct_hbm_peak": round(100 * f_b / t_fused / 1e9 / HBM_PEAK_GBS, 2), "bytes": f_b,
+                            "unfused_us": round((t_qkv + t_attn) * 1e6, 2),
+                            "scope": "the block's q/k/v and the attention in one call (split-K GEMM, a "
+                                     "reduce that rotates Q into a bf16 hi/lo pair and K, then the attention); "
+                                     "unfused_us = block_qkv + block_attn; not in the timed step"},
         "timing": "block_attn: HIP events around every timed call; the other calls: events in a %d-step "
                   "pass after the timed region" % N_SPLIT,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

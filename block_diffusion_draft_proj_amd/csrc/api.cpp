@@ -644,10 +644,11 @@ int dflash_gdn_tape_replay(int32_t batch, int32_t n_heads, int32_t d_k, int32_t 
 struct FusedPlan {
   QkvPlan qkv;
   AttnPlan attn;
-  int tile_rows, ncols;
-  size_t off_tile, off_qhi, off_qlo, off_k, off_v, ws_bytes;
+  size_t off_part, off_qhi, off_qlo, off_k, off_v, ws_bytes;
 };
 
+// Workspace: the attention's own region first (its error word and counters at the
+// start), then the q/k/v product's fp32 split partials and the attention's inputs.
 static FusedPlan plan_fused(const dflash_dims* dims, int32_t max_ctx_len) {
   FusedPlan f{};
   const int M = dims->batch * DFLASH_BLOCK;
@@ -656,12 +657,10 @@ static FusedPlan plan_fused(const dflash_dims* dims, int32_t max_ctx_len) {
   f.qkv = plan_block_qkv(M, dims->hidden, n_out, kPlanCUs);
   f.attn = plan_block_attn(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
                            attended_keys(dims, max_ctx_len), kPlanCUs);
-  f.tile_rows = M <= 128 ? 32 * ((M + 31) / 32) : 256;  // 16 * MT of the largest skinny chunk
-  f.ncols = (n_out + 127) / 128;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = align(f.attn.ws_bytes);
-  f.off_tile = off;
-  off = align(off + sizeof(float) * (size_t)f.ncols * f.qkv.splits * f.tile_rows * 128);
+  f.off_part = off;
+  off = align(off + sizeof(float) * (size_t)f.qkv.splits * M * n_out);
   f.off_qhi = off;
   off = align(off + 2 * (size_t)M * nq);
   f.off_qlo = off;
@@ -676,7 +675,7 @@ static FusedPlan plan_fused(const dflash_dims* dims, int32_t max_ctx_len) {
 
 size_t dflash_block_qkv_attn_workspace_size(const dflash_dims* dims, int32_t max_ctx_len) {
   if (check_qkv_dims(dims) != DFLASH_OK || max_ctx_len < 0) return 0;
-  if (dims->batch * DFLASH_BLOCK > 512 || (int64_t)dims->batch * dims->n_kv_heads > kMaxCountSlots) return 0;
+  if ((int64_t)dims->batch * dims->n_kv_heads > kMaxCountSlots) return 0;
   return plan_fused(dims, max_ctx_len).ws_bytes;
 }
 
@@ -688,7 +687,6 @@ int dflash_block_qkv_attn(const dflash_dims* dims, const void* h, int64_t ld_h, 
   int st = check_qkv_dims(dims);
   if (st != DFLASH_OK) return st;
   if (!h || !w_qkv || !k_cache || !v_cache || !ctx_len || !rope_cos || !rope_sin || !out) return DFLASH_ERR_NULL;
-  if (dims->batch * DFLASH_BLOCK > 512) return DFLASH_ERR_UNSUPPORTED;  // the skinny product's rows
   if (ld_h < dims->hidden) return DFLASH_ERR_SHAPE;
   if ((ld_h & 7) || !aligned16(h) || !aligned16(w_qkv)) return DFLASH_ERR_ALIGN;
   if (max_ctx_len < 0 || max_ctx_len > (1 << 24)) return DFLASH_ERR_SHAPE;
@@ -699,45 +697,46 @@ int dflash_block_qkv_attn(const dflash_dims* dims, const void* h, int64_t ld_h, 
   char* ws = static_cast<char*>(workspace);
   const int M = dims->batch * DFLASH_BLOCK;
   const int nq = dims->n_q_heads * dims->head_dim, nk = dims->n_kv_heads * dims->head_dim;
-  // The attention's checks first (nothing is launched before both parts validate); the
-  // q/k/v outputs are the attention's inputs.
+  const int n_out = nq + 2 * nk;
   uint16_t* qhi = reinterpret_cast<uint16_t*>(ws + f.off_qhi);
   uint16_t* qlo = reinterpret_cast<uint16_t*>(ws + f.off_qlo);
   uint16_t* kr = reinterpret_cast<uint16_t*>(ws + f.off_k);
   uint16_t* vv = reinterpret_cast<uint16_t*>(ws + f.off_v);
+  // The attention's checks first (nothing is launched before every part validates); the
+  // q/k/v outputs are its inputs.
   st = block_attn_run(dims, qhi, kr, vv, k_cache, v_cache, page_table, ctx_len, max_ctx_len, rope_cos, rope_sin,
                       max_pos, out, ws, f.attn.ws_bytes, nullptr, nullptr, nullptr, qlo, /*launch=*/false);
-  if (st != DFLASH_OK) return st;
-  uint32_t xcc_mask = 0;
-  st = check_device(&xcc_mask);
   if (st != DFLASH_OK) return st;
   GemmParams g{};
   g.a_seg[0] = static_cast<const uint16_t*>(h);
   g.lda = ld_h;
   g.seg_k = dims->hidden;
   g.b0 = g.b1 = static_cast<const uint16_t*>(w_qkv);
-  g.n_b0 = nq + 2 * nk;
+  g.n_b0 = n_out;
   g.M = M;
-  g.N = nq + 2 * nk;
+  g.N = n_out;
   g.K = dims->hidden;
   g.k_per_split = f.qkv.kps;
-  g.cnt = reinterpret_cast<uint32_t*>(ws + 256);  // the counter region, shared with the attention
-  g.tile = reinterpret_cast<float*>(ws + f.off_tile);
-  g.tile_rows = f.tile_rows;
-  g.ctx_len = ctx_len;
-  g.max_ctx = max_ctx_len;
-  g.rope_cos = rope_cos;
-  g.rope_sin = rope_sin;
-  g.head_dim = dims->head_dim;
-  g.nq = nq;
-  g.nk = nk;
-  g.q_hi = qhi;
-  g.q_lo = qlo;
-  g.k_out = kr;
-  g.v_out = vv;
-  g.err = reinterpret_cast<uint32_t*>(ws);
-  g.xcc_mask = xcc_mask;
-  if (launch_qkv_fused(g, f.qkv.splits, stream) != hipSuccess) return DFLASH_ERR_LAUNCH;
+  g.out = reinterpret_cast<float*>(ws + f.off_part);
+  if (launch_gemm_nt(g, f.qkv.splits, f.qkv.small, stream) != hipSuccess) return DFLASH_ERR_LAUNCH;
+  QkvRopeParams r{};
+  r.part = g.out;
+  r.splits = f.qkv.splits;
+  r.M = M;
+  r.N = n_out;
+  r.nq = nq;
+  r.nk = nk;
+  r.head_dim = dims->head_dim;
+  r.ctx_len = ctx_len;
+  r.max_ctx = max_ctx_len;
+  r.rope_cos = rope_cos;
+  r.rope_sin = rope_sin;
+  r.q_hi = qhi;
+  r.q_lo = qlo;
+  r.k_out = kr;
+  r.v_out = vv;
+  r.err = reinterpret_cast<uint32_t*>(ws);  // the attention's error word
+  if (launch_qkv_rope(r, stream) != hipSuccess) return DFLASH_ERR_LAUNCH;
   return block_attn_run(dims, qhi, kr, vv, k_cache, v_cache, page_table, ctx_len, max_ctx_len, rope_cos, rope_sin,
                         max_pos, out, ws, f.attn.ws_bytes, nullptr, nullptr, stream, qlo);
 }

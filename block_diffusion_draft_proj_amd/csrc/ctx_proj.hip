@@ -168,162 +168,13 @@ struct SkGeo {
   static_assert(NS >= 3, "two stages in flight");
 };
 
-constexpr int kQkvSpinLimit = 1 << 20;  // polls of the stored count (~0.5 s) before giving up
-
-// The fused q/k/v epilogue of one 128-column tile (weight rows n0 .. n0 + 127) of the
-// chunk's activation rows.  acc: this split's products in the D layout (lane: row
-// 16*(MTW*wt + mt) + r, columns 32*wr + 16*rt + 4q .. +3).
-//  1. Hand-off (splits > 1): a split counts its arrival first; every split but the last
-//     stores its partial tile write-through (the L2 keeps a valid copy), waits for the
-//     acknowledgement and counts it as stored; the last waits until all others are
-//     stored, clears the counter and sums the tiles in split order (so the result does
-//     not depend on which split arrived last).  Arrivals are L2 atomics: every split of
-//     the tile runs on one XCD (decode above).
-//  2. The summed tile goes through LDS (a RoPE pair (j, j + d/2) lies in two waves).
-//  3. Per element: q -> rotated at its block position in fp64 (products of fp32 values
-//     are exact), stored as hi = bf16(y) and lo = bf16(y - hi); k -> the rotation rounded
-//     once to bf16 (exactly); v -> bf16.
-template <int MT>
-__device__ __forceinline__ void qkv_epilogue(const GemmParams& p, f32x4 (&acc)[SK_RT][SkGeo<MT>::MTW], char* lds,
-                                             uint32_t& s_last, int z, int col, int splits, int w, int lane) {
-  using SG = SkGeo<MT>;
-  constexpr int MTW = SG::MTW;
-  const int tid = threadIdx.x, r = lane & 15, q = lane >> 4;
-  const int wr = w % SK_RW, wt = w / SK_RW;
-  const int n0 = col * SK_ROWS;
-  constexpr int kWT = 1 | 16;  // sc0 | sc1: write-through
-  constexpr int kL2 = 1;       // sc0: served by the L2
-  const int64_t slot_elems = (int64_t)p.tile_rows * SK_ROWS;
-  float* slot0 = p.tile + (int64_t)col * splits * slot_elems;
-  auto off = [&](int rt, int mt) { return ((wt * MTW + mt) * 16 + r) * SK_ROWS + wr * 32 + rt * 16 + 4 * q; };
-  if (splits > 1) {
-    uint32_t* cnt = p.cnt + (int64_t)col * 32;
-    uint32_t prev = 0;
-    if (tid == 0) {
-      prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      s_last = (prev & 0xffffu) == (uint32_t)(splits - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (!__builtin_amdgcn_readfirstlane(s_last)) {
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(slot0 + z * slot_elems, 0,
-                                                                          (int)(slot_elems * 4), 0x00020000);
-#pragma unroll
-      for (int rt = 0; rt < SK_RT; ++rt)
-#pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[rt][mt]), rs, off(rt, mt) * 4, 0, kWT);
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      wait_vmcnt<0>();  // this wave's tile rows are in the L2
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __syncthreads();  // ... and every other wave's
-      if (tid == 0) __hip_atomic_fetch_add(cnt, 1u << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      return;
-    }
-    if (tid == 0) {
-      uint32_t v = prev;
-      for (int spin = 0; (v >> 16) != (uint32_t)(splits - 1); ++spin) {
-        if (spin >= kQkvSpinLimit) {  // cannot happen while the stored splits run; never hang
-          set_dev_error(p.err, kDevErrMerge);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-        uint32_t zero;  // an atomic add of an opaque zero, performed in the L2 (a load would hit L1)
-        asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
-        v = __hip_atomic_fetch_add(cnt, zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    __syncthreads();
-    f32x4 sum[SK_RT][MTW];
-#pragma unroll
-    for (int rt = 0; rt < SK_RT; ++rt)
-#pragma unroll
-      for (int mt = 0; mt < MTW; ++mt) sum[rt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    for (int zz = 0; zz < splits; ++zz) {
-      if (zz == z) {
-#pragma unroll
-        for (int rt = 0; rt < SK_RT; ++rt)
-#pragma unroll
-          for (int mt = 0; mt < MTW; ++mt) sum[rt][mt] += acc[rt][mt];
-        continue;
-      }
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(slot0 + zz * slot_elems, 0,
-                                                                          (int)(slot_elems * 4), 0x00020000);
-      u32x4 v[SK_RT][MTW];
-#pragma unroll
-      for (int rt = 0; rt < SK_RT; ++rt)
-#pragma unroll
-        for (int mt = 0; mt < MTW; ++mt) v[rt][mt] = __builtin_amdgcn_raw_buffer_load_b128(rs, off(rt, mt) * 4, 0, kL2);
-#pragma unroll
-      for (int rt = 0; rt < SK_RT; ++rt)
-#pragma unroll
-        for (int mt = 0; mt < MTW; ++mt) sum[rt][mt] += __builtin_bit_cast(f32x4, v[rt][mt]);
-    }
-#pragma unroll
-    for (int rt = 0; rt < SK_RT; ++rt)
-#pragma unroll
-      for (int mt = 0; mt < MTW; ++mt) acc[rt][mt] = sum[rt][mt];
-  }
-  // The summed tile through LDS (the ring is free once every wave passed its last stage).
-  __syncthreads();
-  float* t = reinterpret_cast<float*>(lds);  // [TR][128]
-#pragma unroll
-  for (int rt = 0; rt < SK_RT; ++rt)
-#pragma unroll
-    for (int mt = 0; mt < MTW; ++mt) *reinterpret_cast<f32x4*>(t + off(rt, mt)) = acc[rt][mt];
-  __syncthreads();
-  const int d = p.head_dim, half = d / 2;
-  const int hq = p.nq / d, hk = p.nk / d;
-  for (int idx = tid; idx < p.m_rows * SK_ROWS; idx += SG::WAVES * 64) {
-    const int m = idx / SK_ROWS, nl = idx - m * SK_ROWS;
-    const int n = n0 + nl;
-    if (n >= p.N) continue;
-    const int mg = p.m_off + m;  // row of the block batch: sequence mg / 16, block row mg % 16
-    const float x0 = t[m * SK_ROWS + nl];
-    if (n >= p.nq + p.nk) {  // v
-      p.v_out[(int64_t)mg * p.nk + (n - p.nq - p.nk)] = f32_to_bf16(x0);
-      continue;
-    }
-    const bool is_q = n < p.nq;
-    const int nn = is_q ? n : n - p.nq;
-    const int head = nn / d, j = nn - head * d;
-    if (j >= half) continue;  // handled with its pair partner j - d/2
-    const float x1 = t[m * SK_ROWS + nl + half];
-    int L = p.ctx_len[mg / kBlock];
-    if (L < 0 || L > p.max_ctx) {
-      if ((mg & (kBlock - 1)) == 0 && j == 0 && head == 0 && is_q) set_dev_error(p.err, kDevErrCtxLen);
-      L = L < 0 ? 0 : p.max_ctx;
-    }
-    const int pos = L + (mg & (kBlock - 1));
-    const float c = p.rope_cos[(int64_t)pos * half + j], s = p.rope_sin[(int64_t)pos * half + j];
-    if (is_q) {
-      const double y0 = (double)x0 * (double)c - (double)x1 * (double)s;
-      const double y1 = (double)x1 * (double)c + (double)x0 * (double)s;
-      const uint16_t h0 = bf16_of_exact_sum(y0, 0.0), h1 = bf16_of_exact_sum(y1, 0.0);
-      const int64_t o = ((int64_t)mg * hq + head) * d + j;
-      p.q_hi[o] = h0;
-      p.q_hi[o + half] = h1;
-      p.q_lo[o] = bf16_of_exact_sum(y0, -(double)bf16_to_f32(h0));
-      p.q_lo[o + half] = bf16_of_exact_sum(y1, -(double)bf16_to_f32(h1));
-    } else {
-      uint16_t y0, y1;
-      rope_pair_bf16(x0, x1, c, s, y0, y1);
-      const int64_t o = ((int64_t)mg * hk + head) * d + j;
-      p.k_out[o] = y0;
-      p.k_out[o + half] = y1;
-    }
-  }
-}
-
 // PACKED: activations come packed as [K/64][mp][64] steps (written by
 // fc_reduce_kernel for the K/V product); else they are read in place from the
 // segments a_seg[] ([M][lda] each, seg_k columns of K per segment).
-// QKV: the fused q/k/v epilogue (see GemmParams) instead of storing fp32 partials.
-template <int MT, bool PACKED, bool QKV = false>
+template <int MT, bool PACKED>
 __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(GemmParams p) {
   using SG = SkGeo<MT>;
   __shared__ __attribute__((aligned(1024))) char lds[SG::NS * SG::STAGE];
-  __shared__ uint32_t s_last;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
@@ -332,19 +183,10 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
   // ranges as possible, so the activation slice of its range (16*MT rows x K/splits)
   // stays in that XCD's L2 while all column tiles stream their weights past it.
   // The planner makes `splits` a divisor or a multiple of 8.
-  // QKV: the splits of a column tile share one XCD instead (column c on XCD c % 8), so
-  // they hand their partial tiles over inside its L2; each XCD then reads all of the
-  // (small) activation block.
   const int splits = (p.K + p.k_per_split - 1) / p.k_per_split;
   const int id = blockIdx.x;
   int z, col;
-  if constexpr (QKV) {
-    if (tid == 0 && ((xcc_id() ^ (uint32_t)id) & p.xcc_mask) != 0) set_dev_error(p.err, kDevErrXcd);
-    const int j = id / kNumXcd;
-    z = j % splits;
-    col = id % kNumXcd + kNumXcd * (j / splits);
-    if (col * SK_ROWS >= p.N) return;
-  } else if (splits % kNumXcd == 0) {
+  if (splits % kNumXcd == 0) {
     const int per = splits / kNumXcd, j = id / kNumXcd;
     z = id % kNumXcd + kNumXcd * (j % per);
     col = j / per;
@@ -451,11 +293,6 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
     }
   }
 
-  if constexpr (QKV) {
-    qkv_epilogue<MT>(p, acc, lds, s_last, z, col, splits, w, lane);
-    return;
-  }
-
   // D layout: lane holds activation row 16*(MTW*wt + mt) + r and weight rows 4q .. 4q+3 of
   // the 16-row tile: 4 consecutive outputs of one row, one 16-byte store.
   float* out = p.out + (int64_t)z * p.M * p.N;
@@ -540,6 +377,72 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(QkvReduceParams p) {
   else if (n < p.nq + p.nk) dst = p.k + m * p.nk + (n - p.nq);
   else dst = p.v + m * p.nk + (n - p.nq - p.nk);
   *reinterpret_cast<u32x2*>(dst) = v;
+}
+
+// The block's q/k/v handed to the attention: thread = (row, head of q, k or v, 4
+// consecutive j < d/2), i.e. columns j .. j+3 and j+d/2 .. j+d/2+3 of one head.  The
+// split sums are issued before the row's position is known.
+//   q: rotated at the position (fp64 products and sum, then fp32: within 2^-24
+//      relative), kept as hi = bf16(y) and lo = bf16(y - hi) (y - hi is exact in fp32),
+//      which carry y to about 2^-17 relative;
+//   k: the exact rotation rounded once to bf16;  v: bf16.
+__global__ __launch_bounds__(256) void qkv_rope_kernel(QkvRopeParams p) {
+  const int half = p.head_dim / 2;
+  const int per_row = p.N / 8;  // (Hq + 2 Hkv) heads x d/8 column groups
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)p.M * per_row) return;
+  const int m = (int)(i / per_row);
+  const int rem = (int)(i - (int64_t)m * per_row);
+  const int head = rem / (half / 4);            // over q, k and v heads in column order
+  const int j = (rem - head * (half / 4)) * 4;
+  const int c0 = head * p.head_dim + j;         // columns c0 .. c0+3 and c0+half ..
+  const float* base = p.part + (int64_t)m * p.N;
+  const int64_t zs = (int64_t)p.M * p.N;
+  const f32x4 x0 = sum_splits(base + c0, zs, p.splits);
+  const f32x4 x1 = sum_splits(base + c0 + half, zs, p.splits);
+  if (c0 >= p.nq + p.nk) {  // v
+    uint16_t* dst = p.v_out + (int64_t)m * p.nk + (c0 - p.nq - p.nk);
+    *reinterpret_cast<u32x2*>(dst) = (u32x2){pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3])};
+    *reinterpret_cast<u32x2*>(dst + half) = (u32x2){pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
+    return;
+  }
+  const int seq = m / kBlock;
+  int L = p.ctx_len[seq];
+  if (L < 0 || L > p.max_ctx) {
+    if ((m & (kBlock - 1)) == 0 && rem == 0) set_dev_error(p.err, kDevErrCtxLen);
+    L = L < 0 ? 0 : p.max_ctx;
+  }
+  const int pos = L + (m & (kBlock - 1));
+  const f32x4 c = *reinterpret_cast<const f32x4*>(p.rope_cos + (int64_t)pos * half + j);
+  const f32x4 s = *reinterpret_cast<const f32x4*>(p.rope_sin + (int64_t)pos * half + j);
+  if (c0 >= p.nq) {  // k
+    uint16_t y0[4], y1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rope_pair_bf16(x0[e], x1[e], c[e], s[e], y0[e], y1[e]);
+    uint16_t* dst = p.k_out + (int64_t)m * p.nk + (c0 - p.nq);
+    *reinterpret_cast<u32x2*>(dst) = (u32x2){y0[0] | (uint32_t)y0[1] << 16, y0[2] | (uint32_t)y0[3] << 16};
+    *reinterpret_cast<u32x2*>(dst + half) = (u32x2){y1[0] | (uint32_t)y1[1] << 16, y1[2] | (uint32_t)y1[3] << 16};
+    return;
+  }
+  uint16_t h0[4], h1[4], l0[4], l1[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // products of fp32 values are exact in fp64: one rounding there, one to fp32
+    const float y0 = (float)((double)x0[e] * c[e] - (double)x1[e] * s[e]);
+    const float y1 = (float)((double)x1[e] * c[e] + (double)x0[e] * s[e]);
+    h0[e] = f32_to_bf16(y0);
+    h1[e] = f32_to_bf16(y1);
+    l0[e] = f32_to_bf16(y0 - bf16_to_f32(h0[e]));
+    l1[e] = f32_to_bf16(y1 - bf16_to_f32(h1[e]));
+  }
+  const int64_t o = (int64_t)m * p.nq + c0;
+  auto pack4 = [](const uint16_t (&v)[4]) {
+    return (u32x2){v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16};
+  };
+  *reinterpret_cast<u32x2*>(p.q_hi + o) = pack4(h0);
+  *reinterpret_cast<u32x2*>(p.q_hi + o + half) = pack4(h1);
+  *reinterpret_cast<u32x2*>(p.q_lo + o) = pack4(l0);
+  *reinterpret_cast<u32x2*>(p.q_lo + o + half) = pack4(l1);
 }
 
 // K/V rows: sum splits, rotate K (pairs j, j+d/2) at the row's position (exactly,
@@ -731,27 +634,6 @@ hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStre
   return hipGetLastError();
 }
 
-// Fused q/k/v product: chunks of up to kSkinnyChunk rows, each a pass over the
-// weights; column tile c's splits on XCD c % 8.
-hipError_t launch_qkv_fused(const GemmParams& p, int splits, hipStream_t stream) {
-  const int ncols = (p.N + SK_ROWS - 1) / SK_ROWS;
-  const dim3 grid(kNumXcd * splits * ((ncols + kNumXcd - 1) / kNumXcd), 1, 1);
-  for (int m_off = 0; m_off < max(p.M, 1); m_off += kSkinnyChunk) {
-    GemmParams c = p;
-    c.m_off = m_off;
-    c.m_rows = min(kSkinnyChunk, p.M - m_off);
-    switch ((c.m_rows + 31) / 32) {
-      case 0:
-      case 1: hipLaunchKernelGGL((gemm_skinny_kernel<2, false, true>), grid, dim3(SkGeo<2>::WAVES * 64), 0, stream, c); break;
-      case 2: hipLaunchKernelGGL((gemm_skinny_kernel<4, false, true>), grid, dim3(SkGeo<4>::WAVES * 64), 0, stream, c); break;
-      case 3: hipLaunchKernelGGL((gemm_skinny_kernel<6, false, true>), grid, dim3(SkGeo<6>::WAVES * 64), 0, stream, c); break;
-      case 4: hipLaunchKernelGGL((gemm_skinny_kernel<8, false, true>), grid, dim3(SkGeo<8>::WAVES * 64), 0, stream, c); break;
-      default: hipLaunchKernelGGL((gemm_skinny_kernel<16, false, true>), grid, dim3(SkGeo<16>::WAVES * 64), 0, stream, c); break;
-    }
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_pack_rows(const PackParams& p, hipStream_t stream) {
   const int64_t n = (int64_t)(p.K / 64) * p.mp * 8;
   hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p);
@@ -767,6 +649,12 @@ hipError_t launch_fc_reduce(const FcReduceParams& p, hipStream_t stream) {
 hipError_t launch_qkv_reduce(const QkvReduceParams& p, hipStream_t stream) {
   const int64_t n4 = (int64_t)p.M * p.N / 4;
   hipLaunchKernelGGL(qkv_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_rope(const QkvRopeParams& p, hipStream_t stream) {
+  const int64_t n = (int64_t)p.M * (p.N / 8);
+  hipLaunchKernelGGL(qkv_rope_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

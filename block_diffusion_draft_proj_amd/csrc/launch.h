@@ -107,25 +107,7 @@ struct GemmParams {
   const uint16_t* xp;                  // skinny path: A packed as [K/64][mp][64] (64-K steps)
   int mp;                              // rows of a packed step (M rounded up to 32)
   int m_off, m_rows;                   // skinny path: this launch's rows [m_off, m_off + m_rows) of M
-  // Fused q/k/v epilogue (the block's q/k/v feeding the attention directly): the K
-  // splits of a 128-column tile hand their partial tiles over inside one XCD's L2 and
-  // the last one writes the rotated Q as a bf16 hi/lo pair, the rotated block K and V.
-  uint32_t* cnt;                       // [ncols][32] arrival counters, zero between calls
-  float* tile;                         // [ncols][splits][tile_rows][128] partial tiles
-  int tile_rows;                       // rows of a tile slot (>= 16 * MT of every chunk)
-  const int32_t* ctx_len;              // [B] committed lengths: block row i at position L + i
-  int max_ctx;
-  const float* rope_cos;
-  const float* rope_sin;
-  int head_dim, nq, nk;                // nq = Hq d, nk = Hkv d; N = nq + 2 nk
-  uint16_t* q_hi;                      // [M][nq] bf16: the rotated q, rounded
-  uint16_t* q_lo;                      // [M][nq] bf16: what the rounding left
-  uint16_t* k_out;                     // [M][nk] bf16: the rotated k
-  uint16_t* v_out;                     // [M][nk] bf16
-  uint32_t* err;
-  uint32_t xcc_mask;
 };
-hipError_t launch_qkv_fused(const GemmParams& p, int splits, hipStream_t stream);
 struct PackParams {
   const uint16_t* a_seg[kMaxLayers];  // as GemmParams
   int64_t lda;
@@ -170,6 +152,24 @@ struct QkvReduceParams {
   uint16_t *q, *k, *v; // [M][nq], [M][nk], [M][nk] bf16
 };
 hipError_t launch_qkv_reduce(const QkvReduceParams& p, hipStream_t stream);
+
+// The block's q/k/v for the attention directly: sum of the splits, then per RoPE pair
+// (j, j + d/2) q rotated at the row's block position and kept as a bf16 hi/lo pair, k
+// rotated exactly and rounded once to bf16, v rounded to bf16.
+struct QkvRopeParams {
+  const float* part;         // [splits][M][N], N = nq + 2 nk
+  int splits, M, N, nq, nk, head_dim;
+  const int32_t* ctx_len;    // [M / 16]: block row i of sequence b at position ctx_len[b] + i
+  int max_ctx;
+  const float* rope_cos;     // [max_pos][d/2]
+  const float* rope_sin;
+  uint16_t* q_hi;            // [M][nq] bf16: the rotated q, rounded
+  uint16_t* q_lo;            // [M][nq] bf16: what that rounding left, rounded
+  uint16_t* k_out;           // [M][nk] bf16: the rotated k
+  uint16_t* v_out;           // [M][nk] bf16
+  uint32_t* err;
+};
+hipError_t launch_qkv_rope(const QkvRopeParams& p, hipStream_t stream);
 
 struct KvEpilogueParams {
   const float* part;   // [splits][M][2*Hkv*d]

@@ -274,13 +274,15 @@ int dflash_block_qkv(const dflash_dims* dims, const void* h, int64_t ld_h, const
  *   K_blk  = bf16(RoPE(k)),  V_blk = bf16(v)       (rounded once)
  *   out    = the attention of dflash_block_attn over [context ; block] (dims->window
  *            honoured), fp32.
- * The q/k/v product's K splits of each 128-column tile hand their partial tiles over
- * inside one XCD's L2; the last split rotates and rounds them into the attention's
- * inputs, so no separate reduce kernel runs.  Arguments as for dflash_block_qkv (h,
- * ld_h, w_qkv; batch <= 32, i.e. at most 512 block rows: DFLASH_ERR_UNSUPPORTED above)
- * and dflash_block_attn (cache, ctx_len, max_ctx_len, rope tables, out).  The
- * workspace (dflash_block_qkv_attn_workspace_size) also holds the q/k/v outputs; zero
- * it once before first use, as for the attention. */
+ * Three launches on `stream`: the split-K q/k/v product (fp32 partial sums), one
+ * kernel that sums the splits and writes Q (hi, lo), K_blk and V_blk, and the
+ * attention, which reads Q as hi + lo and K_blk already rotated.  Arguments as for
+ * dflash_block_qkv (h, ld_h, w_qkv) and dflash_block_attn (cache, ctx_len,
+ * max_ctx_len, rope tables, out).  The workspace
+ * (dflash_block_qkv_attn_workspace_size) holds the attention's region, then the
+ * partial sums and the q/k/v outputs; zero it once before first use, as for the
+ * attention.  A ctx_len outside [0, max_ctx_len] is clamped and reported in the
+ * attention's error word (DFLASH_DEVERR_CTX_LEN), as there. */
 size_t dflash_block_qkv_attn_workspace_size(const dflash_dims* dims, int32_t max_ctx_len);
 int dflash_block_qkv_attn(const dflash_dims* dims, const void* h, int64_t ld_h, const void* w_qkv,
                           const void* k_cache, const void* v_cache, const int32_t* page_table,

@@ -2,7 +2,7 @@
 call) against the oracle's one-step definition (block_qkv_attn_ref): exact
 products, the rotated Q unrounded, the rotated block K and V rounded once.
 
-The kernel carries Q as a bf16 hi/lo pair from an fp32-accumulated product
+The call carries Q as a bf16 hi/lo pair from an fp32-accumulated product
 (relative error ~1e-6 before the split, ~2^-17 after it), so the attention sees
 Q within ~1e-5 of the oracle's; block K / V differ from the oracle's exact
 rounding by one bf16 step where fp32 accumulation straddles a midpoint (rare,
@@ -60,7 +60,7 @@ def _run(cfg, at, qi, window=0, units=None, ws=None):
     log(f"  max-abs err {err:.3e}")
     assert np.all(np.isfinite(got))
     assert int(ws[:4].cpu().numpy().view(np.uint32)[0]) == 0
-    assert not ws[256:256 + 128 * 4096].any()          # every arrival counter back at zero
+    assert not ws[256:256 + 128 * 4096].any()          # the attention's counters back at zero
     assert err <= TOL, err
     return got, ws
 
@@ -83,6 +83,7 @@ def test_block_qkv_attn_ragged_paged_sampled():
     (20, 4, 2, 64, True, 0),      # 320 rows: two chunks of the product; d = 64; paged
     (5, 12, 2, 128, False, 0),    # 6 heads per group: one wave group
     (2, 8, 2, 128, True, 1024),   # sliding window over a paged ring
+    (40, 8, 2, 64, False, 0),     # 640 rows: the tiled product (above the skinny kernel's 512)
 ])
 def test_block_qkv_attn_shapes(B, hq, hkv, d, paged, window):
     cfg = dataclasses.replace(synth.CONFIGS["qwen3_8b"], batch=B, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
