@@ -70,6 +70,17 @@ int check_cache_dims(const dflash_dims* d) {
   return DFLASH_OK;
 }
 
+// The attention's sizes (shared by the calls and their workspace queries).
+int check_attn_sizes(const dflash_dims* dims, int32_t max_ctx_len) {
+  const int st = check_cache_dims(dims);
+  if (st != DFLASH_OK) return st;
+  if (dims->n_q_heads < dims->n_kv_heads || dims->n_q_heads % dims->n_kv_heads) return DFLASH_ERR_SHAPE;
+  if ((int64_t)dims->batch * dims->n_kv_heads > kMaxCountSlots) return DFLASH_ERR_SHAPE;
+  if (dims->n_q_heads / dims->n_kv_heads > 8) return DFLASH_ERR_UNSUPPORTED;
+  if (max_ctx_len < 0 || max_ctx_len > (1 << 24)) return DFLASH_ERR_SHAPE;
+  return DFLASH_OK;
+}
+
 // Context keys a call attends per sequence at most: the window bounds them.
 int32_t attended_keys(const dflash_dims* d, int32_t max_ctx_len) {
   return d->window > 0 && d->window < max_ctx_len ? d->window : max_ctx_len;
@@ -257,9 +268,7 @@ int dflash_block_qkv(const dflash_dims* dims, const void* h, int64_t ld_h, const
 
 // ------------------------------------------------------------------ block attention
 size_t dflash_block_attn_workspace_size(const dflash_dims* dims, int32_t max_ctx_len) {
-  if (check_cache_dims(dims) != DFLASH_OK || max_ctx_len < 0) return 0;
-  if ((int64_t)dims->batch * dims->n_kv_heads > kMaxCountSlots) return 0;
-  if (dims->n_q_heads < dims->n_kv_heads || dims->n_q_heads % dims->n_kv_heads) return 0;
+  if (check_attn_sizes(dims, max_ctx_len) != DFLASH_OK) return 0;
   return plan_block_attn(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
                          attended_keys(dims, max_ctx_len), kPlanCUs)
       .ws_bytes;
@@ -281,11 +290,9 @@ int block_attn_run(const dflash_dims* dims, const void* q_blk, const void* k_blk
   if (!q_blk || !k_blk || !v_blk || !k_cache || !v_cache || !ctx_len || !rope_cos || !rope_sin || !out)
     return DFLASH_ERR_NULL;
   if (dims->page_size > 0 && !page_table) return DFLASH_ERR_NULL;
-  if (dims->n_q_heads < dims->n_kv_heads || dims->n_q_heads % dims->n_kv_heads) return DFLASH_ERR_SHAPE;
-  if ((int64_t)dims->batch * dims->n_kv_heads > kMaxCountSlots) return DFLASH_ERR_SHAPE;
+  st = check_attn_sizes(dims, max_ctx_len);
+  if (st != DFLASH_OK) return st;
   const int group = dims->n_q_heads / dims->n_kv_heads;
-  if (group > 8) return DFLASH_ERR_UNSUPPORTED;
-  if (max_ctx_len < 0 || max_ctx_len > (1 << 24)) return DFLASH_ERR_SHAPE;
   const int64_t cap_tokens =
       dims->page_size > 0 ? (int64_t)dims->kv_capacity * dims->page_size : (int64_t)dims->kv_capacity;
   if (dims->window == 0 && max_ctx_len > cap_tokens) return DFLASH_ERR_CAPACITY;
@@ -386,8 +393,20 @@ int dflash_block_attn_noalloc(const dflash_dims* dims, const void* q_blk, const 
 }
 
 // ------------------------------------------------------------------ context projection
+// The projection's sizes (shared by the call and its workspace query): rows, layers,
+// and the two widths, so that every product below stays far inside int32.
+static int check_proj_sizes(const dflash_dims* dims, int32_t n_rows, int32_t n_layers, int32_t d_target) {
+  const int st = check_cache_dims(dims);
+  if (st != DFLASH_OK) return st;
+  if (n_rows < 0 || n_rows > (1 << 22)) return DFLASH_ERR_SHAPE;
+  if (n_layers < 1 || n_layers > kMaxLayers) return DFLASH_ERR_SHAPE;
+  if (dims->hidden < 64 || dims->hidden % 64 || dims->hidden > (1 << 16)) return DFLASH_ERR_SHAPE;
+  if (d_target < 64 || d_target % 64 || d_target > (1 << 16)) return DFLASH_ERR_SHAPE;
+  return DFLASH_OK;
+}
+
 size_t dflash_ctx_proj_workspace_size(const dflash_dims* dims, int32_t n_rows, int32_t n_layers, int32_t d_target) {
-  if (check_cache_dims(dims) != DFLASH_OK || n_rows < 0 || n_layers < 1 || d_target < 1) return 0;
+  if (check_proj_sizes(dims, n_rows, n_layers, d_target) != DFLASH_OK) return 0;
   // Planned for the fc path; the same size also serves a call without fc.
   return plan_ctx_proj(n_rows, n_layers * d_target, dims->hidden, 2 * dims->n_kv_heads * dims->head_dim, true,
                        kPlanCUs)
@@ -404,10 +423,8 @@ int dflash_ctx_proj(const dflash_dims* dims, int32_t n_rows, const void* const* 
   if (!x_layers || !row_seq || !row_pos || !w_k || !w_v || !rope_cos || !rope_sin || !k_cache || !v_cache)
     return DFLASH_ERR_NULL;
   if (dims->page_size > 0 && !page_table) return DFLASH_ERR_NULL;
-  if (n_rows < 0 || n_rows > (1 << 22)) return DFLASH_ERR_SHAPE;
-  if (n_layers < 1 || n_layers > kMaxLayers) return DFLASH_ERR_SHAPE;
-  if (dims->hidden < 64 || dims->hidden % 64 || dims->hidden > (1 << 16)) return DFLASH_ERR_SHAPE;
-  if (d_target < 64 || d_target % 64 || d_target > (1 << 16)) return DFLASH_ERR_SHAPE;
+  st = check_proj_sizes(dims, n_rows, n_layers, d_target);
+  if (st != DFLASH_OK) return st;
   if (ld_x < d_target) return DFLASH_ERR_SHAPE;
   if (!w_fc && (n_layers != 1 || d_target != dims->hidden || c_out)) return DFLASH_ERR_SHAPE;
   if (max_pos < 1) return DFLASH_ERR_CAPACITY;
@@ -674,8 +691,7 @@ static FusedPlan plan_fused(const dflash_dims* dims, int32_t max_ctx_len) {
 }
 
 size_t dflash_block_qkv_attn_workspace_size(const dflash_dims* dims, int32_t max_ctx_len) {
-  if (check_qkv_dims(dims) != DFLASH_OK || max_ctx_len < 0) return 0;
-  if ((int64_t)dims->batch * dims->n_kv_heads > kMaxCountSlots) return 0;
+  if (check_qkv_dims(dims) != DFLASH_OK || check_attn_sizes(dims, max_ctx_len) != DFLASH_OK) return 0;
   return plan_fused(dims, max_ctx_len).ws_bytes;
 }
 

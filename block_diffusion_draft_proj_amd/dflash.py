@@ -15,7 +15,10 @@ from typing import Optional, Sequence
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libdflash.so")
+# DFLASH_LIB names another build of the same library (the host-sanitizer build of
+# build_sanitized.py); by default the in-tree build.
+_LIB_PATH = os.environ.get("DFLASH_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
+                                                         "libdflash.so")
 
 BLOCK = 16
 DEVERR_CTX_LEN, DEVERR_PAGE_ID, DEVERR_ROW, DEVERR_MERGE, DEVERR_XCD, DEVERR_ACCEPT = 1, 2, 4, 8, 16, 32
