@@ -220,13 +220,15 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
   };
   const uint64_t sb0 = uniform_ptr(0), sb1 = uniform_ptr(1), sb2 = uniform_ptr(2), sb3 = uniform_ptr(3);
   const uint64_t sb4 = uniform_ptr(4), sb5 = uniform_ptr(5), sb6 = uniform_ptr(6), sb7 = uniform_ptr(7);
-  auto issue = [&](int st) {
+  // issue(st, i0, i1): this wave's loads i0 .. i1-1 of stage st.
+  auto issue = [&](int st, int i0, int i1) {
     const int ks = st + rot < n_st ? st + rot : st + rot - n_st;
     const int k0 = kbeg + ks * BK;
     const uint16_t* xstep = PACKED ? p.xp + ((int64_t)(k0 / BK) * p.mp + p.m_off) * BK : nullptr;
     const uint32_t stage = ring + (uint32_t)((st % SG::NS) * SG::STAGE);
 #pragma unroll
     for (int i = 0; i < SG::LW; ++i) {
+      if (i < i0 || i >= i1) continue;
       const int li = i * SG::WAVES + w;  // wave-uniform
       if (li < SG::W_TILE / 1024) {
         const int row = li * 8 + lrow;
@@ -264,7 +266,12 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
 
 #pragma unroll
   for (int st = 0; st < SG::NS - 1; ++st)
-    if (st < n_st) issue(st);
+    if (st < n_st) issue(st, 0, SG::LW);
+  // The refill of stage it + NS - 1 is spread over the stage's two K halves, each part
+  // issued once that half's LDS reads are in flight: right after the barrier all waves
+  // would otherwise queue their loads at the CU's address unit at once and only then
+  // start their MFMAs (per-stage timestamps: 844 of ~1880 cycles spent issuing).
+  constexpr int LH = (SG::LW + 1) / 2;  // loads issued in the first half
   for (int it = 0; it < n_st; ++it) {
     // stage `it` landed for this wave: at most min(NS-2, n_st-1-it) younger stages in flight
     const int after = min(SG::NS - 2, n_st - 1 - it);
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
     else if (after == 1) wait_vmcnt<SG::LW>();
     else wait_vmcnt<0>();
     __syncthreads();  // every wave's part of stage `it` landed; stage it-1 is free again
-    if (it + SG::NS - 1 < n_st) issue(it + SG::NS - 1);
+    const bool refill = it + SG::NS - 1 < n_st;
     const char* sw = lds + (it % SG::NS) * SG::STAGE;
     const char* sx = sw + SG::W_TILE;
 #pragma unroll
@@ -286,6 +293,7 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
 #pragma unroll
       for (int mt = 0; mt < MTW; ++mt)
         xb[mt] = *reinterpret_cast<const bf16x8*>(sx + swz_off((wt * MTW + mt) * 16 + r, kh * 4 + q));
+      if (refill) issue(it + SG::NS - 1, kh == 0 ? 0 : LH, kh == 0 ? LH : SG::LW);
 #pragma unroll
       for (int rt = 0; rt < SK_RT; ++rt)
 #pragma unroll
