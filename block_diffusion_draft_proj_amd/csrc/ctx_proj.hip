@@ -27,101 +27,139 @@ namespace dflash {
 
 namespace {
 
-// Tile of one workgroup: 128 rows (A / activations) x 64 columns (B / weight
-// rows), K consumed in 64-element stages.  Each stage lands in LDS through
-// global_load_lds (A tile 16 KB, B tile 8 KB) in a 3-stage ring, so two stages
-// are in flight while one feeds the MFMAs; two workgroups fit on a CU.
-// Eight waves each own 16 rows x 64 columns of the tile.  The 24 wave-wide
-// 1 KB loads of a stage are dealt round-robin (load i to wave i % 8), so the
-// weight loads, which miss every cache, are spread over all waves instead of
-// queueing behind one wave's memory counter (measured: 2.4x faster than giving
-// each wave a contiguous run of loads).
-// The weights are read exactly once (non-temporal); the activation tile is
-// re-read by every column tile and is left cacheable.
-constexpr int BK = 64;
+// Tiled product for many activation rows (prefill chunks: more than 512 rows).  A
+// workgroup owns a 256 (rows of A) x 256 (rows of B) output tile.  K goes in 32-element
+// stages, A and B tiles (16 KB each) global -> XOR-swizzled LDS by global_load_lds in a
+// four-stage ring (128 KB: one workgroup per CU), so three stages (96 KB) are in flight
+// while one feeds the MFMAs.  Eight waves each own 128 x 64 of the tile: per stage
+// 8 A and 4 B operand reads feed 32 MFMAs, so the MFMA pipes, not the LDS, set the pace
+// (per stage and SIMD: 1024 MFMA cycles against ~768 cycles of LDS reads per CU).
+// Tile order (workgroup i runs on XCD i % 8): with at least 8 rows of tiles, XCD x takes
+// tile rows x, x + 8, ... in bands of 4 rows, column-major within a band, so the 32
+// workgroups resident on a die at a time cover 4 x 8 tiles and share their A and B
+// panels in its L2; with fewer, each XCD takes a contiguous run of row-major tiles.
+constexpr int BK = 64;  // the skinny kernel's stage (128-byte LDS rows)
 constexpr int kThreads = 512;
 constexpr int kGemmWaves = kThreads / kWave;
-constexpr int GBM = 128, GBN = 64, GNST = 3;
-constexpr int A_TILE = GBM * BK * 2;
-constexpr int B_TILE = GBN * BK * 2;
+constexpr int TBK = 32;  // the tiled kernel's stage (64-byte LDS rows)
+constexpr int GBM = 256, GBN = 256, GNS = 4;
+constexpr int A_TILE = GBM * TBK * 2;
+constexpr int B_TILE = GBN * TBK * 2;
 constexpr int G_STAGE = A_TILE + B_TILE;
-constexpr int G_LOADS_W = G_STAGE / 1024 / kGemmWaves;  // wave-wide 1 KB loads per wave per stage (3)
-static_assert(GBM == 16 * kGemmWaves, "one 16-row MFMA strip per wave");
+constexpr int G_LOADS_W = G_STAGE / 1024 / kGemmWaves;  // wave-wide 1 KB loads per wave per stage (4)
+constexpr int kBand = 4;                                // tile rows per band of the tile order
 static_assert(G_STAGE % (1024 * kGemmWaves) == 0, "stage loads split evenly over the waves");
 
 // 128-byte rows (64 bf16 of K); 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7):
 // the 16 rows read by one 16-lane MFMA operand group hit distinct banks.
 __device__ __forceinline__ int swz_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
+// 64-byte rows (32 bf16 of K); chunk c of row r at c ^ ((r >> 1) & 3): any 8 consecutive
+// rows' reads of one chunk cover the 128 bytes of banks once.
+__device__ __forceinline__ int swz64_off(int row, int c) { return row * 64 + ((c ^ ((row >> 1) & 3)) << 4); }
+
+// Tile (tm, tn) of workgroup index i in the order above; false if i has none.
+__device__ __forceinline__ bool tile_of(int i, int ntm, int ntn, int& tm, int& tn) {
+  const int x = i % kNumXcd, j = i / kNumXcd;
+  if (ntm >= kNumXcd) {
+    const int rows = (ntm - x + kNumXcd - 1) / kNumXcd;  // tile rows x, x + 8, ... of this XCD
+    const int band = j / (kBand * ntn);
+    if (band * kBand >= rows) return false;
+    const int gh = min(kBand, rows - band * kBand);  // rows of this band
+    const int k = j - band * kBand * ntn;
+    if (k >= gh * ntn) return false;                  // past a short last band
+    tm = x + kNumXcd * (band * kBand + k % gh);
+    tn = k / gh;
+    return true;
+  }
+  const int tiles = ntm * ntn, per = (tiles + kNumXcd - 1) / kNumXcd;
+  const int t = x * per + j;
+  if (j >= per || t >= tiles) return false;
+  tm = t / ntn;
+  tn = t % ntn;
+  return true;
+}
 
 __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) char lds[GNST * G_STAGE];
-  const int n0 = blockIdx.x * GBN, m0 = blockIdx.y * GBM, z = blockIdx.z;
+  __shared__ __attribute__((aligned(1024))) char lds[GNS * G_STAGE];
+  const int ntn = (p.N + GBN - 1) / GBN, ntm = (p.M + GBM - 1) / GBM;
+  int tm, tn;
+  if (!tile_of((int)blockIdx.x, ntm, ntn, tm, tn)) return;
+  const int n0 = tn * GBN, m0 = tm * GBM, z = blockIdx.y;
   const int kbeg = z * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
-  const int n_st = (kend - kbeg) / BK;
+  const int n_st = (kend - kbeg) / TBK;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
-  const int lrow = lane >> 3, pch = lane & 7;  // one wave-wide load = 8 rows x 128 bytes
+  const int lrow = lane >> 2, pch = lane & 3;  // one wave-wide load = 16 rows x 64 bytes
+  const int wm = w >> 2, wn = w & 3;          // rows 128 wm .. of A, 64 wn .. of B
+  const uint32_t ring = (uint32_t)(uintptr_t)(LDS_AS char*)lds;
 
-  // Rows past M or N are clamped to the last real row: every load is in bounds
-  // and the extra results are never stored.
+  // This wave's loads of stage st (load i is wave-wide load i*8 + w of the stage: 0..15
+  // the A tile, 16..31 the B tile).  Rows past M or N are clamped to the last real row:
+  // every load is in bounds and the extra results are never stored.
   auto issue = [&](int st) {
-    const int k0 = kbeg + st * BK;
-    const int seg = k0 / p.seg_k;
+    const int k0 = kbeg + st * TBK;
+    const int seg = k0 / p.seg_k;  // wave-uniform; seg_k is a multiple of 64
     const uint16_t* abase = p.a_seg[seg] + (k0 - seg * p.seg_k);
-    char* stage = lds + (st % GNST) * G_STAGE;
+    const uint32_t stage = ring + (uint32_t)((st % GNS) * G_STAGE);
 #pragma unroll
     for (int i = 0; i < G_LOADS_W; ++i) {
-      const int li = i * kGemmWaves + w;  // 0..15: A tile, 16..23: B tile (wave-uniform)
+      const int li = i * kGemmWaves + w;  // wave-uniform
+      const int row = (li & 15) * 16 + lrow;
+      const int sw = (pch ^ ((row >> 1) & 3)) << 3;
       if (li < A_TILE / 1024) {
-        const int row = li * 8 + lrow;
         const int m = min(m0 + row, p.M - 1);
-        lds_dma16(abase + (int64_t)m * p.lda + ((pch ^ ((row >> 1) & 7)) << 3), stage + li * 1024);
+        lds_dma16_m0(abase + (int64_t)m * p.lda + sw, stage + li * 1024);
       } else {
-        const int row = (li - A_TILE / 1024) * 8 + lrow;
         const int n = min(n0 + row, p.N - 1);
         const uint16_t* brow = n < p.n_b0 ? p.b0 + (int64_t)n * p.K : p.b1 + (int64_t)(n - p.n_b0) * p.K;
-        lds_dma16_nt(brow + k0 + ((pch ^ ((row >> 1) & 7)) << 3), stage + li * 1024);
+        lds_dma16_nt_m0(brow + k0 + sw, stage + li * 1024);
       }
     }
   };
 
-  f32x4 acc[4];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int ma = 0; ma < 8; ++ma)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[ma][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int st = 0; st < GNST - 1; ++st)
+  for (int st = 0; st < GNS - 1; ++st)
     if (st < n_st) issue(st);
   for (int it = 0; it < n_st; ++it) {
-    if (it + 1 < n_st) wait_vmcnt<G_LOADS_W>();  // stage it landed, stage it+1 may still fly
+    // stage it landed for this wave: at most min(GNS - 2, n_st - 1 - it) younger stages fly
+    const int after = min(GNS - 2, n_st - 1 - it);
+    if (after >= 2) wait_vmcnt<2 * G_LOADS_W>();
+    else if (after == 1) wait_vmcnt<G_LOADS_W>();
     else wait_vmcnt<0>();
-    __syncthreads();
-    if (it + GNST - 1 < n_st) issue(it + GNST - 1);
-    const char* sa = lds + (it % GNST) * G_STAGE;
+    __syncthreads();  // ... for every wave; the slot of stage it-1 is free again
+    const char* sa = lds + (it % GNS) * G_STAGE;
     const char* sb = sa + A_TILE;
+    bf16x8 bw[4], ax[8];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 b[4];
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sa + swz_off(w * 16 + r, ks * 4 + q));
+    for (int nb = 0; nb < 4; ++nb) bw[nb] = *reinterpret_cast<const bf16x8*>(sb + swz64_off(wn * 64 + nb * 16 + r, q));
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) b[nt] = *reinterpret_cast<const bf16x8*>(sb + swz_off(nt * 16 + r, ks * 4 + q));
+    for (int ma = 0; ma < 8; ++ma) ax[ma] = *reinterpret_cast<const bf16x8*>(sa + swz64_off(wm * 128 + ma * 16 + r, q));
+    if (it + GNS - 1 < n_st) issue(it + GNS - 1);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt] = mfma16x16x32(a, b[nt], acc[nt]);
-    }
+    for (int ma = 0; ma < 8; ++ma)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[ma][nb] = mfma16x16x32(bw[nb], ax[ma], acc[ma][nb]);
   }
 
-  // C tile: lane holds column n0 + 16nt + r, rows m0 + 16w + 4q + v.
+  // D layout: lane holds A row m0 + 128 wm + 16 ma + r and B rows 4q .. 4q+3 of its
+  // 16-row group: 4 consecutive outputs of one row, one 16-byte store (N % 4 == 0).
   float* out = p.out + (int64_t)z * p.M * p.N;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int n = n0 + nt * 16 + r;
-    if (n >= p.N) continue;
+  for (int ma = 0; ma < 8; ++ma) {
+    const int m = m0 + wm * 128 + ma * 16 + r;
+    if (m >= p.M) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = m0 + w * 16 + 4 * q + v;
-      if (m < p.M) out[(int64_t)m * p.N + n] = acc[nt][v];
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = n0 + wn * 64 + nb * 16 + 4 * q;
+      if (n < p.N) *reinterpret_cast<f32x4*>(out + (int64_t)m * p.N + n) = acc[ma][nb];
     }
   }
 }
@@ -511,13 +549,14 @@ __global__ __launch_bounds__(256) void kv_epilogue_kernel(KvEpilogueParams p) {
   *reinterpret_cast<u32x2*>(vd + j + half) = (u32x2){pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
 }
 
-// Split K so that ~2 workgroups land on every CU, while the fp32 partial sums
-// (splits x M x N x 4 bytes, written and read back once) stay under a quarter of
-// the weight bytes (N x K x 2) and every split keeps >= 4 stages.
-int split_count(int tiles, int M, int K, int target) {
+// Tiled path: split K so that the tiles fill the CUs (one workgroup each), while
+// the fp32 partial sums (splits x M x N x 4 bytes, written and read back once) stay
+// within the operand bytes ((M + N) x K x 2) and every split keeps >= 4 stages.
+int split_count(int tiles, int M, int N, int K, int num_cu) {
   if (tiles < 1) tiles = 1;
-  int splits = (target + tiles - 1) / tiles;
-  const int by_traffic = (int)((int64_t)K / (8 * (int64_t)(M > 0 ? M : 1)));
+  int splits = (num_cu + tiles - 1) / tiles;
+  const int64_t mn = (int64_t)(M > 0 ? M : 1) * (N > 0 ? N : 1);
+  const int by_traffic = (int)(((int64_t)(M + N) * K) / (2 * mn));
   const int by_depth = K / (4 * BK);
   splits = min(splits, max(1, by_traffic));
   splits = min(splits, max(1, by_depth));
@@ -552,17 +591,16 @@ int skinny_splits(int N, int M, int K, int num_cu) {
 ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_fc, int num_cu) {
   ProjPlan pl{};
   const int cus = num_cu > 0 ? num_cu : 256;
-  const int target = 2 * cus;
   const int mtiles = (n_rows + GBM - 1) / GBM;
   pl.fc_small = pl.kv_small = n_rows <= kSkinnyMaxRows;  // skinny weight-streaming kernel
   if (has_fc) {
     const int sp = pl.fc_small ? skinny_splits(hidden, n_rows, k_fc, cus)
-                               : split_count(mtiles * ((hidden + GBN - 1) / GBN), n_rows, k_fc, target);
+                               : split_count(mtiles * ((hidden + GBN - 1) / GBN), n_rows, hidden, k_fc, cus);
     pl.fc_kps = k_per_split(k_fc, sp);
     pl.fc_splits = (k_fc + pl.fc_kps - 1) / pl.fc_kps;  // every split has a non-empty K range
   }
   const int sp = pl.kv_small ? skinny_splits(kv_width, n_rows, hidden, cus)
-                             : split_count(mtiles * ((kv_width + GBN - 1) / GBN), n_rows, hidden, target);
+                             : split_count(mtiles * ((kv_width + GBN - 1) / GBN), n_rows, kv_width, hidden, cus);
   pl.kv_kps = k_per_split(hidden, sp);
   pl.kv_splits = (hidden + pl.kv_kps - 1) / pl.kv_kps;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -593,7 +631,7 @@ QkvPlan plan_block_qkv(int n_rows, int hidden, int n_out, int num_cu) {
   const int mtiles = (n_rows + GBM - 1) / GBM;
   pl.small = n_rows <= kSkinnyMaxRows;
   const int sp = pl.small ? skinny_splits(n_out, n_rows, hidden, cus)
-                          : split_count(mtiles * ((n_out + GBN - 1) / GBN), n_rows, hidden, 2 * cus);
+                          : split_count(mtiles * ((n_out + GBN - 1) / GBN), n_rows, n_out, hidden, cus);
   pl.kps = k_per_split(hidden, sp);
   pl.splits = (hidden + pl.kps - 1) / pl.kps;
   pl.mp = n_rows <= 128 ? 32 * ((n_rows + 31) / 32) : kSkinnyChunk * ((n_rows + kSkinnyChunk - 1) / kSkinnyChunk);
@@ -637,7 +675,16 @@ hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStre
     }
     return hipGetLastError();
   }
-  dim3 grid((p.N + GBN - 1) / GBN, (p.M + GBM - 1) / GBM, splits);
+  // Workgroups per XCD: all tiles of its rows of tiles (x, x + 8, ...), or a contiguous
+  // run of tiles below 8 rows of tiles.
+  const int ntm = (p.M + GBM - 1) / GBM, ntn = (p.N + GBN - 1) / GBN;
+  int64_t per_xcd;
+  if (ntm >= kNumXcd) {
+    per_xcd = (int64_t)((ntm + kNumXcd - 1) / kNumXcd) * ntn;  // rows of the XCD with most
+  } else {
+    per_xcd = ((int64_t)ntm * ntn + kNumXcd - 1) / kNumXcd;
+  }
+  const dim3 grid((unsigned)(kNumXcd * per_xcd), (unsigned)splits, 1);
   hipLaunchKernelGGL(gemm_nt_kernel, grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
