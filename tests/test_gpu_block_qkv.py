@@ -84,3 +84,15 @@ def test_block_qkv_degenerate_shapes(B, Hq, Hkv, d, hidden):
     import dataclasses
     cfg = dataclasses.replace(synth.CONFIGS["tiny"], n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, hidden=hidden)
     _check(cfg, synth.block_qkv_inputs(cfg, batch=B, seed=64 + B), B, f"{Hq}q/{Hkv}kv d={d} hidden={hidden}")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,hidden", [
+    (768, 4, 2, 64, 256),    # 12288 rows: 48 rows of tiles, six per XCD, in bands of 4 and 2
+    (200, 8, 2, 64, 128),    # 3200 rows: 13 rows of tiles (one or two per XCD); 3 column tiles, the last partial
+])
+def test_block_qkv_tiled_tile_order(B, Hq, Hkv, d, hidden):
+    # The tiled product's per-XCD tile order with several bands, a short last band and a
+    # partial last column of tiles: every output element is written exactly once.
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, hidden=hidden)
+    _check(cfg, synth.block_qkv_inputs(cfg, batch=B, seed=90 + B), B, f"{16 * B} rows, {Hq}q/{Hkv}kv d={d}")
