@@ -947,14 +947,16 @@ AttnPlan plan_block_attn(int batch, int n_q_heads, int n_kv_heads, int head_dim,
   const int64_t target_wg = num_cu > 0 ? num_cu : 256;
   int64_t kps = (units * (int64_t)max_ctx + target_wg - 1) / target_wg;
   kps = ((kps + 2 * TK - 1) / (2 * TK)) * (2 * TK);
-  // At most a quarter of the longest context per split, an eighth when there are at
+  // At most a quarter of the longest context per split, a sixteenth when there are at
   // least as many units as CUs (the GPU is full without splitting, so splits serve
   // balance only): the host does not know the lengths of a ragged batch, and its
-  // longest sequences then come in 4 or 8 pieces that the dispatcher spreads over
+  // longest sequences then come in 4 or 16 pieces that the dispatcher spreads over
   // the CUs.  A uniform batch that leaves CUs to fill is unaffected: there the bound
   // above is already <= max_ctx / 4.  (Ragged batch of 32 x 8 units: 715 us with
-  // 8192-key splits, 352 us with a quarter, 291 us with an eighth.)
-  const int64_t div = units >= target_wg ? 8 : 4;
+  // 8192-key splits, 352 us with a quarter, 291 us with an eighth; later, with an
+  // eighth 308 us against 298 us with a sixteenth, whose 16 splits take the separate
+  // merge kernel.)
+  const int64_t div = units >= target_wg ? 16 : 4;
   const int64_t quarter = ((max_ctx / div + 2 * TK - 1) / (2 * TK)) * (2 * TK);
   if (kps > quarter) kps = quarter;
   if (kps < 256) kps = 256;
