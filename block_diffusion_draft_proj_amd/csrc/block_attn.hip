@@ -334,8 +334,9 @@ __device__ __forceinline__ void wait_packs(int after) {
   }
 }
 
-// QHL: the q / k inputs come already rotated by the fused q/k/v product: Q as a bf16
-// hi/lo pair (q_blk = hi, q_lo = lo; no RoPE here), the block K rotated and rounded.
+// QHL: the q / k inputs come already rotated (dflash_block_qkv_attn's reduce kernel):
+// Q as a bf16 hi/lo pair (q_blk = hi, q_lo = lo; no RoPE here), the block K rotated
+// and rounded.
 template <int D, int G, bool PAGED, bool QHL>
 __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnParams p) {
   using GE = Geo<D>;
