@@ -42,8 +42,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "b041c95c9947997bec2968e49a9aa3d627e9c85a180b50bac880dd6830c20cf0",
-                "workload": "batched", "read": 276988421, "write": 8505188}
+ATTN_TRAFFIC = {"sha256": "a3446780dd2162dbebe35fae9b49d56535fbb831adff26ae4ddcb39b47c7012d",
+                "workload": "batched", "read": 276988389, "write": 8504871}
 
 
 def sources_sha256(paths):
