@@ -16,8 +16,15 @@
  *     1 + accept tokens and crop of the KV length ("dflash-mlx", "single-forward
  *     verify" steps 6-9 and guarantees 2-3; "DFlash dual implementations", §3);
  *   - around them, the rest of a cycle on the device: the block's own q / k / v
- *     (the attention's inputs, same §2) and the draft-side greedy tokens at the
- *     15 mask slots ("dflash-mlx", "single-forward verify" steps 3-4).
+ *     (the attention's inputs, same §2), alone or in one call with the attention
+ *     (Q carried unrounded as a bf16 hi/lo pair); the draft-side greedy tokens
+ *     at the 15 mask slots ("dflash-mlx", "single-forward verify" steps 3-4); the
+ *     rest of a draft layer (RMSNorm, o_proj, SwiGLU MLP: "DFlash dual
+ *     implementations", §1); the sliding-window cache (dflash_dims.window, §3);
+ *     and the rollback of recurrent state by replaying the accepted steps of an
+ *     innovation tape ("dflash-mlx", guarantee 3);
+ *   - the block attention once more, for callers that cannot allocate: a form
+ *     that takes no workspace (a fixed scratch array inside the library).
  *
  * Conventions shared by every entry point:
  *   - All tensor arguments are DEVICE pointers owned by the caller unless a
