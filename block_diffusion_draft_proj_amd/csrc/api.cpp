@@ -626,6 +626,8 @@ int dflash_gdn_tape_replay(int32_t batch, int32_t n_heads, int32_t d_k, int32_t 
   if (!state_in || !state_out || !k_tape || !g_tape || !delta_tape || !accept_len) return DFLASH_ERR_NULL;
   if (batch < 1 || n_heads < 1 || (int64_t)batch * n_heads > (1 << 24)) return DFLASH_ERR_SHAPE;
   if (d_k < 4 || d_k > 256 || d_k % 4 || d_v < 1 || d_v > 4096) return DFLASH_ERR_SHAPE;
+  // one workgroup of 256 threads per 32 state rows: the grid's thread count fits 32 bits
+  if ((int64_t)batch * n_heads * ((d_v + 31) / 32) > (1 << 24)) return DFLASH_ERR_SHAPE;
   const void* ptrs[] = {state_in, state_out, k_tape, g_tape, delta_tape};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return DFLASH_ERR_ALIGN;

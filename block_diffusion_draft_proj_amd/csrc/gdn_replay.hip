@@ -13,10 +13,11 @@
 // so each state element is replayed on its own: no S k product, no reduction.
 //
 // gfx950 mapping: HBM-bound (the fp32 state is read and written once; the tape is
-// small).  One workgroup per (sequence, head, 32 state rows): the accepted
-// steps' keys (as fp32), innovations and decays go to LDS, then every thread
-// loads all its float4 chunks of the state first (all loads in flight), replays
-// the steps on them in registers and stores them back.
+// small).  One workgroup per (sequence, head, 16 or 32 state rows): every thread
+// first issues the loads of all its float4 chunks of the state (streamed past the
+// caches, all in flight at once), then the accepted steps' keys (as fp32),
+// innovations and decays go to LDS while those loads are outstanding; the steps
+// are replayed on the chunks in registers and the chunks are streamed back.
 #include <math.h>
 
 #include "common.h"
@@ -27,11 +28,15 @@ namespace dflash {
 namespace {
 
 constexpr int kReplayThreads = 256;
-constexpr int kReplayRows = 32;     // state rows (value dims) per workgroup
 constexpr int kMaxDk = 256;
-constexpr int kMaxChunksPerThread = kReplayRows * (kMaxDk / 4) / kReplayThreads;  // 8
 
+// ROWS state rows (value dims) per workgroup: 32, or 16 where 32 would give fewer
+// than 8 workgroups per CU (a short grid then finishes sooner with twice the
+// workgroups; with a full grid the larger share per workgroup is faster).
+template <int ROWS>
 __global__ __launch_bounds__(kReplayThreads) void gdn_replay_kernel(GdnReplayParams p) {
+  constexpr int kReplayRows = ROWS;
+  constexpr int kMaxChunksPerThread = kReplayRows * (kMaxDk / 4) / kReplayThreads;
   __shared__ float s_k[kBlock][kMaxDk];
   __shared__ float s_d[kBlock][kReplayRows];
   __shared__ float s_alpha[kBlock];
@@ -46,6 +51,18 @@ __global__ __launch_bounds__(kReplayThreads) void gdn_replay_kernel(GdnReplayPar
   }
   const int n = a + 1;  // committed steps: the staged token and the accepted drafts
   const int row0 = part * kReplayRows;
+  // The state loads go first (they do not depend on the tape), so their latency
+  // overlaps the tape's staging in LDS.
+  const int cpr = p.dk / 4;                       // float4 chunks per state row
+  const int rows = min(kReplayRows, p.dv - row0);
+  const int n_chunks = rows * cpr;
+  const int64_t base = ((int64_t)unit * p.dv + row0) * p.dk;
+  f32x4 s[kMaxChunksPerThread];
+#pragma unroll
+  for (int u = 0; u < kMaxChunksPerThread; ++u) {
+    const int c = tid + u * kReplayThreads;
+    if (c < n_chunks) s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.state_in + base + (int64_t)c * 4));
+  }
   for (int i = tid; i < n * p.dk; i += kReplayThreads) {
     const int t = i / p.dk, j = i - t * p.dk;
     s_k[t][j] = bf16_to_f32(p.k_tape[(((int64_t)b * kBlock + t) * p.n_heads + h) * p.dk + j]);
@@ -57,17 +74,6 @@ __global__ __launch_bounds__(kReplayThreads) void gdn_replay_kernel(GdnReplayPar
   }
   if (tid < n) s_alpha[tid] = expf(p.g_tape[((int64_t)b * kBlock + tid) * p.n_heads + h]);
   __syncthreads();
-
-  const int cpr = p.dk / 4;                       // float4 chunks per state row
-  const int rows = min(kReplayRows, p.dv - row0);
-  const int n_chunks = rows * cpr;
-  const int64_t base = ((int64_t)unit * p.dv + row0) * p.dk;
-  f32x4 s[kMaxChunksPerThread];
-#pragma unroll
-  for (int u = 0; u < kMaxChunksPerThread; ++u) {
-    const int c = tid + u * kReplayThreads;
-    if (c < n_chunks) s[u] = *reinterpret_cast<const f32x4*>(p.state_in + base + (int64_t)c * 4);
-  }
 #pragma unroll
   for (int u = 0; u < kMaxChunksPerThread; ++u) {
     const int c = tid + u * kReplayThreads;
@@ -80,16 +86,21 @@ __global__ __launch_bounds__(kReplayThreads) void gdn_replay_kernel(GdnReplayPar
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = v[e] * al + d * k[e];
     }
-    *reinterpret_cast<f32x4*>(p.state_out + base + (int64_t)c * 4) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.state_out + base + (int64_t)c * 4));
   }
 }
 
 }  // namespace
 
 hipError_t launch_gdn_replay(const GdnReplayParams& p, hipStream_t stream) {
-  const int parts = (p.dv + kReplayRows - 1) / kReplayRows;
-  const int64_t grid = (int64_t)p.batch * p.n_heads * parts;
-  hipLaunchKernelGGL(gdn_replay_kernel, dim3((unsigned)grid), dim3(kReplayThreads), 0, stream, p);
+  const int64_t units = (int64_t)p.batch * p.n_heads;
+  if (units * ((p.dv + 31) / 32) < 2048) {
+    const int64_t grid = units * ((p.dv + 15) / 16);
+    hipLaunchKernelGGL(gdn_replay_kernel<16>, dim3((unsigned)grid), dim3(kReplayThreads), 0, stream, p);
+  } else {
+    const int64_t grid = units * ((p.dv + 31) / 32);
+    hipLaunchKernelGGL(gdn_replay_kernel<32>, dim3((unsigned)grid), dim3(kReplayThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

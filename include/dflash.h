@@ -378,7 +378,8 @@ int dflash_draft_layer_post(const dflash_dims* dims, int32_t intermediate, const
  *               dflash_verify_accept's output
  *   dev_err     optional uint32 (device): DFLASH_DEVERR_ACCEPT is OR-ed in when an
  *               accept_len lies outside [0, 15] (it is clamped)
- * d_k a multiple of 4 in [4, 256], d_v in [1, 4096].  No workspace. */
+ * d_k a multiple of 4 in [4, 256], d_v in [1, 4096], batch x n_heads x ceil(d_v / 32) at
+ * most 2^24 (else DFLASH_ERR_SHAPE).  No workspace. */
 int dflash_gdn_tape_replay(int32_t batch, int32_t n_heads, int32_t d_k, int32_t d_v,
                            const float* state_in, float* state_out, const void* k_tape,
                            const float* g_tape, const float* delta_tape, const int32_t* accept_len,

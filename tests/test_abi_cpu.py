@@ -359,6 +359,7 @@ def test_gdn_tape_replay_rejects_bad_arguments():
     assert call(k=MIS) == -3
     assert call(err=ctypes.c_void_p(0x100002)) == -3
     assert call(so=ctypes.c_void_p(0x100000 + 4096)) == -2   # partial overlap with state_in
+    assert call(B=1 << 16, H=256, dv=33) == -2    # 2^24 units x 2 workgroups: grid too large
 
 
 def test_binding_prepared_attention_call_checks_sizes_once():

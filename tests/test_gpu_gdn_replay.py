@@ -47,7 +47,10 @@ def _run(inp, accept, in_place):
 
 
 @pytest.mark.parametrize("in_place", [False, True])
-@pytest.mark.parametrize("B,H,dk,dv", [(1, 2, 64, 64), (8, 32, 128, 128), (3, 3, 96, 40), (16, 1, 4, 1)])
+# The kernel takes 16 state rows per workgroup where 32 rows would give fewer than 2048
+# workgroups, else 32: the last two shapes take the 32-row form (the last with a ragged d_v).
+@pytest.mark.parametrize("B,H,dk,dv", [(1, 2, 64, 64), (8, 32, 128, 128), (3, 3, 96, 40), (16, 1, 4, 1),
+                                       (16, 32, 64, 128), (20, 32, 64, 100)])
 def test_gdn_replay_matches_oracle(B, H, dk, dv, in_place):
     inp = synth.gdn_tape_inputs(B, H, dk, dv, seed=B * 1000 + dk)
     accept = inp.accept if B != 16 else np.arange(16, dtype=np.int32)   # every accept length once
