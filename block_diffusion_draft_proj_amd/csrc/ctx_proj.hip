@@ -28,37 +28,38 @@ namespace dflash {
 namespace {
 
 // Tiled product for many activation rows (prefill chunks: more than 512 rows).  A
-// workgroup owns a 256 (rows of A) x 256 (rows of B) output tile.  K goes in 32-element
-// stages, A and B tiles (16 KB each) global -> XOR-swizzled LDS by global_load_lds in a
-// four-stage ring (128 KB: one workgroup per CU), so three stages (96 KB) are in flight
-// while one feeds the MFMAs.  Eight waves each own 128 x 64 of the tile: per stage
-// 8 A and 4 B operand reads feed 32 MFMAs, so the MFMA pipes, not the LDS, set the pace
-// (per stage and SIMD: 1024 MFMA cycles against ~768 cycles of LDS reads per CU).
-// Measured ~25 % of the bf16 MFMA peak on 32768 rows: per-stage timestamps put the
-// limit at the CU's address unit (a wave-wide load of 64-byte rows touches 16 cache
-// lines) and at the ring's lookahead, not at the MFMAs.
+// workgroup owns a 256 (rows of A) x 256 (rows of B) output tile; eight waves each own
+// 128 x 64 of it (per 32-wide K step 8 A and 4 B operand reads feed 32 MFMAs).  K goes
+// in 64-element stages: 128-byte LDS rows, so a wave-wide load covers 8 rows in 8 cache
+// lines (64-byte rows take 16 lines per load, and the CU's address unit then sets the
+// pace).  A stage is an A tile and a B tile of 32 KB each; LDS holds a ring of five such
+// tiles (160 KB).  While the waves read the tiles of stage it, the B tile of stage
+// it + 1 and the A tile of stage it + 2 stream in, so half of the data is asked for one
+// and a half stages ahead.  Each wave's eight loads of an iteration are spread over its
+// 64 MFMAs (one before every eighth): issued together after the barrier, the loads of
+// all waves queue at the address unit and hold every wave off its MFMAs.
+// The operand base addresses are wave-uniform register values, chosen with scalar
+// selects: a base indexed at run time (a segment table, or a per-lane choice between
+// the two weight pointers) compiles to a load inside the loop whose wait also waits
+// for every stage load in flight, which empties the ring at each stage.
 // Tile order (workgroup i runs on XCD i % 8): with at least 8 rows of tiles, XCD x takes
 // tile rows x, x + 8, ... in bands of 4 rows, column-major within a band, so the 32
 // workgroups resident on a die at a time cover 4 x 8 tiles and share their A and B
 // panels in its L2; with fewer, each XCD takes a contiguous run of row-major tiles.
-constexpr int BK = 64;  // the skinny kernel's stage (128-byte LDS rows)
+constexpr int BK = 64;  // K stage of both products (128-byte LDS rows)
 constexpr int kThreads = 512;
 constexpr int kGemmWaves = kThreads / kWave;
-constexpr int TBK = 32;  // the tiled kernel's stage (64-byte LDS rows)
-constexpr int GBM = 256, GBN = 256, GNS = 4;
-constexpr int A_TILE = GBM * TBK * 2;
-constexpr int B_TILE = GBN * TBK * 2;
-constexpr int G_STAGE = A_TILE + B_TILE;
-constexpr int G_LOADS_W = G_STAGE / 1024 / kGemmWaves;  // wave-wide 1 KB loads per wave per stage (4)
-constexpr int kBand = 4;                                // tile rows per band of the tile order
-static_assert(G_STAGE % (1024 * kGemmWaves) == 0, "stage loads split evenly over the waves");
+constexpr int GBM = 256, GBN = 256;
+constexpr int G_TILE = GBM * BK * 2;                   // one operand tile of a stage (32 KB)
+constexpr int G_SLOTS = 5;                             // LDS ring of operand tiles (160 KB)
+constexpr int G_LOADS_W = G_TILE / 1024 / kGemmWaves;  // wave-wide 1 KB loads per tile and wave (4)
+constexpr int kBand = 4;                               // tile rows per band of the tile order
+static_assert(GBM == GBN, "A and B tiles share the slot size");
+static_assert(G_TILE % (1024 * kGemmWaves) == 0, "tile loads split evenly over the waves");
 
 // 128-byte rows (64 bf16 of K); 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7):
 // the 16 rows read by one 16-lane MFMA operand group hit distinct banks.
 __device__ __forceinline__ int swz_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
-// 64-byte rows (32 bf16 of K); chunk c of row r at c ^ ((r >> 1) & 3): any 8 consecutive
-// rows' reads of one chunk cover the 128 bytes of banks once.
-__device__ __forceinline__ int swz64_off(int row, int c) { return row * 64 + ((c ^ ((row >> 1) & 3)) << 4); }
 
 // Tile (tm, tn) of workgroup index i in the order above; false if i has none.
 __device__ __forceinline__ bool tile_of(int i, int ntm, int ntn, int& tm, int& tn) {
@@ -82,43 +83,63 @@ __device__ __forceinline__ bool tile_of(int i, int ntm, int ntn, int& tm, int& t
   return true;
 }
 
+// A 64-bit pointer made a provably wave-uniform value (two readfirstlanes).
+__device__ __forceinline__ uint64_t uniform_u64(const void* ptr) {
+  const uint64_t a = (uint64_t)(uintptr_t)ptr;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) char lds[GNS * G_STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[G_SLOTS * G_TILE];
   const int ntn = (p.N + GBN - 1) / GBN, ntm = (p.M + GBM - 1) / GBM;
   int tm, tn;
   if (!tile_of((int)blockIdx.x, ntm, ntn, tm, tn)) return;
   const int n0 = tn * GBN, m0 = tm * GBM, z = blockIdx.y;
   const int kbeg = z * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
-  const int n_st = (kend - kbeg) / TBK;
+  const int n_st = (kend - kbeg) / BK;
+  const int n_h = 2 * n_st;  // operand tiles: 2 st (A of stage st), 2 st + 1 (B)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
-  const int lrow = lane >> 2, pch = lane & 3;  // one wave-wide load = 16 rows x 64 bytes
+  const int lrow = lane >> 3, pch = lane & 7;  // one wave-wide load = 8 rows x 128 bytes
   const int wm = w >> 2, wn = w & 3;          // rows 128 wm .. of A, 64 wn .. of B
   const uint32_t ring = (uint32_t)(uintptr_t)(LDS_AS char*)lds;
 
-  // This wave's loads of stage st (load i is wave-wide load i*8 + w of the stage: 0..15
-  // the A tile, 16..31 the B tile).  Rows past M or N are clamped to the last real row:
-  // every load is in bounds and the extra results are never stored.
-  auto issue = [&](int st) {
-    const int k0 = kbeg + st * TBK;
-    const int seg = k0 / p.seg_k;  // wave-uniform; seg_k is a multiple of 64
-    const uint16_t* abase = p.a_seg[seg] + (k0 - seg * p.seg_k);
-    const uint32_t stage = ring + (uint32_t)((st % GNS) * G_STAGE);
+  static_assert(kMaxLayers == 8, "one register value per segment below");
+  const uint64_t sb0 = uniform_u64(p.a_seg[0]), sb1 = uniform_u64(p.a_seg[1]), sb2 = uniform_u64(p.a_seg[2]);
+  const uint64_t sb3 = uniform_u64(p.a_seg[3]), sb4 = uniform_u64(p.a_seg[4]), sb5 = uniform_u64(p.a_seg[5]);
+  const uint64_t sb6 = uniform_u64(p.a_seg[6]), sb7 = uniform_u64(p.a_seg[7]);
+  const uint64_t bb0 = uniform_u64(p.b0), bb1 = uniform_u64(p.b1);
+  // Loads of this wave, fixed for the whole K loop: load i covers rows 8 (8 i + w) ..
+  // + 7 of a tile; each lane brings 16 bytes of its row, global chunk pch ^ swizzle, so
+  // LDS holds the row's chunk c at c ^ swizzle.  Rows past M or N are clamped to the
+  // last real row: every load is in bounds and the extra results are never stored.
+  int64_t a_row[G_LOADS_W];
+  uint64_t b_row[G_LOADS_W];
 #pragma unroll
-    for (int i = 0; i < G_LOADS_W; ++i) {
-      const int li = i * kGemmWaves + w;  // wave-uniform
-      const int row = (li & 15) * 16 + lrow;
-      const int sw = (pch ^ ((row >> 1) & 3)) << 3;
-      if (li < A_TILE / 1024) {
-        const int m = min(m0 + row, p.M - 1);
-        lds_dma16_m0(abase + (int64_t)m * p.lda + sw, stage + li * 1024);
-      } else {
-        const int n = min(n0 + row, p.N - 1);
-        const uint16_t* brow = n < p.n_b0 ? p.b0 + (int64_t)n * p.K : p.b1 + (int64_t)(n - p.n_b0) * p.K;
-        lds_dma16_nt_m0(brow + k0 + sw, stage + li * 1024);
-      }
+  for (int i = 0; i < G_LOADS_W; ++i) {
+    const int row = (i * kGemmWaves + w) * 8 + lrow;
+    const int sw = (pch ^ ((row >> 1) & 7)) << 3;
+    const int m = min(m0 + row, p.M - 1);
+    const int n = min(n0 + row, p.N - 1);
+    a_row[i] = (int64_t)m * p.lda + sw;
+    b_row[i] = (n < p.n_b0 ? bb0 + 2 * ((uint64_t)n * p.K) : bb1 + 2 * ((uint64_t)(n - p.n_b0) * p.K)) + 2 * sw;
+  }
+  // load i of operand tile h (A of stage h / 2 if h is even, else its B)
+  auto issue = [&](int h, int i) {
+    const int k0 = kbeg + (h >> 1) * BK;
+    const uint32_t dst = ring + (uint32_t)((h % G_SLOTS) * G_TILE) + (uint32_t)((i * kGemmWaves + w) * 1024);
+    if ((h & 1) == 0) {
+      const int seg = k0 / p.seg_k;  // wave-uniform; a 64-wide stage lies in one segment
+      const uint64_t base = seg == 0 ? sb0 : seg == 1 ? sb1 : seg == 2 ? sb2 : seg == 3 ? sb3
+                          : seg == 4 ? sb4 : seg == 5 ? sb5 : seg == 6 ? sb6 : sb7;
+      const uint16_t* src = reinterpret_cast<const uint16_t*>((uintptr_t)base);
+      lds_dma16_m0(src + a_row[i] + (k0 - seg * p.seg_k), dst);
+    } else {
+      lds_dma16_m0(reinterpret_cast<const char*>((uintptr_t)b_row[i]) + 2 * (int64_t)k0, dst);
     }
   };
 
@@ -128,28 +149,37 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[ma][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+  // Tiles 0, 1 (stage 0) and 2 (A of stage 1) before the loop; iteration it then asks
+  // for tiles 2 it + 3 and 2 it + 4, in that order, into the slots of stage it - 1.
+  for (int h = 0; h < 3 && h < n_h; ++h)
 #pragma unroll
-  for (int st = 0; st < GNS - 1; ++st)
-    if (st < n_st) issue(st);
+    for (int i = 0; i < G_LOADS_W; ++i) issue(h, i);
   for (int it = 0; it < n_st; ++it) {
-    // stage it landed for this wave: at most min(GNS - 2, n_st - 1 - it) younger stages fly
-    const int after = min(GNS - 2, n_st - 1 - it);
-    if (after >= 2) wait_vmcnt<2 * G_LOADS_W>();
-    else if (after == 1) wait_vmcnt<G_LOADS_W>();
+    // the tiles of stage it landed for this wave: at most tile 2 it + 2 still flies
+    if (2 * it + 2 < n_h) wait_vmcnt<G_LOADS_W>();
     else wait_vmcnt<0>();
-    __syncthreads();  // ... for every wave; the slot of stage it-1 is free again
-    const char* sa = lds + (it % GNS) * G_STAGE;
-    const char* sb = sa + A_TILE;
-    bf16x8 bw[4], ax[8];
+    __syncthreads();  // ... for every wave; the slots of stage it - 1 are free again
+    const char* sa = lds + ((2 * it) % G_SLOTS) * G_TILE;
+    const char* sb = lds + ((2 * it + 1) % G_SLOTS) * G_TILE;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) bw[nb] = *reinterpret_cast<const bf16x8*>(sb + swz64_off(wn * 64 + nb * 16 + r, q));
+    for (int kh = 0; kh < 2; ++kh) {
+      bf16x8 bw[4], ax[8];
 #pragma unroll
-    for (int ma = 0; ma < 8; ++ma) ax[ma] = *reinterpret_cast<const bf16x8*>(sa + swz64_off(wm * 128 + ma * 16 + r, q));
-    if (it + GNS - 1 < n_st) issue(it + GNS - 1);
+      for (int nb = 0; nb < 4; ++nb) bw[nb] = *reinterpret_cast<const bf16x8*>(sb + swz_off(wn * 64 + nb * 16 + r, kh * 4 + q));
 #pragma unroll
-    for (int ma = 0; ma < 8; ++ma)
+      for (int ma = 0; ma < 8; ++ma) ax[ma] = *reinterpret_cast<const bf16x8*>(sa + swz_off(wm * 128 + ma * 16 + r, kh * 4 + q));
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[ma][nb] = mfma16x16x32(bw[nb], ax[ma], acc[ma][nb]);
+      for (int ma = 0; ma < 8; ++ma) {
+        if ((ma & 1) == 0) {  // load (kh * 8 + ma) / 2 of this iteration's eight
+          const int g = (kh * 8 + ma) >> 1;
+          const int h = 2 * it + 3 + (g >> 2);
+          if (h < n_h) issue(h, g & 3);
+          __builtin_amdgcn_sched_barrier(0);  // keep the load between these MFMAs
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[ma][nb] = mfma16x16x32(bw[nb], ax[ma], acc[ma][nb]);
+      }
+    }
   }
 
   // D layout: lane holds A row m0 + 128 wm + 16 ma + r and B rows 4q .. 4q+3 of its
@@ -252,13 +282,7 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
   // run time instead puts a scalar load in every stage, whose wait counter also
   // counts LDS reads.)
   static_assert(kMaxLayers == 8, "one register value per segment below");
-  auto uniform_ptr = [&](int l) -> uint64_t {
-    if (PACKED) return 0;
-    const uint64_t a = (uint64_t)(uintptr_t)p.a_seg[l];
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-    return ((uint64_t)hi << 32) | lo;
-  };
+  auto uniform_ptr = [&](int l) -> uint64_t { return PACKED ? 0 : uniform_u64(p.a_seg[l]); };
   const uint64_t sb0 = uniform_ptr(0), sb1 = uniform_ptr(1), sb2 = uniform_ptr(2), sb3 = uniform_ptr(3);
   const uint64_t sb4 = uniform_ptr(4), sb5 = uniform_ptr(5), sb6 = uniform_ptr(6), sb7 = uniform_ptr(7);
   // issue(st, i0, i1): this wave's loads i0 .. i1-1 of stage st.
