@@ -100,7 +100,6 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
   const int kbeg = z * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
   const int n_st = (kend - kbeg) / BK;
-  const int n_h = 2 * n_st;  // operand tiles: 2 st (A of stage st), 2 st + 1 (B)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
@@ -117,30 +116,37 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
   // + 7 of a tile; each lane brings 16 bytes of its row, global chunk pch ^ swizzle, so
   // LDS holds the row's chunk c at c ^ swizzle.  Rows past M or N are clamped to the
   // last real row: every load is in bounds and the extra results are never stored.
-  int64_t a_row[G_LOADS_W];
-  uint64_t b_row[G_LOADS_W];
+  uint64_t a_row[G_LOADS_W], b_row[G_LOADS_W];  // byte offset in a layer, byte address
 #pragma unroll
   for (int i = 0; i < G_LOADS_W; ++i) {
     const int row = (i * kGemmWaves + w) * 8 + lrow;
     const int sw = (pch ^ ((row >> 1) & 7)) << 3;
     const int m = min(m0 + row, p.M - 1);
     const int n = min(n0 + row, p.N - 1);
-    a_row[i] = (int64_t)m * p.lda + sw;
+    a_row[i] = 2 * ((uint64_t)m * p.lda + sw);
     b_row[i] = (n < p.n_b0 ? bb0 + 2 * ((uint64_t)n * p.K) : bb1 + 2 * ((uint64_t)(n - p.n_b0) * p.K)) + 2 * sw;
   }
-  // load i of operand tile h (A of stage h / 2 if h is even, else its B)
-  auto issue = [&](int h, int i) {
-    const int k0 = kbeg + (h >> 1) * BK;
-    const uint32_t dst = ring + (uint32_t)((h % G_SLOTS) * G_TILE) + (uint32_t)((i * kGemmWaves + w) * 1024);
-    if ((h & 1) == 0) {
-      const int seg = k0 / p.seg_k;  // wave-uniform; a 64-wide stage lies in one segment
-      const uint64_t base = seg == 0 ? sb0 : seg == 1 ? sb1 : seg == 2 ? sb2 : seg == 3 ? sb3
-                          : seg == 4 ? sb4 : seg == 5 ? sb5 : seg == 6 ? sb6 : sb7;
-      const uint16_t* src = reinterpret_cast<const uint16_t*>((uintptr_t)base);
-      lds_dma16_m0(src + a_row[i] + (k0 - seg * p.seg_k), dst);
-    } else {
-      lds_dma16_m0(reinterpret_cast<const char*>((uintptr_t)b_row[i]) + 2 * (int64_t)k0, dst);
-    }
+  auto seg_base = [&](int seg) -> uint64_t {
+    return seg == 0 ? sb0 : seg == 1 ? sb1 : seg == 2 ? sb2 : seg == 3 ? sb3
+         : seg == 4 ? sb4 : seg == 5 ? sb5 : seg == 6 ? sb6 : sb7;
+  };
+  // Load i of an A tile whose K columns start at byte `a_k` of the layer rows (a
+  // wave-uniform address: the layer base plus the column offset), and of the B tile
+  // of the stage starting at column k0; into ring slot `slot`.
+  auto issue_a = [&](uint64_t a_k, int slot, int i) {
+    lds_dma16_m0(reinterpret_cast<const char*>((uintptr_t)(a_k + a_row[i])),
+                 ring + (uint32_t)(slot * G_TILE) + (uint32_t)((i * kGemmWaves + w) * 1024));
+  };
+  auto issue_b = [&](int k0, int slot, int i) {
+    lds_dma16_m0(reinterpret_cast<const char*>((uintptr_t)b_row[i]) + 2 * (int64_t)k0,
+                 ring + (uint32_t)(slot * G_TILE) + (uint32_t)((i * kGemmWaves + w) * 1024));
+  };
+  // A stage's 64 columns lie in one layer (seg_k is a multiple of 64).  The layer and
+  // column of the next A tile to issue are stepped once per stage, so the division
+  // and the select chain run only when a layer boundary is crossed.
+  auto a_addr = [&](int k0) -> uint64_t {
+    const int seg = k0 / p.seg_k;
+    return seg_base(seg) + 2 * (uint64_t)(k0 - seg * p.seg_k);
   };
 
   f32x4 acc[8][4];
@@ -149,14 +155,26 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[ma][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // Tiles 0, 1 (stage 0) and 2 (A of stage 1) before the loop; iteration it then asks
-  // for tiles 2 it + 3 and 2 it + 4, in that order, into the slots of stage it - 1.
-  for (int h = 0; h < 3 && h < n_h; ++h)
+  // Operand tile h is the A tile of stage h / 2 for even h, its B tile for odd h, in
+  // ring slot h % 5.  Tiles 0, 1 (stage 0) and 2 (A of stage 1) go before the loop;
+  // iteration it then asks for tiles 2 it + 3 (B of stage it + 1) and 2 it + 4 (A of
+  // stage it + 2), in that order, into the slots of stage it - 1.
+  if (n_st > 0) {
 #pragma unroll
-    for (int i = 0; i < G_LOADS_W; ++i) issue(h, i);
+    for (int i = 0; i < G_LOADS_W; ++i) issue_a(a_addr(kbeg), 0, i);
+#pragma unroll
+    for (int i = 0; i < G_LOADS_W; ++i) issue_b(kbeg, 1, i);
+  }
+  if (n_st > 1) {
+#pragma unroll
+    for (int i = 0; i < G_LOADS_W; ++i) issue_a(a_addr(kbeg + BK), 2, i);
+  }
+  // the next A tile to issue: stage 2, in layer a_seg at column a_col
+  int a_seg = (kbeg + 2 * BK) / p.seg_k, a_col = kbeg + 2 * BK - a_seg * p.seg_k;
+  uint64_t a_next = seg_base(a_seg) + 2 * (uint64_t)a_col;
   for (int it = 0; it < n_st; ++it) {
     // the tiles of stage it landed for this wave: at most tile 2 it + 2 still flies
-    if (2 * it + 2 < n_h) wait_vmcnt<G_LOADS_W>();
+    if (it + 1 < n_st) wait_vmcnt<G_LOADS_W>();
     else wait_vmcnt<0>();
     __syncthreads();  // ... for every wave; the slots of stage it - 1 are free again
     const char* sa = lds + ((2 * it) % G_SLOTS) * G_TILE;
@@ -172,13 +190,22 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
       for (int ma = 0; ma < 8; ++ma) {
         if ((ma & 1) == 0) {  // load (kh * 8 + ma) / 2 of this iteration's eight
           const int g = (kh * 8 + ma) >> 1;
-          const int h = 2 * it + 3 + (g >> 2);
-          if (h < n_h) issue(h, g & 3);
+          if (g < 4) {
+            if (it + 1 < n_st) issue_b(kbeg + (it + 1) * BK, (2 * it + 3) % G_SLOTS, g);
+          } else {
+            if (it + 2 < n_st) issue_a(a_next, (2 * it + 4) % G_SLOTS, g - 4);
+          }
           __builtin_amdgcn_sched_barrier(0);  // keep the load between these MFMAs
         }
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[ma][nb] = mfma16x16x32(bw[nb], ax[ma], acc[ma][nb]);
       }
+    }
+    a_col += BK;
+    a_next += 2 * BK;
+    if (a_col >= p.seg_k) {  // the next A tile starts the next layer
+      a_col = 0;
+      a_next = seg_base(++a_seg);
     }
   }
 
