@@ -35,9 +35,11 @@ namespace {
 // pace).  A stage is an A tile and a B tile of 32 KB each; LDS holds a ring of five such
 // tiles (160 KB).  While the waves read the tiles of stage it, the B tile of stage
 // it + 1 and the A tile of stage it + 2 stream in, so half of the data is asked for one
-// and a half stages ahead.  Each wave's eight loads of an iteration are spread over its
-// 64 MFMAs (one before every eighth): issued together after the barrier, the loads of
-// all waves queue at the address unit and hold every wave off its MFMAs.
+// and a half stages ahead.  Waves 0..3, one on each SIMD, issue all loads, sixteen
+// per iteration spread over their 64 MFMAs (one before every fourth): a wave held at the
+// address unit then leaves its SIMD to the other wave there, which never issues a load.
+// (Issued together after the barrier, the loads of all waves queue at the address unit
+// and hold every wave off its MFMAs.)
 // The operand base addresses are wave-uniform register values, chosen with scalar
 // selects: a base indexed at run time (a segment table, or a per-lane choice between
 // the two weight pointers) compiles to a load inside the loop whose wait also waits
@@ -48,14 +50,14 @@ namespace {
 // panels in its L2; with fewer, each XCD takes a contiguous run of row-major tiles.
 constexpr int BK = 64;  // K stage of both products (128-byte LDS rows)
 constexpr int kThreads = 512;
-constexpr int kGemmWaves = kThreads / kWave;
 constexpr int GBM = 256, GBN = 256;
 constexpr int G_TILE = GBM * BK * 2;                   // one operand tile of a stage (32 KB)
 constexpr int G_SLOTS = 5;                             // LDS ring of operand tiles (160 KB)
-constexpr int G_LOADS_W = G_TILE / 1024 / kGemmWaves;  // wave-wide 1 KB loads per tile and wave (4)
+constexpr int kIssueWaves = 4;                        // waves 0..3 (one per SIMD) issue the loads
+constexpr int G_LOADS_W = G_TILE / 1024 / kIssueWaves;  // wave-wide 1 KB loads per tile and issuing wave (8)
 constexpr int kBand = 4;                               // tile rows per band of the tile order
 static_assert(GBM == GBN, "A and B tiles share the slot size");
-static_assert(G_TILE % (1024 * kGemmWaves) == 0, "tile loads split evenly over the waves");
+static_assert(G_TILE % (1024 * kIssueWaves) == 0, "tile loads split evenly over the issuing waves");
 
 // 128-byte rows (64 bf16 of K); 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7):
 // the 16 rows read by one 16-lane MFMA operand group hit distinct banks.
@@ -112,14 +114,14 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
   const uint64_t sb3 = uniform_u64(p.a_seg[3]), sb4 = uniform_u64(p.a_seg[4]), sb5 = uniform_u64(p.a_seg[5]);
   const uint64_t sb6 = uniform_u64(p.a_seg[6]), sb7 = uniform_u64(p.a_seg[7]);
   const uint64_t bb0 = uniform_u64(p.b0), bb1 = uniform_u64(p.b1);
-  // Loads of this wave, fixed for the whole K loop: load i covers rows 8 (8 i + w) ..
-  // + 7 of a tile; each lane brings 16 bytes of its row, global chunk pch ^ swizzle, so
+  // Loads of an issuing wave, fixed for the whole K loop: load i covers rows 8 (4 i + w)
+  // .. + 7 of a tile; each lane brings 16 bytes of its row, global chunk pch ^ swizzle, so
   // LDS holds the row's chunk c at c ^ swizzle.  Rows past M or N are clamped to the
   // last real row: every load is in bounds and the extra results are never stored.
   uint64_t a_row[G_LOADS_W], b_row[G_LOADS_W];  // byte offset in a layer, byte address
 #pragma unroll
   for (int i = 0; i < G_LOADS_W; ++i) {
-    const int row = (i * kGemmWaves + w) * 8 + lrow;
+    const int row = (i * kIssueWaves + w) * 8 + lrow;
     const int sw = (pch ^ ((row >> 1) & 7)) << 3;
     const int m = min(m0 + row, p.M - 1);
     const int n = min(n0 + row, p.N - 1);
@@ -135,11 +137,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
   // of the stage starting at column k0; into ring slot `slot`.
   auto issue_a = [&](uint64_t a_k, int slot, int i) {
     lds_dma16_m0(reinterpret_cast<const char*>((uintptr_t)(a_k + a_row[i])),
-                 ring + (uint32_t)(slot * G_TILE) + (uint32_t)((i * kGemmWaves + w) * 1024));
+                 ring + (uint32_t)(slot * G_TILE) + (uint32_t)((i * kIssueWaves + w) * 1024));
   };
   auto issue_b = [&](int k0, int slot, int i) {
     lds_dma16_m0(reinterpret_cast<const char*>((uintptr_t)b_row[i]) + 2 * (int64_t)k0,
-                 ring + (uint32_t)(slot * G_TILE) + (uint32_t)((i * kGemmWaves + w) * 1024));
+                 ring + (uint32_t)(slot * G_TILE) + (uint32_t)((i * kIssueWaves + w) * 1024));
   };
   // A stage's 64 columns lie in one layer (seg_k is a multiple of 64).  The layer and
   // column of the next A tile to issue are stepped once per stage, so the division
@@ -159,13 +161,14 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
   // ring slot h % 5.  Tiles 0, 1 (stage 0) and 2 (A of stage 1) go before the loop;
   // iteration it then asks for tiles 2 it + 3 (B of stage it + 1) and 2 it + 4 (A of
   // stage it + 2), in that order, into the slots of stage it - 1.
-  if (n_st > 0) {
+  const bool issuer = w < kIssueWaves;
+  if (issuer && n_st > 0) {
 #pragma unroll
     for (int i = 0; i < G_LOADS_W; ++i) issue_a(a_addr(kbeg), 0, i);
 #pragma unroll
     for (int i = 0; i < G_LOADS_W; ++i) issue_b(kbeg, 1, i);
   }
-  if (n_st > 1) {
+  if (issuer && n_st > 1) {
 #pragma unroll
     for (int i = 0; i < G_LOADS_W; ++i) issue_a(a_addr(kbeg + BK), 2, i);
   }
@@ -174,8 +177,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
   uint64_t a_next = seg_base(a_seg) + 2 * (uint64_t)a_col;
   for (int it = 0; it < n_st; ++it) {
     // the tiles of stage it landed for this wave: at most tile 2 it + 2 still flies
-    if (it + 1 < n_st) wait_vmcnt<G_LOADS_W>();
-    else wait_vmcnt<0>();
+    if (!issuer) {
+    } else if (it + 1 < n_st) {
+      wait_vmcnt<G_LOADS_W>();
+    } else {
+      wait_vmcnt<0>();
+    }
     __syncthreads();  // ... for every wave; the slots of stage it - 1 are free again
     const char* sa = lds + ((2 * it) % G_SLOTS) * G_TILE;
     const char* sb = lds + ((2 * it + 1) % G_SLOTS) * G_TILE;
@@ -188,12 +195,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
       for (int ma = 0; ma < 8; ++ma) ax[ma] = *reinterpret_cast<const bf16x8*>(sa + swz_off(wm * 128 + ma * 16 + r, kh * 4 + q));
 #pragma unroll
       for (int ma = 0; ma < 8; ++ma) {
-        if ((ma & 1) == 0) {  // load (kh * 8 + ma) / 2 of this iteration's eight
-          const int g = (kh * 8 + ma) >> 1;
-          if (g < 4) {
+        if (issuer) {  // load kh * 8 + ma of this iteration's sixteen
+          const int g = kh * 8 + ma;
+          if (g < G_LOADS_W) {
             if (it + 1 < n_st) issue_b(kbeg + (it + 1) * BK, (2 * it + 3) % G_SLOTS, g);
           } else {
-            if (it + 2 < n_st) issue_a(a_next, (2 * it + 4) % G_SLOTS, g - 4);
+            if (it + 2 < n_st) issue_a(a_next, (2 * it + 4) % G_SLOTS, g - G_LOADS_W);
           }
           __builtin_amdgcn_sched_barrier(0);  // keep the load between these MFMAs
         }
