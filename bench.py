@@ -42,8 +42,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "a3446780dd2162dbebe35fae9b49d56535fbb831adff26ae4ddcb39b47c7012d",
-                "workload": "batched", "read": 276988389, "write": 8504871}
+ATTN_TRAFFIC = {"sha256": "c853b1676efe093531104eaf9f47ce6a50265fe58c6b1d4dbdbe68647eddcd96",
+                "workload": "batched", "read": 276988401, "write": 8504483}
 
 
 def sources_sha256(paths):
