@@ -224,6 +224,19 @@ def test_ctx_proj_ragged_prefill_1000_rows_strided_layers():
     _check(cfg, n, seq, pos, capacity=700, label="ragged prefill 1000 rows, ld_x > d_target", ld_pad=64)
 
 
+# Narrow layers on the tiled path: with 64-wide layers every K stage of the A operand
+# starts a new layer, with 128-wide ones every second stage; 1024 columns of K take two
+# K splits, the second starting inside the layer list.
+@pytest.mark.parametrize("d_target", [64, 128])
+def test_ctx_proj_tiled_narrow_layers(d_target):
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], n_target_layers=8, target_hidden=d_target)
+    n = 600
+    seq = np.zeros(n, np.int32)
+    pos = np.arange(n, dtype=np.int32) + 5
+    pos[::11] = -1
+    _check(cfg, n, seq, pos, capacity=n + 16, label=f"tiled, 8 layers of {d_target}")
+
+
 def test_ctx_proj_paged_prefill_700_rows():
     cfg = dataclasses.replace(synth.CONFIGS["qwen3_8b"], n_target_layers=2)
     n = 700
