@@ -247,11 +247,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
 // are read in place from their rows (the fc product walks the target layers' rows,
 // the q/k/v and draft-layer products their activation rows), see PACKED below.
 constexpr int SK_RW = 4;                     // weight-row wave groups (32 rows each)
-// Up to kSkinnyMaxRows activation rows take the skinny kernel, in chunks of up to
-// kSkinnyChunk rows (MT = 16 at 129..256 rows): every chunk streams the weights once,
-// where the tiled kernel's 128-row tiles would stream them once per 128 rows.
-constexpr int kSkinnyChunk = 256;
-constexpr int kSkinnyMaxRows = 512;
+// Up to kSkinnyMaxRows activation rows take the skinny kernel (MT = 16 at 129..256
+// rows), one pass over the weights.  Above that the tiled kernel is faster: the
+// qwen3_8b-shaped projection (5 x 4096 -> 4096 -> 2 x 1024) at 384 rows 169 against
+// 151 us, at 512 rows (two skinny passes) 195 against 154 us; at 256 rows the skinny
+// pass wins, 110 against 126 us.
+constexpr int kSkinnyMaxRows = 256;
 constexpr int SK_RT = 2;                     // 16-row weight tiles per wave
 constexpr int SK_ROWS = SK_RW * SK_RT * 16;  // weight rows per workgroup (128)
 
@@ -672,12 +673,11 @@ ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_
   if (has_fc) off = align(off + 2 * (size_t)n_rows * hidden);
   pl.off_kv = off;
   off = align(off + sizeof(float) * (size_t)pl.kv_splits * n_rows * kv_width);
-  // Rows of a packed step: every skinny chunk reads 16*MT <= 32*ceil(chunk rows / 32)
-  // rows from its offset, so with more than one chunk the steps hold whole chunks.
-  // Rows past n_rows hold whatever the workspace held (zero from pack_rows_kernel);
-  // an MFMA output row depends on its own activation row only, and the products of
-  // those rows are never stored.
-  pl.mp = n_rows <= 128 ? 32 * ((n_rows + 31) / 32) : kSkinnyChunk * ((n_rows + kSkinnyChunk - 1) / kSkinnyChunk);
+  // Rows of a packed step (skinny path only): the skinny kernel reads 16*MT rows,
+  // 32*ceil(rows / 32) up to 128 rows and 256 above.  Rows past n_rows hold whatever the
+  // workspace held (zero from pack_rows_kernel); an MFMA output row depends on its own
+  // activation row only, and the products of those rows are never stored.
+  pl.mp = n_rows <= 128 ? 32 * ((n_rows + 31) / 32) : kSkinnyMaxRows;
   pl.off_cp = off;
   if (pl.kv_small) off = align(off + 2 * (size_t)hidden * pl.mp);
   pl.ws_bytes = off;
@@ -695,7 +695,7 @@ QkvPlan plan_block_qkv(int n_rows, int hidden, int n_out, int num_cu) {
                           : split_count(mtiles * ((n_out + GBN - 1) / GBN), n_rows, n_out, hidden, cus);
   pl.kps = k_per_split(hidden, sp);
   pl.splits = (hidden + pl.kps - 1) / pl.kps;
-  pl.mp = n_rows <= 128 ? 32 * ((n_rows + 31) / 32) : kSkinnyChunk * ((n_rows + kSkinnyChunk - 1) / kSkinnyChunk);
+  pl.mp = n_rows <= 128 ? 32 * ((n_rows + 31) / 32) : kSkinnyMaxRows;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 256;  // word 0: device error mask
   pl.off_part = off;
@@ -710,7 +710,7 @@ void launch_skinny(const GemmParams& p, int splits, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_skinny_kernel<MT, PACKED>), grid, dim3(SkGeo<MT>::WAVES * 64), 0, stream, p);
 }
 
-// One chunk of up to kSkinnyChunk rows; activation tiles in pairs of 16 rows.
+// Up to kSkinnyMaxRows rows; activation tiles in pairs of 16 rows.
 template <bool PACKED>
 void launch_skinny_chunk(const GemmParams& c, int splits, hipStream_t stream) {
   switch ((c.m_rows + 31) / 32) {
@@ -725,15 +725,14 @@ void launch_skinny_chunk(const GemmParams& c, int splits, hipStream_t stream) {
 
 hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStream_t stream) {
   if (small_m) {
-    // Chunks of up to kSkinnyChunk rows, each a full pass over the weights; activation
-    // tiles in pairs of 16 rows (stage loads split evenly over the waves).
-    for (int m_off = 0; m_off < max(p.M, 1); m_off += kSkinnyChunk) {
-      GemmParams c = p;
-      c.m_off = m_off;
-      c.m_rows = min(kSkinnyChunk, p.M - m_off);
-      if (p.xp) launch_skinny_chunk<true>(c, splits, stream);
-      else launch_skinny_chunk<false>(c, splits, stream);
-    }
+    // All rows in one pass over the weights; activation tiles in pairs of 16 rows
+    // (stage loads split evenly over the waves).
+    if (p.M > kSkinnyMaxRows) return hipErrorInvalidValue;
+    GemmParams c = p;
+    c.m_off = 0;
+    c.m_rows = p.M;
+    if (p.xp) launch_skinny_chunk<true>(c, splits, stream);
+    else launch_skinny_chunk<false>(c, splits, stream);
     return hipGetLastError();
   }
   // Workgroups per XCD: all tiles of its rows of tiles (x, x + 8, ...), or a contiguous

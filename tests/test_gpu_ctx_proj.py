@@ -171,8 +171,9 @@ def test_ctx_proj_ragged_paged_block_rows():
     _check(cfg, 16 * cfg.batch, seq, pos, capacity=0, table=table, num_pages=len(need), label="ragged paged")
 
 
-# 300 rows: a 256-row chunk then a 44-row one; 80 rows: 6 activation tiles (MT = 6).
-@pytest.mark.parametrize("n", [300, 80])
+# 300 rows: the tiled kernel, last row tile ragged; 200 rows: the skinny kernel's 16
+# activation tiles (MT = 16) with the last 56 rows clamped; 80 rows: 6 tiles (MT = 6).
+@pytest.mark.parametrize("n", [300, 200, 80])
 def test_ctx_proj_prefill_chunk_with_ragged_row_tail(n):
     cfg = dataclasses.replace(synth.CONFIGS["qwen3_8b"], n_target_layers=2)
     seq = np.zeros(n, np.int32)
@@ -200,7 +201,7 @@ def test_ctx_proj_bad_rows_flagged_and_skipped():
     assert np.count_nonzero(np.any(kc != 0, axis=-1)) == 7 * cfg.n_kv_heads
 
 
-# Above 512 rows (prefill chunks) the projection takes the tiled MFMA GEMM, whose A
+# Above 256 rows (prefill chunks) the projection takes the tiled MFMA GEMM, whose A
 # operand walks the layers' row pointers at run time and whose C is row-major.
 def test_ctx_proj_qwen3_8b_full_prefill_2048_rows():
     cfg = synth.CONFIGS["qwen3_8b"]
@@ -248,7 +249,7 @@ def test_ctx_proj_paged_prefill_700_rows():
 
 
 def test_ctx_proj_skinny_rows_strided_layers():
-    # Per-cycle rows (<= 512) read the layers in place too: layer rows ld_x > d_target apart.
+    # Per-cycle rows (<= 256) read the layers in place too: layer rows ld_x > d_target apart.
     cfg = synth.CONFIGS["batched"]
     n = 128
     seq = np.repeat(np.arange(cfg.batch, dtype=np.int32), 16)
