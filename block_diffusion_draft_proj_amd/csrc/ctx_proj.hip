@@ -632,22 +632,32 @@ int k_per_split(int K, int splits) {
 
 }  // namespace
 
-// Skinny plan: one workgroup of 128 weight rows per CU, K split to fill the CUs,
-// while the fp32 partial sums (splits x M x N x 4 bytes, written and read back
-// once) stay within half the weight bytes (N x K x 2; twice them above 128 rows) and
-// every split keeps >= 2 steps.
+// Skinny plan: workgroups of 128 weight rows, one per CU at a time.  K is split to
+// minimise the time of the rounds of workgroups: rounds (tiles x splits / CUs, rounded
+// up) times a workgroup's steps (K / 64 / splits) plus a fixed cost of about eight
+// steps (ring fill and partial store).  The draft layer's gate/up product (192 column
+// tiles over 4096 of K) then takes one split, 192 workgroups of 64 steps: with two (a
+// full round and a half-empty one) the layer's post-attention call took 122.3 us, with
+// four 128.1, with one 115.7.  The fp32 partial sums (splits x M x N x 4 bytes, written
+// and read back once) stay within half the weight bytes (N x K x 2; twice them above
+// 128 rows) and every split keeps >= 2 steps.  Ties go to fewer splits.
 int skinny_splits(int N, int M, int K, int num_cu) {
   const int tiles = (N + SK_ROWS - 1) / SK_ROWS;
-  int splits = (num_cu + tiles - 1) / tiles;
   // fp32 partials within half the weight bytes at <= 128 rows; within twice them above,
-  // where a half-weight budget left the K/V product 2 splits (32 workgroups) at 512
-  // rows (ragged batch: 490 us per step against 523 us).
-  splits = min(splits, max(1, (int)((int64_t)K / ((M > 128 ? 1 : 4) * (int64_t)(M > 0 ? M : 1)))));
-  splits = min(splits, max(1, K / (2 * BK)));
-  splits = max(1, splits);
-  // a divisor of 8 (1, 2, 4) or a multiple of 8, for the XCD-aware decode
-  if (splits >= 8) return splits - splits % 8;
-  return splits >= 4 ? 4 : (splits >= 2 ? 2 : 1);
+  // where a half-weight budget left the K/V product 2 splits (32 workgroups) at 256
+  // rows and more.
+  const int cap = max(1, min((int)((int64_t)K / ((M > 128 ? 1 : 4) * (int64_t)(M > 0 ? M : 1))), K / (2 * BK)));
+  constexpr int64_t kFixedSteps = 8;
+  const int64_t steps = (K + BK - 1) / BK;
+  auto cost = [&](int s) {  // in steps x splits, to compare without division
+    const int64_t rounds = ((int64_t)tiles * s + num_cu - 1) / num_cu;
+    return rounds * (steps + kFixedSteps * s);
+  };
+  // candidates: a divisor of 8 (1, 2, 4) or a multiple of 8, for the XCD-aware decode
+  int best = 1;
+  for (int s = 2; s <= cap; s = s < 8 ? 2 * s : s + 8)
+    if (cost(s) * best < cost(best) * s) best = s;  // cost(s) / s < cost(best) / best
+  return best;
 }
 
 ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_fc, int num_cu) {
