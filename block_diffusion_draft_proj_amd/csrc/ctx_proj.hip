@@ -722,7 +722,7 @@ void launch_skinny(const GemmParams& p, int splits, hipStream_t stream) {
 
 // Up to kSkinnyMaxRows rows; activation tiles in pairs of 16 rows.
 template <bool PACKED>
-void launch_skinny_chunk(const GemmParams& c, int splits, hipStream_t stream) {
+void launch_skinny_rows(const GemmParams& c, int splits, hipStream_t stream) {
   switch ((c.m_rows + 31) / 32) {
     case 0:
     case 1: launch_skinny<2, PACKED>(c, splits, stream); break;
@@ -741,8 +741,8 @@ hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStre
     GemmParams c = p;
     c.m_off = 0;
     c.m_rows = p.M;
-    if (p.xp) launch_skinny_chunk<true>(c, splits, stream);
-    else launch_skinny_chunk<false>(c, splits, stream);
+    if (p.xp) launch_skinny_rows<true>(c, splits, stream);
+    else launch_skinny_rows<false>(c, splits, stream);
     return hipGetLastError();
   }
   // Workgroups per XCD: all tiles of its rows of tiles (x, x + 8, ...), or a contiguous
