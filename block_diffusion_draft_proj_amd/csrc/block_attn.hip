@@ -353,7 +353,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   constexpr int QST = NGRP > 1 ? 32 * D * (G + 2) : 0;
   __shared__ __attribute__((aligned(1024))) char lds[NST * GE::STAGE + QST];
   char* const qst = lds + NST * GE::STAGE;
-  __shared__ uint32_t s_last;
+  __shared__ uint32_t s_last, s_early;
   __shared__ int32_t s_pt[PAGED ? kMaxPtEntries : 1];
 
   // XCD-aware decode: WG i runs on XCD i % 8; every split of a unit shares one XCD.
@@ -675,6 +675,23 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   constexpr int DTG = DT / NGRP;
   const int dt0 = grp * DTG;
   f32x4 oh[DTG];
+
+  // Fused merge, early hand-off.  The split that attends to the block keys (the last
+  // one) usually ends its loop after the others.  It reads its unit's counter before
+  // the wave-group fold, so the read's round trip overlaps the fold: if the other
+  // ns - 1 splits have all stored their partials, it is the last arrival and goes
+  // straight to the merge, with no arrival to count and no wait (its loads, issued
+  // after that read, see every stored partial in the L2).  Otherwise it takes the
+  // hand-off below.
+  uint32_t* cnt = p.count + (int64_t)u * kCntStride;
+  const bool try_early = p.fused && ns > 1 && last_split;
+  uint32_t early_v = 0;
+  if (try_early && tid == 0) {
+    uint32_t zero;  // an opaque zero: see the poll below
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+    early_v = __hip_atomic_fetch_add(cnt, zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+
   if constexpr (NGRP > 1) {
     static_assert(NGRP == 2, "two wave groups");
     __syncthreads();
@@ -685,6 +702,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
     for (int j = 0; j < DTG; ++j)
       *reinterpret_cast<f32x4*>(give + (j * 64 + lane) * 4) = grp ? o[j] : o[DTG + j];
     *reinterpret_cast<float2*>(xml + ((grp * G + hw) * 64 + lane) * 2) = make_float2(m, lsum);
+    if (try_early && tid == 0) s_early = (early_v >> 16) == (uint32_t)(ns - 1) ? 1u : 0u;
     __syncthreads();
     const int oth = 1 - grp;
     const float* take = xo + (oth * G + hw) * DTG * 256;
@@ -705,7 +723,12 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   } else {
 #pragma unroll
     for (int j = 0; j < DTG; ++j) oh[j] = o[j];
+    if (try_early) {
+      if (tid == 0) s_early = (early_v >> 16) == (uint32_t)(ns - 1) ? 1u : 0u;
+      __syncthreads();
+    }
   }
+  const bool early = try_early && __builtin_amdgcn_readfirstlane(s_early) != 0u;
   // Every wave now holds the split's (m, lsum) for query head hw and its O for
   // dimension tiles dt0 .. dt0 + DTG - 1.
 
@@ -750,41 +773,45 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   // (those splits already arrived, so they are running and only storing), clears
   // the counter for the next call and combines all ns states (log-sum-exp, in
   // split order).
-  uint32_t* cnt = p.count + (int64_t)u * kCntStride;
-  uint32_t prev = 0;
-  if (tid == 0) {
-    prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    s_last = (prev & 0xffffu) == (uint32_t)(ns - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!__builtin_amdgcn_readfirstlane(s_last)) {
-    store_partial();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    wait_vmcnt<0>();  // this wave's partial is in the L2
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();  // ... and every other wave's
-    if (tid == 0) __hip_atomic_fetch_add(cnt, 1u << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return;
-  }
-  if (tid == 0) {
-    uint32_t v = prev;
-    for (int spin = 0; (v >> 16) != (uint32_t)(ns - 1); ++spin) {
-      if (spin >= kMergeSpinLimit) {  // cannot happen while the stored splits run; never hang
-        set_dev_error(p.err, kDevErrMerge);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-      // Re-read the count with an atomic add of an opaque zero, performed in the L2.
-      // A load would not do: the first one brings the line into this CU's L1 and the
-      // next ones hit that stale copy (a workgroup-scope invalidate does not drop
-      // it), and the compiler turns an atomic add of a literal zero into such a load.
-      uint32_t zero;
-      asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
-      v = __hip_atomic_fetch_add(cnt, zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (early) {
+    // every other split arrived and stored: clear the counter for the next call
+    if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else {
+    uint32_t prev = 0;
+    if (tid == 0) {
+      prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      s_last = (prev & 0xffffu) == (uint32_t)(ns - 1) ? 1u : 0u;
     }
-    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(s_last)) {
+      store_partial();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      wait_vmcnt<0>();  // this wave's partial is in the L2
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __syncthreads();  // ... and every other wave's
+      if (tid == 0) __hip_atomic_fetch_add(cnt, 1u << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return;
+    }
+    if (tid == 0) {
+      uint32_t v = prev;
+      for (int spin = 0; (v >> 16) != (uint32_t)(ns - 1); ++spin) {
+        if (spin >= kMergeSpinLimit) {  // cannot happen while the stored splits run; never hang
+          set_dev_error(p.err, kDevErrMerge);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        // Re-read the count with an atomic add of an opaque zero, performed in the L2.
+        // A load would not do: the first one brings the line into this CU's L1 and the
+        // next ones hit that stale copy (a workgroup-scope invalidate does not drop
+        // it), and the compiler turns an atomic add of a literal zero into such a load.
+        uint32_t zero;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+        v = __hip_atomic_fetch_add(cnt, zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // The merge: every wave combines its DTG dimension tiles of its head over all
   // splits: its own split from registers, the others from the shared L2 (sc0
