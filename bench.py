@@ -42,8 +42,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "c853b1676efe093531104eaf9f47ce6a50265fe58c6b1d4dbdbe68647eddcd96",
-                "workload": "batched", "read": 276988401, "write": 8504483}
+ATTN_TRAFFIC = {"sha256": "112430767ba115231691f6b08c39ecb632f4315210819fccfa5a01695b48799a",
+                "workload": "batched", "read": 276989188, "write": 8506169}
 
 
 def sources_sha256(paths):
