@@ -26,10 +26,10 @@ namespace dflash {
 
 namespace {
 
-constexpr int kRowThreads = 256;  // one workgroup per row: 4 waves
+constexpr int kRowThreads = 512;  // one workgroup per row: 8 waves (8 columns per thread per pass)
 
 // Sum over the workgroup in a fixed order: xor butterflies inside each wave (every
-// lane ends with the same value), then the four wave totals in wave order.
+// lane ends with the same value), then the wave totals in wave order.
 __device__ __forceinline__ double block_sum(double v, double* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -89,17 +89,28 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(RmsNormParams p) {
   }
 }
 
-// Sum of the split partials of 4 consecutive outputs, in split order.
+// Sum of the split partials of 4 consecutive outputs, in split order.  The loads of
+// up to 8 splits are all issued before the first add (a split past the last reads the
+// last one's address and is dropped), so 8 splits cost one memory round trip.
 __device__ __forceinline__ f32x4 sum4(const float* base, int64_t stride, int splits) {
+  constexpr int kBatch = 8;
   f32x4 s = *reinterpret_cast<const f32x4*>(base);
-  for (int z = 1; z < splits; ++z) s += *reinterpret_cast<const f32x4*>(base + z * stride);
+  for (int z0 = 1; z0 < splits; z0 += kBatch) {
+    f32x4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      v[u] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(z0 + u, splits - 1) * stride);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (z0 + u < splits) s += v[u];
+  }
   return s;
 }
 
 // x1 = bf16(x + sum of the o_proj partials), then n2 = RMSNorm(x1; w_post): one
 // workgroup per row.  The row's x1 chunks stay in registers between the passes
 // (cols <= kRowThreads * 8 * kMaxChunks).
-constexpr int kMaxChunks = 8;  // hidden <= 16384
+constexpr int kMaxChunks = 4;  // hidden <= 16384
 __global__ __launch_bounds__(kRowThreads) void residual_norm_kernel(LayerPostParams p) {
   __shared__ double red[kRowThreads / 64];
   const int m = blockIdx.x;
