@@ -21,6 +21,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "split_sum.h"
 
 namespace dflash {
 
@@ -89,23 +90,6 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(RmsNormParams p) {
   }
 }
 
-// Sum of the split partials of 4 consecutive outputs, in split order.  The loads of
-// up to 8 splits are all issued before the first add (a split past the last reads the
-// last one's address and is dropped), so 8 splits cost one memory round trip.
-__device__ __forceinline__ f32x4 sum4(const float* base, int64_t stride, int splits) {
-  constexpr int kBatch = 8;
-  f32x4 s = *reinterpret_cast<const f32x4*>(base);
-  for (int z0 = 1; z0 < splits; z0 += kBatch) {
-    f32x4 v[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      v[u] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(z0 + u, splits - 1) * stride);
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (z0 + u < splits) s += v[u];
-  }
-  return s;
-}
 
 // x1 = bf16(x + sum of the o_proj partials), then n2 = RMSNorm(x1; w_post): one
 // workgroup per row.  The row's x1 chunks stay in registers between the passes
@@ -124,8 +108,8 @@ __global__ __launch_bounds__(kRowThreads) void residual_norm_kernel(LayerPostPar
     if (c >= D) break;
     double xr[8];
     unpack8(ld16(p.x + (int64_t)m * D + c), xr);
-    const f32x4 s0 = sum4(p.part_o + (int64_t)m * D + c, zs, p.splits_o);
-    const f32x4 s1 = sum4(p.part_o + (int64_t)m * D + c + 4, zs, p.splits_o);
+    const f32x4 s0 = sum_splits(p.part_o + (int64_t)m * D + c, zs, p.splits_o);
+    const f32x4 s1 = sum_splits(p.part_o + (int64_t)m * D + c + 4, zs, p.splits_o);
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -156,8 +140,8 @@ __global__ __launch_bounds__(256) void swiglu_kernel(LayerPostParams p) {
   const int64_t m = 4 * i / I;
   const int j = (int)(4 * i - m * I);
   const int64_t zs = (int64_t)p.M * 2 * I;
-  const f32x4 g = sum4(p.part_gu + m * 2 * I + j, zs, p.splits_gu);
-  const f32x4 u = sum4(p.part_gu + m * 2 * I + I + j, zs, p.splits_gu);
+  const f32x4 g = sum_splits(p.part_gu + m * 2 * I + j, zs, p.splits_gu);
+  const f32x4 u = sum_splits(p.part_gu + m * 2 * I + I + j, zs, p.splits_gu);
   float a[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) a[e] = g[e] / (1.f + expf(-g[e])) * u[e];
@@ -169,7 +153,7 @@ __global__ __launch_bounds__(256) void residual_add_kernel(LayerPostParams p) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int D = p.hidden;
   if (i >= (int64_t)p.M * D / 4) return;
-  const f32x4 s = sum4(p.part_d + 4 * i, (int64_t)p.M * D, p.splits_d);
+  const f32x4 s = sum_splits(p.part_d + 4 * i, (int64_t)p.M * D, p.splits_d);
   const u32x2 x = *reinterpret_cast<const u32x2*>(p.x1 + 4 * i);
   const float v0 = bf16_lo(x[0]) + s[0], v1 = bf16_hi(x[0]) + s[1];
   const float v2 = bf16_lo(x[1]) + s[2], v3 = bf16_hi(x[1]) + s[3];
