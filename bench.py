@@ -43,7 +43,7 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
 ATTN_TRAFFIC = {"sha256": "112430767ba115231691f6b08c39ecb632f4315210819fccfa5a01695b48799a",
-                "workload": "batched", "read": 276989188, "write": 8506169}
+                "workload": "batched", "read": 276989196, "write": 8506218}
 
 
 def sources_sha256(paths):
