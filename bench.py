@@ -145,6 +145,12 @@ def attn_bytes(cfg, ctx_len):
     return b
 
 
+def window_size(cfg, max_ctx):
+    """The window the bench times the sliding-window attention with: half the longest
+    context, a multiple of 16 (a whole number of pages), at least 16."""
+    return max(16, (max_ctx // 2) // 16 * 16)
+
+
 def verify_bytes(cfg, B):
     return 2 * 16 * B * cfg.vocab + 4 * 16 * B * 3 + 4 * B * 4
 
@@ -356,7 +362,7 @@ def main():
     # next_token as its staged tokens.
     N_SPLIT = 50
     PASS_HOLD_CYCLES = 2_000_000  # ~1 ms of the shader clock: longer than the host needs to enqueue a pass step
-    NEV = 10
+    NEV = 11
     tev = HipTimingEvents(2 * args.steps, torch.cuda.current_stream().cuda_stream)
     sev = HipTimingEvents(NEV * N_SPLIT, torch.cuda.current_stream().cuda_stream)
     dblk = z(B, 16)
@@ -384,6 +390,13 @@ def main():
     # the same hidden states and weight as dflash_block_qkv, into its own output
     ws_f = dfl.workspace(dfl.dflash_block_qkv_attn_workspace_size(dims, max_ctx), dev)
     out_f = torch.empty_like(out)
+    # ... and the attention over a sliding window (a ring cache of W rows per sequence and
+    # kv head: the context is the last min(L, W) positions), on the same cache buffers
+    W = window_size(cfg, max_ctx)
+    dims_w = dfl.make_dims(B, Hq, Hkv, d, hidden=cfg.hidden, page_size=cfg.page_size, kv_capacity=at.capacity,
+                           num_pages=at.num_pages, window=W)
+    ws_w = dfl.workspace(dfl.dflash_block_attn_workspace_size(dims_w, max_ctx), dev)
+    out_w = torch.empty_like(out)
 
     # The attention calls are prepared once per input copy (checks and argument conversion
     # done here), so the event before a call is followed at once by the launch: with an
@@ -391,6 +404,8 @@ def main():
     # marshalling time.
     attn_calls = [dfl.bind_block_attn(dims, q, k, v, kcs[i], vcs[i], table, ctx, max_ctx, cos, sin, out, ws_a)
                   for i in range(R)]
+    attn_w_calls = [dfl.bind_block_attn(dims_w, q, k, v, kcs[i], vcs[i], table, ctx, max_ctx, cos, sin, out_w, ws_w)
+                    for i in range(R)]
 
     def step(i, ev=None, base=0, split=False):
         if ev is not None:
@@ -418,6 +433,8 @@ def main():
             ev.record(base + 8)
             dfl.dflash_block_qkv_attn(dims, h_blk, w_qkv, kcs[i], vcs[i], table, ctx, max_ctx, cos, sin, out_f, ws_f)
             ev.record(base + 9)
+            attn_w_calls[i]()
+            ev.record(base + 10)
 
     n_settle = 0
     t_settle = time.perf_counter()
@@ -448,7 +465,9 @@ def main():
     span = lambda i, j: float(np.mean([sev.elapsed_ms(NEV * s + i, NEV * s + j) for s in range(N_SPLIT)])) * 1e-3
     t_ver, t_proj, t_draft, t_qkv = span(1, 2), span(2, 3), span(3, 4), span(4, 5)
     t_norm, t_post, t_replay, t_fused = span(5, 6), span(6, 7), span(7, 8), span(8, 9)
+    t_win = span(9, 10)
     f_b = fused_bytes(cfg, at.ctx_len)
+    w_b = attn_bytes(cfg, np.minimum(at.ctx_len, W))
     nb, pb = layer_bytes(cfg, B)
     rb = replay_bytes(B, GH, GD, GD, acc.cpu().numpy())
     d_b = draft_bytes(cfg, B)
@@ -504,6 +523,10 @@ def main():
                             "scope": "the block's q/k/v and the attention in one call (split-K GEMM, a "
                                      "reduce that rotates Q into a bf16 hi/lo pair and K, then the attention); "
                                      "unfused_us = block_qkv + block_attn; not in the timed step"},
+        "block_attn_window": {"window": W, "us": round(t_win * 1e6, 2), "GB_s": round(w_b / t_win / 1e9, 1),
+                              "pct_hbm_peak": round(100 * w_b / t_win / 1e9 / HBM_PEAK_GBS, 2), "bytes": w_b,
+                              "scope": "the attention over a sliding window: the context is the last min(L, W) "
+                                       "positions of a ring cache of W rows; not in the timed step"},
         "timing": "block_attn: HIP events around every timed call; the other calls: events in a %d-step "
                   "pass after the timed region, each pass step enqueued behind a short spin kernel so that "
                   "its spans hold no host time" % N_SPLIT,

@@ -37,6 +37,17 @@ def test_algorithmic_bytes_at_the_batched_workload():
     assert bench.qkv_bytes(cfg, B) == 2 * (n_out * 4096 + 16 * B * 4096 + 16 * B * n_out) == 52_953_088
 
 
+def test_sliding_window_bytes_at_the_batched_workload():
+    # the window is half the longest context, in whole pages; only the last W positions
+    # of each context are read
+    cfg = synth.CONFIGS["batched"]
+    B, Hq, Hkv, d = 8, 32, 8, 128
+    W = bench.window_size(cfg, 8192)
+    assert W == 4096 and bench.window_size(cfg, 40) == 16 and bench.window_size(cfg, 100) == 48
+    win = 2 * 2 * B * Hkv * W * d + 2 * B * 16 * Hq * d + 2 * 2 * B * 16 * Hkv * d + 4 * B * 16 * Hq * d + 4 * B
+    assert bench.attn_bytes(cfg, np.minimum(np.full(B, 8192, np.int32), W)) == win == 137_887_776
+
+
 def test_traffic_figure_only_for_its_workload_and_sources():
     t = bench.ATTN_TRAFFIC
     assert bench.measured_traffic("ragged") is None
