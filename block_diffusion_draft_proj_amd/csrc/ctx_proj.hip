@@ -232,15 +232,16 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
   }
 }
 
-// Skinny product (M <= 128 rows of activations, the per-cycle case): a weight
-// stream.  Each workgroup owns 128 weight rows (4 row waves x 32) and one K range,
-// and sees all 16*MT activation rows (MT = 4 or 8: two wave groups of 4, each on
-// half of the activation tiles).  A 64-K stage holds the weight tile
+// Skinny product (M <= 256 rows of activations, the per-cycle case): a weight
+// stream.  Each workgroup owns 128 weight rows (4 row waves x 32; 64 rows, 4 x 16,
+// when the grid would otherwise leave half of the CUs idle, see launch_skinny) and
+// one K range, and sees all 16*MT activation rows (MT = 4, 8 or 16: two wave groups
+// of 4, each on half of the activation tiles).  A 64-K stage holds the weight tile
 // (128 rows, 16 KB) and the activation tile (16*MT rows, MT x 2 KB); stages go
 // global -> swizzled LDS by global_load_lds through a 4-stage ring (128 KB at
 // MT = 8), so three stages are in flight while one feeds the MFMAs.
-// Per stage a wave reads its own 32 weight rows (4 KB) and its activation tiles
-// from LDS and does 2 x MTW x 2 MFMAs; each weight byte crosses LDS 1 + TG times
+// Per stage a wave reads its own 16 x RT weight rows and its activation tiles
+// from LDS and does 2 x MTW x RT MFMAs; each weight byte crosses LDS 1 + TG times
 // and each activation byte five times (vs. thirteen for a square-tile GEMM).
 // The activations either come packed step by step ([K/64][16*MT rows][64]: the K/V
 // product reads C packed by fc_reduce_kernel, or by pack_rows_kernel when the rows
@@ -254,12 +255,13 @@ constexpr int SK_RW = 4;                     // weight-row wave groups (32 rows 
 // 151 us, at 512 rows (two skinny passes) 195 against 154 us; at 256 rows the skinny
 // pass wins, 110 against 126 us.
 constexpr int kSkinnyMaxRows = 256;
-constexpr int SK_RT = 2;                     // 16-row weight tiles per wave
-constexpr int SK_ROWS = SK_RW * SK_RT * 16;  // weight rows per workgroup (128)
+constexpr int SK_RT = 2;                     // 16-row weight tiles per wave (1 on small grids)
+constexpr int SK_ROWS = SK_RW * SK_RT * 16;  // weight rows per workgroup (128; the planner's tile)
 
-template <int MT>
+template <int MT, int RT = SK_RT>
 struct SkGeo {
-  static constexpr int W_TILE = SK_ROWS * BK * 2;             // 16 KB
+  static constexpr int ROWS = SK_RW * RT * 16;                // weight rows per workgroup
+  static constexpr int W_TILE = ROWS * BK * 2;                // RT x 8 KB
   static constexpr int X_TILE = 16 * MT * BK * 2;             // MT x 2 KB
   static constexpr int STAGE = W_TILE + X_TILE;
   static constexpr int NS = (160 * 1024) / STAGE < 4 ? (160 * 1024) / STAGE : 4;  // ring stages
@@ -278,9 +280,9 @@ struct SkGeo {
 // PACKED: activations come packed as [K/64][mp][64] steps (written by
 // fc_reduce_kernel for the K/V product); else they are read in place from the
 // segments a_seg[] ([M][lda] each, seg_k columns of K per segment).
-template <int MT, bool PACKED>
-__global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(GemmParams p) {
-  using SG = SkGeo<MT>;
+template <int MT, bool PACKED, int RT>
+__global__ __launch_bounds__((SkGeo<MT, RT>::WAVES * 64)) void gemm_skinny_kernel(GemmParams p) {
+  using SG = SkGeo<MT, RT>;
   __shared__ __attribute__((aligned(1024))) char lds[SG::NS * SG::STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
     z = id % splits;
     col = id / splits;
   }
-  const int n0 = col * SK_ROWS;
+  const int n0 = col * SG::ROWS;
   const int kbeg = z * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
   const int n_st = (kend - kbeg) / BK;
@@ -359,9 +361,9 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
 
   constexpr int MTW = SG::MTW;
   const int wr = w % SK_RW, wt = w / SK_RW;  // weight rows 32wr.., activation tiles MTW*wt..
-  f32x4 acc[SK_RT][MTW];
+  f32x4 acc[RT][MTW];
 #pragma unroll
-  for (int rt = 0; rt < SK_RT; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt) acc[rt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
@@ -387,16 +389,16 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
     const char* sx = sw + SG::W_TILE;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      bf16x8 a[SK_RT], xb[MTW];
+      bf16x8 a[RT], xb[MTW];
 #pragma unroll
-      for (int rt = 0; rt < SK_RT; ++rt)
-        a[rt] = *reinterpret_cast<const bf16x8*>(sw + swz_off(wr * 32 + rt * 16 + r, kh * 4 + q));
+      for (int rt = 0; rt < RT; ++rt)
+        a[rt] = *reinterpret_cast<const bf16x8*>(sw + swz_off(wr * (16 * RT) + rt * 16 + r, kh * 4 + q));
 #pragma unroll
       for (int mt = 0; mt < MTW; ++mt)
         xb[mt] = *reinterpret_cast<const bf16x8*>(sx + swz_off((wt * MTW + mt) * 16 + r, kh * 4 + q));
       if (refill) issue(it + SG::NS - 1, kh == 0 ? 0 : LH, kh == 0 ? LH : SG::LW);
 #pragma unroll
-      for (int rt = 0; rt < SK_RT; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt) acc[rt][mt] = mfma16x16x32(a[rt], xb[mt], acc[rt][mt]);
     }
@@ -406,8 +408,8 @@ __global__ __launch_bounds__(SkGeo<MT>::WAVES * 64) void gemm_skinny_kernel(Gemm
   // the 16-row tile: 4 consecutive outputs of one row, one 16-byte store.
   float* out = p.out + (int64_t)z * p.M * p.N;
 #pragma unroll
-  for (int rt = 0; rt < SK_RT; ++rt) {
-    const int n = n0 + wr * 32 + rt * 16 + 4 * q;
+  for (int rt = 0; rt < RT; ++rt) {
+    const int n = n0 + wr * (16 * RT) + rt * 16 + 4 * q;
     if (n >= p.N) continue;
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt) {
@@ -696,10 +698,23 @@ QkvPlan plan_block_qkv(int n_rows, int hidden, int n_out, int num_cu) {
   return pl;
 }
 
+template <int MT, bool PACKED, int RT>
+void launch_skinny_rt(const GemmParams& p, int splits, hipStream_t stream) {
+  using SG = SkGeo<MT, RT>;
+  dim3 grid(((p.N + SG::ROWS - 1) / SG::ROWS) * splits, 1, 1);
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT, PACKED, RT>), grid, dim3(SG::WAVES * 64), 0, stream, p);
+}
+
+// The planner splits K for 128-row weight tiles.  Where its tiles times splits fill at
+// most half of the CUs (the K/V product at 128 rows: 16 tiles x 8 splits), each
+// workgroup takes 64 weight rows instead, so twice the workgroups stream the same
+// weights with the same splits (and the same fp32 partials): the batched projection
+// 57.6 -> 56.3 us per call (interleaved A/B inside the step, events).
 template <int MT, bool PACKED>
 void launch_skinny(const GemmParams& p, int splits, hipStream_t stream) {
-  dim3 grid(((p.N + SK_ROWS - 1) / SK_ROWS) * splits, 1, 1);
-  hipLaunchKernelGGL((gemm_skinny_kernel<MT, PACKED>), grid, dim3(SkGeo<MT>::WAVES * 64), 0, stream, p);
+  const int64_t tiles = (p.N + SK_ROWS - 1) / SK_ROWS;
+  if (2 * tiles * splits <= kPlanCUs) launch_skinny_rt<MT, PACKED, 1>(p, splits, stream);
+  else launch_skinny_rt<MT, PACKED, SK_RT>(p, splits, stream);
 }
 
 // Up to kSkinnyMaxRows rows; activation tiles in pairs of 16 rows.
