@@ -133,6 +133,14 @@ __device__ __forceinline__ float max_across_rows(float x) {
   const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
   return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
+// Sum over the same four lanes: each permute returns the two values of a lane pair,
+// one per result, so the sum is the same whichever is which.
+__device__ __forceinline__ float sum_across_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
 
 // bf16 hi/lo split of two probabilities: hi = RNE(x), lo = RNE(x - hi), packed.
 __device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
@@ -732,8 +740,7 @@ __global__ __launch_bounds__(64 * ngrp<G>() * G) void block_attn_kernel(AttnPara
   // Every wave now holds the split's (m, lsum) for query head hw and its O for
   // dimension tiles dt0 .. dt0 + DTG - 1.
 
-  float lt = lsum + __shfl_xor(lsum, 16);
-  lt += __shfl_xor(lt, 32);
+  const float lt = sum_across_rows(lsum);
 
   float* outp = p.out + (((int64_t)b * kBlock + r) * p.n_q_heads + h) * D + 4 * q;
   if (ns == 1) {

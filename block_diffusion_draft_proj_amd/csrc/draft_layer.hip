@@ -29,11 +29,44 @@ namespace {
 
 constexpr int kRowThreads = 512;  // one workgroup per row: 8 waves (8 columns per thread per pass)
 
-// Sum over the workgroup in a fixed order: xor butterflies inside each wave (every
-// lane ends with the same value), then the wave totals in wave order.
+// A double moved across lanes by DPP (its two halves): a VALU move, no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// v + (the same lane's value in the paired row): the row-swap permute returns the two
+// values of each lane pair {l, l ^ 16} (or l ^ 32), one per result, and their sum does
+// not depend on which is which.
+__device__ __forceinline__ double add_pair(uint32_t lo0, uint32_t hi0, uint32_t lo1, uint32_t hi1) {
+  return __longlong_as_double((long long)(((uint64_t)hi0 << 32) | lo0)) +
+         __longlong_as_double((long long)(((uint64_t)hi1 << 32) | lo1));
+}
+__device__ __forceinline__ double sum_rows16(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+  return add_pair(lo[0], hi[0], lo[1], hi[1]);
+}
+__device__ __forceinline__ double sum_rows32(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+  return add_pair(lo[0], hi[0], lo[1], hi[1]);
+}
+
+// Sum over the workgroup in a fixed order: a balanced tree inside each wave (pairs, then
+// quads, then the four quads of a 16-lane row, then rows 0 + 1 and 2 + 3, then the two
+// halves), whose result lane 0 holds, then the wave totals in wave order.
 __device__ __forceinline__ double block_sum(double v, double* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  v += dpp_f64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x124>(v);  // row_ror 4
+  v += dpp_f64<0x128>(v);  // row_ror 8
+  v = sum_rows16(v);
+  v = sum_rows32(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();  // red[] free (an earlier call's readers are done)
   if ((threadIdx.x & 63) == 0) red[w] = v;

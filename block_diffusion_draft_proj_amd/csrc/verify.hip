@@ -65,15 +65,44 @@ constexpr uint32_t kNegInfBits2 = 0xff80ff80u;
 __device__ __forceinline__ bool is_zero_key(uint32_t k) { return k == 0x7fffu || k == 0x8000u; }
 __device__ __forceinline__ bool is_nan_key(uint32_t k) { return k < kKeyNegInf || k > kKeyPosInf; }
 
-template <typename T, typename Op>
-__device__ __forceinline__ T wg_reduce(T v, Op op, T* s_buf) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = op(v, __shfl_xor(v, off));
+// DPP lane moves (gfx9 encodings): swaps inside quads, rotations inside 16-lane rows.
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Reduction of an associative, commutative op over the 16 lanes of each row: after the
+// two quad swaps every lane holds its quad's result, after the rotations by 4 and 8 its
+// row's.  All VALU: no LDS round trip per step, as a shuffle would take.
+template <typename Op>
+__device__ __forceinline__ uint32_t row_reduce(uint32_t v, Op op) {
+  v = op(v, dpp<kDppQuadXor1>(v));
+  v = op(v, dpp<kDppQuadXor2>(v));
+  v = op(v, dpp<kDppRowRor4>(v));
+  return op(v, dpp<kDppRowRor8>(v));
+}
+// ... then over the four rows with the gfx950 row-swap permutes (lanes l ^ 16, l ^ 32).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+  v = row_reduce(v, op);
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(a[0], a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(c[0], c[1]);
+}
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wg_reduce(uint32_t v, Op op, uint32_t* s_buf) {
+  v = wave_reduce(v, op);
   const int wave = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) s_buf[wave] = v;
   __syncthreads();
-  T r = s_buf[0];
+  uint32_t r = s_buf[0];
 #pragma unroll
   for (int w = 1; w < kThreads / kWave; ++w) r = op(r, s_buf[w]);
   return r;
@@ -120,8 +149,9 @@ __device__ __forceinline__ uint64_t chunk_key(const VerifyParams& p, int row, in
   }
   const uint32_t tmax = max(kmax & 0xffffu, kmax >> 16);
   const uint32_t tmin = min(kmin & 0xffffu, kmin >> 16);
-  const uint32_t cmax = wg_reduce(tmax, [](uint32_t a, uint32_t c) { return max(a, c); }, s_red);
-  const uint32_t cmin = wg_reduce(tmin, [](uint32_t a, uint32_t c) { return min(a, c); }, s_red);
+  // One reduction for both: the maximum in the high half, 0xffff - minimum in the low.
+  const uint32_t both = wg_reduce((tmax << 16) | (0xffffu - tmin), [](uint32_t a, uint32_t c) { return pk_max(a, c); }, s_red);
+  const uint32_t cmax = both >> 16, cmin = 0xffffu - (both & 0xffffu);
 
   // Pass 2: first element index holding the chunk maximum.
   const bool has_nan = (cmin < kKeyNegInf) || (cmax > kKeyPosInf);
@@ -201,13 +231,12 @@ __device__ __forceinline__ uint64_t row_best(const VerifyParams& p, int row, int
     const uint64_t k = pr[c];
     best = k > best ? k : best;
   }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)best, off), hi = __shfl_xor((uint32_t)(best >> 32), off);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    best = o > best ? o : best;
-  }
-  return best;
+  auto max64 = [](uint64_t a, uint64_t c) { return a > c ? a : c; };
+  auto step = [&](uint64_t v, uint32_t lo, uint32_t hi) { return max64(v, ((uint64_t)hi << 32) | lo); };
+  best = step(best, dpp<kDppQuadXor1>((uint32_t)best), dpp<kDppQuadXor1>((uint32_t)(best >> 32)));
+  best = step(best, dpp<kDppQuadXor2>((uint32_t)best), dpp<kDppQuadXor2>((uint32_t)(best >> 32)));
+  best = step(best, dpp<kDppRowRor4>((uint32_t)best), dpp<kDppRowRor4>((uint32_t)(best >> 32)));
+  return step(best, dpp<kDppRowRor8>((uint32_t)best), dpp<kDppRowRor8>((uint32_t)(best >> 32)));
 }
 __device__ __forceinline__ int32_t key_index(uint64_t key) { return (int32_t)(0xffffffffu - (uint32_t)key); }
 
