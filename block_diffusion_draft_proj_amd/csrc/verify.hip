@@ -17,11 +17,15 @@
 //    held in registers, by only the threads whose own maximum matched;
 //  * each chunk publishes one 64-bit key (value key << 32 | ~index), so the row
 //    maximum with the lowest index is an order-independent max();
+//  * cross-lane steps use DPP lane moves and the gfx950 row-swap permutes, not LDS
+//    shuffles;
 //  * with 8 or more sequences, the last workgroup of each sequence reduces its 16
 //    rows and runs accept / commit / crop inside the same kernel: all workgroups
 //    of a sequence sit on one XCD and hand over through its L2 (arrival counted by
-//    an L2 atomic), with no device-wide fence;
-//  * with fewer sequences, a second kernel (one workgroup per sequence) does that
+//    an L2 atomic), with no device-wide fence.  Only wave 0 takes part in the
+//    hand-off and the accept step, so the other waves leave once the chunk key is
+//    known and their slots go to the remaining workgroups;
+//  * with fewer sequences, a second kernel (one wave per sequence) does that
 //    step: a kernel boundary is then the cheapest device-wide hand-off, since
 //    handing off across XCDs inside one kernel would need an L2 writeback
 //    (agent-scope release) from every workgroup.  No host round trip.
@@ -201,82 +205,75 @@ __global__ __launch_bounds__(kThreads) void verify_argmax_kernel(VerifyParams p)
   if (threadIdx.x == 0) p.part[(int64_t)row * p.n_chunks + chunk] = key;
 }
 
-// One workgroup per sequence: reduce the chunk keys of its 16 rows, then accept,
-// next staged token, KV-length crop, commit positions and page count.  Running
-// after the argmax kernel on the same stream, it sees every chunk key without
-// any device-wide fence.  Every global load is issued up front (16 threads per
-// row over the chunk keys, the 16 block tokens, the input length), so the kernel
-// costs one memory round trip; a chain of dependent loads would cost one each.
-constexpr int kAcceptThreads = 16 * kBlock;
-static_assert(kAcceptThreads == kThreads, "the fused kernel runs the accept step with its own threads");
+// The accept step runs on one wave (64 lanes, 4 per block row: lane = 4 * row + sub), so
+// the fused kernel's other three waves of every workgroup leave as soon as the chunk key
+// is known.  No LDS and no barrier: the row maxima are combined by DPP quad swaps and the
+// per-row values are exchanged across lanes.
+constexpr int kAcceptThreads = kWave;
+constexpr int kRowLoads = 8;  // chunk keys per lane in flight (up to 32 chunks per round trip)
 
-struct AcceptShared {
-  int32_t post[kBlock], blk[kBlock];
-  int32_t accept, kvin;
-};
-
-// Sequence b: reduce the chunk keys of its 16 rows, then accept, next staged
-// token, KV-length crop, commit positions and page count.  256 threads.  Every
-// global load is issued up front (16 threads per row over the chunk keys, the 16
-// block tokens, the input length), so the step costs one memory round trip; a
-// chain of dependent loads would cost one each.
-// Largest chunk key of logit row `row` over its first n_chunks chunks, reduced
-// over the 16 lanes that share tid >> 4 (lane `sub` reads chunks sub, sub+16, ...).
-// Every lane of the group returns it.
+// Largest chunk key of logit row `row` over its first n_chunks chunks, reduced over the 4
+// lanes of the row (lane `sub` reads chunks sub, sub + 4, ...).  Every lane of the row
+// returns it (0 when n_chunks is 0).  All loads of a round are issued before any is
+// compared.
 __device__ __forceinline__ uint64_t row_best(const VerifyParams& p, int row, int sub, int n_chunks) {
   const uint64_t* pr = p.part + (int64_t)row * p.n_chunks;
   uint64_t best = 0;
-#pragma unroll 4
-  for (int c = sub; c < n_chunks; c += 16) {
-    const uint64_t k = pr[c];
-    best = k > best ? k : best;
+  for (int c0 = 0; c0 < n_chunks; c0 += 4 * kRowLoads) {
+    // Chunks past the end re-read the last one: a repeated key leaves the maximum
+    // unchanged, and unconditional loads all go out before the first wait.
+    uint64_t k[kRowLoads];
+#pragma unroll
+    for (int i = 0; i < kRowLoads; ++i) k[i] = pr[min(c0 + sub + 4 * i, n_chunks - 1)];
+#pragma unroll
+    for (int i = 0; i < kRowLoads; ++i) best = k[i] > best ? k[i] : best;
   }
-  auto max64 = [](uint64_t a, uint64_t c) { return a > c ? a : c; };
-  auto step = [&](uint64_t v, uint32_t lo, uint32_t hi) { return max64(v, ((uint64_t)hi << 32) | lo); };
+  auto step = [](uint64_t v, uint32_t lo, uint32_t hi) {
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > v ? o : v;
+  };
   best = step(best, dpp<kDppQuadXor1>((uint32_t)best), dpp<kDppQuadXor1>((uint32_t)(best >> 32)));
-  best = step(best, dpp<kDppQuadXor2>((uint32_t)best), dpp<kDppQuadXor2>((uint32_t)(best >> 32)));
-  best = step(best, dpp<kDppRowRor4>((uint32_t)best), dpp<kDppRowRor4>((uint32_t)(best >> 32)));
-  return step(best, dpp<kDppRowRor8>((uint32_t)best), dpp<kDppRowRor8>((uint32_t)(best >> 32)));
+  return step(best, dpp<kDppQuadXor2>((uint32_t)best), dpp<kDppQuadXor2>((uint32_t)(best >> 32)));
 }
 __device__ __forceinline__ int32_t key_index(uint64_t key) { return (int32_t)(0xffffffffu - (uint32_t)key); }
 
-__device__ __forceinline__ void accept_seq(const VerifyParams& p, int b, AcceptShared& sh) {
-  const int tid = threadIdx.x;
-  const int row = tid >> 4, sub = tid & 15;  // 16 threads per row, rows aligned to 16 lanes
-  if (tid < kBlock) sh.blk[tid] = p.block_tokens[b * kBlock + tid];
-  if (tid == 0) sh.kvin = p.kv_len_in[b];
-  const uint64_t best = row_best(p, b * kBlock + row, sub, p.n_chunks);
-  if (sub == 0) {
-    const int32_t post = key_index(best);
-    sh.post[row] = post;
-    p.posterior[b * kBlock + row] = post;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int a = 0;
-    while (a < kBlock - 1 && sh.blk[a + 1] == sh.post[a]) ++a;
-    sh.accept = a;
-    const int32_t kv_out = sh.kvin + 1 + a;
+// Sequence b: reduce the chunk keys of its 16 rows, then accept, next staged token,
+// KV-length crop, commit positions and page count.  One wave; every global load (chunk
+// keys, block tokens, input length) is issued before the first is used.
+__device__ __forceinline__ void accept_seq(const VerifyParams& p, int b) {
+  const int lane = threadIdx.x;
+  const int row = lane >> 2, sub = lane & 3;
+  const int32_t blk = lane < kBlock ? p.block_tokens[b * kBlock + lane] : 0;
+  const int32_t kvin = p.kv_len_in[b];
+  const int32_t post = key_index(row_best(p, b * kBlock + row, sub, p.n_chunks));
+  if (sub == 0) p.posterior[b * kBlock + row] = post;
+  // Lane t < 15 compares draft token t + 1 with the target's token at position t.
+  const int t = lane < kBlock - 1 ? lane : kBlock - 2;
+  const int32_t post_t = __shfl(post, 4 * t);
+  const int32_t blk_next = __shfl(blk, t + 1);
+  const uint64_t miss = __ballot(lane < kBlock - 1 && blk_next != post_t);
+  const int a = miss ? (int)__builtin_ctzll(miss) : kBlock - 1;  // leading matches, uniform
+  const int32_t next = __builtin_amdgcn_readlane(post, 4 * a);
+  const int32_t kv_out = kvin + 1 + a;
+  if (lane == 0) {
     p.accept_len[b] = a;
-    p.next_token[b] = sh.post[a];
+    p.next_token[b] = next;
     p.kv_len_out[b] = kv_out;
     if (p.n_pages) p.n_pages[b] = (int32_t)(((int64_t)kv_out + p.page_size - 1) / p.page_size);
   }
-  __syncthreads();
-  if (p.commit_pos && tid < kBlock)
-    p.commit_pos[b * kBlock + tid] = (tid <= sh.accept) ? sh.kvin + tid : -1;
+  if (p.commit_pos && lane < kBlock) p.commit_pos[b * kBlock + lane] = (lane <= a) ? kvin + lane : -1;
 }
 
-// Sequence b's draft tokens: the argmax of each mask row (1..15) from its chunk
-// keys, written to block[b][1..15]; slot 0 gets staged[b] when staged is given.
-// Row 0's keys are never computed, so its lanes take no chunks (they still join
-// the shuffles of their own 16-lane group, which reads no other group).
+// Sequence b's draft tokens: the argmax of each mask row (1..15) from its chunk keys,
+// written to block[b][1..15]; slot 0 gets staged[b] when staged is given.  Row 0's keys
+// are never computed, so its lanes take no chunks (they still join the quad swaps of
+// their own row, which read no other row).
 __device__ __forceinline__ void draft_seq(const VerifyParams& p, int b) {
-  const int tid = threadIdx.x;
-  const int row = tid >> 4, sub = tid & 15;
+  const int lane = threadIdx.x;
+  const int row = lane >> 2, sub = lane & 3;
   const uint64_t best = row_best(p, b * kBlock + row, sub, row ? p.n_chunks : 0);
   if (sub == 0 && row) p.draft_block[b * kBlock + row] = key_index(best);
-  if (tid == 0 && p.staged) p.draft_block[b * kBlock] = p.staged[b];
+  if (lane == 0 && p.staged) p.draft_block[b * kBlock] = p.staged[b];
 }
 
 // Second kernel of the two-kernel form: one workgroup per sequence.  Running after
@@ -284,9 +281,8 @@ __device__ __forceinline__ void draft_seq(const VerifyParams& p, int b) {
 // device-wide fence.
 template <bool DRAFT>
 __global__ __launch_bounds__(kAcceptThreads) void verify_accept_kernel(VerifyParams p) {
-  __shared__ AcceptShared sh;
   if (DRAFT) draft_seq(p, blockIdx.x);
-  else accept_seq(p, blockIdx.x, sh);
+  else accept_seq(p, blockIdx.x);
 }
 
 // One-kernel form for batch >= 8 (every XCD holds whole sequences): workgroup i runs
@@ -300,8 +296,6 @@ __global__ __launch_bounds__(kAcceptThreads) void verify_accept_kernel(VerifyPar
 template <bool DRAFT>
 __global__ __launch_bounds__(kThreads) void verify_fused_kernel(VerifyParams p, int batch) {
   __shared__ uint32_t s_red[kThreads / kWave];
-  __shared__ uint32_t s_last;
-  __shared__ AcceptShared sh;
   const int per = kRowsPerSeq<DRAFT> * p.n_chunks;  // workgroups per sequence
   // A workgroup off the expected die would count its arrival in another L2, and the
   // sequence's accept step would never run: raise DEVERR_XCD instead of staying silent.
@@ -313,6 +307,10 @@ __global__ __launch_bounds__(kThreads) void verify_fused_kernel(VerifyParams p, 
   const int row_in = rem / p.n_chunks, chunk = rem - row_in * p.n_chunks;
   const int row = seq_row<DRAFT>(b, row_in);
   const uint64_t key = chunk_key(p, row, chunk, s_red);
+  // Waves 1..3 are done: leaving now frees their slots for the next workgroups while
+  // wave 0 hands the key over.
+  if (threadIdx.x >= kWave) return;
+  uint32_t last = 0;
   if (threadIdx.x == 0) {
     p.part[(int64_t)row * p.n_chunks + chunk] = key;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -320,18 +318,16 @@ __global__ __launch_bounds__(kThreads) void verify_fused_kernel(VerifyParams p, 
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     uint32_t* cnt = p.count + (int64_t)b * kVerifyCntStride;
     const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const uint32_t last = prev == (uint32_t)(per - 1) ? 1u : 0u;
+    last = prev == (uint32_t)(per - 1) ? 1u : 0u;
     if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    s_last = last;
   }
-  __syncthreads();
-  if (!__builtin_amdgcn_readfirstlane(s_last)) return;
+  if (!__builtin_amdgcn_readlane(last, 0)) return;
   // The loads below are served by the L2: the sequence's chunk keys are read once,
   // here, and its key block (16 rows x n_chunks x 8 bytes = 128 * n_chunks bytes
   // from a 256-byte aligned base) shares no cache line with another sequence's, so
   // no CU can hold an older copy of them in its L1 (which every launch starts empty).
   if (DRAFT) draft_seq(p, b);
-  else accept_seq(p, b, sh);
+  else accept_seq(p, b);
 }
 
 template <bool DRAFT>
