@@ -42,8 +42,8 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/common.h",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
-ATTN_TRAFFIC = {"sha256": "112430767ba115231691f6b08c39ecb632f4315210819fccfa5a01695b48799a",
-                "workload": "batched", "read": 276989196, "write": 8506218}
+ATTN_TRAFFIC = {"sha256": "9ee554d0129fcebedc8610fb10cc0e443509bec627b7428b5471e562bc7a8208",
+                "workload": "batched", "read": 274058757, "write": 8506415}
 
 
 def sources_sha256(paths):
