@@ -13,11 +13,15 @@
 // so each state element is replayed on its own: no S k product, no reduction.
 //
 // gfx950 mapping: HBM-bound (the fp32 state is read and written once; the tape is
-// small).  One workgroup per (sequence, head, 16 or 32 state rows): every thread
-// first issues the loads of all its float4 chunks of the state (streamed past the
-// caches, all in flight at once), then the accepted steps' keys (as fp32),
-// innovations and decays go to LDS while those loads are outstanding; the steps
-// are replayed on the chunks in registers and the chunks are streamed back.
+// small).  One workgroup per (sequence, head, 16 or 32 state rows).  Every load is
+// issued before the first wait, so the workgroup costs one memory round trip: first the
+// tape (the accepted steps' keys in 8-byte pieces, this workgroup's innovations, the
+// decays), then all float4 chunks of the state, streamed past the caches.  The tape goes
+// to LDS (as fp32) while the state is still in flight -- waiting for the tape loads does
+// not wait for the younger state loads -- and the steps are replayed on the chunks in
+// registers, which are streamed back.  All loads are unconditional (indices clamped into
+// their buffers; the extra values are never used), so the compiler's wait before the
+// first use of the tape counts exactly the younger state loads.
 #include <math.h>
 
 #include "common.h"
@@ -35,12 +39,13 @@ constexpr int kMaxDk = 256;
 // workgroups; with a full grid the larger share per workgroup is faster).
 template <int ROWS>
 __global__ __launch_bounds__(kReplayThreads) void gdn_replay_kernel(GdnReplayParams p) {
-  constexpr int kReplayRows = ROWS;
-  constexpr int kMaxChunksPerThread = kReplayRows * (kMaxDk / 4) / kReplayThreads;
+  constexpr int kMaxChunksPerThread = ROWS * (kMaxDk / 4) / kReplayThreads;
+  constexpr int kKeyPieces = kBlock * kMaxDk / 4 / kReplayThreads;  // 8-byte key pieces per thread
+  constexpr int kDeltas = kBlock * ROWS / kReplayThreads;            // innovations per thread
   __shared__ float s_k[kBlock][kMaxDk];
-  __shared__ float s_d[kBlock][kReplayRows];
+  __shared__ float s_d[kBlock][ROWS];
   __shared__ float s_alpha[kBlock];
-  const int parts = (p.dv + kReplayRows - 1) / kReplayRows;
+  const int parts = (p.dv + ROWS - 1) / ROWS;
   const int unit = blockIdx.x / parts, part = blockIdx.x - unit * parts;
   const int b = unit / p.n_heads, h = unit - b * p.n_heads;
   const int tid = threadIdx.x;
@@ -50,36 +55,65 @@ __global__ __launch_bounds__(kReplayThreads) void gdn_replay_kernel(GdnReplayPar
     a = a < 0 ? 0 : kBlock - 1;
   }
   const int n = a + 1;  // committed steps: the staged token and the accepted drafts
-  const int row0 = part * kReplayRows;
-  // The state loads go first (they do not depend on the tape), so their latency
-  // overlaps the tape's staging in LDS.
-  const int cpr = p.dk / 4;                       // float4 chunks per state row
-  const int rows = min(kReplayRows, p.dv - row0);
+  const int row0 = part * ROWS;
+  const int64_t step0 = (int64_t)b * kBlock * p.n_heads + h;  // (b, t = 0, h); step t adds t * n_heads
+
+  // The tape: keys, innovations of rows row0.., decays.
+  const int kq = p.dk / 4, nk = n * kq;  // 8-byte pieces per step (d_k % 4 == 0), in all
+  u32x2 kr[kKeyPieces];
+#pragma unroll
+  for (int u = 0; u < kKeyPieces; ++u) {
+    const int i = min(tid + u * kReplayThreads, nk - 1);
+    const int t = i / kq, j = (i - t * kq) * 4;
+    kr[u] = *reinterpret_cast<const u32x2*>(p.k_tape + (step0 + (int64_t)t * p.n_heads) * p.dk + j);
+  }
+  float dr[kDeltas];
+#pragma unroll
+  for (int u = 0; u < kDeltas; ++u) {
+    const int i = tid + u * kReplayThreads;
+    const int t = min(i / ROWS, n - 1), row = min(row0 + i % ROWS, p.dv - 1);
+    dr[u] = p.delta_tape[(step0 + (int64_t)t * p.n_heads) * p.dv + row];
+  }
+  const float gr = p.g_tape[step0 + (int64_t)min(tid, n - 1) * p.n_heads];
+
+  // The state: every float4 chunk of rows row0 .. row0 + ROWS - 1.
+  const int cpr = p.dk / 4;  // float4 chunks per state row
+  const int rows = min(ROWS, p.dv - row0);
   const int n_chunks = rows * cpr;
   const int64_t base = ((int64_t)unit * p.dv + row0) * p.dk;
-  f32x4 s[kMaxChunksPerThread];
+  f32x4 sv[kMaxChunksPerThread];
 #pragma unroll
   for (int u = 0; u < kMaxChunksPerThread; ++u) {
-    const int c = tid + u * kReplayThreads;
-    if (c < n_chunks) s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.state_in + base + (int64_t)c * 4));
+    const int c = min(tid + u * kReplayThreads, n_chunks - 1);
+    sv[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.state_in + base + (int64_t)c * 4));
   }
-  for (int i = tid; i < n * p.dk; i += kReplayThreads) {
-    const int t = i / p.dk, j = i - t * p.dk;
-    s_k[t][j] = bf16_to_f32(p.k_tape[(((int64_t)b * kBlock + t) * p.n_heads + h) * p.dk + j]);
+
+  // Stage the tape in LDS while the state loads are in flight.  The stores are as
+  // unconditional as the loads (a guarded store would let the compiler sink its load
+  // past the state loads): lanes past the end rewrite the last piece with the same value.
+#pragma unroll
+  for (int u = 0; u < kKeyPieces; ++u) {
+    const int i = min(tid + u * kReplayThreads, nk - 1);
+    const int t = i / kq, j = (i - t * kq) * 4;
+    *reinterpret_cast<f32x4*>(&s_k[t][j]) =
+        (f32x4){__uint_as_float(kr[u][0] << 16), __uint_as_float(kr[u][0] & 0xffff0000u),
+                __uint_as_float(kr[u][1] << 16), __uint_as_float(kr[u][1] & 0xffff0000u)};
   }
-  for (int i = tid; i < n * kReplayRows; i += kReplayThreads) {
-    const int t = i / kReplayRows, r = i - t * kReplayRows;
-    const int row = row0 + r;
-    s_d[t][r] = row < p.dv ? p.delta_tape[(((int64_t)b * kBlock + t) * p.n_heads + h) * p.dv + row] : 0.f;
+#pragma unroll
+  for (int u = 0; u < kDeltas; ++u) {
+    const int i = tid + u * kReplayThreads;
+    const int t = min(i / ROWS, n - 1), r = i % ROWS;
+    s_d[t][r] = row0 + r < p.dv ? dr[u] : 0.f;
   }
-  if (tid < n) s_alpha[tid] = expf(p.g_tape[((int64_t)b * kBlock + tid) * p.n_heads + h]);
-  __syncthreads();
+  s_alpha[min(tid, n - 1)] = expf(gr);
+  lds_barrier();  // LDS only: the state loads stay in flight
+
 #pragma unroll
   for (int u = 0; u < kMaxChunksPerThread; ++u) {
     const int c = tid + u * kReplayThreads;
     if (c >= n_chunks) break;
     const int r = c / cpr, j = (c - r * cpr) * 4;
-    f32x4 v = s[u];
+    f32x4 v = sv[u];
     for (int t = 0; t < n; ++t) {
       const float al = s_alpha[t], d = s_d[t][r];
       const f32x4 k = *reinterpret_cast<const f32x4*>(&s_k[t][j]);
