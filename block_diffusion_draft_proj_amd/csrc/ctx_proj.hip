@@ -288,10 +288,11 @@ __global__ __launch_bounds__((SkGeo<MT, RT>::WAVES * 64)) void gemm_skinny_kerne
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
   const int lrow = lane >> 3, pch = lane & 7;  // one wave-wide load = 8 rows x 128 bytes
-  // XCD-aware decode (workgroup i runs on XCD i % 8): every XCD works on as few K
-  // ranges as possible, so the activation slice of its range (16*MT rows x K/splits)
-  // stays in that XCD's L2 while all column tiles stream their weights past it.
-  // The planner makes `splits` a divisor or a multiple of 8.
+  // XCD-aware decode (workgroup i runs on XCD i % 8): with a multiple of 8 splits every
+  // XCD works on as few K ranges as possible, so the activation slice of its range
+  // (16*MT rows x K/splits) stays in that XCD's L2 while all column tiles stream their
+  // weights past it.  With 1, 2 or 4 splits the plain decode below does the same; with
+  // 3, 5, 6 or 7 (at most 8 splits, small activation slices) an XCD reads several.
   const int splits = (p.K + p.k_per_split - 1) / p.k_per_split;
   const int id = blockIdx.x;
   int z, col;
@@ -637,9 +638,14 @@ int skinny_splits(int N, int M, int K, int num_cu) {
     const int64_t rounds = ((int64_t)tiles * s + num_cu - 1) / num_cu;
     return rounds * (steps + kFixedSteps * s);
   };
-  // candidates: a divisor of 8 (1, 2, 4) or a multiple of 8, for the XCD-aware decode
+  // candidates: every count up to 8, then multiples of 8 (the XCD-aware decode needs
+  // a multiple of 8; below that the activations of a K range are at most a few MB and
+  // every XCD reads them whole).  Counts between the powers of two fill a round that
+  // they would leave short: the block q/k/v product (48 tiles) takes 5 splits, 240
+  // workgroups (26.0 -> 24.7 us per call), the long-context fc product (40 tiles) 6
+  // instead of 24 splits in four rounds (its projection 65.1 -> 58.9 us, interleaved A/B).
   int best = 1;
-  for (int s = 2; s <= cap; s = s < 8 ? 2 * s : s + 8)
+  for (int s = 2; s <= cap; s = s < 8 ? s + 1 : s + 8)
     if (cost(s) * best < cost(best) * s) best = s;  // cost(s) / s < cost(best) / best
   return best;
 }
