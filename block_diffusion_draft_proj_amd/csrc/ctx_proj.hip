@@ -280,7 +280,11 @@ struct SkGeo {
 // PACKED: activations come packed as [K/64][mp][64] steps (written by
 // fc_reduce_kernel for the K/V product); else they are read in place from the
 // segments a_seg[] ([M][lda] each, seg_k columns of K per segment).
-template <int MT, bool PACKED, int RT>
+// SWIGLU: one split, and each workgroup's 128 weight rows are 64 gate rows (B0 rows
+// j0 .. j0 + 63, waves 0 and 1) over the same 64 up rows (B1, waves 2 and 3), so the
+// epilogue has both results of its columns and writes bf16(silu(g) * u) instead of
+// partial sums.
+template <int MT, bool PACKED, int RT, bool SWIGLU = false>
 __global__ __launch_bounds__((SkGeo<MT, RT>::WAVES * 64)) void gemm_skinny_kernel(GemmParams p) {
   using SG = SkGeo<MT, RT>;
   __shared__ __attribute__((aligned(1024))) char lds[SG::NS * SG::STAGE];
@@ -336,7 +340,13 @@ __global__ __launch_bounds__((SkGeo<MT, RT>::WAVES * 64)) void gemm_skinny_kerne
       const int li = i * SG::WAVES + w;  // wave-uniform
       if (li < SG::W_TILE / 1024) {
         const int row = li * 8 + lrow;
-        const int n = min(n0 + row, p.N - 1);
+        int n;
+        if constexpr (SWIGLU) {
+          const int j = min(col * 64 + (row & 63), p.n_b0 - 1);
+          n = row < 64 ? j : p.n_b0 + j;
+        } else {
+          n = min(n0 + row, p.N - 1);
+        }
         const uint16_t* brow = n < p.n_b0 ? p.b0 + (int64_t)n * p.K : p.b1 + (int64_t)(n - p.n_b0) * p.K;
         lds_dma16_nt_m0(brow + k0 + ((pch ^ ((row >> 1) & 7)) << 3), stage + li * 1024);
       } else {
@@ -407,6 +417,38 @@ __global__ __launch_bounds__((SkGeo<MT, RT>::WAVES * 64)) void gemm_skinny_kerne
 
   // D layout: lane holds activation row 16*(MTW*wt + mt) + r and weight rows 4q .. 4q+3 of
   // the 16-row tile: 4 consecutive outputs of one row, one 16-byte store.
+  if constexpr (SWIGLU) {
+    static_assert(RT == 2 && SK_RW == 4, "gate rows in waves 0 and 1, the same up rows in waves 2 and 3");
+    // Wave wr + 2 holds the up results of wave wr's gate columns, in the same lanes: it
+    // hands them over through the ring, which every wave has finished reading.
+    __syncthreads();
+    f32x4* xch = reinterpret_cast<f32x4*>(lds) + ((wt * 2 + (wr & 1)) * RT * MTW) * 64 + lane;
+    if (wr >= 2) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt) xch[(rt * MTW + mt) * 64] = acc[rt][mt];
+    }
+    __syncthreads();
+    if (wr >= 2) return;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int j = col * 64 + wr * 32 + rt * 16 + 4 * q;
+      if (j >= p.n_b0) continue;
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
+        const int m = (wt * MTW + mt) * 16 + r;
+        if (m >= p.m_rows) continue;
+        const f32x4 g = acc[rt][mt], u = xch[(rt * MTW + mt) * 64];
+        float a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = g[e] / (1.f + expf(-g[e])) * u[e];
+        *reinterpret_cast<u32x2*>(p.act + (int64_t)(p.m_off + m) * p.n_b0 + j) =
+            (u32x2){pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+      }
+    }
+    return;
+  }
   float* out = p.out + (int64_t)z * p.M * p.N;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -734,6 +776,23 @@ void launch_skinny_rows(const GemmParams& c, int splits, hipStream_t stream) {
     case 4: launch_skinny<8, PACKED>(c, splits, stream); break;
     default: launch_skinny<16, PACKED>(c, splits, stream); break;
   }
+}
+
+hipError_t launch_gemm_swiglu(const GemmParams& p, hipStream_t stream) {
+  if (p.M > kSkinnyMaxRows || p.k_per_split < p.K || p.N != 2 * p.n_b0) return hipErrorInvalidValue;
+  GemmParams c = p;
+  c.m_off = 0;
+  c.m_rows = p.M;
+  const dim3 grid((p.n_b0 + 63) / 64), block(SkGeo<8, 2>::WAVES * 64);
+  switch ((c.m_rows + 31) / 32) {
+    case 0:
+    case 1: hipLaunchKernelGGL((gemm_skinny_kernel<2, false, 2, true>), grid, dim3(SkGeo<2, 2>::WAVES * 64), 0, stream, c); break;
+    case 2: hipLaunchKernelGGL((gemm_skinny_kernel<4, false, 2, true>), grid, dim3(SkGeo<4, 2>::WAVES * 64), 0, stream, c); break;
+    case 3: hipLaunchKernelGGL((gemm_skinny_kernel<6, false, 2, true>), grid, dim3(SkGeo<6, 2>::WAVES * 64), 0, stream, c); break;
+    case 4: hipLaunchKernelGGL((gemm_skinny_kernel<8, false, 2, true>), grid, block, 0, stream, c); break;
+    default: hipLaunchKernelGGL((gemm_skinny_kernel<16, false, 2, true>), grid, dim3(SkGeo<16, 2>::WAVES * 64), 0, stream, c); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStream_t stream) {

@@ -267,9 +267,17 @@ hipError_t launch_draft_layer_post(const LayerPostParams& p, const LayerPlan& pl
   g.K = p.hidden;
   g.k_per_split = pl.gu.kps;
   g.out = p.part_gu;
-  e = launch_gemm_nt(g, pl.gu.splits, pl.gu.small, stream);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(swiglu_kernel, dim3(blocks(M * p.inter / 4, 256)), dim3(256), 0, stream, p);
+  if (pl.gu.small && pl.gu.splits == 1) {
+    // One split: the product holds whole results, so it applies the SwiGLU itself
+    // (no fp32 partials of [M][2I], no separate kernel).
+    g.act = p.act;
+    e = launch_gemm_swiglu(g, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    e = launch_gemm_nt(g, pl.gu.splits, pl.gu.small, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(swiglu_kernel, dim3(blocks(M * p.inter / 4, 256)), dim3(256), 0, stream, p);
+  }
   g = GemmParams{};
   g.a_seg[0] = p.act;
   g.lda = p.inter;

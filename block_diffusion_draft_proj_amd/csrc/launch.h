@@ -107,6 +107,7 @@ struct GemmParams {
   const uint16_t* xp;                  // skinny path: A packed as [K/64][mp][64] (64-K steps)
   int mp;                              // rows of a packed step (M rounded up to 32)
   int m_off, m_rows;                   // skinny path: this launch's rows [m_off, m_off + m_rows) of M
+  uint16_t* act;                       // SwiGLU epilogue: bf16(silu(B0 row) * B1 row) as [M][n_b0]
 };
 struct PackParams {
   const uint16_t* a_seg[kMaxLayers];  // as GemmParams
@@ -126,6 +127,9 @@ struct ProjPlan {
 };
 ProjPlan plan_ctx_proj(int n_rows, int k_fc, int hidden, int kv_width, bool has_fc, int num_cu);
 hipError_t launch_gemm_nt(const GemmParams& p, int splits, bool small_m, hipStream_t stream);
+// One-split skinny product of B0 = gate and B1 = up rows (n_b0 each) with the SwiGLU of
+// the two results as its epilogue: act = bf16(silu(x w_gate^T) * (x w_up^T)).  M <= 256.
+hipError_t launch_gemm_swiglu(const GemmParams& p, hipStream_t stream);
 
 struct FcReduceParams {
   const float* part;   // [splits][M][N]
