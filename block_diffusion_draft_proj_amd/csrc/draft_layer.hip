@@ -13,7 +13,8 @@
 // weights, 335 MB at a Qwen3-8B-shaped layer, dominate the bytes), so they run on
 // the split-K skinny MFMA GEMM of the projection; the small kernels here fold the
 // split partial sums into the next step: residual add + RMSNorm in one row-wise
-// pass, the SwiGLU product, the last residual add.  The RMSNorm factor is
+// pass, the SwiGLU product (inside the gate/up product itself when that takes one K
+// split), the last residual add.  The RMSNorm factor is
 // computed in fp64 (a row of D bf16 squares, then one rsqrt) and each output is
 // rounded once from its fp64 value, so it agrees with an exact evaluation except
 // within fp64 error of a bf16 rounding midpoint.
