@@ -176,6 +176,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmParams p) {
   // the next A tile to issue: stage 2, in layer a_seg at column a_col
   int a_seg = (kbeg + 2 * BK) / p.seg_k, a_col = kbeg + 2 * BK - a_seg * p.seg_k;
   uint64_t a_next = seg_base(a_seg) + 2 * (uint64_t)a_col;
+  // The issuing wave of each SIMD carries the loads besides the same MFMAs as its partner
+  // and reaches the barrier last; with the higher priority the SIMD favours it when both
+  // are ready (prefill chunk of 2048 / 8192 / 32768 rows 0.7-1.5 % faster, interleaved
+  // A/B; the reverse order is 7-10 % slower).
+  if (issuer) __builtin_amdgcn_s_setprio(1);
   for (int it = 0; it < n_st; ++it) {
     // the tiles of stage it landed for this wave: at most tile 2 it + 2 still flies
     if (!issuer) {
