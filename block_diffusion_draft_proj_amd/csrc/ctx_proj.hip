@@ -376,7 +376,7 @@ __global__ __launch_bounds__((SkGeo<MT, RT>::WAVES * 64)) void gemm_skinny_kerne
   };
 
   constexpr int MTW = SG::MTW;
-  const int wr = w % SK_RW, wt = w / SK_RW;  // weight rows 32wr.., activation tiles MTW*wt..
+  const int wr = w % SK_RW, wt = w / SK_RW;  // weight rows 16*RT*wr.., activation tiles MTW*wt..
   f32x4 acc[RT][MTW];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
