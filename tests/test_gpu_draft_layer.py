@@ -96,12 +96,15 @@ def test_draft_layer_post(name):
 
 
 def test_draft_layer_post_sizes_and_workspace_reuse():
-    # Three batch sizes on one buffer sized for the largest (the workspace keeps no state).
+    # Four batch sizes on one buffer sized for the largest (the workspace keeps no state).
+    # 192, 80, 32 and 48 rows: 16, 6, 2 and 4 activation tiles, the gate/up product with
+    # its SwiGLU epilogue (one K split) at 192, 80 and 48 rows and with separate partials
+    # (two splits) at 32.
     cfg = synth.CONFIGS["tiny"]
-    big = dataclasses.replace(cfg, batch=5)
-    dims = dfl.make_dims(5, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, hidden=cfg.hidden)
+    big = dataclasses.replace(cfg, batch=12)
+    dims = dfl.make_dims(12, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, hidden=cfg.hidden)
     ws = dfl.workspace(dfl.dflash_draft_layer_post_workspace_size(dims, cfg.inter), DEV)
-    for B in (5, 2, 3):
+    for B in (12, 5, 2, 3):
         c = dataclasses.replace(big, batch=B)
         li = synth.draft_layer_inputs(c, seed=900 + B)
         d = dfl.make_dims(B, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, hidden=cfg.hidden)
