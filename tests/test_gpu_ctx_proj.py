@@ -134,6 +134,18 @@ def _check(cfg, n_rows, row_seq, row_pos, capacity, table=None, num_pages=0, wit
         assert np.all(np.abs(c - ref["C"]) <= 0.5 * ulp_bf16(ref["C"]) + 1e-4 * rms_c)
 
 
+def test_ctx_proj_tiny_rows_on_64_row_weight_tiles():
+    # 200 rows of the tiny shape: both products run on 16 activation tiles (MT = 16) with
+    # 64-row weight tiles (their grids of 4 and 2 workgroups fill far less than half the
+    # CUs), the fc product reading the layers in place, the K/V product the packed C.
+    cfg = synth.CONFIGS["tiny"]
+    n = 200
+    seq = np.zeros(n, np.int32)
+    pos = np.arange(n, dtype=np.int32) + 100
+    pos[::5] = -1
+    _check(cfg, n, seq, pos, capacity=320, label="tiny 200 rows")
+
+
 def test_ctx_proj_tiny_prefill_dense_and_paged():
     cfg = synth.CONFIGS["tiny"]
     n = 64
