@@ -43,7 +43,7 @@ ATTN_TRAFFIC_SOURCES = ("block_diffusion_draft_proj_amd/csrc/block_attn.hip",
                         "block_diffusion_draft_proj_amd/csrc/launch.h",
                         "block_diffusion_draft_proj_amd/csrc/api.cpp")
 ATTN_TRAFFIC = {"sha256": "23037427eeb941e41dd5c6434b069e214b9cb0d73d26cf1da1a0b3295ddc1d26",
-                "workload": "batched", "read": 274138137, "write": 8506081}
+                "workload": "batched", "read": 273973818, "write": 8505784}
 
 
 def sources_sha256(paths):
